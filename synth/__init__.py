@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs shared by the GPU path's tests/bench and the oracle.
+
+This module holds no attention arithmetic: it only draws random tensors,
+request lengths and dense 0/1 masks from a seeded CPU generator.  Both the
+oracle and the GPU library read what it returns; neither is imported here.
+
+Recipe (one ``torch.Generator('cpu')`` per workload, seeded with the
+workload's seed; draws happen in this order): request lengths (ragged decode
+only), then Q, K, V as ``torch.randn(float32)`` rounded to the storage dtype
+with round-to-nearest-even, then the random blocks of the sparse mask.
+
+Workload shapes follow the pages' workloads:
+  * grouped-query attention heads shaped like Llama-3-8B (32 query / 8 KV
+    heads, head_dim 128) and Qwen3-32B (64 / 8, head_dim 128), the models of
+    the Cleave article's layer benchmarks (tip.co.jp, "評価結果");
+  * ragged serving-trace-like decode batches with log-uniform KV lengths,
+    standing in for the production serving traces (9 operators, 303 shapes)
+    that are not available;
+  * the Longformer/Bigbird-style masks at sequence length 4096 of the STOF
+    evaluation (gist.science STOF explainer, "実験結果").
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = [
+    "Workload", "WORKLOADS", "workload", "gen", "randn", "loguniform_lengths", "indptr",
+    "decode_inputs", "prefill_inputs", "sparse_mask", "window_mask",
+]
+
+
+def gen(seed: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return g
+
+
+def randn(shape, dtype, g: torch.Generator) -> torch.Tensor:
+    """N(0,1) in float32, then rounded (nearest-even) to ``dtype``."""
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def loguniform_lengths(B: int, lo: int, hi: int, g: torch.Generator) -> list[int]:
+    """n_b = clamp(floor(exp(ln lo + u (ln hi - ln lo))), lo, hi), u ~ U[0,1) in fp64."""
+    u = torch.rand((B,), generator=g, dtype=torch.float64)
+    a, b = math.log(lo), math.log(hi)
+    n = torch.floor(torch.exp(a + u * (b - a))).to(torch.int64).clamp(lo, hi)
+    return [int(x) for x in n]
+
+
+def indptr(lengths) -> torch.Tensor:
+    """Exclusive prefix sum as int32 [B+1]."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+def decode_inputs(B, Hq, Hkv, D, lengths, dtype, seed, g=None):
+    """One query token per request.  q [B,Hq,D]; k, v [sum(lengths),Hkv,D]."""
+    g = g if g is not None else gen(seed)
+    total = int(sum(lengths))
+    q = randn((B, Hq, D), dtype, g)
+    k = randn((total, Hkv, D), dtype, g)
+    v = randn((total, Hkv, D), dtype, g)
+    return q, k, v, indptr(lengths)
+
+
+def prefill_inputs(B, L_q, L_kv, Hq, Hkv, D, dtype, seed, g=None):
+    """Packed ragged layout with equal lengths.  q [B*L_q,Hq,D]; k, v [B*L_kv,Hkv,D]."""
+    g = g if g is not None else gen(seed)
+    q = randn((B * L_q, Hq, D), dtype, g)
+    k = randn((B * L_kv, Hkv, D), dtype, g)
+    v = randn((B * L_kv, Hkv, D), dtype, g)
+    return q, k, v, indptr([L_q] * B), indptr([L_kv] * B)
+
+
+def window_mask(L: int, window: int) -> torch.Tensor:
+    """uint8 [L, L]: 1 where 0 <= i - j < window (causal sliding window)."""
+    i = torch.arange(L).view(-1, 1)
+    j = torch.arange(L).view(1, -1)
+    d = i - j
+    return ((d >= 0) & (d < window)).to(torch.uint8)
+
+
+def sparse_mask(L: int, g: torch.Generator, window: int = 256, block: int = 64,
+                globals_per_block: int = 2, symmetric_globals: bool = True,
+                random_blocks: int = 6) -> torch.Tensor:
+    """Longformer/Bigbird-style dense 0/1 mask, uint8 [L, L], 1 = attend.
+
+    Union of: the causal sliding window of ``window`` keys (self included);
+    ``globals_per_block`` global tokens at the start of every ``block``-token
+    block (columns always; rows too when ``symmetric_globals``); and, per
+    query block row, ``random_blocks`` distinct key blocks drawn with
+    ``randperm`` from ``g`` in block-row order.
+    """
+    m = window_mask(L, window).bool()
+    nb = L // block
+    glob = torch.zeros(L, dtype=torch.bool)
+    for b in range(nb):
+        glob[b * block: b * block + globals_per_block] = True
+    m |= glob.view(1, -1)
+    if symmetric_globals:
+        m |= glob.view(-1, 1)
+    for qb in range(nb):
+        for kb in torch.randperm(nb, generator=g)[:random_blocks].tolist():
+            m[qb * block:(qb + 1) * block, kb * block:(kb + 1) * block] = True
+    return m.to(torch.uint8)
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str            # "decode", "prefill", "bsr"
+    seed: int
+    dtype: torch.dtype
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    L: int = 0           # prefill / bsr sequence length, or uniform decode KV length
+    ragged: tuple = ()   # (lo, hi) log-uniform decode lengths
+    causal: bool = False
+    splits: tuple = ()   # forced split counts to check (decode)
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def make(self):
+        """Draw this workload's inputs (deterministic for its seed)."""
+        g = gen(self.seed)
+        if self.kind == "decode":
+            lengths = loguniform_lengths(self.B, *self.ragged, g) if self.ragged else [self.L] * self.B
+            q, k, v, kv = decode_inputs(self.B, self.Hq, self.Hkv, self.D, lengths, self.dtype,
+                                        self.seed, g)
+            return dict(q=q, k=k, v=v, kv_indptr=kv, lengths=lengths)
+        if self.kind == "prefill":
+            q, k, v, qo, kv = prefill_inputs(self.B, self.L, self.L, self.Hq, self.Hkv, self.D,
+                                             self.dtype, self.seed, g)
+            return dict(q=q, k=k, v=v, qo_indptr=qo, kv_indptr=kv)
+        if self.kind == "bsr":
+            q = randn((self.B, self.L, self.Hq, self.D), self.dtype, g)
+            k = randn((self.B, self.L, self.Hkv, self.D), self.dtype, g)
+            v = randn((self.B, self.L, self.Hkv, self.D), self.dtype, g)
+            mask = sparse_mask(self.L, g, **self.extra)
+            return dict(q=q, k=k, v=v, mask=mask)
+        raise ValueError(self.kind)
+
+
+WORKLOADS = {
+    "tiny_decode_fp32": Workload("tiny_decode_fp32", "decode", 1, torch.float32, B=1, Hq=4,
+                                 Hkv=1, D=64, L=256, splits=(1, 2, 4)),
+    "llama3_8b_decode_bf16": Workload("llama3_8b_decode_bf16", "decode", 2, torch.bfloat16,
+                                      B=16, Hq=32, Hkv=8, D=128, L=4096),
+    "ragged_decode_bf16": Workload("ragged_decode_bf16", "decode", 3, torch.bfloat16, B=64,
+                                   Hq=64, Hkv=8, D=128, ragged=(128, 32768)),
+    "causal_prefill_bf16": Workload("causal_prefill_bf16", "prefill", 4, torch.bfloat16, B=2,
+                                    Hq=32, Hkv=8, D=128, L=4096, causal=True),
+    "bsr_prefill_fp16": Workload("bsr_prefill_fp16", "bsr", 5, torch.float16, B=1, Hq=16,
+                                 Hkv=16, D=64, L=4096),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
