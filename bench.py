@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention hot path on one MI355X.
+
+Headline: split-KV GQA decode (partial kernel + LSE merge) on the
+Llama-3-8B-shaped workload -- 16 requests, 32 query / 8 KV heads, head_dim
+128, 4096 keys each, bf16 in / fp32 accumulate -- reported as whole-step
+HBM throughput in GB/s of algorithmic bytes (K + V + Q read, O + LSE
+written, indptr read), with inputs resident in HBM before timing starts.
+Three copies of K/V are rotated across steps so that consecutive steps do
+not hit the 256 MB Infinity Cache (one copy of K + V is 268 MB).
+
+Also measured in the same run (reported under "also"): causal prefill
+(B 2, L 4096, 32/8 heads, D 128, bf16) in TFLOP/s of the lower triangle,
+ragged serving-like decode (64 requests, 64/8 heads, lengths log-uniform in
+[128, 32768]) in GB/s, and block-sparse prefill (B 1, L 4096, 16 heads,
+D 64, fp16) in TFLOP/s at outer-tile granularity.
+
+Prints one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+METRIC = "split-KV GQA decode HBM GB/s (% peak); causal prefill TFLOP/s (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--splits", type=int, default=0, help="force the decode split count")
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "copy"], default=None,
+                   help="time one workload only (for profiler runs)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return p.parse_args()
+
+
+class Timer:
+    """HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def run(self, fn, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev[i][0].record(self.stream)
+            fn(warmup + i)
+            ev[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = [a.elapsed_time(b) for a, b in ev]
+        return ms, wall
+
+
+def median(x):
+    s = sorted(x)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def decode_bytes(B, Hq, Hkv, D, total_kv, elem):
+    kv = 2 * total_kv * Hkv * D * elem
+    q = B * Hq * D * elem
+    o = B * Hq * D * elem
+    lse = B * Hq * 4
+    indptr = (B + 1) * 4
+    return kv, q, o, lse, indptr
+
+
+def bench_decode(torch, ra, synth, wname, args, timer, rotate=3):
+    w = synth.workload(wname)
+    inp = w.make("cuda:0")
+    dev = torch.device("cuda:0")
+    lengths = inp["lengths"]
+    max_len = max(lengths)
+    total = sum(lengths)
+    q = inp["q"].to(dev)
+    kvp = inp["kv_indptr"].to(dev)
+    sets = [(inp["k"].to(dev), inp["v"].to(dev))]
+    for _ in range(rotate - 1):
+        sets.append((sets[0][0].clone(), sets[0][1].clone()))
+    s = args.splits or ra.attn_decode_choose_splits(w.B, w.Hq, w.Hkv, w.D, total, max_len)
+    ws = torch.empty(ra.attn_decode_workspace_bytes(w.B, w.Hq, w.D, s), dtype=torch.uint8,
+                     device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        k, v = sets[i % rotate]
+        ra.attn_decode_splitkv(q, k, v, kvp, max_len, num_splits=s, o=o, lse=lse, workspace=ws,
+                               stream=stream)
+
+    ms, wall = timer.run(step, args.steps, args.warmup)
+    # the merge kernel alone, on the same workspace partials, to split the step time
+    op, mp, lp = ra.decode_workspace_views(ws, w.B, w.Hq, w.D, s)
+    o2 = torch.empty_like(q).view(w.B * w.Hq, w.D)
+    l2 = torch.empty((w.B * w.Hq,), dtype=torch.float32, device=dev)
+    ms_merge, _ = timer.run(lambda i: ra.attn_merge_lse(op, mp, lp, o_dtype=q.dtype, o=o2, lse=l2,
+                                                        stream=stream), args.steps, 2)
+    elem = q.element_size()
+    kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, total, elem)
+    step_ms = median(ms)
+    merge_ms = median(ms_merge)
+    partial_ms = max(step_ms - merge_ms, 1e-6)
+    step_bytes = kvb + qb + ob + lb + ib
+    partial_bytes = kvb + qb + ib  # what the partial kernel must read
+    return dict(workload=wname, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, total_kv=total,
+                max_kv_len=max_len, splits=s, chunk=-(-max_len // s), dtype=str(q.dtype),
+                step_ms=step_ms, step_ms_p10=sorted(ms)[len(ms) // 10],
+                step_ms_p90=sorted(ms)[(9 * len(ms)) // 10], merge_ms=merge_ms,
+                partial_ms=partial_ms, step_bytes=step_bytes, partial_bytes=partial_bytes,
+                gbs=step_bytes / step_ms / 1e6, partial_gbs=partial_bytes / partial_ms / 1e6,
+                wall_s=wall, kv_copies_rotated=rotate)
+
+
+def causal_flops(B, Hq, L, D):
+    # QK^T and PV over the lower triangle including the diagonal: 2 * 2 * D per pair
+    return 4 * D * (L * (L + 1) // 2) * B * Hq
+
+
+def bench_prefill(torch, ra, synth, args, timer):
+    w = synth.workload("causal_prefill_bf16")
+    inp = w.make("cuda:0")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qo, kv = inp["qo_indptr"].to(dev), inp["kv_indptr"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], w.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ms, wall = timer.run(lambda i: ra.attn_prefill(q, k, v, qo, kv, w.L, w.L, causal=True, o=o,
+                                                   lse=lse, stream=stream), args.steps, args.warmup)
+    flops = causal_flops(w.B, w.Hq, w.L, w.D)
+    t = median(ms)
+    return dict(workload=w.name, B=w.B, L=w.L, Hq=w.Hq, Hkv=w.Hkv, D=w.D, dtype="bf16",
+                ms=t, flops=flops, tflops=flops / t / 1e9,
+                frac=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
+
+
+def bench_bsr(torch, ra, synth, args, timer):
+    w = synth.workload("bsr_prefill_fp16")
+    inp = w.make("cuda:0")
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    m = ra.attn_bsr_encode_host(inp["mask"])
+    enc_s = time.perf_counter() - t0
+    md = m.to(dev)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.L, w.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ms, _ = timer.run(lambda i: ra.attn_prefill_bsr(q, k, v, md, o=o, lse=lse, stream=stream),
+                      args.steps, args.warmup)
+    n_ot = m.nnz_full + m.nnz_part
+    flops_ot = 4 * w.D * 64 * 64 * n_ot * w.Hq * w.B
+    valid = int(inp["mask"].to(torch.int64).sum())
+    flops_valid = 4 * w.D * valid * w.Hq * w.B
+    t = median(ms)
+    return dict(workload=w.name, B=w.B, L=w.L, H=w.Hq, D=w.D, dtype="fp16", ms=t,
+                nnz_full=m.nnz_full, nnz_part=m.nnz_part,
+                density=valid / (w.L * w.L), flops_ot=flops_ot,
+                tflops_ot=flops_ot / t / 1e9, tflops_valid=flops_valid / t / 1e9,
+                frac_ot=flops_ot / t / 1e9 / MFMA_BF16_PEAK_TFS, host_encode_s=enc_s)
+
+
+def bench_copy(torch, args, timer):
+    """A plain device copy of known size: the calibration of the HBM byte counters."""
+    n = 1 << 30
+    dev = torch.device("cuda:0")
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    ms, _ = timer.run(lambda i: b.copy_(a), args.steps, args.warmup)
+    return dict(bytes_read=n, bytes_written=n, ms=median(ms), gbs=2 * n / median(ms) / 1e6)
+
+
+def cpu_baseline(torch, synth, budget_s):
+    """The fp64 oracle on a bounded sample of the headline decode workload."""
+    import oracle
+    w = synth.workload("llama3_8b_decode_bf16")
+    inp = w.make("cuda:0")
+    threads = len(os.sched_getaffinity(0))
+    threads = min(threads, 16)
+    B, Hq = w.B, w.Hq
+    qo = list(range(B + 1))
+    # sample: whole KV groups (all G query heads of a KV head) of consecutive requests
+    rows_all = [(b, h) for b in range(B) for h in range(Hq)]
+    n = 8
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        sel = rows_all[done: done + n] if done + n <= len(rows_all) else rows_all[:n]
+        oracle.attention(inp["q"], inp["k"], inp["v"], qo, inp["kv_indptr"], w.scale,
+                         rows=torch.tensor(sel), nthreads=threads)
+        done += len(sel)
+        el = time.perf_counter() - t0
+        if el >= budget_s or done >= 4 * len(rows_all):
+            break
+        if el < budget_s / 8:
+            n = min(n * 2, len(rows_all))
+    elem = 2
+    kvb, qb, ob, lb, ib = decode_bytes(B, Hq, w.Hkv, w.D, B * w.L, elem)
+    step_bytes = kvb + qb + ob + lb + ib
+    frac = done / len(rows_all)
+    return dict(value=step_bytes * frac / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{done} of the {len(rows_all)} (request, query head) rows of the decode "
+                       f"workload ({frac:.2f} steps) in {el:.1f} s, fp64 two-pass, OpenMP "
+                       f"{threads} threads; GB/s = the same algorithmic bytes per row as the GPU")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has "
+              "no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import reduction_attention_amd as ra
+    import synth
+    ra._lib.load()
+    stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
+    log(f"device: {torch.cuda.get_device_name(0)}, CUs: {ra.attn_device_cu_count()}")
+
+    if args.only:
+        fn = {"decode": lambda: bench_decode(torch, ra, synth, "llama3_8b_decode_bf16", args, timer),
+              "ragged": lambda: bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, 1),
+              "prefill": lambda: bench_prefill(torch, ra, synth, args, timer),
+              "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
+              "copy": lambda: bench_copy(torch, args, timer)}[args.only]
+        r = fn()
+        print(json.dumps({"only": args.only, **r}))
+        return
+
+    d = bench_decode(torch, ra, synth, "llama3_8b_decode_bf16", args, timer)
+    log(f"decode: {d['step_ms']*1e3:.1f} us/step, {d['gbs']:.0f} GB/s (partial kernel "
+        f"{d['partial_ms']*1e3:.1f} us, merge {d['merge_ms']*1e3:.1f} us), s={d['splits']}")
+    traffic = None
+    try:
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("kernel_source_hash") == source_hash():
+            traffic = tj.get("decode_partial_bytes")
+    except (OSError, ValueError):
+        pass
+    roofline = dict(bound="hbm", achieved=round(d["partial_gbs"], 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(d["partial_gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    kernel="decode_partial_mfma<BF16,128,4>",
+                    algorithmic_bytes=d["partial_bytes"], avg_launch_us=round(d["partial_ms"] * 1e3, 2))
+    out = {
+        "metric": METRIC,
+        "value": round(d["gbs"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": d["workload"], "batch": d["B"], "q_heads": d["Hq"],
+                   "kv_heads": d["Hkv"], "head_dim": d["D"], "kv_len": d["max_kv_len"],
+                   "splits": d["splits"], "chunk": d["chunk"], "parallelism": "single-gpu",
+                   "kv_copies_rotated": d["kv_copies_rotated"]},
+        "roofline": roofline,
+        "frac_of_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
+    }
+    if not args.no_also:
+        also = {}
+        p = bench_prefill(torch, ra, synth, args, timer)
+        log(f"prefill: {p['ms']*1e3:.1f} us, {p['tflops']:.1f} TFLOP/s ({100*p['frac']:.1f}% of peak)")
+        also["causal_prefill"] = dict(workload=p["workload"], ms=round(p["ms"], 4),
+                                      tflops=round(p["tflops"], 1), frac=round(p["frac"], 4),
+                                      roofline=dict(bound="mfma", achieved=round(p["tflops"], 1),
+                                                    peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
+                                                    frac=round(p["frac"], 4),
+                                                    algorithmic_flops=p["flops"]))
+        r = bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, rotate=1)
+        log(f"ragged decode: {r['step_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, s={r['splits']}")
+        also["ragged_decode"] = dict(workload=r["workload"], ms=round(r["step_ms"], 4),
+                                     gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                     total_kv=r["total_kv"], splits=r["splits"],
+                                     note="one K/V copy (1.5 GB) exceeds the 256 MB cache")
+        b = bench_bsr(torch, ra, synth, args, timer)
+        log(f"bsr: {b['ms']*1e3:.1f} us, {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
+        also["bsr_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}
+        out["also"] = also
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(torch, synth, args.cpu_seconds)
+        log(f"cpu baseline: {out['cpu_baseline']['value']:.3f} GB/s on "
+            f"{out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out))
+
+
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device.hpp"):
+        with open(os.path.join(ROOT, "reduction_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,229 @@
+/*
+ * attn.h -- C ABI of the fused multi-reduction attention library for AMD
+ * MI355X (gfx950).  Library file: reduction_attention_amd/libattn.so.
+ *
+ * The operation is scaled dot-product attention with its multiple
+ * reductions fused into one pass: S = scale * Q K^T, the row max, the row
+ * sum of exp(S - max), and P V, computed tile by tile with an online
+ * softmax so that the score matrix is never stored.  Sources (web pages):
+ *   [CA] tip.co.jp article on the Cleave ML compiler (2026-10-10), sections
+ *        "Split演算子によるSplit-Kの対応" (Split operator with a split count s
+ *        over a reduction dimension) and "複数リダクションのスケジューリング"
+ *        (iterative tiling of the reduction dimension; horizontal fusion of
+ *        reductions that share a producer; dynamic batch and sequence
+ *        dimensions kept as runtime loop bounds).
+ *   [AB] arXiv abstract "Cleave: Scaling Tensor Program Optimization via
+ *        Decoupled Algebraic Search and Operator Scheduling" (FlashAttention
+ *        and FlashDecoding as the hand-written kernels the method targets;
+ *        the Split operator; iterative tiling and horizontal fusion).
+ *   [ST] gist.science explainer of "Accelerating Sparse Transformer
+ *        Inference on GPU" (STOF), 技術概要, "1. 統合 MHA モジュール":
+ *        two-level BSR + bitmap mask storage (full / part outer tiles kept
+ *        through pointer arrays, one uint64 bitmap per 8x8 inner tile) and
+ *        the block-wise kernel that stages Q/K/V sub-blocks on chip.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are caller-owned device buffers, densely packed, 16-byte
+ *     aligned.  The library never allocates or frees device memory, keeps
+ *     no pointer after returning, and never synchronises the stream except
+ *     in the attn_debug_* exports.
+ *   - All device work is enqueued, in order, on `hip_stream` (a
+ *     hipStream_t; NULL = the default stream).  Calls return before the
+ *     work finishes.
+ *   - Every argument is validated on the host before any HIP call; on an
+ *     error status nothing has been enqueued and no output is written.  A
+ *     launch failure returns ATTN_EHIP; attn_last_error() gives details.
+ *   - GQA: query head h reads KV head floor(h / G), G = Hq / Hkv.
+ *   - LSE outputs are natural-log log-sum-exp of the scaled scores; a query
+ *     with no valid key gets O = 0 and LSE = -inf.
+ *   - Offsets are computed in 64-bit arithmetic.
+ *   - The host cannot read device-resident indptr arrays without a
+ *     synchronisation, so it trusts them: they must be non-decreasing, start
+ *     at 0 and agree with the length hints passed alongside them.
+ */
+#ifndef REDUCTION_ATTENTION_AMD_ATTN_H
+#define REDUCTION_ATTENTION_AMD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int attn_status_t;
+enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* null pointer, bad size, inconsistent arguments */
+  ATTN_EUNSUPPORTED = 2,  /* valid request outside what is built (dtype, D, G) */
+  ATTN_EWORKSPACE = 3,    /* workspace missing or too small */
+  ATTN_EHIP = 4           /* the HIP runtime reported an error */
+};
+
+/* Element types of Q/K/V/O. */
+enum { ATTN_F32 = 0, ATTN_BF16 = 1, ATTN_F16 = 2 };
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(attn_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Number of compute units of the current device (cached on first use);
+ * returns 256 when no device can be queried. */
+int attn_device_cu_count(void);
+
+/* ---- split-KV grouped-query decode ------------------------------------- */
+
+/* Workspace bytes attn_decode_splitkv needs for `num_splits` splits:
+ * num_splits * B * Hq * (D + 2) * 4 (fp32 partial outputs, maxima, sums),
+ * rounded up to 256 bytes.  Returns 0 for invalid arguments. */
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
+
+/* The split count s the library picks when num_splits = 0: the largest chunk
+ * c (a power of two, at least 256 keys) that still yields about four
+ * workgroups per compute unit, then s = ceil(max_kv_len / c), clamped to
+ * [1, 256].  [CA] leaves the concrete s to the scheduler; this is that
+ * scheduler's rule. */
+int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
+                              int max_kv_len);
+
+/*
+ * Split-KV decode: one query token per request attends to the request's
+ * packed keys, with the key (reduction) dimension cut by the Split operator
+ * into s chunks [CA "Split演算子によるSplit-Kの対応"; AB], each reduced by one
+ * workgroup with an online softmax over key tiles [CA "複数リダクションの
+ * スケジューリング"], then merged by log-sum-exp weights (attn_merge_lse).
+ *
+ * q         [B, Hq, D]            element type `dtype`
+ * k, v      [total_kv, Hkv, D]    request b owns rows kv_indptr[b] .. kv_indptr[b+1]-1
+ * kv_indptr [B + 1] int32, device
+ * o         [B, Hq, D]            element type `dtype`
+ * lse       [B, Hq] fp32, or NULL
+ * max_kv_len  the largest n_b = kv_indptr[b+1] - kv_indptr[b] (>= 1);
+ * total_kv    kv_indptr[B].
+ * num_splits  s in [1, 256], or 0 to use attn_decode_choose_splits.
+ *   Chunk length c = ceil(max_kv_len / s); request b uses ceil(n_b / c)
+ *   chunks, chunk i covering keys [i*c, min((i+1)*c, n_b)) of the request.
+ *   A request with n_b = 0 yields O = 0, LSE = -inf.
+ * workspace   device memory of at least attn_decode_workspace_bytes(B, Hq, D, s)
+ *   bytes; its contents on entry do not matter.  Layout: o_part [s, B*Hq, D],
+ *   then m_part [s, B*Hq], then l_part [s, B*Hq], all fp32.
+ * Supported: dtype ATTN_F32 (VALU path) or ATTN_BF16 / ATTN_F16 (MFMA
+ * path); D in {64, 128}; 1 <= G <= 16.
+ */
+attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
+                                  const int32_t* kv_indptr, void* o, float* lse, int B,
+                                  int Hq, int Hkv, int D, int max_kv_len, long long total_kv,
+                                  float scale, int num_splits, int dtype, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Merge of Split partials [CA "Split演算子によるSplit-Kの対応"]: for each row r,
+ *   M = max_i m_i over partials with l_i > 0;  w_i = l_i exp(m_i - M);
+ *   O = sum_i w_i o_i / sum_i w_i;  LSE = M + ln sum_i w_i.
+ * Partials with l_i <= 0 are skipped without reading o_i (an unused split
+ * carries m = -inf, l = 0).  A row with no usable partial gets O = 0 and
+ * LSE = -inf.
+ * o_part [num_splits, rows, D] fp32 (each o_i already normalised by its l_i);
+ * m_part, l_part [num_splits, rows] fp32, natural-log units;
+ * o [rows, D] of type o_dtype (ATTN_F32, ATTN_BF16 or ATTN_F16);
+ * lse [rows] fp32 or NULL.  1 <= num_splits <= 256; D in {64, 128}.
+ */
+attn_status_t attn_merge_lse(const float* o_part, const float* m_part, const float* l_part,
+                             int num_splits, int rows, int D, void* o, int o_dtype, float* lse,
+                             void* hip_stream);
+
+/* ---- prefill ----------------------------------------------------------- */
+
+/*
+ * Fused prefill attention over a ragged batch, MFMA path: query tiles stay
+ * on chip while key/value tiles stream through LDS (iterative tiling of the
+ * key dimension), and the row max and row sum are updated in the same loop
+ * over the same score tile (horizontal fusion) [CA "複数リダクションの
+ * スケジューリング"; AB].
+ *
+ * q, o  [total_q, Hq, D];  k, v  [total_kv, Hkv, D]  (element type dtype)
+ * qo_indptr, kv_indptr [B + 1] int32, device: request b owns query rows
+ *   qo_indptr[b] .. qo_indptr[b+1]-1 and key rows kv_indptr[b] .. kv_indptr[b+1]-1.
+ * lse [total_q, Hq] fp32, or NULL.
+ * max_q_len, max_kv_len: the largest per-request lengths (bounds of the grid).
+ * causal: 0 = every key of the request; 1 = key j is valid for query i iff
+ *   j <= i + n_kv - n_q (bottom-right aligned; plain j <= i when n_q = n_kv).
+ * Supported: dtype ATTN_BF16 or ATTN_F16; D in {64, 128}; any G >= 1.
+ */
+attn_status_t attn_prefill(const void* q, const void* k, const void* v,
+                           const int32_t* qo_indptr, const int32_t* kv_indptr, void* o,
+                           float* lse, int B, int Hq, int Hkv, int D, int max_q_len,
+                           int max_kv_len, float scale, int causal, int dtype,
+                           void* hip_stream);
+
+/* ---- block-sparse prefill (BSR outer tiles + 8x8 bitmaps) -------------- */
+
+/*
+ * Two-level sparse mask of [ST "2 段階ストレージ形式"]: the L x L mask is cut
+ * into 64 x 64 outer tiles (OTs).  An OT whose elements are all valid is a
+ * "full" OT; one with valid and invalid elements is a "part" OT; an OT with
+ * no valid element is not stored and never read.  Per query block row
+ * (64 queries), the stored OTs are listed by key block in CSR form, full and
+ * part separately, each list ascending.  A part OT carries 64 uint64 inner
+ * tile bitmaps: word ir*8 + ic covers queries 8*ir .. 8*ir+7 and keys
+ * 8*ic .. 8*ic+7 of the OT; bit r*8 + c (LSB first) is 1 iff query 8*ir+r
+ * may attend key 8*ic+c.
+ * The struct lives in host memory; its array pointers are device memory
+ * (for attn_prefill_bsr and attn_debug_bsr_decode).
+ */
+typedef struct {
+  int seq_len;                  /* L, a multiple of 64 */
+  int num_blocks;               /* L / 64 */
+  int nnz_full, nnz_part;       /* stored OT counts */
+  const int32_t* full_indptr;   /* [num_blocks + 1] */
+  const int32_t* full_kblock;   /* [nnz_full] key-block index of each full OT */
+  const int32_t* part_indptr;   /* [num_blocks + 1] */
+  const int32_t* part_kblock;   /* [nnz_part] */
+  const uint64_t* part_bits;    /* [nnz_part * 64] inner-tile bitmaps */
+} attn_bsr_mask;
+
+/*
+ * Encode a dense 0/1 mask (host memory, uint8 [L, L], row = query, nonzero =
+ * attend) into the canonical two-level form above, on the host.  Call once
+ * with all output pointers NULL to get nnz_full / nnz_part, then again with
+ * arrays of those sizes (host memory) to fill them.
+ */
+attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_indptr,
+                                   int32_t* full_kblock, int32_t* part_indptr,
+                                   int32_t* part_kblock, uint64_t* part_bits, int* nnz_full,
+                                   int* nnz_part);
+
+/*
+ * Block-sparse prefill: the block-wise kernel of [ST "デュアルカーネル戦略"].
+ * Per (query block, head, batch) a workgroup walks only the stored OTs of
+ * its block row; full OTs take no per-element test, part OTs apply their
+ * bitmaps as a predicate before the row max; unstored OTs are never read.
+ * q, o [B, L, Hq, D]; k, v [B, L, Hkv, D]; lse [B, L, Hq] fp32 or NULL.
+ * One mask serves every batch entry and head.
+ * Supported: dtype ATTN_F16 or ATTN_BF16; D in {64, 128}; L % 64 == 0.
+ */
+attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
+                               const attn_bsr_mask* mask, void* o, float* lse, int B, int L,
+                               int Hq, int Hkv, int D, float scale, int dtype,
+                               void* hip_stream);
+
+/* ---- test exports ------------------------------------------------------ */
+
+/* Write, with the device code the decode kernels use, every split's key range
+ * into ranges [B, num_splits, 2] int32 (device): [begin, end) as offsets
+ * within the request, or -1, -1 for a split the request does not use.
+ * Synchronises the stream before returning. */
+attn_status_t attn_debug_split_ranges(const int32_t* kv_indptr, int B, int max_kv_len,
+                                      int num_splits, int32_t* ranges, void* hip_stream);
+
+/* Expand a two-level mask to dense uint8 [L, L] (device) with the predicate
+ * the block-sparse kernel applies.  Synchronises the stream. */
+attn_status_t attn_debug_bsr_decode(const attn_bsr_mask* mask, uint8_t* dense,
+                                    void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

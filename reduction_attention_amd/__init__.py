@@ -1,0 +1,20 @@
+"""Fused multi-reduction attention for AMD MI355X (gfx950).
+
+C ABI: include/attn.h, implemented by libattn.so (HIP kernels).  This
+package is its thin Python binding; see ``api`` for the entry points.
+"""
+from .api import (  # noqa: F401
+    BsrMask,
+    attn_bsr_encode_host,
+    attn_debug_bsr_decode,
+    attn_debug_split_ranges,
+    attn_decode_choose_splits,
+    attn_decode_splitkv,
+    attn_decode_workspace_bytes,
+    attn_device_cu_count,
+    attn_merge_lse,
+    attn_prefill,
+    attn_prefill_bsr,
+    decode_workspace_views,
+)
+from ._lib import ATTN_BF16, ATTN_F16, ATTN_F32, AttnError  # noqa: F401

@@ -1,0 +1,315 @@
+// api.cpp -- the C ABI declared in include/attn.h: argument validation,
+// status reporting, the split-count rule, workspace sizing, the host-side
+// BSR encoder, and dispatch to the kernel launchers.  No HIP call is made
+// before an argument check has passed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/attn.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+attn_status_t ok() {
+  g_last_error.clear();
+  return ATTN_OK;
+}
+
+attn_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == ATTN_F32 || dt == ATTN_BF16 || dt == ATTN_F16; }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplits = 256;
+constexpr int kMaxGroup = 16;
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_EINVAL: return "ATTN_EINVAL: invalid argument";
+    case ATTN_EUNSUPPORTED: return "ATTN_EUNSUPPORTED: unsupported configuration";
+    case ATTN_EWORKSPACE: return "ATTN_EWORKSPACE: workspace missing or too small";
+    case ATTN_EHIP: return "ATTN_EHIP: HIP runtime error";
+  }
+  return "unknown attn status";
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_device_cu_count(void) {
+  static std::once_flag once;
+  static int cus = 256;
+  std::call_once(once, [] {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+        prop.multiProcessorCount > 0)
+      cus = prop.multiProcessorCount;
+    else
+      (void)hipGetLastError();
+  });
+  return cus;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
+  const size_t rows = size_t(B) * size_t(Hq);
+  const size_t bytes = size_t(num_splits) * rows * (size_t(D) + 2) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv, int max_kv_len) {
+  (void)Hq;
+  (void)D;
+  if (B <= 0 || Hkv <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
+  const long long target = 4LL * attn_device_cu_count();  // workgroups to aim for
+  long long c = 1;
+  while (c < max_kv_len) c <<= 1;  // one split per request at most
+  // largest power-of-two chunk >= 256 whose estimated workgroup count reaches target
+  while (c > 256) {
+    const long long wgs = (long long)Hkv * ((total_kv + c - 1) / c + B / 2);
+    if (wgs >= target) break;
+    c >>= 1;
+  }
+  long long s = (max_kv_len + c - 1) / c;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return int(s);
+}
+
+attn_status_t attn_merge_lse(const float* o_part, const float* m_part, const float* l_part,
+                             int num_splits, int rows, int D, void* o, int o_dtype, float* lse,
+                             void* hip_stream) {
+  if (!o_part || !m_part || !l_part || !o) return fail(ATTN_EINVAL, "merge: null pointer");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "merge: num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+  if (rows < 0) return fail(ATTN_EINVAL, "merge: rows %d < 0", rows);
+  if (rows > (1 << 30)) return fail(ATTN_EUNSUPPORTED, "merge: rows above 2^30");
+  if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "merge: D = %d (supported: 64, 128)", D);
+  if (!valid_dtype(o_dtype)) return fail(ATTN_EUNSUPPORTED, "merge: o_dtype %d", o_dtype);
+  rattn::MergeArgs a{o_part, m_part, l_part, num_splits, rows, D, o, o_dtype, lse};
+  return hip_status(rattn::launch_merge(a, static_cast<hipStream_t>(hip_stream)), "merge launch");
+}
+
+attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
+                                  const int32_t* kv_indptr, void* o, float* lse, int B, int Hq,
+                                  int Hkv, int D, int max_kv_len, long long total_kv, float scale,
+                                  int num_splits, int dtype, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  if (!q || !k || !v || !kv_indptr || !o) return fail(ATTN_EINVAL, "decode: null pointer");
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "decode: B, Hq, Hkv must be >= 1");
+  if (B > 65535 || Hkv > 65535) return fail(ATTN_EUNSUPPORTED, "decode: B or Hkv above 65535");
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "decode: Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  if (Hq / Hkv > kMaxGroup)
+    return fail(ATTN_EUNSUPPORTED, "decode: group size %d above %d", Hq / Hkv, kMaxGroup);
+  if ((long long)B * Hq > (1LL << 30)) return fail(ATTN_EUNSUPPORTED, "decode: B * Hq above 2^30");
+  if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "decode: D = %d (supported: 64, 128)", D);
+  if (!valid_dtype(dtype)) return fail(ATTN_EUNSUPPORTED, "decode: dtype %d", dtype);
+  if (max_kv_len < 0 || total_kv < 0) return fail(ATTN_EINVAL, "decode: negative length");
+  if ((long long)max_kv_len > total_kv)
+    return fail(ATTN_EINVAL, "decode: max_kv_len %d exceeds total_kv %lld", max_kv_len, total_kv);
+  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "decode: scale is not finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "decode: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_EINVAL, "decode: q, k, v, o must be 16-byte aligned");
+  const int s = num_splits ? num_splits
+                           : attn_decode_choose_splits(B, Hq, Hkv, D, total_kv, max_kv_len);
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, s);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_EWORKSPACE, "decode: workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned16(workspace)) return fail(ATTN_EINVAL, "decode: workspace must be 16-byte aligned");
+
+  const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
+  const size_t rows = size_t(B) * Hq;
+  float* ws = static_cast<float*>(workspace);
+  rattn::DecodeArgs a{q, k, v, kv_indptr, ws, ws + size_t(s) * rows * D,
+                      ws + size_t(s) * rows * D + size_t(s) * rows,
+                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype};
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = rattn::launch_decode_partial(a, st);
+  if (e != hipSuccess) return hip_status(e, "decode partial launch");
+  rattn::MergeArgs m{a.o_part, a.m_part, a.l_part, s, int(rows), D, o, dtype, lse};
+  return hip_status(rattn::launch_merge(m, st), "decode merge launch");
+}
+
+attn_status_t attn_prefill(const void* q, const void* k, const void* v, const int32_t* qo_indptr,
+                           const int32_t* kv_indptr, void* o, float* lse, int B, int Hq, int Hkv,
+                           int D, int max_q_len, int max_kv_len, float scale, int causal,
+                           int dtype, void* hip_stream) {
+  if (!q || !k || !v || !qo_indptr || !kv_indptr || !o)
+    return fail(ATTN_EINVAL, "prefill: null pointer");
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill: B, Hq, Hkv must be >= 1");
+  if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill: B or Hq above 65535");
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill: Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill: D = %d (supported: 64, 128)", D);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_EUNSUPPORTED, "prefill: dtype %d (supported: bf16, f16)", dtype);
+  if (max_q_len < 0 || max_kv_len < 0) return fail(ATTN_EINVAL, "prefill: negative length");
+  if (causal != 0 && causal != 1) return fail(ATTN_EINVAL, "prefill: causal must be 0 or 1");
+  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "prefill: scale is not finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_EINVAL, "prefill: q, k, v, o must be 16-byte aligned");
+  rattn::PrefillArgs a{q, k, v, qo_indptr, kv_indptr, o, lse, B, Hq, Hkv, D, Hq / Hkv,
+                       max_q_len, max_kv_len, scale * kLog2e, causal, dtype};
+  return hip_status(rattn::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "prefill launch");
+}
+
+attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_indptr,
+                                   int32_t* full_kblock, int32_t* part_indptr,
+                                   int32_t* part_kblock, uint64_t* part_bits, int* nnz_full,
+                                   int* nnz_part) {
+  if (!dense || !nnz_full || !nnz_part) return fail(ATTN_EINVAL, "bsr_encode: null pointer");
+  if (L <= 0 || L % 64) return fail(ATTN_EINVAL, "bsr_encode: L = %d is not a positive multiple of 64", L);
+  const bool fill = full_indptr || full_kblock || part_indptr || part_kblock || part_bits;
+  if (fill && !(full_indptr && part_indptr && part_bits && (full_kblock || *nnz_full == 0) &&
+                (part_kblock || *nnz_part == 0)))
+    return fail(ATTN_EINVAL, "bsr_encode: fill pass needs every output array");
+  const int nb = L / 64;
+  int nf = 0, np = 0;
+  if (fill) {
+    full_indptr[0] = 0;
+    part_indptr[0] = 0;
+  }
+  for (int qb = 0; qb < nb; ++qb) {
+    for (int kb = 0; kb < nb; ++kb) {
+      uint64_t words[64];
+      int valid = 0;
+      for (int ir = 0; ir < 8; ++ir)
+        for (int ic = 0; ic < 8; ++ic) {
+          uint64_t wd = 0;
+          for (int r = 0; r < 8; ++r)
+            for (int c = 0; c < 8; ++c) {
+              const size_t row = size_t(qb) * 64 + ir * 8 + r;
+              const size_t col = size_t(kb) * 64 + ic * 8 + c;
+              if (dense[row * size_t(L) + col]) {
+                wd |= uint64_t(1) << (r * 8 + c);
+                ++valid;
+              }
+            }
+          words[ir * 8 + ic] = wd;
+        }
+      if (valid == 0) continue;  // empty OT: not stored
+      if (valid == 64 * 64) {
+        if (fill) {
+          if (nf >= *nnz_full) return fail(ATTN_EINVAL, "bsr_encode: nnz_full too small");
+          full_kblock[nf] = kb;
+        }
+        ++nf;
+      } else {
+        if (fill) {
+          if (np >= *nnz_part) return fail(ATTN_EINVAL, "bsr_encode: nnz_part too small");
+          part_kblock[np] = kb;
+          std::memcpy(part_bits + size_t(np) * 64, words, sizeof words);
+        }
+        ++np;
+      }
+    }
+    if (fill) {
+      full_indptr[qb + 1] = nf;
+      part_indptr[qb + 1] = np;
+    }
+  }
+  if (fill && (nf != *nnz_full || np != *nnz_part))
+    return fail(ATTN_EINVAL, "bsr_encode: sizes differ from the mask (%d/%d full, %d/%d part)", nf,
+                *nnz_full, np, *nnz_part);
+  *nnz_full = nf;
+  *nnz_part = np;
+  return ok();
+}
+
+static attn_status_t check_mask(const attn_bsr_mask* m, const char* who) {
+  if (!m) return fail(ATTN_EINVAL, "%s: null mask", who);
+  if (m->seq_len <= 0 || m->seq_len % 64)
+    return fail(ATTN_EINVAL, "%s: mask seq_len %d not a positive multiple of 64", who, m->seq_len);
+  if (m->num_blocks != m->seq_len / 64)
+    return fail(ATTN_EINVAL, "%s: mask num_blocks %d != seq_len / 64", who, m->num_blocks);
+  if (m->nnz_full < 0 || m->nnz_part < 0) return fail(ATTN_EINVAL, "%s: negative nnz", who);
+  if (!m->full_indptr || !m->part_indptr) return fail(ATTN_EINVAL, "%s: null mask indptr", who);
+  if ((m->nnz_full && !m->full_kblock) || (m->nnz_part && (!m->part_kblock || !m->part_bits)))
+    return fail(ATTN_EINVAL, "%s: null mask array", who);
+  return ATTN_OK;
+}
+
+attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
+                               const attn_bsr_mask* mask, void* o, float* lse, int B, int L, int Hq,
+                               int Hkv, int D, float scale, int dtype, void* hip_stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "prefill_bsr: null pointer");
+  attn_status_t ms = check_mask(mask, "prefill_bsr");
+  if (ms != ATTN_OK) return ms;
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill_bsr: B, Hq, Hkv must be >= 1");
+  if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill_bsr: B or Hq above 65535");
+  if (L != mask->seq_len) return fail(ATTN_EINVAL, "prefill_bsr: L %d != mask seq_len %d", L, mask->seq_len);
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill_bsr: Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill_bsr: D = %d (supported: 64, 128)", D);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_EUNSUPPORTED, "prefill_bsr: dtype %d (supported: f16, bf16)", dtype);
+  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "prefill_bsr: scale is not finite");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_EINVAL, "prefill_bsr: q, k, v, o must be 16-byte aligned");
+  if (mask->nnz_part && (reinterpret_cast<uintptr_t>(mask->part_bits) & 7u))
+    return fail(ATTN_EINVAL, "prefill_bsr: part_bits must be 8-byte aligned");
+  rattn::BsrArgs a{q, k, v, mask->full_indptr, mask->full_kblock, mask->part_indptr,
+                   mask->part_kblock, mask->part_bits, o, lse, B, L, Hq, Hkv, D, Hq / Hkv,
+                   mask->num_blocks, scale * kLog2e, dtype};
+  return hip_status(rattn::launch_prefill_bsr(a, static_cast<hipStream_t>(hip_stream)),
+                    "prefill_bsr launch");
+}
+
+attn_status_t attn_debug_split_ranges(const int32_t* kv_indptr, int B, int max_kv_len,
+                                      int num_splits, int32_t* ranges, void* hip_stream) {
+  if (!kv_indptr || !ranges) return fail(ATTN_EINVAL, "split_ranges: null pointer");
+  if (B < 1 || max_kv_len < 0) return fail(ATTN_EINVAL, "split_ranges: bad B or max_kv_len");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "split_ranges: num_splits %d outside [1, %d]", num_splits, kMaxSplits);
+  const int chunk = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 0;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = rattn::launch_split_ranges(kv_indptr, B, num_splits, chunk, ranges, st);
+  if (e != hipSuccess) return hip_status(e, "split_ranges launch");
+  return hip_status(hipStreamSynchronize(st), "split_ranges sync");
+}
+
+attn_status_t attn_debug_bsr_decode(const attn_bsr_mask* mask, uint8_t* dense, void* hip_stream) {
+  attn_status_t ms = check_mask(mask, "bsr_decode");
+  if (ms != ATTN_OK) return ms;
+  if (!dense) return fail(ATTN_EINVAL, "bsr_decode: null output");
+  if (mask->nnz_part && (reinterpret_cast<uintptr_t>(mask->part_bits) & 7u))
+    return fail(ATTN_EINVAL, "bsr_decode: part_bits must be 8-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = rattn::launch_bsr_decode(mask->full_indptr, mask->full_kblock, mask->part_indptr,
+                                          mask->part_kblock, mask->part_bits, mask->num_blocks,
+                                          dense, st);
+  if (e != hipSuccess) return hip_status(e, "bsr_decode launch");
+  return hip_status(hipStreamSynchronize(st), "bsr_decode sync");
+}
+
+}  // extern "C"

@@ -1,0 +1,458 @@
+// decode.hip -- split-KV grouped-query decode on gfx950.
+//
+// The key dimension of each request is cut by the Split operator into
+// chunks of c keys (Cleave article on tip.co.jp, "Split演算子によるSplit-Kの
+// 対応"; Cleave arXiv abstract).  One workgroup reduces one
+// (chunk, KV head, request) and emits, for each of the G query heads that
+// share the KV head, a normalised partial output with its running max and
+// sum (m, l).  Inside a chunk the key dimension is tiled (32 keys per wave
+// step) and the max and sum reductions run in the same loop over the same
+// score tile -- the online softmax that the article's iterative tiling and
+// horizontal fusion describe ("複数リダクションのスケジューリング").  A
+// second kernel merges the partials with log-sum-exp weights.
+//
+// Memory: each K/V byte of the request is read exactly once, by the one
+// workgroup whose chunk holds it, for all G query heads at once; every
+// read is a 16-byte vector load, 16 lanes covering a 256-byte row.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace rattn {
+
+// Key range [lo, hi) (offsets inside request b) of split i with chunk c.
+// An unused split gets lo >= hi.  Shared by the partial kernels and the
+// split-range export so that the export shows what the kernels do.
+struct SplitRange {
+  int64_t base;  // kv_indptr[b]
+  int lo, hi;
+};
+
+__device__ __forceinline__ SplitRange split_range(const int32_t* kv_indptr, int b, int i, int c) {
+  SplitRange r;
+  const int64_t b0 = kv_indptr[b], b1 = kv_indptr[b + 1];
+  const int n = int(b1 - b0);
+  r.base = b0;
+  const int64_t lo = int64_t(i) * c;
+  r.lo = lo < n ? int(lo) : n;
+  r.hi = lo + c < n ? int(lo + c) : n;
+  return r;
+}
+
+// -------------------------------------------------------------------------
+// MFMA partial kernel (16-bit K/V/Q, fp32 accumulation).
+//
+// Per wave step the scores of 32 keys against the (up to 16, zero padded)
+// query heads are S^T = K Q^T: two 16x16x32 MFMA tiles of 16 keys, the
+// head-dimension contraction split into D/32 slabs.  Lane l = (c16, h4)
+// (c16 = l % 16, h4 = l / 16) loads K row (key 16a + c16) at dims
+// (D/4)*h4 .. +D/4: contiguous, 4 lanes per 256-byte row.  The accumulator
+// gives lane l head c16 and keys 16a + 4*h4 + r.
+// The value update is O^T += V^T P^T with 16x16x32 MFMAs: the reduction
+// slots of lane (c16, h4) are the keys it already holds scores for,
+// kappa(h4, i) = 16*(i/4) + 4*h4 + i%4, so P^T needs no lane exchange;
+// MFMA j covers head-dim rows d = (D/16)*rho + j, rho = 0..15, so each
+// lane loads D/16 contiguous elements of the rows of its 8 keys (16 lanes
+// per 256-byte row) and re-packs them with byte permutes.  Lane (c16, h4)
+// ends with head c16, dims (D/4)*h4 .. +D/4 of the output.
+// -------------------------------------------------------------------------
+template <class T, int D>
+struct DecodeTile {
+  static constexpr int NU = D / 32;   // QK slabs of 32 dims
+  static constexpr int NJ = D / 16;   // PV MFMAs (one per d residue)
+  static constexpr int VR = D / 32;   // 32-bit registers per V row piece
+  u32x4 k[2][NU];                     // K rows of the two 16-key tiles
+  uint32_t v[8][VR];                  // V row pieces of the lane's 8 keys
+};
+
+template <class T, int D>
+__device__ __forceinline__ void decode_load(DecodeTile<T, D>& t, const uint16_t* kbase,
+                                            const uint16_t* vbase, int64_t row_stride,
+                                            int key0, int hi, int c16, int h4) {
+  constexpr int NU = D / 32;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    int key = key0 + 16 * a + c16;
+    key = key < hi ? key : hi - 1;
+    const uint16_t* p = kbase + int64_t(key) * row_stride + (D / 4) * h4;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) t.k[a][u] = ldg128(p + 8 * u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int key = key0 + 16 * (i / 4) + 4 * h4 + (i % 4);
+    key = key < hi ? key : hi - 1;
+    const uint16_t* p = vbase + int64_t(key) * row_stride + (D / 16) * c16;
+    if constexpr (D == 128) {
+      u32x4 x = ldg128(p);
+      t.v[i][0] = x[0]; t.v[i][1] = x[1]; t.v[i][2] = x[2]; t.v[i][3] = x[3];
+    } else {
+      u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      t.v[i][0] = x[0]; t.v[i][1] = x[1];
+    }
+  }
+}
+
+template <class T, int D>
+struct DecodeState {
+  f32x4 o[D / 16];   // O^T accumulators: o[j][r] is dim (D/4)*h4 + (D/16)*r + j
+  float m;           // running max of head c16 (log2 units), same in all 4 h4 lanes
+  float l;           // this lane's share of the running sum
+};
+
+template <class T, int D>
+__device__ __forceinline__ void decode_step(DecodeState<T, D>& st, const DecodeTile<T, D>& t,
+                                            const u32x4 (&qb)[D / 32], int key0, int hi,
+                                            float sl2, int h4) {
+  typedef typename T::vec8 vec8;
+  constexpr int NU = D / 32, NJ = D / 16;
+  // scores: S^T tiles of 16 keys x 16 heads
+  f32x4 s[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    s[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NU; ++u) s[a] = T::mfma16(as<vec8>(t.k[a][u]), as<vec8>(qb[u]), s[a]);
+  }
+  float x[8];
+  const bool tail = key0 + 32 > hi;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float y = s[a][r] * sl2;
+      if (tail && key0 + 16 * a + 4 * h4 + r >= hi) y = -INFINITY;
+      x[4 * a + r] = y;
+    }
+  float mx = max3(x[0], x[1], max3(x[2], x[3], max3(x[4], x[5], fmaxf(x[6], x[7]))));
+  mx = fmaxf(mx, shfl_xor(mx, 16));
+  mx = fmaxf(mx, shfl_xor(mx, 32));
+  // every step holds at least one valid key, so mx and m_new are finite
+  const float m_new = fmaxf(st.m, mx);
+  const float alpha = fexp2(st.m - m_new);
+  st.m = m_new;
+  f32x8 p;
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fexp2(x[i] - m_new);
+    psum += p[i];
+  }
+  st.l = st.l * alpha + psum;
+  const vec8 pb = T::cvt8(p);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    u32x4 a;
+    const int w = j / 2;
+#pragma unroll
+    for (int pr = 0; pr < 4; ++pr)
+      a[pr] = (j & 1) ? pack_hi(t.v[2 * pr][w], t.v[2 * pr + 1][w])
+                      : pack_lo(t.v[2 * pr][w], t.v[2 * pr + 1][w]);
+    st.o[j] *= alpha;
+    st.o[j] = T::mfma16(as<vec8>(a), pb, st.o[j]);
+  }
+}
+
+template <class T, int D, int W>
+__global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args) {
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = args.G, Hq = args.Hq;
+  const int64_t rows = int64_t(args.B) * Hq;
+  const SplitRange sr = split_range(args.kv_indptr, b, i, args.chunk);
+  const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
+  if (sr.lo >= sr.hi) {  // split unused by this request
+    if (threadIdx.x < G) {
+      args.m_part[int64_t(i) * rows + row0 + threadIdx.x] = -INFINITY;
+      args.l_part[int64_t(i) * rows + row0 + threadIdx.x] = 0.f;
+    }
+    return;
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c16 = lane & 15, h4 = lane >> 4;
+  const int64_t row_stride = int64_t(args.Hkv) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(args.k) + (sr.base + sr.lo) * row_stride +
+                          int64_t(g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(args.v) + (sr.base + sr.lo) * row_stride +
+                          int64_t(g) * D;
+  const int n = sr.hi - sr.lo;
+
+  // Q^T operand: head c16 (zero past G), dims (D/4)*h4 + 8u .. +8
+  u32x4 qb[D / 32];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(args.q) + (row0 + (c16 < G ? c16 : 0)) * D +
+                         (D / 4) * h4;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      qb[u] = ldg128(qp + 8 * u);
+      if (c16 >= G) qb[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  DecodeState<T, D> st;
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  // wave w takes 32-key steps w, w + W, w + 2W, ...; two register buffers
+  // keep the next step's loads in flight while the current one computes.
+  const int nsteps = (n + 31) / 32;
+  DecodeTile<T, D> t0, t1;
+  int s0 = w;
+  if (s0 < nsteps) decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * s0, n, c16, h4);
+  for (; s0 < nsteps; s0 += 2 * W) {
+    const int s1 = s0 + W;
+    if (s1 < nsteps) decode_load<T, D>(t1, kbase, vbase, row_stride, 32 * s1, n, c16, h4);
+    decode_step<T, D>(st, t0, qb, 32 * s0, n, args.scale_log2, h4);
+    if (s1 >= nsteps) break;
+    const int s2 = s1 + W;
+    if (s2 < nsteps) decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * s2, n, c16, h4);
+    decode_step<T, D>(st, t1, qb, 32 * s1, n, args.scale_log2, h4);
+  }
+
+  // lane sums -> head sums (the four h4 lanes of head c16)
+  float l = st.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+
+  // combine the W waves through LDS
+  __shared__ float red_m[W][16];
+  __shared__ float red_l[W][16];
+  __shared__ float red_o[W][16][D + 4];
+  if (c16 < G) {
+    if (h4 == 0) {
+      red_m[w][c16] = st.m;  // -inf for a wave that had no step
+      red_l[w][c16] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_o[w][c16][(D / 4) * h4 + (D / 16) * r + j] = st.o[j][r];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < G * D; e += 64 * W) {
+    const int h = e / D, d = e % D;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, red_m[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const float f = fexp2(red_m[ww][h] - M);
+      L += red_l[ww][h] * f;
+      O += red_o[ww][h][d] * f;
+    }
+    const int64_t row = row0 + h;
+    args.o_part[(int64_t(i) * rows + row) * D + d] = O / L;
+    if (d == 0) {
+      args.m_part[int64_t(i) * rows + row] = M * kLn2;
+      args.l_part[int64_t(i) * rows + row] = L;
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// fp32 partial kernel (VALU).  One wave per (split, KV head, request); lane
+// j scores key j of each 64-key tile against the G query heads, the wave
+// keeps per-head running max and sum, and lane d accumulates output dims d
+// and d + 64.  Used for fp32 inputs, whose sizes here are small.
+// -------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
+  constexpr int DL = (D + 63) / 64;  // output dims per lane
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = args.G, Hq = args.Hq;
+  const int64_t rows = int64_t(args.B) * Hq;
+  const SplitRange sr = split_range(args.kv_indptr, b, i, args.chunk);
+  const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
+  const int lane = threadIdx.x;
+  if (sr.lo >= sr.hi) {
+    if (lane < G) {
+      args.m_part[int64_t(i) * rows + row0 + lane] = -INFINITY;
+      args.l_part[int64_t(i) * rows + row0 + lane] = 0.f;
+    }
+    return;
+  }
+  __shared__ float qs[16][D];
+  __shared__ float ps[64][17];
+  const float* q = static_cast<const float*>(args.q);
+  for (int e = lane; e < G * D; e += 64) qs[e / D][e % D] = q[(row0 + e / D) * D + e % D];
+  __syncthreads();
+  const int64_t row_stride = int64_t(args.Hkv) * D;
+  const float* kb = static_cast<const float*>(args.k) + (sr.base + sr.lo) * row_stride + int64_t(g) * D;
+  const float* vb = static_cast<const float*>(args.v) + (sr.base + sr.lo) * row_stride + int64_t(g) * D;
+  const int n = sr.hi - sr.lo;
+  float m[16], l[16], acc[16][DL];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int x = 0; x < DL; ++x) acc[h][x] = 0.f;
+  }
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int key = t0 + lane;
+    const bool valid = key < n;
+    const float* kr = kb + int64_t(valid ? key : n - 1) * row_stride;
+    float sc[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) sc[h] = 0.f;
+    for (int d = 0; d < D; d += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
+#pragma unroll
+      for (int h = 0; h < 16; ++h)
+        if (h < G)
+          sc[h] += qs[h][d] * kv.x + qs[h][d + 1] * kv.y + qs[h][d + 2] * kv.z + qs[h][d + 3] * kv.w;
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      if (h >= G) break;
+      const float x = valid ? sc[h] * args.scale_log2 : -INFINITY;
+      float mx = x;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+      const float m_new = fmaxf(m[h], mx);  // finite: key t0 is valid
+      const float alpha = fexp2(m[h] - m_new);
+      const float p = fexp2(x - m_new);
+      m[h] = m_new;
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int xx = 0; xx < DL; ++xx) acc[h][xx] *= alpha;
+      ps[lane][h] = p;
+    }
+    __syncthreads();
+    const int kmax = n - t0 < 64 ? n - t0 : 64;
+    for (int j = 0; j < kmax; ++j) {
+      const float* vr = vb + int64_t(t0 + j) * row_stride;
+#pragma unroll
+      for (int xx = 0; xx < DL; ++xx) {
+        const int d = lane + 64 * xx;
+        if (d < D) {
+          const float vv = vr[d];
+#pragma unroll
+          for (int h = 0; h < 16; ++h)
+            if (h < G) acc[h][xx] += ps[j][h] * vv;
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h >= G) break;
+    float ls = l[h];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ls += shfl_xor(ls, off);
+    const int64_t row = row0 + h;
+#pragma unroll
+    for (int xx = 0; xx < DL; ++xx) {
+      const int d = lane + 64 * xx;
+      if (d < D) args.o_part[(int64_t(i) * rows + row) * D + d] = acc[h][xx] / ls;
+    }
+    if (lane == 0) {
+      args.m_part[int64_t(i) * rows + row] = m[h] * kLn2;
+      args.l_part[int64_t(i) * rows + row] = ls;
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// LSE merge: one wave per row; lane d handles dims d, d + 64.
+// -------------------------------------------------------------------------
+template <int D, class OutT>
+__global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
+  constexpr int DL = (D + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int64_t rows = a.rows;
+  float M = -INFINITY;
+  for (int i = 0; i < a.s; ++i) {
+    const float li = a.l_part[int64_t(i) * rows + row];
+    const float mi = a.m_part[int64_t(i) * rows + row];
+    if (li > 0.f) M = fmaxf(M, mi);
+  }
+  float acc[DL];
+#pragma unroll
+  for (int x = 0; x < DL; ++x) acc[x] = 0.f;
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < a.s; ++i) {
+      const float li = a.l_part[int64_t(i) * rows + row];
+      if (!(li > 0.f)) continue;
+      const float wgt = li * fexp2((a.m_part[int64_t(i) * rows + row] - M) * kLog2e);
+      wsum += wgt;
+      const float* op = a.o_part + (int64_t(i) * rows + row) * D;
+#pragma unroll
+      for (int x = 0; x < DL; ++x) {
+        const int d = lane + 64 * x;
+        if (d < D) acc[x] += wgt * op[d];
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  OutT* o = static_cast<OutT*>(a.o) + row * D;
+#pragma unroll
+  for (int x = 0; x < DL; ++x) {
+    const int d = lane + 64 * x;
+    if (d < D) o[d] = OutT(acc[x] * inv);
+  }
+  if (a.lse && lane == 0) a.lse[row] = wsum > 0.f ? M + flog2(wsum) * kLn2 : -INFINITY;
+}
+
+__global__ void split_ranges_kernel(const int32_t* kv_indptr, int B, int s, int chunk,
+                                    int32_t* ranges) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= B * s) return;
+  const int b = e / s, i = e % s;
+  const SplitRange sr = split_range(kv_indptr, b, i, chunk);
+  ranges[2 * e] = sr.lo < sr.hi ? sr.lo : -1;
+  ranges[2 * e + 1] = sr.lo < sr.hi ? sr.hi : -1;
+}
+
+// ---- launchers -----------------------------------------------------------
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.s, a.Hkv, a.B);
+  if (a.dtype == 0) {  // fp32
+    if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
+  } else {
+    constexpr int W = 4;
+    if (a.dtype == 1) {
+      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), grid, dim3(64 * W), 0, st, a);
+      else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), grid, dim3(64 * W), 0, st, a);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), grid, dim3(64 * W), 0, st, a);
+      else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), grid, dim3(64 * W), 0, st, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
+  const dim3 grid((a.rows + 3) / 4);
+  if (a.rows == 0) return hipSuccess;
+#define RATTN_MERGE(DD, TT) hipLaunchKernelGGL((merge_lse_kernel<DD, TT>), grid, dim3(256), 0, st, a)
+  if (a.D == 64) {
+    if (a.o_dtype == 0) RATTN_MERGE(64, float);
+    else if (a.o_dtype == 1) RATTN_MERGE(64, __bf16);
+    else RATTN_MERGE(64, _Float16);
+  } else {
+    if (a.o_dtype == 0) RATTN_MERGE(128, float);
+    else if (a.o_dtype == 1) RATTN_MERGE(128, __bf16);
+    else RATTN_MERGE(128, _Float16);
+  }
+#undef RATTN_MERGE
+  return hipGetLastError();
+}
+
+hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
+                               hipStream_t st) {
+  const int n = B * s;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(split_ranges_kernel, dim3((n + 255) / 256), dim3(256), 0, st, kv_indptr, B, s,
+                     chunk, ranges);
+  return hipGetLastError();
+}
+
+}  // namespace rattn

@@ -1,0 +1,87 @@
+// device.hpp -- gfx950 building blocks shared by the attention kernels:
+// element types, 128-bit vectors, MFMA wrappers, cross-lane reductions.
+//
+// MFMA operand convention used throughout.  For v_mfma_f32_32x32x16_{bf16,f16}
+// lane l supplies row (l % 32) of A and column (l % 32) of B, and eight
+// consecutive reduction "slots" selected by its half (l / 32) and register
+// position.  A and B use the same slot numbering, so any assignment of the
+// reduction index to (half, position) gives the right contraction provided
+// both operands follow it; the kernels pick assignments that make their
+// memory reads contiguous.  The 32x32 accumulator gives lane l column
+// (l % 32) and rows 8*(r/4) + 4*(l/32) + (r%4), r = 0..15.
+// For v_mfma_f32_16x16x32_* lane l supplies row/column (l % 16), slots by
+// (l / 16) and position; the 16x16 accumulator gives lane l column (l % 16)
+// and rows 4*(l/16) + r, r = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-bit element traits: the storage type, its 8-wide MFMA operand vector,
+// the MFMA builtins and the fp32 -> 16-bit conversion (round to nearest even).
+struct BF16 {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec8 cvt8(f32x8 x) { return __builtin_convertvector(x, vec8); }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    return __uint_as_float(uint32_t(bits) << 16);
+  }
+};
+
+struct F16 {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma32(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(vec8 a, vec8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ vec8 cvt8(f32x8 x) { return __builtin_convertvector(x, vec8); }
+  static __device__ __forceinline__ float to_f32(uint16_t bits) {
+    _Float16 h = __builtin_bit_cast(_Float16, bits);
+    return float(h);
+  }
+};
+
+template <class V>
+__device__ __forceinline__ V as(u32x4 x) { return __builtin_bit_cast(V, x); }
+
+// 128-bit global load / store through the vector memory path.
+__device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void stg128(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
+
+// Pick 16-bit halves: lo16(a) | lo16(b) << 16, and hi16(a) | hi16(b) << 16.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
+
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+}  // namespace rattn

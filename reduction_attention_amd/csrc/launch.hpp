@@ -1,0 +1,78 @@
+// launch.hpp -- host-side launchers of the HIP kernels.  Arguments are
+// validated by api.cpp before any launcher runs; launchers only pick a
+// template instance, size the grid and enqueue on the given stream.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rattn {
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* kv_indptr;
+  float* o_part;   // [s, B*Hq, D]
+  float* m_part;   // [s, B*Hq]
+  float* l_part;   // [s, B*Hq]
+  int B, Hq, Hkv, D, G;
+  int s;           // split count
+  int chunk;       // keys per split, ceil(max_kv_len / s)
+  float scale_log2;  // scale * log2(e)
+  int dtype;
+};
+
+struct MergeArgs {
+  const float* o_part;
+  const float* m_part;
+  const float* l_part;
+  int s, rows, D;
+  void* o;
+  int o_dtype;
+  float* lse;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, D, G;
+  int max_q_len, max_kv_len;
+  float scale_log2;
+  int causal;
+  int dtype;
+};
+
+struct BsrArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* full_indptr;
+  const int32_t* full_kblock;
+  const int32_t* part_indptr;
+  const int32_t* part_kblock;
+  const uint64_t* part_bits;
+  void* o;
+  float* lse;
+  int B, L, Hq, Hkv, D, G, num_blocks;
+  float scale_log2;
+  int dtype;
+};
+
+hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
+                               hipStream_t st);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st);
+hipError_t launch_bsr_decode(const int32_t* full_indptr, const int32_t* full_kblock,
+                             const int32_t* part_indptr, const int32_t* part_kblock,
+                             const uint64_t* part_bits, int num_blocks, uint8_t* dense,
+                             hipStream_t st);
+
+}  // namespace rattn

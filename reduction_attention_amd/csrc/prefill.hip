@@ -1,0 +1,289 @@
+// prefill.hip -- fused prefill attention on gfx950: dense / causal over a
+// ragged batch, and block-sparse over STOF's two-level mask.
+//
+// Both kernels stream key/value tiles of 64 keys through a two-stage LDS
+// ring while the query tile stays in registers, and fuse QK^T, the row
+// max, the exp-sum and PV into one loop (attn_core.hpp).  The dense kernel
+// follows the iterative tiling and horizontal fusion of the Cleave article
+// (tip.co.jp, "複数リダクションのスケジューリング"), with dynamic batch and
+// sequence lengths read from indptr arrays at run time so one compiled
+// kernel serves every shape (same section, last paragraph).  The sparse
+// kernel is the block-wise kernel of the STOF explainer (gist.science,
+// 技術概要, "1. 統合 MHA モジュール", "デュアルカーネル戦略"): it visits only the
+// stored outer tiles of its query block row, skips the element test on
+// full tiles and applies the 8x8 inner-tile bitmaps on part tiles.
+#include "attn_core.hpp"
+#include "launch.hpp"
+
+namespace rattn {
+
+// ---------------------------------------------------------------------------
+// Dense / causal prefill.  Workgroup = 4 waves = 128 query rows of one query
+// head; grid (query tiles, Hq, B).  Causal tiles are issued heaviest first.
+// ---------------------------------------------------------------------------
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+  constexpr int NT = 256, BQ = 128;
+  typedef TileGeom<D> Gm;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Gm::STAGE];
+
+  const int b = blockIdx.z, hq = blockIdx.y;
+  const int qt = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+  const int64_t q_begin = a.qo_indptr[b];
+  const int n_q = int(a.qo_indptr[b + 1] - q_begin);
+  const int64_t k_begin = a.kv_indptr[b];
+  const int n_kv = int(a.kv_indptr[b + 1] - k_begin);
+  const int q_start = qt * BQ;
+  if (q_start >= n_q) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int g = hq / a.G;
+  const int off = n_kv - n_q;  // causal: key j valid for query i iff j <= i + off
+  const int q_last_wg = (q_start + BQ < n_q ? q_start + BQ : n_q) - 1;
+  int kv_end = n_kv;
+  if (CAUSAL) kv_end = q_last_wg + 1 + off < n_kv ? q_last_wg + 1 + off : n_kv;
+  const int ntiles = kv_end > 0 ? (kv_end + Gm::BK - 1) / Gm::BK : 0;
+
+  const int q0w = q_start + 32 * w;
+  const int my_q = q0w + (lane & 31);
+  const bool wave_has_rows = q0w < n_q;
+  const int wave_q_last = (q0w + 31 < n_q ? q0w + 31 : n_q - 1);
+  const int64_t q_row = q_begin + (my_q < n_q ? my_q : n_q - 1);
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  u32x4 qb[D / 16];
+  load_q<D>(qb, Q + (q_row * a.Hq + hq) * D, lane);
+
+  RowState<D> st;
+  row_state_init(st);
+
+  const int64_t row_stride = int64_t(a.Hkv) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + k_begin * row_stride + int64_t(g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
+  const int key_last = n_kv - 1;
+
+  TileRegs<D, NT> tr;
+  if (ntiles > 0) {
+    tile_load<D, NT>(tr, kbase, vbase, row_stride, 0, key_last, tid);
+    tile_store<D, NT>(tr, lds, tid);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const int k0 = j * Gm::BK;
+    if (j + 1 < ntiles) tile_load<D, NT>(tr, kbase, vbase, row_stride, k0 + Gm::BK, key_last, tid);
+    const uint16_t* cur = lds + (j & 1) * Gm::STAGE;
+    bool active = wave_has_rows;
+    if (CAUSAL) active = active && (k0 <= wave_q_last + off);
+    if (active) {
+      f32x16 s[2];
+      qk_tile<T, D>(s, cur, qb, lane);
+      float x[2][16];
+      const bool need_mask = (k0 + Gm::BK > n_kv) || (CAUSAL && k0 + Gm::BK - 1 > q0w + off);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            bool ok = key < n_kv;
+            if (CAUSAL) ok = ok && key <= my_q + off;
+            x[kb][r] = ok ? s[kb][r] * a.scale_log2 : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] = s[kb][r] * a.scale_log2;
+      }
+      softmax_pv<T, D>(st, x, cur, lane);
+    }
+    if (j + 1 < ntiles) tile_store<D, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
+    __syncthreads();
+  }
+
+  const bool row_ok = my_q < n_q;
+  uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + ((q_begin + my_q) * a.Hq + hq) * D : nullptr;
+  float* lse = (row_ok && a.lse) ? a.lse + (q_begin + my_q) * a.Hq + hq : nullptr;
+  row_store<T, D>(st, orow, lse, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse prefill.  Workgroup = 2 waves = one 64-query outer-tile row of
+// one head; grid (L/64, Hq, B).  Tiles: the row's full OTs, then its part OTs.
+// ---------------------------------------------------------------------------
+
+// Part-OT bitmaps in LDS, re-laid so that one lane's eight bytes are
+// adjacent: byte (ir*8 + r)*8 + ic = row r of inner tile (ir, ic), i.e.
+// byte r of bitmap word ir*8 + ic.
+__device__ __forceinline__ void bitmap_store(uint64_t word, uint8_t* bm, int tid) {
+  if (tid < 64) {
+    const int ir = tid >> 3, ic = tid & 7;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) bm[(ir * 8 + r) * 8 + ic] = uint8_t(word >> (8 * r));
+  }
+}
+
+// The part-OT predicate: x[kb][r] -> -inf where query (32*w + lane%32) of the
+// OT may not attend key 32*kb + 8*(r/4) + 4*h + r%4 of the OT.
+__device__ __forceinline__ void apply_part_mask(float (&x)[2][16], const uint8_t* bm, int w,
+                                                int lane) {
+  const int rq = 32 * w + (lane & 31);
+  const int h = lane >> 5;
+  const uint64_t bytes = *reinterpret_cast<const uint64_t*>(bm + rq * 8);  // [ic] for row rq
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const uint32_t nib = uint32_t(bytes >> (8 * (4 * kb + r4) + 4 * h)) & 0xFu;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (!((nib >> e) & 1u)) x[kb][4 * r4 + e] = -INFINITY;
+    }
+}
+
+template <class T, int D>
+__global__ __launch_bounds__(128, 4) void bsr_kernel(BsrArgs a) {
+  constexpr int NT = 128;
+  typedef TileGeom<D> Gm;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Gm::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
+
+  const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = hq / a.G;
+  const int f0 = a.full_indptr[qblk], n_full = a.full_indptr[qblk + 1] - f0;
+  const int p0 = a.part_indptr[qblk], n_part = a.part_indptr[qblk + 1] - p0;
+  const int ntiles = n_full + n_part;
+
+  const int64_t L = a.L;
+  const int my_q = qblk * 64 + 32 * w + (lane & 31);
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  u32x4 qb[D / 16];
+  load_q<D>(qb, Q + ((int64_t(b) * L + my_q) * a.Hq + hq) * D, lane);
+
+  RowState<D> st;
+  row_state_init(st);
+
+  const int64_t row_stride = int64_t(a.Hkv) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
+
+  TileRegs<D, NT> tr;
+  uint64_t word = 0;
+  auto fetch = [&](int j) {
+    const bool part = j >= n_full;
+    const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
+    tile_load<D, NT>(tr, kbase, vbase, row_stride, kblk * 64, int(L) - 1, tid);
+    if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
+  };
+  if (ntiles > 0) {
+    fetch(0);
+    tile_store<D, NT>(tr, lds, tid);
+    if (n_full == 0) bitmap_store(word, bm[0], tid);
+  }
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    if (j + 1 < ntiles) fetch(j + 1);
+    const uint16_t* cur = lds + (j & 1) * Gm::STAGE;
+    f32x16 s[2];
+    qk_tile<T, D>(s, cur, qb, lane);
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kb][r] = s[kb][r] * a.scale_log2;
+    if (j >= n_full) apply_part_mask(x, bm[j & 1], w, lane);
+    softmax_pv<T, D>(st, x, cur, lane);
+    if (j + 1 < ntiles) {
+      tile_store<D, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
+      if (j + 1 >= n_full) bitmap_store(word, bm[(j + 1) & 1], tid);
+    }
+    __syncthreads();
+  }
+
+  const int64_t orow_idx = (int64_t(b) * L + my_q) * a.Hq + hq;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + orow_idx * D;
+  row_store<T, D>(st, orow, a.lse ? a.lse + orow_idx : nullptr, lane);
+}
+
+// Dense expansion of the two-level mask with the kernel's own predicate:
+// workgroup = 2 waves = one query block row, lanes laid out as in bsr_kernel.
+__global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_indptr,
+                                                         const int32_t* full_kblock,
+                                                         const int32_t* part_indptr,
+                                                         const int32_t* part_kblock,
+                                                         const uint64_t* part_bits, int nblk,
+                                                         uint8_t* dense) {
+  __shared__ __attribute__((aligned(16))) uint8_t bm[512];
+  const int qblk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int64_t L = int64_t(nblk) * 64;
+  const int my_q = qblk * 64 + 32 * w + (lane & 31);
+  uint8_t* drow = dense + my_q * L;
+  for (int64_t e = tid; e < 64 * L; e += 128) dense[int64_t(qblk) * 64 * L + e] = 0;
+  __syncthreads();
+  for (int j = full_indptr[qblk]; j < full_indptr[qblk + 1]; ++j) {
+    const int kb0 = full_kblock[j] * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) drow[kb0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3)] = 1;
+  }
+  for (int j = part_indptr[qblk]; j < part_indptr[qblk + 1]; ++j) {
+    __syncthreads();
+    bitmap_store(tid < 64 ? part_bits[int64_t(j) * 64 + tid] : 0, bm, tid);
+    __syncthreads();
+    float x[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[kb][r] = 0.f;
+    apply_part_mask(x, bm, w, lane);
+    const int kb0 = part_kblock[j] * 64;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        drow[kb0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3)] = x[kb][r] == 0.f ? 1 : 0;
+  }
+}
+
+// ---- launchers -------------------------------------------------------------
+
+template <class T, int D>
+static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
+  const dim3 grid((a.max_q_len + 127) / 128, a.Hq, a.B);
+  if (a.causal) hipLaunchKernelGGL((prefill_kernel<T, D, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  if (a.max_q_len <= 0) return hipSuccess;
+  if (a.dtype == 1) {
+    if (a.D == 64) launch_prefill_t<BF16, 64>(a, st); else launch_prefill_t<BF16, 128>(a, st);
+  } else {
+    if (a.D == 64) launch_prefill_t<F16, 64>(a, st); else launch_prefill_t<F16, 128>(a, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st) {
+  const dim3 grid(a.num_blocks, a.Hq, a.B);
+  if (a.dtype == 1) {
+    if (a.D == 64) hipLaunchKernelGGL((bsr_kernel<BF16, 64>), grid, dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((bsr_kernel<BF16, 128>), grid, dim3(128), 0, st, a);
+  } else {
+    if (a.D == 64) hipLaunchKernelGGL((bsr_kernel<F16, 64>), grid, dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((bsr_kernel<F16, 128>), grid, dim3(128), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bsr_decode(const int32_t* full_indptr, const int32_t* full_kblock,
+                             const int32_t* part_indptr, const int32_t* part_kblock,
+                             const uint64_t* part_bits, int num_blocks, uint8_t* dense,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(bsr_decode_kernel, dim3(num_blocks), dim3(128), 0, st, full_indptr,
+                     full_kblock, part_indptr, part_kblock, part_bits, num_blocks, dense);
+  return hipGetLastError();
+}
+
+}  // namespace rattn

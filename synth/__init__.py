@@ -1,13 +1,19 @@
 """Seeded synthetic inputs shared by the GPU path's tests/bench and the oracle.
 
 This module holds no attention arithmetic: it only draws random tensors,
-request lengths and dense 0/1 masks from a seeded CPU generator.  Both the
+request lengths and dense 0/1 masks from seeded generators.  Both the
 oracle and the GPU library read what it returns; neither is imported here.
 
-Recipe (one ``torch.Generator('cpu')`` per workload, seeded with the
-workload's seed; draws happen in this order): request lengths (ragged decode
-only), then Q, K, V as ``torch.randn(float32)`` rounded to the storage dtype
-with round-to-nearest-even, then the random blocks of the sparse mask.
+Recipe of a named workload (``Workload.make``): two generators seeded with
+the workload's seed.  A CPU ``torch.Generator`` draws the shapes -- the
+request lengths (ragged decode) and then the random blocks of the sparse
+mask.  A generator on the target device draws Q, K, V, in that order, as
+``torch.randn(float32)`` rounded to the storage dtype (round to nearest
+even); on a GPU this takes milliseconds for the largest workloads, which a
+CPU generator needs tens of seconds for.  Values drawn on a GPU and on the
+CPU differ for the same seed; every consumer (GPU path and oracle) reads the
+same drawn tensors.  The small helpers (``decode_inputs`` ...) draw
+everything from one CPU generator.
 
 Workload shapes follow the pages' workloads:
   * grouped-query attention heads shaped like Llama-3-8B (32 query / 8 KV
@@ -131,25 +137,41 @@ class Workload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.D)
 
-    def make(self):
-        """Draw this workload's inputs (deterministic for its seed)."""
-        g = gen(self.seed)
+    def make(self, device="cpu"):
+        """Draw this workload's inputs (deterministic for its seed and device)."""
+        g_shape = gen(self.seed)
+        g_data = torch.Generator(device=device)
+        g_data.manual_seed(int(self.seed))
+
+        def rn(shape):
+            return torch.randn(shape, generator=g_data, device=device,
+                               dtype=torch.float32).to(self.dtype)
+
         if self.kind == "decode":
-            lengths = loguniform_lengths(self.B, *self.ragged, g) if self.ragged else [self.L] * self.B
-            q, k, v, kv = decode_inputs(self.B, self.Hq, self.Hkv, self.D, lengths, self.dtype,
-                                        self.seed, g)
-            return dict(q=q, k=k, v=v, kv_indptr=kv, lengths=lengths)
+            lengths = (loguniform_lengths(self.B, *self.ragged, g_shape) if self.ragged
+                       else [self.L] * self.B)
+            total = sum(lengths)
+            q = rn((self.B, self.Hq, self.D))
+            k = rn((total, self.Hkv, self.D))
+            v = rn((total, self.Hkv, self.D))
+            return dict(q=q, k=k, v=v, kv_indptr=indptr(lengths).to(device), lengths=lengths)
         if self.kind == "prefill":
-            q, k, v, qo, kv = prefill_inputs(self.B, self.L, self.L, self.Hq, self.Hkv, self.D,
-                                             self.dtype, self.seed, g)
-            return dict(q=q, k=k, v=v, qo_indptr=qo, kv_indptr=kv)
+            q = rn((self.B * self.L, self.Hq, self.D))
+            k = rn((self.B * self.L, self.Hkv, self.D))
+            v = rn((self.B * self.L, self.Hkv, self.D))
+            ind = indptr([self.L] * self.B).to(device)
+            return dict(q=q, k=k, v=v, qo_indptr=ind, kv_indptr=ind.clone())
         if self.kind == "bsr":
-            q = randn((self.B, self.L, self.Hq, self.D), self.dtype, g)
-            k = randn((self.B, self.L, self.Hkv, self.D), self.dtype, g)
-            v = randn((self.B, self.L, self.Hkv, self.D), self.dtype, g)
-            mask = sparse_mask(self.L, g, **self.extra)
+            mask = self.mask(g_shape)
+            q = rn((self.B, self.L, self.Hq, self.D))
+            k = rn((self.B, self.L, self.Hkv, self.D))
+            v = rn((self.B, self.L, self.Hkv, self.D))
             return dict(q=q, k=k, v=v, mask=mask)
         raise ValueError(self.kind)
+
+    def mask(self, g_shape=None) -> torch.Tensor:
+        """The workload's dense 0/1 mask (CPU uint8), drawn from the shape generator."""
+        return sparse_mask(self.L, g_shape if g_shape is not None else gen(self.seed), **self.extra)
 
 
 WORKLOADS = {

@@ -1,0 +1,216 @@
+"""Host-side tests of the C ABI (no GPU needed, no compute call is made).
+
+* libattn.so loads and exports every function include/attn.h declares;
+* every argument check returns its status before any device work;
+* the split-count rule and workspace size follow their stated formulas;
+* the host BSR encoder is canonical and decodes back to the dense mask
+  (decoded here by the bit layout the header states, not by library code).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from reduction_attention_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from reduction_attention_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    from reduction_attention_amd import _lib
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.attn_status_string(code).decode().startswith("ATTN_")
+
+
+def test_workspace_formula(lib):
+    for B, Hq, D, s in [(16, 32, 128, 8), (1, 4, 64, 4), (64, 64, 128, 16)]:
+        raw = s * B * Hq * (D + 2) * 4
+        assert lib.attn_decode_workspace_bytes(B, Hq, D, s) == (raw + 255) // 256 * 256
+    assert lib.attn_decode_workspace_bytes(1, 4, 64, 0) == 0
+    assert lib.attn_decode_workspace_bytes(1, 4, 64, 257) == 0
+
+
+def test_split_rule(lib):
+    # no device here: the CU count falls back to 256, so the target is 1024 workgroups
+    assert lib.attn_device_cu_count() == 256
+    # Llama-3-8B-shaped decode: 16 requests x 4096 keys, 8 KV heads -> c = 512, s = 8
+    assert lib.attn_decode_choose_splits(16, 32, 8, 128, 16 * 4096, 4096) == 8
+    assert lib.attn_decode_choose_splits(1, 4, 1, 64, 256, 256) == 1
+    # s never exceeds 256 and never drops below 1
+    assert lib.attn_decode_choose_splits(1, 8, 1, 128, 1 << 26, 1 << 26) <= 256
+    assert lib.attn_decode_choose_splits(4, 8, 8, 128, 10, 5) == 1
+
+
+P = ctypes.c_void_p(16)  # a non-null, aligned placeholder: never dereferenced on error paths
+
+
+def decode_call(lib, **kw):
+    a = dict(q=P, k=P, v=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, maxlen=100,
+             total=150, scale=0.1, s=2, dt=1, ws=P, wsb=1 << 20, st=None)
+    a.update(kw)
+    return lib.attn_decode_splitkv(a["q"], a["k"], a["v"], a["kv"], a["o"], a["lse"], a["B"],
+                                   a["Hq"], a["Hkv"], a["D"], a["maxlen"], a["total"], a["scale"],
+                                   a["s"], a["dt"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(B=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(Hq=34, Hkv=2), 2), (dict(D=96), 2), (dict(dt=7), 2), (dict(maxlen=-1), 1),
+    (dict(maxlen=200, total=150), 1), (dict(scale=float("inf")), 1), (dict(s=-1), 1),
+    (dict(s=257), 1), (dict(ws=None), 3), (dict(wsb=100), 3), (dict(q=ctypes.c_void_p(18)), 1),
+])
+def test_decode_validation(lib, kw, status):
+    assert decode_call(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def prefill_call(lib, **kw):
+    a = dict(q=P, k=P, v=P, qo=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, mq=64, mk=64,
+             scale=0.1, causal=1, dt=1, st=None)
+    a.update(kw)
+    return lib.attn_prefill(a["q"], a["k"], a["v"], a["qo"], a["kv"], a["o"], a["lse"], a["B"],
+                            a["Hq"], a["Hkv"], a["D"], a["mq"], a["mk"], a["scale"], a["causal"],
+                            a["dt"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(qo=None), 1), (dict(Hq=5, Hkv=2), 1), (dict(D=32), 2),
+    (dict(dt=0), 2), (dict(causal=2), 1), (dict(mq=-3), 1), (dict(scale=float("nan")), 1),
+    (dict(k=ctypes.c_void_p(24)), 1), (dict(B=70000), 2),
+])
+def test_prefill_validation(lib, kw, status):
+    assert prefill_call(lib, **kw) == status
+
+
+def test_merge_validation(lib):
+    f = lib.attn_merge_lse
+    assert f(None, P, P, 2, 4, 128, P, 1, None, None) == 1
+    assert f(P, P, P, 0, 4, 128, P, 1, None, None) == 1
+    assert f(P, P, P, 2, -1, 128, P, 1, None, None) == 1
+    assert f(P, P, P, 2, 4, 80, P, 1, None, None) == 2
+    assert f(P, P, P, 2, 4, 128, P, 9, None, None) == 2
+
+
+def test_bsr_validation(lib):
+    from reduction_attention_amd._lib import AttnBsrMask
+    m = AttnBsrMask(256, 4, 0, 0, 16, 0, 16, 0, 0)
+    f = lib.attn_prefill_bsr
+    bad = AttnBsrMask(250, 4, 0, 0, 16, 0, 16, 0, 0)
+    assert f(P, P, P, ctypes.byref(bad), P, None, 1, 250, 2, 2, 64, 0.1, 2, None) == 1
+    assert f(P, P, P, ctypes.byref(m), P, None, 1, 512, 2, 2, 64, 0.1, 2, None) == 1  # L != seq_len
+    assert f(P, P, P, ctypes.byref(m), P, None, 1, 256, 2, 2, 64, 0.1, 0, None) == 2  # fp32
+    assert f(P, P, P, ctypes.byref(m), P, None, 1, 256, 3, 2, 64, 0.1, 2, None) == 1
+    nobits = AttnBsrMask(256, 4, 0, 3, 16, 0, 16, 16, 0)
+    assert f(P, P, P, ctypes.byref(nobits), P, None, 1, 256, 2, 2, 64, 0.1, 2, None) == 1
+    assert lib.attn_debug_bsr_decode(ctypes.byref(bad), P, None) == 1
+    assert lib.attn_debug_split_ranges(P, 2, 10, 0, P, None) == 1
+
+
+# ---- host BSR encoder -------------------------------------------------------
+
+def decode_by_definition(bm, L):
+    """Dense mask from the two-level form, by the layout the header states."""
+    nb = L // 64
+    out = torch.zeros((L, L), dtype=torch.uint8)
+    fi, fk = bm.full_indptr.tolist(), bm.full_kblock.tolist()
+    pi, pk = bm.part_indptr.tolist(), bm.part_kblock.tolist()
+    words = bm.part_bits.tolist()
+    for qb in range(nb):
+        for j in range(fi[qb], fi[qb + 1]):
+            out[qb * 64:(qb + 1) * 64, fk[j] * 64:(fk[j] + 1) * 64] = 1
+        for j in range(pi[qb], pi[qb + 1]):
+            for ir in range(8):
+                for ic in range(8):
+                    w = words[j * 64 + ir * 8 + ic] & ((1 << 64) - 1)
+                    for bit in range(64):
+                        if (w >> bit) & 1:
+                            r, c = divmod(bit, 8)
+                            out[qb * 64 + ir * 8 + r, pk[j] * 64 + ic * 8 + c] = 1
+    return out
+
+
+def check_canonical(bm, dense):
+    L = dense.shape[0]
+    nb = L // 64
+    blocks = dense.view(nb, 64, nb, 64).permute(0, 2, 1, 3).reshape(nb, nb, 4096).sum(-1)
+    fi, fk = bm.full_indptr.tolist(), bm.full_kblock.tolist()
+    pi, pk = bm.part_indptr.tolist(), bm.part_kblock.tolist()
+    for qb in range(nb):
+        full = fk[fi[qb]:fi[qb + 1]]
+        part = pk[pi[qb]:pi[qb + 1]]
+        assert full == sorted(full) and part == sorted(part)
+        assert full == [kb for kb in range(nb) if blocks[qb, kb] == 4096]
+        assert part == [kb for kb in range(nb) if 0 < blocks[qb, kb] < 4096]
+
+
+@pytest.mark.parametrize("kind", ["ones", "zeros", "causal", "window", "sparse", "random"])
+def test_encoder_roundtrip(lib, kind):
+    import reduction_attention_amd as ra
+    L = 192
+    if kind == "ones":
+        dense = torch.ones(L, L, dtype=torch.uint8)
+    elif kind == "zeros":
+        dense = torch.zeros(L, L, dtype=torch.uint8)
+    elif kind == "causal":
+        dense = torch.ones(L, L, dtype=torch.uint8).tril()
+    elif kind == "window":
+        dense = synth.window_mask(L, 70)
+    elif kind == "sparse":
+        dense = synth.sparse_mask(L, synth.gen(3), window=64, block=64, globals_per_block=2,
+                                  random_blocks=1)
+    else:
+        dense = (torch.rand(L, L, generator=synth.gen(4)) < 0.3).to(torch.uint8)
+        dense[:, 64:128] = 0
+    bm = ra.attn_bsr_encode_host(dense)
+    assert torch.equal(decode_by_definition(bm, L), dense)
+    check_canonical(bm, dense)
+    if kind == "ones":
+        assert bm.nnz_part == 0 and bm.nnz_full == 9
+    if kind == "zeros":
+        assert bm.nnz_part == 0 and bm.nnz_full == 0
+    if kind == "causal":
+        assert bm.nnz_full == 3 and bm.nnz_part == 3  # below diagonal full, diagonal part
+
+
+def test_encoder_rejects_bad_sizes(lib):
+    d = torch.ones(100, 100, dtype=torch.uint8)
+    nf, np_ = ctypes.c_int(0), ctypes.c_int(0)
+    assert lib.attn_bsr_encode_host(ctypes.c_void_p(d.data_ptr()), 100, None, None, None, None,
+                                    None, ctypes.byref(nf), ctypes.byref(np_)) == 1
+
+
+def test_workload_mask_statistics(lib):
+    """The sparse-prefill workload's mask at L = 4096: density and tile counts."""
+    import reduction_attention_amd as ra
+    w = synth.workload("bsr_prefill_fp16")
+    mask = w.mask()
+    bm = ra.attn_bsr_encode_host(mask)
+    density = mask.float().mean().item()
+    assert 0.15 < density < 0.25
+    assert bm.nnz_full + bm.nnz_part == 64 * 64  # every outer tile holds a global token

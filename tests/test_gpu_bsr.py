@@ -1,0 +1,120 @@
+"""GPU parity of block-sparse prefill (BSR outer tiles + 8x8 bitmaps)."""
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, TOL_O, check
+
+pytestmark = pytest.mark.gpu
+
+
+def ra():
+    import reduction_attention_amd
+    return reduction_attention_amd
+
+
+def bsr(q, k, v, dense):
+    m = ra().attn_bsr_encode_host(dense).to(DEV)
+    o, lse = ra().attn_prefill_bsr(q.to(DEV), k.to(DEV), v.to(DEV), m)
+    torch.cuda.synchronize()
+    return o, lse, m
+
+
+def qkv(B, L, Hq, Hkv, D, dtype, seed):
+    g = synth.gen(seed)
+    return (synth.randn((B, L, Hq, D), dtype, g), synth.randn((B, L, Hkv, D), dtype, g),
+            synth.randn((B, L, Hkv, D), dtype, g))
+
+
+def oracle_bsr(q, k, v, dense, scale):
+    B, L = q.shape[:2]
+    outs, lses = [], []
+    for b in range(B):
+        o, lse = oracle.attention(q[b], k[b], v[b], [0, L], [0, L], scale, oracle.MASK_DENSE, dense)
+        outs.append(o)
+        lses.append(lse)
+    return torch.stack(outs), torch.stack(lses)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["sparse", "window", "random", "causal"])
+def test_small_masks(dtype, D, kind):
+    L, B, Hq, Hkv = 384, 2, 4, 2
+    if kind == "sparse":
+        dense = synth.sparse_mask(L, synth.gen(31), window=96, block=64, globals_per_block=2,
+                                  random_blocks=1)
+    elif kind == "window":
+        dense = synth.window_mask(L, 100)
+    elif kind == "random":
+        dense = (torch.rand(L, L, generator=synth.gen(32)) < 0.2).to(torch.uint8)
+        dense[:, 128:256] = 0
+        dense[70] = 0  # a query row with no valid key
+    else:
+        dense = torch.ones(L, L, dtype=torch.uint8).tril()
+    q, k, v = qkv(B, L, Hq, Hkv, D, dtype, 33 + D)
+    o_ref, lse_ref = oracle_bsr(q, k, v, dense, 1 / D ** 0.5)
+    o, lse, _ = bsr(q, k, v, dense)
+    check(f"bsr {dtype} D={D} {kind}", o, o_ref, lse, lse_ref, dtype)
+
+
+def test_workload_sampled():
+    """B 1, L 4096, 16 heads, D 64, fp16; window 256 + 2 globals/64 + 6 random blocks."""
+    w = synth.workload("bsr_prefill_fp16")
+    inp = w.make(DEV)
+    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"])
+    print(f"mask density={inp['mask'].float().mean().item():.4f} full={m.nnz_full} "
+          f"part={m.nnz_part}", flush=True)
+    g = synth.gen(77)
+    n = 4000
+    t = torch.randint(0, w.L, (n,), generator=g)
+    h = torch.randint(0, w.Hq, (n,), generator=g)
+    rows = torch.stack([t, h], 1)
+    o_ref, lse_ref = oracle.attention(inp["q"][0], inp["k"][0], inp["v"][0], [0, w.L], [0, w.L],
+                                      w.scale, oracle.MASK_DENSE, inp["mask"], rows=rows)
+    check("bsr 4096 sampled", o[0][t.to(DEV), h.to(DEV)], o_ref, lse[0][t.to(DEV), h.to(DEV)],
+          lse_ref, torch.float16)
+    assert bool(torch.isfinite(o).all())
+
+
+def test_unstored_tiles_never_read():
+    """NaN in K/V of every key block no query row may see leaves the output bit-identical."""
+    L, D = 512, 64
+    dense = synth.window_mask(L, 100)
+    dense[:, 192:256] = 0  # key block 3 is empty in every row
+    q, k, v = qkv(1, L, 2, 2, D, torch.float16, 41)
+    o1, l1, m = bsr(q, k, v, dense)
+    k2, v2 = k.clone(), v.clone()
+    # poison key block 3, which no query block row stores
+    k2[:, 192:256] = float("nan")
+    v2[:, 192:256] = float("nan")
+    o2, l2, _ = bsr(q, k2, v2, dense)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_causal_mask_equals_causal_prefill():
+    L, Hq, Hkv, D = 512, 4, 2, 128
+    q, k, v = qkv(1, L, Hq, Hkv, D, torch.bfloat16, 42)
+    dense = torch.ones(L, L, dtype=torch.uint8).tril()
+    o_b, lse_b, _ = bsr(q, k, v, dense)
+    ind = synth.indptr([L]).to(DEV)
+    o_p, lse_p = ra().attn_prefill(q[0].to(DEV), k[0].to(DEV), v[0].to(DEV), ind, ind, L, L,
+                                   causal=True)
+    torch.cuda.synchronize()
+    assert (o_b[0].float() - o_p.float()).abs().max().item() <= 2 * TOL_O[torch.bfloat16]
+    assert (lse_b[0] - lse_p).abs().max().item() <= 2e-3
+
+
+@pytest.mark.parametrize("kind", ["sparse", "random", "workload"])
+def test_device_decode_bit_exact(kind):
+    if kind == "workload":
+        dense = synth.workload("bsr_prefill_fp16").mask()
+    elif kind == "sparse":
+        dense = synth.sparse_mask(512, synth.gen(51), window=100, block=64, globals_per_block=2,
+                                  random_blocks=2)
+    else:
+        dense = (torch.rand(256, 256, generator=synth.gen(52)) < 0.5).to(torch.uint8)
+    m = ra().attn_bsr_encode_host(dense).to(DEV)
+    got = ra().attn_debug_bsr_decode(m).cpu()
+    assert torch.equal(got, dense)

@@ -1,0 +1,147 @@
+"""GPU parity of split-KV decode and the LSE merge against the fp64 oracle."""
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, TOL_O, check, report
+
+pytestmark = pytest.mark.gpu
+
+
+def ra():
+    import reduction_attention_amd
+    return reduction_attention_amd
+
+
+def run_decode(w_inputs, max_len, s, **kw):
+    q, k, v, kv = (w_inputs[x].to(DEV) for x in ("q", "k", "v", "kv_indptr"))
+    o, lse = ra().attn_decode_splitkv(q, k, v, kv, max_len, num_splits=s, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def oracle_decode(inp, scale):
+    B = inp["q"].shape[0]
+    return oracle.attention(inp["q"], inp["k"], inp["v"], list(range(B + 1)), inp["kv_indptr"],
+                            scale)
+
+
+def test_tiny_fp32_split_counts_agree():
+    """Tiny GQA decode, fp32: 4 query heads on 1 KV head, D 64, 256 keys, s in {1, 2, 4}."""
+    w = synth.workload("tiny_decode_fp32")
+    inp = w.make()
+    o_ref, lse_ref = oracle_decode(inp, w.scale)
+    outs = []
+    for s in w.splits:
+        o, lse = run_decode(inp, w.L, s)
+        check(f"tiny fp32 s={s}", o, o_ref, lse, lse_ref, torch.float32)
+        outs.append(o.double().cpu())
+    for a in outs[1:]:
+        assert (a - outs[0]).abs().max().item() <= 2 * TOL_O[torch.float32]
+
+
+def test_llama3_8b_decode_full_parity():
+    """B 16, 32/8 heads, D 128, 4096 keys each, bf16, automatic s (every row checked)."""
+    w = synth.workload("llama3_8b_decode_bf16")
+    inp = w.make(DEV)
+    o_ref, lse_ref = oracle_decode(inp, w.scale)
+    s_auto = ra().attn_decode_choose_splits(w.B, w.Hq, w.Hkv, w.D, w.B * w.L, w.L)
+    print(f"automatic split count s={s_auto}", flush=True)
+    o, lse = run_decode(inp, w.L, 0)
+    check("llama3-8b decode auto-s", o, o_ref, lse, lse_ref, torch.bfloat16)
+    o1, lse1 = run_decode(inp, w.L, 1)
+    check("llama3-8b decode s=1", o1, o_ref, lse1, lse_ref, torch.bfloat16)
+
+
+def test_ragged_serving_decode_full_parity():
+    """64 requests, 64/8 heads, D 128, log-uniform lengths in [128, 32768], bf16."""
+    w = synth.workload("ragged_decode_bf16")
+    inp = w.make(DEV)
+    lengths = inp["lengths"]
+    print(f"ragged lengths: total={sum(lengths)} min={min(lengths)} max={max(lengths)}", flush=True)
+    o_ref, lse_ref = oracle_decode(inp, w.scale)
+    o, lse = run_decode(inp, max(lengths), 0)
+    check("ragged decode auto-s", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+def test_small_ragged_shapes(dtype, D, G):
+    lengths = [1, 31, 32, 33, 0, 300, 64, 517]
+    Hkv = 2
+    q, k, v, kv = synth.decode_inputs(len(lengths), G * Hkv, Hkv, D, lengths, dtype, seed=D + G)
+    inp = dict(q=q, k=k, v=v, kv_indptr=kv)
+    scale = 1.0 / D ** 0.5
+    o_ref, lse_ref = oracle_decode(inp, scale)
+    for s in (1, 3, 8, 64):
+        o, lse = run_decode(inp, max(lengths), s)
+        check(f"decode {dtype} D={D} G={G} s={s}", o, o_ref, lse, lse_ref, dtype)
+    # the empty request: O = 0, LSE = -inf
+    assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[4]).all())
+
+
+def test_split_ranges_bit_exact():
+    import reduction_attention_amd as r
+    lengths = [1, 31, 32, 33, 0, 300, 4096, 517, 7]
+    kv = synth.indptr(lengths)
+    for s in (1, 2, 3, 8, 17, 256):
+        got = r.attn_debug_split_ranges(kv.to(DEV), max(lengths), s).cpu().to(torch.int64)
+        want = oracle.split_ranges(kv, max(lengths), s)
+        assert torch.equal(got, want), s
+
+
+def test_merge_kernel_matches_oracle_merge():
+    s, rows, D = 6, 50, 128
+    g = synth.gen(11)
+    op = torch.randn((s, rows, D), generator=g)
+    mp = torch.randn((s, rows), generator=g) * 4
+    lp = torch.rand((s, rows), generator=g) * 10 + 0.01
+    # unused partials: m = -inf, l = 0, o = NaN (must not be read)
+    lp[2, :10] = 0
+    mp[2, :10] = float("-inf")
+    op[2, :10] = float("nan")
+    lp[:, 20] = 0
+    mp[:, 20] = float("-inf")  # a row with no partial at all
+    o_ref, lse_ref = oracle.merge(op, mp, lp)
+    for dt in (torch.float32, torch.bfloat16):
+        o, lse = ra().attn_merge_lse(op.to(DEV), mp.to(DEV), lp.to(DEV), o_dtype=dt)
+        torch.cuda.synchronize()
+        check(f"merge -> {dt}", o, o_ref, lse, lse_ref, dt)
+
+
+def test_constant_keys_give_mean_of_v():
+    lengths = [200, 1000]
+    q, k, v, kv = synth.decode_inputs(2, 8, 2, 128, lengths, torch.bfloat16, seed=12)
+    k[:] = k[0:1]  # one key vector everywhere (per KV head)
+    o, lse = run_decode(dict(q=q, k=k, v=v, kv_indptr=kv), 1000, 4)
+    for b, (lo, hi) in enumerate([(0, 200), (200, 1200)]):
+        mean_v = v[lo:hi].double().mean(0)  # [Hkv, D]
+        want = mean_v.repeat_interleave(4, dim=0)
+        assert (o[b].double().cpu() - want).abs().max().item() <= TOL_O[torch.bfloat16]
+
+
+def test_two_runs_bit_identical():
+    w = synth.workload("llama3_8b_decode_bf16")
+    inp = w.make(DEV)
+    o1, l1 = run_decode(inp, w.L, 8)
+    o2, l2 = run_decode(inp, w.L, 8)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_outputs_only_where_expected():
+    """NaN canaries around o and lse stay untouched."""
+    lengths = [100, 40]
+    q, k, v, kv = synth.decode_inputs(2, 8, 2, 128, lengths, torch.bfloat16, seed=13)
+    o_buf = torch.full((3 * 2 * 8 * 128,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    l_buf = torch.full((3 * 16,), float("nan"), dtype=torch.float32, device=DEV)
+    o = o_buf[2 * 8 * 128: 2 * 2 * 8 * 128].view(2, 8, 128)
+    lse = l_buf[16:32].view(2, 8)
+    ra().attn_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV), 100, num_splits=3,
+                             o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(o_buf[:2048]).all()) and bool(torch.isnan(o_buf[4096:]).all())
+    assert bool(torch.isnan(l_buf[:16]).all()) and bool(torch.isnan(l_buf[32:]).all())
+    o_ref, lse_ref = oracle_decode(dict(q=q, k=k, v=v, kv_indptr=kv), 1 / 128 ** 0.5)
+    report("canary decode", o, o_ref, lse, lse_ref)
