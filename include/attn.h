@@ -81,10 +81,11 @@ int attn_device_cu_count(void);
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
 /* The split count s the library picks when num_splits = 0: the largest chunk
- * c (a power of two, at least 256 keys) that still yields about four
- * workgroups per compute unit, then s = ceil(max_kv_len / c), clamped to
- * [1, 256].  [CA] leaves the concrete s to the scheduler; this is that
- * scheduler's rule. */
+ * c (a power of two, at least 256 keys) whose estimated workgroup count
+ * Hkv * (total_kv / c + B / 2) still reaches two workgroups per compute unit
+ * (four when request lengths differ), then s = ceil(max_kv_len / c), clamped
+ * to [1, 256].  [CA] leaves the concrete s to the scheduler; this is that
+ * scheduler's rule, fitted to measured sweeps on MI355X. */
 int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
                               int max_kv_len);
 
@@ -108,7 +109,11 @@ int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
  *   A request with n_b = 0 yields O = 0, LSE = -inf.
  * workspace   device memory of at least attn_decode_workspace_bytes(B, Hq, D, s)
  *   bytes; its contents on entry do not matter.  Layout: o_part [s, B*Hq, D],
- *   then m_part [s, B*Hq], then l_part [s, B*Hq], all fp32.
+ *   then m_part [s, B*Hq], then l_part [s, B*Hq], all fp32.  Calls that share
+ *   one workspace must not overlap in time.
+ * Two kernels are enqueued: the Split partials (a request held by a single
+ * chunk is written to o / lse directly), then the merge of the requests
+ * that span several chunks.
  * Supported: dtype ATTN_F32 (VALU path) or ATTN_BF16 / ATTN_F16 (MFMA
  * path); D in {64, 128}; 1 <= G <= 16.
  */
@@ -117,6 +122,24 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
                                   int Hq, int Hkv, int D, int max_kv_len, long long total_kv,
                                   float scale, int num_splits, int dtype, void* workspace,
                                   size_t workspace_bytes, void* hip_stream);
+
+/*
+ * The Split partials alone [CA "Split演算子によるSplit-Kの対応"]: the first
+ * kernel of attn_decode_splitkv, writing every split's partial instead of
+ * finishing single-split requests.  For a request b and split i < ceil(n_b /
+ * c) it writes o_part[i, b*Hq + h, :] (normalised by its own sum), m_part
+ * (max scaled score, natural-log units) and l_part (sum of exp(score - m));
+ * splits a request does not use get m = -inf, l = 0.  attn_merge_lse turns
+ * the partials into the output, so partials computed over different key
+ * ranges (other calls, other devices) can be merged together.
+ * Arguments as attn_decode_splitkv, with num_splits >= 1 required;
+ * o_part [num_splits, B*Hq, D], m_part, l_part [num_splits, B*Hq] fp32.
+ */
+attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
+                                   const int32_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                                   int max_kv_len, long long total_kv, float scale, int num_splits,
+                                   int dtype, float* o_part, float* m_part, float* l_part,
+                                   void* hip_stream);
 
 /*
  * Merge of Split partials [CA "Split演算子によるSplit-Kの対応"]: for each row r,

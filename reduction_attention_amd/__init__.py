@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     attn_debug_bsr_decode,
     attn_debug_split_ranges,
     attn_decode_choose_splits,
+    attn_decode_partials,
     attn_decode_splitkv,
     attn_decode_workspace_bytes,
     attn_device_cu_count,

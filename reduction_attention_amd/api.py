@@ -83,6 +83,25 @@ def attn_decode_splitkv(q, k, v, kv_indptr, max_kv_len, scale=None, num_splits=0
     return o, lse
 
 
+def attn_decode_partials(q, k, v, kv_indptr, max_kv_len, num_splits, scale=None, o_part=None,
+                         m_part=None, l_part=None, stream=None):
+    """Split partials only: (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) fp32."""
+    _dev(q, k, v, kv_indptr, o_part, m_part, l_part)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    s = int(num_splits)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    o_part = torch.empty((s, B * Hq, D), **f32) if o_part is None else o_part
+    m_part = torch.empty((s, B * Hq), **f32) if m_part is None else m_part
+    l_part = torch.empty((s, B * Hq), **f32) if l_part is None else l_part
+    st = load().attn_decode_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), B, Hq, Hkv, D,
+                                     int(max_kv_len), int(k.shape[0]), scale, s, _dtype_code(q),
+                                     _ptr(o_part), _ptr(m_part), _ptr(l_part), _stream(stream))
+    check(st, "attn_decode_partials")
+    return o_part, m_part, l_part
+
+
 def decode_workspace_views(workspace: torch.Tensor, B: int, Hq: int, D: int, s: int):
     """Views (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) of a decode workspace."""
     rows = B * Hq

@@ -79,6 +79,7 @@ int attn_device_cu_count(void) {
   return cus;
 }
 
+// Workspace layout: o_part [s, B*Hq, D], m_part [s, B*Hq], l_part [s, B*Hq] (fp32).
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   if (B <= 0 || Hq <= 0 || D <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
   const size_t rows = size_t(B) * size_t(Hq);
@@ -90,7 +91,11 @@ int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
   (void)Hq;
   (void)D;
   if (B <= 0 || Hkv <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
-  const long long target = 4LL * attn_device_cu_count();  // workgroups to aim for
+  // Workgroups to aim for: two per compute unit when every request has the
+  // same length (equal chunks finish together), four when lengths differ
+  // (more, smaller chunks even out the uneven last chunks).
+  const bool uniform = (long long)max_kv_len * B == total_kv;
+  const long long target = (uniform ? 2LL : 4LL) * attn_device_cu_count();
   long long c = 1;
   while (c < max_kv_len) c <<= 1;  // one split per request at most
   // largest power-of-two chunk >= 256 whose estimated workgroup count reaches target
@@ -119,12 +124,11 @@ attn_status_t attn_merge_lse(const float* o_part, const float* m_part, const flo
   return hip_status(rattn::launch_merge(a, static_cast<hipStream_t>(hip_stream)), "merge launch");
 }
 
-attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
-                                  const int32_t* kv_indptr, void* o, float* lse, int B, int Hq,
-                                  int Hkv, int D, int max_kv_len, long long total_kv, float scale,
-                                  int num_splits, int dtype, void* workspace,
-                                  size_t workspace_bytes, void* hip_stream) {
-  if (!q || !k || !v || !kv_indptr || !o) return fail(ATTN_EINVAL, "decode: null pointer");
+static attn_status_t check_decode(const void* q, const void* k, const void* v,
+                                  const int32_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                                  int max_kv_len, long long total_kv, float scale, int num_splits,
+                                  int dtype) {
+  if (!q || !k || !v || !kv_indptr) return fail(ATTN_EINVAL, "decode: null pointer");
   if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "decode: B, Hq, Hkv must be >= 1");
   if (B > 65535 || Hkv > 65535) return fail(ATTN_EUNSUPPORTED, "decode: B or Hkv above 65535");
   if (Hq % Hkv) return fail(ATTN_EINVAL, "decode: Hq %d not a multiple of Hkv %d", Hq, Hkv);
@@ -139,8 +143,21 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
   if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "decode: scale is not finite");
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(ATTN_EINVAL, "decode: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
-    return fail(ATTN_EINVAL, "decode: q, k, v, o must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(ATTN_EINVAL, "decode: q, k, v must be 16-byte aligned");
+  return ATTN_OK;
+}
+
+attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
+                                  const int32_t* kv_indptr, void* o, float* lse, int B, int Hq,
+                                  int Hkv, int D, int max_kv_len, long long total_kv, float scale,
+                                  int num_splits, int dtype, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+  attn_status_t cs = check_decode(q, k, v, kv_indptr, B, Hq, Hkv, D, max_kv_len, total_kv, scale,
+                                  num_splits, dtype);
+  if (cs != ATTN_OK) return cs;
+  if (!o) return fail(ATTN_EINVAL, "decode: null output");
+  if (!aligned16(o)) return fail(ATTN_EINVAL, "decode: o must be 16-byte aligned");
   const int s = num_splits ? num_splits
                            : attn_decode_choose_splits(B, Hq, Hkv, D, total_kv, max_kv_len);
   const size_t need = attn_decode_workspace_bytes(B, Hq, D, s);
@@ -152,14 +169,27 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
   const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
   const size_t rows = size_t(B) * Hq;
   float* ws = static_cast<float*>(workspace);
-  rattn::DecodeArgs a{q, k, v, kv_indptr, ws, ws + size_t(s) * rows * D,
+  rattn::DecodeArgs a{q, k, v, kv_indptr, o, lse, ws, ws + size_t(s) * rows * D,
                       ws + size_t(s) * rows * D + size_t(s) * rows,
-                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype};
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = rattn::launch_decode_partial(a, st);
-  if (e != hipSuccess) return hip_status(e, "decode partial launch");
-  rattn::MergeArgs m{a.o_part, a.m_part, a.l_part, s, int(rows), D, o, dtype, lse};
-  return hip_status(rattn::launch_merge(m, st), "decode merge launch");
+                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype, 0};
+  return hip_status(rattn::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+}
+
+attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
+                                   const int32_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                                   int max_kv_len, long long total_kv, float scale, int num_splits,
+                                   int dtype, float* o_part, float* m_part, float* l_part,
+                                   void* hip_stream) {
+  attn_status_t cs = check_decode(q, k, v, kv_indptr, B, Hq, Hkv, D, max_kv_len, total_kv, scale,
+                                  num_splits, dtype);
+  if (cs != ATTN_OK) return cs;
+  if (num_splits < 1) return fail(ATTN_EINVAL, "decode_partials: num_splits must be >= 1");
+  if (!o_part || !m_part || !l_part) return fail(ATTN_EINVAL, "decode_partials: null output");
+  const int chunk = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 0;
+  rattn::DecodeArgs a{q, k, v, kv_indptr, nullptr, nullptr, o_part, m_part, l_part,
+                      B, Hq, Hkv, D, Hq / Hkv, num_splits, chunk, scale * kLog2e, dtype, 1};
+  return hip_status(rattn::launch_decode_partials(a, static_cast<hipStream_t>(hip_stream)),
+                    "decode_partials launch");
 }
 
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, const int32_t* qo_indptr,

@@ -44,9 +44,10 @@ __device__ __forceinline__ SplitRange split_range(const int32_t* kv_indptr, int 
 // Per wave step the scores of 32 keys against the (up to 16, zero padded)
 // query heads are S^T = K Q^T: two 16x16x32 MFMA tiles of 16 keys, the
 // head-dimension contraction split into D/32 slabs.  Lane l = (c16, h4)
-// (c16 = l % 16, h4 = l / 16) loads K row (key 16a + c16) at dims
-// (D/4)*h4 .. +D/4: contiguous, 4 lanes per 256-byte row.  The accumulator
-// gives lane l head c16 and keys 16a + 4*h4 + r.
+// (c16 = l % 16, h4 = l / 16) feeds slab u with dims 32u + 8*h4 .. +8 of K
+// row (key 16a + c16), so the four lanes of a row read 64 contiguous bytes
+// per load instruction.  The accumulator gives lane l head c16 and keys
+// 16a + 4*h4 + r.
 // The value update is O^T += V^T P^T with 16x16x32 MFMAs: the reduction
 // slots of lane (c16, h4) are the keys it already holds scores for,
 // kappa(h4, i) = 16*(i/4) + 4*h4 + i%4, so P^T needs no lane exchange;
@@ -73,9 +74,9 @@ __device__ __forceinline__ void decode_load(DecodeTile<T, D>& t, const uint16_t*
   for (int a = 0; a < 2; ++a) {
     int key = key0 + 16 * a + c16;
     key = key < hi ? key : hi - 1;
-    const uint16_t* p = kbase + int64_t(key) * row_stride + (D / 4) * h4;
+    const uint16_t* p = kbase + int64_t(key) * row_stride + 8 * h4;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) t.k[a][u] = ldg128(p + 8 * u);
+    for (int u = 0; u < NU; ++u) t.k[a][u] = ldg128(p + 32 * u);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -153,16 +154,25 @@ __device__ __forceinline__ void decode_step(DecodeState<T, D>& st, const DecodeT
 }
 
 template <class T, int D, int W>
-__global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args) {
-  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(64 * W, 3) void decode_partial_mfma(DecodeArgs args) {
+  // grid (Hkv, s, B): the KV heads of one chunk are consecutive workgroups,
+  // so the Hkv slices of each packed K/V row are streamed at about the same
+  // time rather than one head's 256-byte slice at a time per row.
+  const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
   const int G = args.G, Hq = args.Hq;
   const int64_t rows = int64_t(args.B) * Hq;
   const SplitRange sr = split_range(args.kv_indptr, b, i, args.chunk);
   const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
   if (sr.lo >= sr.hi) {  // split unused by this request
-    if (threadIdx.x < G) {
-      args.m_part[int64_t(i) * rows + row0 + threadIdx.x] = -INFINITY;
-      args.l_part[int64_t(i) * rows + row0 + threadIdx.x] = 0.f;
+    if (args.partials_only) {
+      if (threadIdx.x < G) {
+        args.m_part[int64_t(i) * rows + row0 + threadIdx.x] = -INFINITY;
+        args.l_part[int64_t(i) * rows + row0 + threadIdx.x] = 0.f;
+      }
+    } else if (i == 0) {    // empty request: O = 0, LSE = -inf
+      typename T::elem* o = static_cast<typename T::elem*>(args.o);
+      for (int e = threadIdx.x; e < G * D; e += 64 * W) o[row0 * D + e] = typename T::elem(0.f);
+      if (args.lse && threadIdx.x < G) args.lse[row0 + threadIdx.x] = -INFINITY;
     }
     return;
   }
@@ -175,14 +185,14 @@ __global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args
                           int64_t(g) * D;
   const int n = sr.hi - sr.lo;
 
-  // Q^T operand: head c16 (zero past G), dims (D/4)*h4 + 8u .. +8
+  // Q^T operand: head c16 (zero past G), slab u -> dims 32u + 8*h4 .. +8
   u32x4 qb[D / 32];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(args.q) + (row0 + (c16 < G ? c16 : 0)) * D +
-                         (D / 4) * h4;
+                         8 * h4;
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
-      qb[u] = ldg128(qp + 8 * u);
+      qb[u] = ldg128(qp + 32 * u);
       if (c16 >= G) qb[u] = u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -193,20 +203,18 @@ __global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // wave w takes 32-key steps w, w + W, w + 2W, ...; two register buffers
-  // keep the next step's loads in flight while the current one computes.
+  // wave w takes 32-key steps w, w + W, w + 2W, ...  Each step's loads are
+  // consumed in issue order; the latency of one wave's loads is covered by
+  // the other waves resident on the same SIMD (the kernel is sized for three
+  // workgroups per compute unit), not by a software prefetch, which would
+  // need a second register buffer and halve that occupancy.
   const int nsteps = (n + 31) / 32;
-  DecodeTile<T, D> t0, t1;
-  int s0 = w;
-  if (s0 < nsteps) decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * s0, n, c16, h4);
-  for (; s0 < nsteps; s0 += 2 * W) {
-    const int s1 = s0 + W;
-    if (s1 < nsteps) decode_load<T, D>(t1, kbase, vbase, row_stride, 32 * s1, n, c16, h4);
-    decode_step<T, D>(st, t0, qb, 32 * s0, n, args.scale_log2, h4);
-    if (s1 >= nsteps) break;
-    const int s2 = s1 + W;
-    if (s2 < nsteps) decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * s2, n, c16, h4);
-    decode_step<T, D>(st, t1, qb, 32 * s1, n, args.scale_log2, h4);
+  for (int s0 = w; s0 < nsteps; s0 += W) {
+    DecodeTile<T, D> t;
+    decode_load<T, D>(t, kbase, vbase, row_stride, 32 * s0, n, c16, h4);
+    // all sixteen 16-byte loads are issued before the first is consumed
+    __builtin_amdgcn_sched_barrier(0);
+    decode_step<T, D>(st, t, qb, 32 * s0, n, args.scale_log2, h4);
   }
 
   // lane sums -> head sums (the four h4 lanes of head c16)
@@ -229,6 +237,13 @@ __global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args
       for (int r = 0; r < 4; ++r) red_o[w][c16][(D / 4) * h4 + (D / 16) * r + j] = st.o[j][r];
   }
   __syncthreads();
+
+  // This workgroup's result for its G heads: O (normalised), M (log2 units),
+  // L.  A request held by a single split is final here; otherwise this is
+  // partial i, merged by decode_merge_kernel.
+  const int n_b = int(args.kv_indptr[b + 1] - sr.base);
+  const int splits_b = args.partials_only ? 0 : (n_b + args.chunk - 1) / args.chunk;
+  typename T::elem* out = static_cast<typename T::elem*>(args.o);
   for (int e = threadIdx.x; e < G * D; e += 64 * W) {
     const int h = e / D, d = e % D;
     float M = red_m[0][h];
@@ -242,10 +257,15 @@ __global__ __launch_bounds__(64 * W, 2) void decode_partial_mfma(DecodeArgs args
       O += red_o[ww][h][d] * f;
     }
     const int64_t row = row0 + h;
-    args.o_part[(int64_t(i) * rows + row) * D + d] = O / L;
-    if (d == 0) {
-      args.m_part[int64_t(i) * rows + row] = M * kLn2;
-      args.l_part[int64_t(i) * rows + row] = L;
+    if (splits_b == 1) {  // the whole request in one split: final output
+      out[row * D + d] = typename T::elem(O / L);
+      if (d == 0 && args.lse) args.lse[row] = (M + flog2(L)) * kLn2;
+    } else {
+      args.o_part[(int64_t(i) * rows + row) * D + d] = O / L;
+      if (d == 0) {
+        args.m_part[int64_t(i) * rows + row] = M * kLn2;
+        args.l_part[int64_t(i) * rows + row] = L;
+      }
     }
   }
 }
@@ -356,7 +376,9 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
 }
 
 // -------------------------------------------------------------------------
-// LSE merge: one wave per row; lane d handles dims d, d + 64.
+// LSE merge (standalone): one wave per row.  Lanes first load the splits'
+// (m, l) side by side and reduce them across the wave; then lane d adds
+// dims d and d + 64 of every usable partial.
 // -------------------------------------------------------------------------
 template <int D, class OutT>
 __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
@@ -366,26 +388,38 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
   if (row >= a.rows) return;
   const int64_t rows = a.rows;
   float M = -INFINITY;
-  for (int i = 0; i < a.s; ++i) {
+  for (int i = lane; i < a.s; i += 64) {
     const float li = a.l_part[int64_t(i) * rows + row];
-    const float mi = a.m_part[int64_t(i) * rows + row];
-    if (li > 0.f) M = fmaxf(M, mi);
+    if (li > 0.f) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
   float acc[DL];
 #pragma unroll
   for (int x = 0; x < DL; ++x) acc[x] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < a.s; ++i) {
-      const float li = a.l_part[int64_t(i) * rows + row];
-      if (!(li > 0.f)) continue;
-      const float wgt = li * fexp2((a.m_part[int64_t(i) * rows + row] - M) * kLog2e);
-      wsum += wgt;
-      const float* op = a.o_part + (int64_t(i) * rows + row) * D;
+    for (int i0 = 0; i0 < a.s; i0 += 64) {
+      const int i = i0 + lane;
+      float wi = 0.f;
+      if (i < a.s) {
+        const float li = a.l_part[int64_t(i) * rows + row];
+        if (li > 0.f) wi = li * fexp2((a.m_part[int64_t(i) * rows + row] - M) * kLog2e);
+      }
+      float ws = wi;
 #pragma unroll
-      for (int x = 0; x < DL; ++x) {
-        const int d = lane + 64 * x;
-        if (d < D) acc[x] += wgt * op[d];
+      for (int off = 32; off >= 1; off >>= 1) ws += shfl_xor(ws, off);
+      wsum += ws;
+      const int n = a.s - i0 < 64 ? a.s - i0 : 64;
+      for (int j = 0; j < n; ++j) {
+        const float wj = __shfl(wi, j, 64);
+        if (wj == 0.f) continue;  // unused partial: its o is never read
+        const float* op = a.o_part + (int64_t(i0 + j) * rows + row) * D;
+#pragma unroll
+        for (int x = 0; x < DL; ++x) {
+          const int d = lane + 64 * x;
+          if (d < D) acc[x] += wj * op[d];
+        }
       }
     }
   }
@@ -397,6 +431,71 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
     if (d < D) o[d] = OutT(acc[x] * inv);
   }
   if (a.lse && lane == 0) a.lse[row] = wsum > 0.f ? M + flog2(wsum) * kLn2 : -INFINITY;
+}
+
+// -------------------------------------------------------------------------
+// Merge inside attn_decode_splitkv: one wave per (request, query head) row.
+// The request's split count comes from kv_indptr and the chunk length, so
+// rows of requests held by one split (already final) and unused splits are
+// never touched; (m, l) of the splits are loaded side by side across lanes.
+// -------------------------------------------------------------------------
+template <int D, class OutT>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int DL = (D + 63) / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = int64_t(a.B) * a.Hq;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int b = int(row / a.Hq);
+  const int n_b = int(a.kv_indptr[b + 1] - a.kv_indptr[b]);
+  const int splits_b = a.chunk > 0 ? (n_b + a.chunk - 1) / a.chunk : 0;
+  if (splits_b <= 1) return;
+  float mi = -INFINITY, li = 0.f;
+  if (lane < splits_b) {
+    mi = a.m_part[int64_t(lane) * rows + row];
+    li = a.l_part[int64_t(lane) * rows + row];
+  }
+  float M = mi;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  for (int i = 64 + lane; i < splits_b; i += 64) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
+  if (splits_b > 64) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  }
+  float acc[DL];
+#pragma unroll
+  for (int x = 0; x < DL; ++x) acc[x] = 0.f;
+  float wsum = 0.f;
+  for (int i0 = 0; i0 < splits_b; i0 += 64) {
+    float wi = 0.f;
+    if (i0 + lane < splits_b) {
+      const float m2 = i0 == 0 ? mi : a.m_part[int64_t(i0 + lane) * rows + row];
+      const float l2 = i0 == 0 ? li : a.l_part[int64_t(i0 + lane) * rows + row];
+      wi = l2 * fexp2((m2 - M) * kLog2e);
+    }
+    float ws = wi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ws += shfl_xor(ws, off);
+    wsum += ws;
+    const int n = splits_b - i0 < 64 ? splits_b - i0 : 64;
+    const float* op = a.o_part + (int64_t(i0) * rows + row) * D + lane;
+#pragma unroll 4
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(wi, j, 64);
+#pragma unroll
+      for (int x = 0; x < DL; ++x)
+        if (lane + 64 * x < D) acc[x] += wj * op[int64_t(j) * rows * D + 64 * x];
+    }
+  }
+  const float inv = 1.f / wsum;
+  OutT* o = static_cast<OutT*>(a.o) + row * D;
+#pragma unroll
+  for (int x = 0; x < DL; ++x) {
+    const int d = lane + 64 * x;
+    if (d < D) o[d] = OutT(acc[x] * inv);
+  }
+  if (a.lse && lane == 0) a.lse[row] = M + flog2(wsum) * kLn2;
 }
 
 __global__ void split_ranges_kernel(const int32_t* kv_indptr, int B, int s, int chunk,
@@ -411,20 +510,52 @@ __global__ void split_ranges_kernel(const int32_t* kv_indptr, int B, int s, int 
 
 // ---- launchers -----------------------------------------------------------
 
-hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
-  if (a.dtype == 0) {  // fp32
+  const dim3 mgrid_mfma(a.Hkv, a.s, a.B);
+  if (a.dtype == 0) {  // fp32: partial kernel, then the standalone merge
     if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
-  } else {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, a.B * a.Hq, a.D, a.o, 0, a.lse};
+    return launch_merge(m, st);
+  } else {  // 16-bit: MFMA partial kernel, then the merge of multi-split requests
     constexpr int W = 4;
     if (a.dtype == 1) {
-      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), grid, dim3(64 * W), 0, st, a);
-      else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), grid, dim3(64 * W), 0, st, a);
+      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+      else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
     } else {
-      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), grid, dim3(64 * W), 0, st, a);
-      else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), grid, dim3(64 * W), 0, st, a);
+      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+      else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.s == 1) return e;  // one split: every request is final
+    const dim3 mgrid(unsigned((int64_t(a.B) * a.Hq + 3) / 4));
+    if (a.dtype == 1) {
+      if (a.D == 64) hipLaunchKernelGGL((decode_merge_kernel<64, __bf16>), mgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((decode_merge_kernel<128, __bf16>), mgrid, dim3(256), 0, st, a);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((decode_merge_kernel<64, _Float16>), mgrid, dim3(256), 0, st, a);
+      else hipLaunchKernelGGL((decode_merge_kernel<128, _Float16>), mgrid, dim3(256), 0, st, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.s, a.Hkv, a.B);
+  const dim3 mgrid_mfma(a.Hkv, a.s, a.B);
+  constexpr int W = 4;
+  if (a.dtype == 0) {
+    if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
+    else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
+  } else if (a.dtype == 1) {
+    if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+  } else {
+    if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+    else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
   }
   return hipGetLastError();
 }

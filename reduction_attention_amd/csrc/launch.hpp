@@ -13,6 +13,8 @@ struct DecodeArgs {
   const void* k;
   const void* v;
   const int32_t* kv_indptr;
+  void* o;         // [B, Hq, D], element type of q
+  float* lse;      // [B, Hq] or nullptr
   float* o_part;   // [s, B*Hq, D]
   float* m_part;   // [s, B*Hq]
   float* l_part;   // [s, B*Hq]
@@ -21,6 +23,9 @@ struct DecodeArgs {
   int chunk;       // keys per split, ceil(max_kv_len / s)
   float scale_log2;  // scale * log2(e)
   int dtype;
+  int partials_only;  // 1: every used split writes a partial, unused splits
+                      // write (m, l) = (-inf, 0); 0: single-split requests are
+                      // written to o / lse directly
 };
 
 struct MergeArgs {
@@ -64,7 +69,8 @@ struct BsrArgs {
   int dtype;
 };
 
-hipError_t launch_decode_partial(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
                                hipStream_t st);

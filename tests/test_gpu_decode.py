@@ -145,3 +145,40 @@ def test_outputs_only_where_expected():
     assert bool(torch.isnan(l_buf[:16]).all()) and bool(torch.isnan(l_buf[32:]).all())
     o_ref, lse_ref = oracle_decode(dict(q=q, k=k, v=v, kv_indptr=kv), 1 / 128 ** 0.5)
     report("canary decode", o, o_ref, lse, lse_ref)
+
+
+def test_workspace_reused_across_calls():
+    """One workspace (with stale contents) serves calls of other shapes."""
+    ws = torch.full((1 << 22,), 255, dtype=torch.uint8, device=DEV)
+    for lengths, Hq, s in [([900, 5, 64, 2000], 8, 8), ([33, 1500], 16, 3), ([900, 5, 64, 2000], 8, 8)]:
+        q, k, v, kv = synth.decode_inputs(len(lengths), Hq, 2, 128, lengths, torch.bfloat16,
+                                          seed=len(lengths) + Hq)
+        o, lse = ra().attn_decode_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV),
+                                          max(lengths), num_splits=s, workspace=ws)
+        torch.cuda.synchronize()
+        o_ref, lse_ref = oracle_decode(dict(q=q, k=k, v=v, kv_indptr=kv), 1 / 128 ** 0.5)
+        check(f"reuse B={len(lengths)} s={s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("s", [1, 3, 8])
+def test_partials_match_oracle_split(s):
+    """attn_decode_partials against the oracle's per-split partials, then merged."""
+    lengths = [700, 1, 64, 0, 513]
+    q, k, v, kv = synth.decode_inputs(len(lengths), 8, 2, 128, lengths, torch.bfloat16, seed=s)
+    o_ref, lse_ref, op_ref, mp_ref, lp_ref = oracle.split_decode(q, k, v, kv, max(lengths),
+                                                                 1 / 128 ** 0.5, s)
+    op, mp, lp = ra().attn_decode_partials(q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV),
+                                           max(lengths), s)
+    torch.cuda.synchronize()
+    used = lp_ref > 0
+    assert torch.equal(lp.cpu() > 0, used)
+    assert bool(torch.isinf(mp.cpu()[~used]).all())
+    do = (op.cpu().double() - op_ref)[used].abs().max().item()
+    dm = (mp.cpu().double() - mp_ref)[used].abs().max().item()
+    dl = ((lp.cpu().double() - lp_ref) / lp_ref)[used].abs().max().item()
+    print(f"partials s={s}: max|do|={do:.2e} max|dm|={dm:.2e} max rel dl={dl:.2e}", flush=True)
+    assert do <= TOL_O[torch.bfloat16] and dm <= 1e-3 and dl <= 1e-3
+    o, lse = ra().attn_merge_lse(op, mp, lp, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(f"partials+merge s={s}", o.view(len(lengths), 8, 128), o_ref, lse.view(len(lengths), 8),
+          lse_ref, torch.bfloat16)
