@@ -173,6 +173,7 @@ attn_status_t attn_merge_lse(const float* o_part, const float* m_part, const flo
  * max_q_len, max_kv_len: the largest per-request lengths (bounds of the grid).
  * causal: 0 = every key of the request; 1 = key j is valid for query i iff
  *   j <= i + n_kv - n_q (bottom-right aligned; plain j <= i when n_q = n_kv).
+ * scale must be positive (as is 1/sqrt(D)).
  * Supported: dtype ATTN_BF16 or ATTN_F16; D in {64, 128}; any G >= 1.
  */
 attn_status_t attn_prefill(const void* q, const void* k, const void* v,
@@ -224,7 +225,7 @@ attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_in
  * its block row; full OTs take no per-element test, part OTs apply their
  * bitmaps as a predicate before the row max; unstored OTs are never read.
  * q, o [B, L, Hq, D]; k, v [B, L, Hkv, D]; lse [B, L, Hq] fp32 or NULL.
- * One mask serves every batch entry and head.
+ * One mask serves every batch entry and head.  scale must be positive.
  * Supported: dtype ATTN_F16 or ATTN_BF16; D in {64, 128}; L % 64 == 0.
  */
 attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,

@@ -200,13 +200,16 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, const in
     return fail(ATTN_EINVAL, "prefill: null pointer");
   if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill: B, Hq, Hkv must be >= 1");
   if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill: B or Hq above 65535");
+  if ((long long)max_q_len > 256LL * 65535)
+    return fail(ATTN_EUNSUPPORTED, "prefill: max_q_len above %lld", 256LL * 65535);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill: Hq %d not a multiple of Hkv %d", Hq, Hkv);
   if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill: D = %d (supported: 64, 128)", D);
   if (dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_EUNSUPPORTED, "prefill: dtype %d (supported: bf16, f16)", dtype);
   if (max_q_len < 0 || max_kv_len < 0) return fail(ATTN_EINVAL, "prefill: negative length");
   if (causal != 0 && causal != 1) return fail(ATTN_EINVAL, "prefill: causal must be 0 or 1");
-  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "prefill: scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "prefill: scale must be finite and positive");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(ATTN_EINVAL, "prefill: q, k, v, o must be 16-byte aligned");
   rattn::PrefillArgs a{q, k, v, qo_indptr, kv_indptr, o, lse, B, Hq, Hkv, D, Hq / Hkv,
@@ -303,7 +306,8 @@ attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
   if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill_bsr: D = %d (supported: 64, 128)", D);
   if (dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_EUNSUPPORTED, "prefill_bsr: dtype %d (supported: f16, bf16)", dtype);
-  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "prefill_bsr: scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "prefill_bsr: scale must be finite and positive");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(ATTN_EINVAL, "prefill_bsr: q, k, v, o must be 16-byte aligned");
   if (mask->nnz_part && (reinterpret_cast<uintptr_t>(mask->part_bits) & 7u))

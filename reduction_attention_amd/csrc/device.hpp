@@ -82,6 +82,13 @@ __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x
 
 __device__ __forceinline__ float shfl_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
+// x from lane (lane ^ 32): one LDS permute with a lane address computed once
+// by the caller (addr = (lane ^ 32) * 4), instead of __shfl_xor's per-call
+// index arithmetic.
+__device__ __forceinline__ float swap_halves(float x, int addr) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x)));
+}
+
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 }  // namespace rattn

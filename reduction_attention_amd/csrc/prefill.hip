@@ -18,17 +18,44 @@
 namespace rattn {
 
 // ---------------------------------------------------------------------------
-// Dense / causal prefill.  Workgroup = 4 waves = 128 query rows of one query
-// head; grid (query tiles, Hq, B).  Causal tiles are issued heaviest first.
+// Dense / causal prefill.  Workgroup = W waves = 32*W query rows of one query
+// head; grid (Hq, B, query tiles), causal tiles issued heaviest first.
+//
+// Key/value tiles of BK keys pass through a three-stage LDS ring: while a
+// wave runs the value update of tile j (stage j % 3) it already computes the
+// scores of tile j + 1 (stage (j+1) % 3), and the workgroup's loads of tile
+// j + 2 are in flight towards stage (j+2) % 3 -- the stage tile j - 1
+// released at the previous barrier.  One barrier per tile.  The scores of
+// tile j + 1 (matrix cores) and the weights of tile j (vector ALU) are
+// independent and sit in one basic block for the scheduler to interleave.
+// Measured on the 2 x 4096 causal workload: W = 8, BK = 64 (one 107 KB ring
+// per compute unit, two waves per SIMD) beat W = 4 with either tile size
+// and W = 8 with 32-key tiles.
 // ---------------------------------------------------------------------------
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
-  constexpr int NT = 256, BQ = 128;
-  typedef TileGeom<D> Gm;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Gm::STAGE];
+// Tile shape, fixed from a sweep on MI355X (see the design notes): waves per
+// workgroup (each owns 32 query rows) and keys per tile.
+#ifndef RATTN_PREFILL_WAVES
+#define RATTN_PREFILL_WAVES 8
+#endif
+#ifndef RATTN_PREFILL_BK
+#define RATTN_PREFILL_BK 64
+#endif
+constexpr int kPrefillWaves = RATTN_PREFILL_WAVES;
+constexpr int kPrefillBK = RATTN_PREFILL_BK;
 
-  const int b = blockIdx.z, hq = blockIdx.y;
-  const int qt = CAUSAL ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWaves >= 8 ? 1 : 2)
+void prefill_kernel(PrefillArgs a) {
+  constexpr int NT = 64 * kPrefillWaves, BQ = 32 * kPrefillWaves, BK = kPrefillBK, NS = 3;
+  typedef TileGeom<D, BK> Gm;
+  typedef typename T::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[NS * Gm::STAGE];
+
+  // grid (Hq, B, query tiles): workgroups are dispatched in linear order, so
+  // with the query tile slowest every causal tile of one size goes out
+  // before any smaller one (heaviest first) and the short ones fill the tail.
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int qt = CAUSAL ? int(gridDim.z) - 1 - int(blockIdx.z) : int(blockIdx.z);
   const int64_t q_begin = a.qo_indptr[b];
   const int n_q = int(a.qo_indptr[b + 1] - q_begin);
   const int64_t k_begin = a.kv_indptr[b];
@@ -42,12 +69,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int q_last_wg = (q_start + BQ < n_q ? q_start + BQ : n_q) - 1;
   int kv_end = n_kv;
   if (CAUSAL) kv_end = q_last_wg + 1 + off < n_kv ? q_last_wg + 1 + off : n_kv;
-  const int ntiles = kv_end > 0 ? (kv_end + Gm::BK - 1) / Gm::BK : 0;
+  const int ntiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
 
+  // this wave's rows and the tiles it takes part in (a prefix of the WG's)
   const int q0w = q_start + 32 * w;
   const int my_q = q0w + (lane & 31);
-  const bool wave_has_rows = q0w < n_q;
-  const int wave_q_last = (q0w + 31 < n_q ? q0w + 31 : n_q - 1);
+  int wnt = 0;
+  if (q0w < n_q) {
+    const int wq_last = q0w + 31 < n_q ? q0w + 31 : n_q - 1;
+    int wkv_end = n_kv;
+    if (CAUSAL) wkv_end = wq_last + 1 + off < n_kv ? wq_last + 1 + off : n_kv;
+    wnt = wkv_end > 0 ? (wkv_end + BK - 1) / BK : 0;
+  }
   const int64_t q_row = q_begin + (my_q < n_q ? my_q : n_q - 1);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
   u32x4 qb[D / 16];
@@ -55,49 +88,67 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
 
   RowState<D> st;
   row_state_init(st);
+  const float c = a.scale_log2;
+  const int xaddr = (lane ^ 32) << 2;
 
   const int64_t row_stride = int64_t(a.Hkv) * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + k_begin * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
   const int key_last = n_kv - 1;
 
-  TileRegs<D, NT> tr;
-  if (ntiles > 0) {
-    tile_load<D, NT>(tr, kbase, vbase, row_stride, 0, key_last, tid);
-    tile_store<D, NT>(tr, lds, tid);
-  }
-  __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const int k0 = j * Gm::BK;
-    if (j + 1 < ntiles) tile_load<D, NT>(tr, kbase, vbase, row_stride, k0 + Gm::BK, key_last, tid);
-    const uint16_t* cur = lds + (j & 1) * Gm::STAGE;
-    bool active = wave_has_rows;
-    if (CAUSAL) active = active && (k0 <= wave_q_last + off);
-    if (active) {
-      f32x16 s[2];
-      qk_tile<T, D>(s, cur, qb, lane);
-      float x[2][16];
-      const bool need_mask = (k0 + Gm::BK > n_kv) || (CAUSAL && k0 + Gm::BK - 1 > q0w + off);
-      if (need_mask) {
+  TileRegs<D, BK, NT> rr;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            bool ok = key < n_kv;
-            if (CAUSAL) ok = ok && key <= my_q + off;
-            x[kb][r] = ok ? s[kb][r] * a.scale_log2 : -INFINITY;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[kb][r] = s[kb][r] * a.scale_log2;
-      }
-      softmax_pv<T, D>(st, x, cur, lane);
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) {
+      tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, t * BK, key_last, tid);
+      tile_store<D, BK, NT>(rr, lds + t * Gm::STAGE, tid);
     }
-    if (j + 1 < ntiles) tile_store<D, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
+  __syncthreads();
+
+  // causal / ragged-tail masking of tile j's scores, needed on few tiles
+  auto mask = [&](f32x16 (&s)[Gm::NKB], int j) {
+    const int k0 = j * BK;
+    if ((k0 + BK > n_kv) || (CAUSAL && k0 + BK - 1 > q0w + off)) {
+#pragma unroll
+      for (int kb = 0; kb < Gm::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          bool ok = key < n_kv;
+          if (CAUSAL) ok = ok && key <= my_q + off;
+          if (!ok) s[kb][r] = -INFINITY;
+        }
+    }
+  };
+  // one tile step: loads of tile j+2, scores of tile j+1 into s_next,
+  // softmax and value update of tile j from s_cur
+  auto step = [&](int j, f32x16 (&s_cur)[Gm::NKB], f32x16 (&s_next)[Gm::NKB]) {
+    const bool more = j + 2 < ntiles;
+    if (more) tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, (j + 2) * BK, key_last, tid);
+    const uint16_t* cur = lds + (j % NS) * Gm::STAGE;
+    const uint16_t* nxt = lds + ((j + 1) % NS) * Gm::STAGE;
+    if (j < wnt) {
+      mask(s_cur, j);
+      const float mref = softmax_max<D, Gm::NKB>(st, s_cur, c, xaddr);
+      vec8 pb[Gm::NKB][2];
+      if (j + 1 < wnt) {  // one block: next tile's scores, this tile's weights and update
+        qk_tile<T, D, BK>(s_next, nxt, qb, lane);
+        softmax_exp<T, D, Gm::NKB>(st, s_cur, c, mref, pb);
+        pv_tile<T, D, BK>(st, pb, cur, lane);
+      } else {
+        softmax_exp<T, D, Gm::NKB>(st, s_cur, c, mref, pb);
+        pv_tile<T, D, BK>(st, pb, cur, lane);
+      }
+    }
+    if (more) tile_store<D, BK, NT>(rr, lds + ((j + 2) % NS) * Gm::STAGE, tid);
     __syncthreads();
+  };
+
+  f32x16 sa[Gm::NKB], sb[Gm::NKB];
+  if (wnt > 0) qk_tile<T, D, BK>(sa, lds, qb, lane);
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < ntiles) step(j + 1, sb, sa);
   }
 
   const bool row_ok = my_q < n_q;
@@ -124,7 +175,7 @@ __device__ __forceinline__ void bitmap_store(uint64_t word, uint8_t* bm, int tid
 
 // The part-OT predicate: x[kb][r] -> -inf where query (32*w + lane%32) of the
 // OT may not attend key 32*kb + 8*(r/4) + 4*h + r%4 of the OT.
-__device__ __forceinline__ void apply_part_mask(float (&x)[2][16], const uint8_t* bm, int w,
+__device__ __forceinline__ void apply_part_mask(f32x16 (&x)[2], const uint8_t* bm, int w,
                                                 int lane) {
   const int rq = 32 * w + (lane & 31);
   const int h = lane >> 5;
@@ -141,9 +192,9 @@ __device__ __forceinline__ void apply_part_mask(float (&x)[2][16], const uint8_t
 }
 
 template <class T, int D>
-__global__ __launch_bounds__(128, 4) void bsr_kernel(BsrArgs a) {
-  constexpr int NT = 128;
-  typedef TileGeom<D> Gm;
+__global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
+  constexpr int NT = 128, BK = 64;
+  typedef TileGeom<D, BK> Gm;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Gm::STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
@@ -167,17 +218,17 @@ __global__ __launch_bounds__(128, 4) void bsr_kernel(BsrArgs a) {
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
 
-  TileRegs<D, NT> tr;
+  TileRegs<D, BK, NT> tr;
   uint64_t word = 0;
   auto fetch = [&](int j) {
     const bool part = j >= n_full;
     const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
-    tile_load<D, NT>(tr, kbase, vbase, row_stride, kblk * 64, int(L) - 1, tid);
+    tile_load<D, BK, NT>(tr, kbase, vbase, row_stride, kblk * 64, int(L) - 1, tid);
     if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
   };
   if (ntiles > 0) {
     fetch(0);
-    tile_store<D, NT>(tr, lds, tid);
+    tile_store<D, BK, NT>(tr, lds, tid);
     if (n_full == 0) bitmap_store(word, bm[0], tid);
   }
   __syncthreads();
@@ -185,16 +236,11 @@ __global__ __launch_bounds__(128, 4) void bsr_kernel(BsrArgs a) {
     if (j + 1 < ntiles) fetch(j + 1);
     const uint16_t* cur = lds + (j & 1) * Gm::STAGE;
     f32x16 s[2];
-    qk_tile<T, D>(s, cur, qb, lane);
-    float x[2][16];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[kb][r] = s[kb][r] * a.scale_log2;
-    if (j >= n_full) apply_part_mask(x, bm[j & 1], w, lane);
-    softmax_pv<T, D>(st, x, cur, lane);
+    qk_tile<T, D, BK>(s, cur, qb, lane);
+    if (j >= n_full) apply_part_mask(s, bm[j & 1], w, lane);
+    softmax_pv<T, D, BK>(st, s, a.scale_log2, cur, lane);
     if (j + 1 < ntiles) {
-      tile_store<D, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
+      tile_store<D, BK, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
       if (j + 1 >= n_full) bitmap_store(word, bm[(j + 1) & 1], tid);
     }
     __syncthreads();
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_ind
     __syncthreads();
     bitmap_store(tid < 64 ? part_bits[int64_t(j) * 64 + tid] : 0, bm, tid);
     __syncthreads();
-    float x[2][16];
+    f32x16 x[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -250,9 +296,11 @@ __global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_ind
 
 template <class T, int D>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  const dim3 grid((a.max_q_len + 127) / 128, a.Hq, a.B);
-  if (a.causal) hipLaunchKernelGGL((prefill_kernel<T, D, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((prefill_kernel<T, D, false>), grid, dim3(256), 0, st, a);
+  constexpr int BQ = 32 * kPrefillWaves;
+  const dim3 grid(a.Hq, a.B, (a.max_q_len + BQ - 1) / BQ);
+  const dim3 block(64 * kPrefillWaves);
+  if (a.causal) hipLaunchKernelGGL((prefill_kernel<T, D, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((prefill_kernel<T, D, false>), grid, block, 0, st, a);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {

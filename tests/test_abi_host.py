@@ -104,7 +104,7 @@ def prefill_call(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(o=None), 1), (dict(qo=None), 1), (dict(Hq=5, Hkv=2), 1), (dict(D=32), 2),
     (dict(dt=0), 2), (dict(causal=2), 1), (dict(mq=-3), 1), (dict(scale=float("nan")), 1),
-    (dict(k=ctypes.c_void_p(24)), 1), (dict(B=70000), 2),
+    (dict(k=ctypes.c_void_p(24)), 1), (dict(B=70000), 2), (dict(scale=-0.5), 1),
 ])
 def test_prefill_validation(lib, kw, status):
     assert prefill_call(lib, **kw) == status
