@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
-    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_partial_traffic.json"))
     return p.parse_args()
 
 
@@ -211,26 +211,28 @@ def cpu_baseline(torch, synth, budget_s):
     """The fp64 oracle on a bounded sample of the headline decode workload."""
     import oracle
     w = synth.workload("llama3_8b_decode_bf16")
-    inp = w.make("cuda:0")
+    inp = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in w.make("cuda:0").items()}
     threads = len(os.sched_getaffinity(0))
     threads = min(threads, 16)
     B, Hq = w.B, w.Hq
     qo = list(range(B + 1))
-    # sample: whole KV groups (all G query heads of a KV head) of consecutive requests
+    # sample: (request, query head) rows in order, wrapping around, in
+    # batches grown until one batch takes about a second, for about budget_s
     rows_all = [(b, h) for b in range(B) for h in range(Hq)]
-    n = 8
-    done = 0
+    n, pos, done = 8, 0, 0
     t0 = time.perf_counter()
     while True:
-        sel = rows_all[done: done + n] if done + n <= len(rows_all) else rows_all[:n]
+        sel = [rows_all[(pos + k) % len(rows_all)] for k in range(n)]
+        pos += n
+        tb = time.perf_counter()
         oracle.attention(inp["q"], inp["k"], inp["v"], qo, inp["kv_indptr"], w.scale,
                          rows=torch.tensor(sel), nthreads=threads)
-        done += len(sel)
+        done += n
         el = time.perf_counter() - t0
-        if el >= budget_s or done >= 4 * len(rows_all):
+        if el >= budget_s:
             break
-        if el < budget_s / 8:
-            n = min(n * 2, len(rows_all))
+        if time.perf_counter() - tb < 1.0:
+            n *= 2
     elem = 2
     kvb, qb, ob, lb, ib = decode_bytes(B, Hq, w.Hkv, w.D, B * w.L, elem)
     step_bytes = kvb + qb + ob + lb + ib
