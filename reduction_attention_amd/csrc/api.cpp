@@ -200,8 +200,8 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, const in
     return fail(ATTN_EINVAL, "prefill: null pointer");
   if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill: B, Hq, Hkv must be >= 1");
   if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill: B or Hq above 65535");
-  if ((long long)max_q_len > 256LL * 65535)
-    return fail(ATTN_EUNSUPPORTED, "prefill: max_q_len above %lld", 256LL * 65535);
+  if ((long long)max_q_len > 128LL * 65535)
+    return fail(ATTN_EUNSUPPORTED, "prefill: max_q_len above %lld", 128LL * 65535);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill: Hq %d not a multiple of Hkv %d", Hq, Hkv);
   if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill: D = %d (supported: 64, 128)", D);
   if (dtype != ATTN_BF16 && dtype != ATTN_F16)

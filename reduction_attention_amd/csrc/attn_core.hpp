@@ -55,70 +55,78 @@ __device__ __forceinline__ bool k_role(int tid) {
   return __builtin_amdgcn_readfirstlane(tid) >= NT / 2;
 }
 
-// Global -> registers.  Rows key0 .. key0+BK-1 of the request.  On the last
-// tile of a request (key0 + BK - 1 > key_last) every row index is clamped to
-// key_last, so every address is in bounds; other tiles take the plain path,
-// whose per-thread offsets do not depend on the tile and stay in registers.
+// Global -> registers: K rows kkey0 .. kkey0+BK-1 (if do_k) and V rows
+// vkey0 .. vkey0+BK-1 (if do_v) of a request of n_keys keys; the two may
+// belong to different tiles.  Each role reads through a buffer resource that
+// ends at the request's last key, so rows past it come back as zeros without
+// a memory access (their scores are masked, and a zero V row adds nothing).
+// A thread's offsets into the tile are fixed, so a tile costs a few scalar
+// instructions for the resource and no per-load address arithmetic.
 template <int D, int BK, int NT>
 __device__ __forceinline__ void tile_load(TileRegs<D, BK, NT>& rr, const uint16_t* kbase,
-                                          const uint16_t* vbase, int64_t row_stride, int key0,
-                                          int key_last, int tid) {
+                                          const uint16_t* vbase, int row_stride, int kkey0,
+                                          int vkey0, int n_keys, int tid, bool do_k = true,
+                                          bool do_v = true) {
   typedef TileRegs<D, BK, NT> R;
   constexpr int CPR = D / 8, HALF = NT / 2;
-  const bool tail = key0 + BK - 1 > key_last;
+  static_assert(HALF % CPR == 0 && HALF % (BK / 4) == 0, "role split must tile the rows");
   if (k_role<NT>(tid)) {
+    if (!do_k) return;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(kbase + int64_t(kkey0) * row_stride, int64_t(n_keys - kkey0) * row_stride * 2);
+    // chunk t + HALF*x: row t/CPR + x*HALF/CPR, dims 8*(t%CPR) ..
     const int t = tid - HALF;
-    const uint16_t* kt = kbase + int64_t(key0) * row_stride;
+    const int base = ((t / CPR) * row_stride + 8 * (t % CPR)) * 2;
 #pragma unroll
-    for (int x = 0; x < R::KPT; ++x) {
-      const int e = t + HALF * x;
-      if (R::KPT * HALF == R::KCHUNKS || e < R::KCHUNKS) {
-        int row = e / CPR;
-        if (tail) row = key0 + row < key_last ? row : key_last - key0;
-        rr.r[x] = ldg128(kt + int64_t(row) * row_stride + 8 * (e % CPR));
-      }
-    }
+    for (int x = 0; x < R::KPT; ++x)
+      if (R::KPT * HALF == R::KCHUNKS || t + HALF * x < R::KCHUNKS)
+        rr.r[x] = buffer_load128(rs, base + x * (HALF / CPR) * row_stride * 2);
   } else {
-    const uint16_t* vt = vbase + int64_t(key0) * row_stride;
+    if (!do_v) return;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(vbase + int64_t(vkey0) * row_stride, int64_t(n_keys - vkey0) * row_stride * 2);
+    // item tid + HALF*x: keys 4*(tid % (BK/4)) .. +4, dims 8*(tid/(BK/4) + x*HALF/(BK/4)) ..
+    const int base = (4 * (tid % (BK / 4)) * row_stride + 8 * (tid / (BK / 4))) * 2;
 #pragma unroll
-    for (int x = 0; x < R::VPT; ++x) {
-      const int e = tid + HALF * x;
-      if (R::VPT * HALF == R::VITEMS || e < R::VITEMS) {
-        const int kg = e % (BK / 4), dc = e / (BK / 4);
+    for (int x = 0; x < R::VPT; ++x)
+      if (R::VPT * HALF == R::VITEMS || tid + HALF * x < R::VITEMS) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          int row = 4 * kg + b;
-          if (tail) row = key0 + row < key_last ? row : key_last - key0;
-          rr.r[4 * x + b] = ldg128(vt + int64_t(row) * row_stride + 8 * dc);
-        }
+        for (int b = 0; b < 4; ++b)
+          rr.r[4 * x + b] = buffer_load128(rs, base + (b * row_stride + 8 * x * (HALF / (BK / 4))) * 2);
       }
-    }
   }
 }
 
-// Registers -> LDS stage (K natural, V transposed into slot order).
+// Registers -> LDS: the K tile, natural, at kdst (if do_k); the V tile,
+// transposed into slot order, at vdst (if do_v).
 template <int D, int BK, int NT>
-__device__ __forceinline__ void tile_store(const TileRegs<D, BK, NT>& rr, uint16_t* lds, int tid) {
+__device__ __forceinline__ void tile_store(const TileRegs<D, BK, NT>& rr, uint16_t* kdst,
+                                           uint16_t* vdst, int tid, bool do_k = true,
+                                           bool do_v = true) {
   typedef TileGeom<D, BK> Gm;
   typedef TileRegs<D, BK, NT> R;
   constexpr int CPR = D / 8, HALF = NT / 2;
   if (k_role<NT>(tid)) {
+    if (!do_k) return;
+    // chunk t + HALF*x goes to row t/CPR + x*HALF/CPR: one base register,
+    // the rest immediate offsets
     const int t = tid - HALF;
+    uint16_t* kp = kdst + (t / CPR) * Gm::KLD + 8 * (t % CPR);
 #pragma unroll
-    for (int x = 0; x < R::KPT; ++x) {
-      const int e = t + HALF * x;
-      if (R::KPT * HALF == R::KCHUNKS || e < R::KCHUNKS)
-        *reinterpret_cast<u32x4*>(lds + (e / CPR) * Gm::KLD + 8 * (e % CPR)) = rr.r[x];
-    }
+    for (int x = 0; x < R::KPT; ++x)
+      if (R::KPT * HALF == R::KCHUNKS || t + HALF * x < R::KCHUNKS)
+        *reinterpret_cast<u32x4*>(kp + x * (HALF / CPR) * Gm::KLD) = rr.r[x];
   } else {
-    uint16_t* lv = lds + Gm::K_ELEMS;
+    if (!do_v) return;
+    // item tid + HALF*x: keys 4*kg .. 4*kg+3 with kg = tid % (BK/4) (so
+    // T = kg / 4, a = (kg / 2) % 2, h = kg % 2), dims 8*dc .. with
+    // dc = tid / (BK/4) + x*HALF/(BK/4)
+    const int kg = tid % (BK / 4);
+    const int pos = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+    uint16_t* vp = vdst + 8 * (tid / (BK / 4)) * Gm::VLD + pos;
 #pragma unroll
-    for (int x = 0; x < R::VPT; ++x) {
-      const int e = tid + HALF * x;
-      if (R::VPT * HALF == R::VITEMS || e < R::VITEMS) {
-        const int kg = e % (BK / 4), dc = e / (BK / 4);
-        // keys 4*kg .. 4*kg+3: T = kg / 4, a = (kg / 2) % 2, h = kg % 2
-        const int pos = 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+    for (int x = 0; x < R::VPT; ++x)
+      if (R::VPT * HALF == R::VITEMS || tid + HALF * x < R::VITEMS) {
         const u32x4* v = rr.r + 4 * x;
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
@@ -131,10 +139,9 @@ __device__ __forceinline__ void tile_store(const TileRegs<D, BK, NT>& rr, uint16
             pk[0] = pack_lo(v[0][w], v[1][w]);
             pk[1] = pack_lo(v[2][w], v[3][w]);
           }
-          *reinterpret_cast<u32x2*>(lv + (8 * dc + jd) * Gm::VLD + pos) = pk;
+          *reinterpret_cast<u32x2*>(vp + (8 * x * (HALF / (BK / 4)) + jd) * Gm::VLD) = pk;
         }
       }
-    }
   }
 }
 
@@ -171,26 +178,31 @@ __device__ __forceinline__ void load_q(u32x4 (&qb)[D / 16], const uint16_t* qrow
   for (int u = 0; u < D / 16; ++u) __asm__ volatile("" ::"v"(qb[u]));
 }
 
-// S^T for one tile: s[kb][r] = q(lane%32) . k(32*kb + 8*(r/4) + 4*h + r%4)
+// One 32-key block of S^T: s[r] = q(lane%32) . k(32*kb + 8*(r/4) + 4*h + r%4)
+// over the K tile at klds.
 template <class T, int D, int BK>
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[BK / 32], const uint16_t* lds,
-                                        const u32x4 (&qb)[D / 16], int lane) {
+__device__ __forceinline__ void qk_block(f32x16& s, const uint16_t* klds, int kb,
+                                         const u32x4 (&qb)[D / 16], int lane) {
   typedef typename T::vec8 vec8;
   typedef TileGeom<D, BK> Gm;
-  const int row = lane & 31, h = lane >> 5;
+  const uint16_t* kp = klds + (32 * kb + (lane & 31)) * Gm::KLD + 8 * (lane >> 5);
+  f32x16 acc;
 #pragma unroll
-  for (int kb = 0; kb < Gm::NKB; ++kb) {
-    f32x16 acc;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    const uint16_t* kp = lds + (32 * kb + row) * Gm::KLD + 8 * h;
-#pragma unroll
-    for (int u = 0; u < D / 16; ++u) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(kp + 16 * u);
-      acc = T::mfma32(as<vec8>(a), as<vec8>(qb[u]), acc);
-    }
-    s[kb] = acc;
+  for (int u = 0; u < D / 16; ++u) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(kp + 16 * u);
+    acc = T::mfma32(as<vec8>(a), as<vec8>(qb[u]), acc);
   }
+  s = acc;
+}
+
+// S^T for one tile: s[kb] for every 32-key block.
+template <class T, int D, int BK>
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[BK / 32], const uint16_t* klds,
+                                        const u32x4 (&qb)[D / 16], int lane) {
+#pragma unroll
+  for (int kb = 0; kb < BK / 32; ++kb) qk_block<T, D, BK>(s[kb], klds, kb, qb, lane);
 }
 
 // The running reference max m of a row is raised only when a tile's max
@@ -200,19 +212,24 @@ __device__ __forceinline__ void qk_tile(f32x16 (&s)[BK / 32], const uint16_t* ld
 // the rescale of the output accumulator.
 constexpr float kRescaleSlack = 8.f;
 
-// Online softmax, first half: the tile's row max over raw scores s (masked
-// entries -inf; c = scale * log2(e) turns a score into log2 units) raises the
-// reference max when needed, rescaling O and l.  Returns the reference the
-// tile's weights are taken against.
-template <int D, int NKB>
-__device__ __forceinline__ float softmax_max(RowState<D>& st, const f32x16 (&s)[NKB], float c,
-                                             int xaddr) {
+// Online softmax, step 1: the tile's row max over raw scores (masked
+// entries -inf), the same in lanes l and l ^ 32.
+template <int NKB>
+__device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[NKB], int xaddr) {
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = max3(mx, s[kb][r], s[kb][r + 1]);
-  mx = fmaxf(mx, swap_halves(mx, xaddr));
+  return fmaxf(mx, swap_halves(mx, xaddr));
+}
+
+// Step 2: raise the reference max to the tile max mx (raw score units; c =
+// scale * log2(e) turns a score into log2 units) when it exceeds the
+// reference by more than the slack, rescaling O and l.  The branch is taken
+// by few tiles and is uniform over the wave.
+template <int D>
+__device__ __forceinline__ void raise_ref(RowState<D>& st, float mx, float c) {
   const float mxs = mx * c;
   const bool need = mxs > st.m + kRescaleSlack;  // st.m = -inf: any valid key
   if (__any(need)) {
@@ -223,38 +240,57 @@ __device__ __forceinline__ float softmax_max(RowState<D>& st, const f32x16 (&s)[
     st.l *= alpha;
     st.m = m_new;
   }
-  // st.m = -inf here means no valid key so far: every s is -inf, p = 0
+}
+
+// The reference the weights are taken against; st.m = -inf means no valid
+// key so far, where every score is -inf and every weight 0.
+template <int D>
+__device__ __forceinline__ float ref_max(const RowState<D>& st) {
   return st.m == -INFINITY ? 0.f : st.m;
 }
 
-// Second half: the tile's weights exp2(s*c - mref), added to l and returned
+// Step 3, one 32-key block: weights exp2(s*c - mref), added to l and returned
 // as the bf16/f16 operands pb of the value update.
+template <class T>
+__device__ __forceinline__ void exp_block(float& l, const f32x16& s, float c, float mref,
+                                          typename T::vec8 (&pb)[2]) {
+  float psum = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    f32x8 p;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fexp2(__builtin_fmaf(s[8 * t + i], c, -mref));
+      psum += p[i];
+    }
+    pb[t] = T::cvt8(p);
+  }
+  l += psum;
+}
+
+// Steps 1 and 2 for a whole tile; returns the reference of its weights.
+template <int D, int NKB>
+__device__ __forceinline__ float softmax_max(RowState<D>& st, const f32x16 (&s)[NKB], float c,
+                                             int xaddr) {
+  raise_ref<D>(st, tile_rowmax<NKB>(s, xaddr), c);
+  return ref_max<D>(st);
+}
+
+// Step 3 for a whole tile.
 template <class T, int D, int NKB>
 __device__ __forceinline__ void softmax_exp(RowState<D>& st, const f32x16 (&s)[NKB], float c,
                                             float mref, typename T::vec8 (&pb)[NKB][2]) {
-  float psum = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x8 p;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fexp2(__builtin_fmaf(s[kb][8 * t + i], c, -mref));
-        psum += p[i];
-      }
-      pb[kb][t] = T::cvt8(p);
-    }
-  st.l += psum;
+  for (int kb = 0; kb < NKB; ++kb) exp_block<T>(st.l, s[kb], c, mref, pb[kb]);
 }
 
 // O^T += V^T P^T over the LDS V^T tile.
 template <class T, int D, int BK>
 __device__ __forceinline__ void pv_tile(RowState<D>& st, const typename T::vec8 (&pb)[BK / 32][2],
-                                        const uint16_t* lds, int lane) {
+                                        const uint16_t* vlds, int lane) {
   typedef typename T::vec8 vec8;
   typedef TileGeom<D, BK> Gm;
-  const uint16_t* vp = lds + Gm::K_ELEMS + (lane & 31) * Gm::VLD + 8 * (lane >> 5);
+  const uint16_t* vp = vlds + (lane & 31) * Gm::VLD + 8 * (lane >> 5);
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -266,13 +302,58 @@ __device__ __forceinline__ void pv_tile(RowState<D>& st, const typename T::vec8 
       }
 }
 
+// Multi-block forms for a wave that owns RB blocks of 32 query rows: every
+// K or V operand read from LDS feeds RB MFMAs, one per row block.
+template <class T, int D, int BK, int RB>
+__device__ __forceinline__ void qk_tile_rb(f32x16 (&s)[RB][BK / 32], const uint16_t* lds,
+                                           const u32x4 (&qb)[RB][D / 16], int lane) {
+  typedef typename T::vec8 vec8;
+  typedef TileGeom<D, BK> Gm;
+  const int row = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < Gm::NKB; ++kb) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[rb][kb][r] = 0.f;
+    const uint16_t* kp = lds + (32 * kb + row) * Gm::KLD + 8 * h;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kp + 16 * u);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        s[rb][kb] = T::mfma32(as<vec8>(a), as<vec8>(qb[rb][u]), s[rb][kb]);
+    }
+  }
+}
+
+template <class T, int D, int BK, int RB>
+__device__ __forceinline__ void pv_tile_rb(RowState<D> (&st)[RB],
+                                           const typename T::vec8 (&pb)[RB][BK / 32][2],
+                                           const uint16_t* vlds, int lane) {
+  typedef typename T::vec8 vec8;
+  typedef TileGeom<D, BK> Gm;
+  const uint16_t* vp = vlds + (lane & 31) * Gm::VLD + 8 * (lane >> 5);
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kb = 0; kb < Gm::NKB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(vp + 32 * db * Gm::VLD + 32 * kb + 16 * t);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          st[rb].o[db] = T::mfma32(as<vec8>(a), pb[rb][kb][t], st[rb].o[db]);
+      }
+}
+
 template <class T, int D, int BK>
 __device__ __forceinline__ void softmax_pv(RowState<D>& st, const f32x16 (&s)[BK / 32], float c,
-                                           const uint16_t* lds, int lane) {
+                                           const uint16_t* vlds, int lane) {
   typename T::vec8 pb[BK / 32][2];
   const float mref = softmax_max<D, BK / 32>(st, s, c, (lane ^ 32) << 2);
   softmax_exp<T, D, BK / 32>(st, s, c, mref, pb);
-  pv_tile<T, D, BK>(st, pb, lds, lane);
+  pv_tile<T, D, BK>(st, pb, vlds, lane);
 }
 
 // Final normalisation and store of the wave's rows.  orow points at dim 0 of

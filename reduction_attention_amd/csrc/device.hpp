@@ -69,6 +69,20 @@ __device__ __forceinline__ V as(u32x4 x) { return __builtin_bit_cast(V, x); }
 __device__ __forceinline__ u32x4 ldg128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void stg128(void* p, u32x4 x) { *reinterpret_cast<u32x4*>(p) = x; }
 
+// Buffer resource over [base, base + bytes): a 16-byte buffer load at byte
+// offset voff (a VGPR) returns zeros, and touches no memory, when voff lies
+// at or beyond bytes.  Word 3 holds the gfx9 raw-buffer format bits (32-bit
+// data, no swizzle, stride 0).  Only the VGPR offset enters the range check,
+// so callers put every row-dependent offset there and pass no scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+  const int64_t cap = 0x7fffffff;
+  const int n = int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load128(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
 // Pick 16-bit halves: lo16(a) | lo16(b) << 16, and hi16(a) | hi16(b) << 16.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -18,43 +18,77 @@
 namespace rattn {
 
 // ---------------------------------------------------------------------------
-// Dense / causal prefill.  Workgroup = W waves = 32*W query rows of one query
-// head; grid (Hq, B, query tiles), causal tiles issued heaviest first.
+// Dense / causal prefill.  Workgroup = W waves, each owning RB blocks of 32
+// query rows of one query head; grid (Hq, B, query tiles), causal tiles
+// issued heaviest first, two workgroups per compute unit.
 //
-// Key/value tiles of BK keys pass through a three-stage LDS ring: while a
-// wave runs the value update of tile j (stage j % 3) it already computes the
-// scores of tile j + 1 (stage (j+1) % 3), and the workgroup's loads of tile
-// j + 2 are in flight towards stage (j+2) % 3 -- the stage tile j - 1
-// released at the previous barrier.  One barrier per tile.  The scores of
-// tile j + 1 (matrix cores) and the weights of tile j (vector ALU) are
-// independent and sit in one basic block for the scheduler to interleave.
-// Measured on the 2 x 4096 causal workload: W = 8, BK = 64 (one 107 KB ring
-// per compute unit, two waves per SIMD) beat W = 4 with either tile size
-// and W = 8 with 32-key tiles.
+// Keys arrive in tiles of BK.  In step j a wave computes the scores of tile
+// j + 1 and the value update of tile j (weights from the previous step),
+// then the weights of tile j + 1.  K therefore runs one tile ahead of V:
+// LDS holds two K stages and two V stages, and the loads issued at the top
+// of step j (K of tile j + 2, V of tile j + 1) land, at its end, in the
+// stages that step j - 1 released.  One barrier per step.  The ring takes
+// 70 KB at D = 128, so two workgroups share a compute unit and one's
+// start-up (its query rows and first tiles coming in from memory) and
+// barriers overlap the other's matrix work.  Shape knobs (waves, row
+// blocks, occupancy) were swept on MI355X; the defaults won.
 // ---------------------------------------------------------------------------
-// Tile shape, fixed from a sweep on MI355X (see the design notes): waves per
-// workgroup (each owns 32 query rows) and keys per tile.
 #ifndef RATTN_PREFILL_WAVES
-#define RATTN_PREFILL_WAVES 8
+#define RATTN_PREFILL_WAVES 4
 #endif
-#ifndef RATTN_PREFILL_BK
-#define RATTN_PREFILL_BK 64
+#ifndef RATTN_PREFILL_RB
+#define RATTN_PREFILL_RB 1
+#endif
+#ifndef RATTN_PREFILL_OCC
+#define RATTN_PREFILL_OCC 2
+#endif
+#ifndef RATTN_PREFILL_XCD
+#define RATTN_PREFILL_XCD 1
 #endif
 constexpr int kPrefillWaves = RATTN_PREFILL_WAVES;
-constexpr int kPrefillBK = RATTN_PREFILL_BK;
+constexpr int kPrefillRB = RATTN_PREFILL_RB;
+constexpr int kPrefillBK = 64;
+constexpr int kPrefillBQ = 32 * kPrefillRB * kPrefillWaves;  // query rows per workgroup
+
+// Workgroups are dealt to the eight XCDs round robin by linear index, and
+// each XCD has its own L2.  With Hq a multiple of 8, grid column x runs head
+// (x % 8) * (Hq / 8) + x / 8, so each XCD serves a contiguous range of query
+// heads -- whole GQA groups -- and fetches their K/V into its own L2 only.
+__device__ __forceinline__ int xcd_head(int x, int hq_count) {
+  if (!RATTN_PREFILL_XCD || (hq_count & 7)) return x;
+  return (x & 7) * (hq_count >> 3) + (x >> 3);
+}
+
+// Schedule of a block of N operand reads from LDS, each feeding RB matrix
+// ops: keep DEPTH reads in flight ahead of the matrix ops.
+#ifndef RATTN_PREFILL_DEPTH
+#define RATTN_PREFILL_DEPTH 4
+#endif
+template <int N, int RB>
+__device__ __forceinline__ void lds_pipeline() {
+#if RATTN_PREFILL_DEPTH
+  __builtin_amdgcn_sched_group_barrier(0x100, RATTN_PREFILL_DEPTH, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+    if (i + RATTN_PREFILL_DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#endif
+}
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kPrefillWaves, kPrefillWaves >= 8 ? 1 : 2)
+__global__ __launch_bounds__(64 * kPrefillWaves, RATTN_PREFILL_OCC)
 void prefill_kernel(PrefillArgs a) {
-  constexpr int NT = 64 * kPrefillWaves, BQ = 32 * kPrefillWaves, BK = kPrefillBK, NS = 3;
+  constexpr int NT = 64 * kPrefillWaves, RB = kPrefillRB, BQ = kPrefillBQ, BK = kPrefillBK;
   typedef TileGeom<D, BK> Gm;
   typedef typename T::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[NS * Gm::STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * Gm::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * Gm::V_ELEMS];
 
   // grid (Hq, B, query tiles): workgroups are dispatched in linear order, so
   // with the query tile slowest every causal tile of one size goes out
   // before any smaller one (heaviest first) and the short ones fill the tail.
-  const int hq = blockIdx.x, b = blockIdx.y;
+  const int hq = xcd_head(blockIdx.x, a.Hq), b = blockIdx.y;
   const int qt = CAUSAL ? int(gridDim.z) - 1 - int(blockIdx.z) : int(blockIdx.z);
   const int64_t q_begin = a.qo_indptr[b];
   const int n_q = int(a.qo_indptr[b + 1] - q_begin);
@@ -63,7 +97,7 @@ void prefill_kernel(PrefillArgs a) {
   const int q_start = qt * BQ;
   if (q_start >= n_q) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = hq / a.G;
   const int off = n_kv - n_q;  // causal: key j valid for query i iff j <= i + off
   const int q_last_wg = (q_start + BQ < n_q ? q_start + BQ : n_q) - 1;
@@ -71,90 +105,113 @@ void prefill_kernel(PrefillArgs a) {
   if (CAUSAL) kv_end = q_last_wg + 1 + off < n_kv ? q_last_wg + 1 + off : n_kv;
   const int ntiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
 
-  // this wave's rows and the tiles it takes part in (a prefix of the WG's)
-  const int q0w = q_start + 32 * w;
-  const int my_q = q0w + (lane & 31);
+  // this wave's rows (RB blocks of 32) and the tiles it takes part in
+  const int q0w = q_start + 32 * RB * w;
   int wnt = 0;
   if (q0w < n_q) {
-    const int wq_last = q0w + 31 < n_q ? q0w + 31 : n_q - 1;
+    const int wq_last = q0w + 32 * RB - 1 < n_q ? q0w + 32 * RB - 1 : n_q - 1;
     int wkv_end = n_kv;
     if (CAUSAL) wkv_end = wq_last + 1 + off < n_kv ? wq_last + 1 + off : n_kv;
     wnt = wkv_end > 0 ? (wkv_end + BK - 1) / BK : 0;
   }
-  const int64_t q_row = q_begin + (my_q < n_q ? my_q : n_q - 1);
+  wnt = __builtin_amdgcn_readfirstlane(wnt);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  u32x4 qb[D / 16];
-  load_q<D>(qb, Q + (q_row * a.Hq + hq) * D, lane);
-
-  RowState<D> st;
-  row_state_init(st);
+  u32x4 qb[RB][D / 16];
+  RowState<D> st[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int mq = q0w + 32 * rb + (lane & 31);
+    load_q<D>(qb[rb], Q + ((q_begin + (mq < n_q ? mq : n_q - 1)) * a.Hq + hq) * D, lane);
+    row_state_init(st[rb]);
+  }
   const float c = a.scale_log2;
-  const int xaddr = (lane ^ 32) << 2;
 
-  const int64_t row_stride = int64_t(a.Hkv) * D;
+  const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + k_begin * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
-  const int key_last = n_kv - 1;
 
+  // prologue: K of tiles 0 and 1, V of tile 0
   TileRegs<D, BK, NT> rr;
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < ntiles) {
-      tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, t * BK, key_last, tid);
-      tile_store<D, BK, NT>(rr, lds + t * Gm::STAGE, tid);
-    }
+  if (ntiles > 0) {
+    tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, 0, 0, n_kv, tid);
+    tile_store<D, BK, NT>(rr, lds_k, lds_v, tid);
+  }
+  if (ntiles > 1) {
+    tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, BK, BK, n_kv, tid, true, false);
+    tile_store<D, BK, NT>(rr, lds_k + Gm::K_ELEMS, lds_v, tid, true, false);
+  }
   __syncthreads();
 
   // causal / ragged-tail masking of tile j's scores, needed on few tiles
-  auto mask = [&](f32x16 (&s)[Gm::NKB], int j) {
+  auto need_mask = [&](int j) {
     const int k0 = j * BK;
-    if ((k0 + BK > n_kv) || (CAUSAL && k0 + BK - 1 > q0w + off)) {
+    return (k0 + BK > n_kv) || (CAUSAL && k0 + BK - 1 > q0w + off);
+  };
+  auto mask = [&](f32x16 (&s)[RB][Gm::NKB], int j) {
+    const int k0 = j * BK;
+    const int ln = lane, hh = ln >> 5;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int mq = q0w + 32 * rb + (ln & 31);
 #pragma unroll
       for (int kb = 0; kb < Gm::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           bool ok = key < n_kv;
-          if (CAUSAL) ok = ok && key <= my_q + off;
-          if (!ok) s[kb][r] = -INFINITY;
+          if (CAUSAL) ok = ok && key <= mq + off;
+          if (!ok) s[rb][kb][r] = -INFINITY;
         }
     }
   };
-  // one tile step: loads of tile j+2, scores of tile j+1 into s_next,
-  // softmax and value update of tile j from s_cur
-  auto step = [&](int j, f32x16 (&s_cur)[Gm::NKB], f32x16 (&s_next)[Gm::NKB]) {
-    const bool more = j + 2 < ntiles;
-    if (more) tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, (j + 2) * BK, key_last, tid);
-    const uint16_t* cur = lds + (j % NS) * Gm::STAGE;
-    const uint16_t* nxt = lds + ((j + 1) % NS) * Gm::STAGE;
-    if (j < wnt) {
-      mask(s_cur, j);
-      const float mref = softmax_max<D, Gm::NKB>(st, s_cur, c, xaddr);
-      vec8 pb[Gm::NKB][2];
-      if (j + 1 < wnt) {  // one block: next tile's scores, this tile's weights and update
-        qk_tile<T, D, BK>(s_next, nxt, qb, lane);
-        softmax_exp<T, D, Gm::NKB>(st, s_cur, c, mref, pb);
-        pv_tile<T, D, BK>(st, pb, cur, lane);
-      } else {
-        softmax_exp<T, D, Gm::NKB>(st, s_cur, c, mref, pb);
-        pv_tile<T, D, BK>(st, pb, cur, lane);
-      }
+  // weights of tile j from its scores: mask, fold the row max into the
+  // reference, exp
+  auto weights = [&](f32x16 (&s)[RB][Gm::NKB], int j, vec8 (&p)[RB][Gm::NKB][2]) {
+    if (need_mask(j)) mask(s, j);
+    const int xaddr = (lane ^ 32) << 2;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      raise_ref<D>(st[rb], tile_rowmax<Gm::NKB>(s[rb], xaddr), c);
+      softmax_exp<T, D, Gm::NKB>(st[rb], s[rb], c, ref_max<D>(st[rb]), p[rb]);
     }
-    if (more) tile_store<D, BK, NT>(rr, lds + ((j + 2) % NS) * Gm::STAGE, tid);
-    __syncthreads();
   };
 
-  f32x16 sa[Gm::NKB], sb[Gm::NKB];
-  if (wnt > 0) qk_tile<T, D, BK>(sa, lds, qb, lane);
-  for (int j = 0; j < ntiles; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < ntiles) step(j + 1, sb, sa);
+  f32x16 sc[RB][Gm::NKB];
+  vec8 pb[RB][Gm::NKB][2];
+  if (wnt > 0) {
+    qk_tile_rb<T, D, BK, RB>(sc, lds_k, qb, lane);
+    weights(sc, 0, pb);
+  }
+  // step 0 refills K stage 0, which every wave must have finished reading
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    const bool kmore = j + 2 < ntiles, vmore = j + 1 < ntiles;
+    if (vmore)
+      tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, (j + 2) * BK, (j + 1) * BK, n_kv, tid,
+                           kmore, true);
+    if (j + 1 < wnt) {
+      qk_tile_rb<T, D, BK, RB>(sc, lds_k + ((j + 1) & 1) * Gm::K_ELEMS, qb, lane);
+      lds_pipeline<Gm::NKB * D / 16, RB>();
+    }
+    if (j < wnt) {
+      pv_tile_rb<T, D, BK, RB>(st, pb, lds_v + (j & 1) * Gm::V_ELEMS, lane);
+      lds_pipeline<2 * Gm::NKB * D / 32, RB>();
+    }
+    if (j + 1 < wnt) weights(sc, j + 1, pb);
+    if (vmore)
+      tile_store<D, BK, NT>(rr, lds_k + (j & 1) * Gm::K_ELEMS, lds_v + ((j + 1) & 1) * Gm::V_ELEMS,
+                            tid, kmore, true);
+    __syncthreads();
   }
 
-  const bool row_ok = my_q < n_q;
-  uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + ((q_begin + my_q) * a.Hq + hq) * D : nullptr;
-  float* lse = (row_ok && a.lse) ? a.lse + (q_begin + my_q) * a.Hq + hq : nullptr;
-  row_store<T, D>(st, orow, lse, lane);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int oq = q0w + 32 * rb + (lane & 31);
+    const bool row_ok = oq < n_q;
+    uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + ((q_begin + oq) * a.Hq + hq) * D : nullptr;
+    float* lse = (row_ok && a.lse) ? a.lse + (q_begin + oq) * a.Hq + hq : nullptr;
+    row_store<T, D>(st[rb], orow, lse, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -214,7 +271,7 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   RowState<D> st;
   row_state_init(st);
 
-  const int64_t row_stride = int64_t(a.Hkv) * D;
+  const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
 
@@ -223,12 +280,12 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   auto fetch = [&](int j) {
     const bool part = j >= n_full;
     const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
-    tile_load<D, BK, NT>(tr, kbase, vbase, row_stride, kblk * 64, int(L) - 1, tid);
+    tile_load<D, BK, NT>(tr, kbase, vbase, row_stride, kblk * 64, kblk * 64, int(L), tid);
     if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
   };
   if (ntiles > 0) {
     fetch(0);
-    tile_store<D, BK, NT>(tr, lds, tid);
+    tile_store<D, BK, NT>(tr, lds, lds + Gm::K_ELEMS, tid);
     if (n_full == 0) bitmap_store(word, bm[0], tid);
   }
   __syncthreads();
@@ -238,9 +295,10 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
     f32x16 s[2];
     qk_tile<T, D, BK>(s, cur, qb, lane);
     if (j >= n_full) apply_part_mask(s, bm[j & 1], w, lane);
-    softmax_pv<T, D, BK>(st, s, a.scale_log2, cur, lane);
+    softmax_pv<T, D, BK>(st, s, a.scale_log2, cur + Gm::K_ELEMS, lane);
     if (j + 1 < ntiles) {
-      tile_store<D, BK, NT>(tr, lds + ((j + 1) & 1) * Gm::STAGE, tid);
+      uint16_t* nxt = lds + ((j + 1) & 1) * Gm::STAGE;
+      tile_store<D, BK, NT>(tr, nxt, nxt + Gm::K_ELEMS, tid);
       if (j + 1 >= n_full) bitmap_store(word, bm[(j + 1) & 1], tid);
     }
     __syncthreads();
@@ -296,7 +354,7 @@ __global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_ind
 
 template <class T, int D>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
-  constexpr int BQ = 32 * kPrefillWaves;
+  constexpr int BQ = kPrefillBQ;
   const dim3 grid(a.Hq, a.B, (a.max_q_len + BQ - 1) / BQ);
   const dim3 block(64 * kPrefillWaves);
   if (a.causal) hipLaunchKernelGGL((prefill_kernel<T, D, true>), grid, block, 0, st, a);
