@@ -283,7 +283,7 @@ def main():
         pass
     roofline = dict(bound="hbm", achieved=round(d["kernel_gbs"], 1), peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=round(d["kernel_gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="rattn::decode_partial_mfma<rattn::BF16, 128, 4>",
+                    kernel="rattn::decode_partial_mfma<rattn::BF16, 128, 4, 1>",
                     algorithmic_bytes=d["kernel_bytes"],
                     avg_launch_us=round(d["kernel_ms"] * 1e3, 2))
     out = {

@@ -80,12 +80,16 @@ int attn_device_cu_count(void);
  * rounded up to 256 bytes.  Returns 0 for invalid arguments. */
 size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 
-/* The split count s the library picks when num_splits = 0: the largest chunk
- * c (a power of two, at least 256 keys) whose estimated workgroup count
- * Hkv * (total_kv / c + B / 2) still reaches two workgroups per compute unit
- * (four when request lengths differ), then s = ceil(max_kv_len / c), clamped
- * to [1, 256].  [CA] leaves the concrete s to the scheduler; this is that
- * scheduler's rule, fitted to measured sweeps on MI355X. */
+/* The split count s the library picks when num_splits = 0, as
+ * s = ceil(max_kv_len / c) clamped to [1, 256], with c the largest power of
+ * two >= 256 keys such that:
+ *  - equal request lengths (max_kv_len * B == total_kv), where a workgroup
+ *    takes up to four KV heads: ceil(Hkv / hpw) * B * ceil(max_kv_len / c)
+ *    workgroups (hpw = 4, 2 or 1, at most Hkv) reach one per compute unit;
+ *  - otherwise, one KV head per workgroup: Hkv * (total_kv / c + B / 2)
+ *    workgroups reach four per compute unit.
+ * [CA] leaves the concrete s to the scheduler; this is that scheduler's
+ * rule, fitted to measured sweeps on MI355X. */
 int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
                               int max_kv_len);
 

@@ -87,22 +87,35 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   return (bytes + 255) & ~size_t(255);
 }
 
+// Every request has max_kv_len keys iff the lengths (each at most
+// max_kv_len) add up to B * max_kv_len.
+static int uniform_lengths(int B, int max_kv_len, long long total_kv) {
+  return (long long)max_kv_len * B == total_kv ? 1 : 0;
+}
+
 int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv, int max_kv_len) {
   (void)Hq;
   (void)D;
   if (B <= 0 || Hkv <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
-  // Workgroups to aim for: two per compute unit when every request has the
-  // same length (equal chunks finish together), four when lengths differ
-  // (more, smaller chunks even out the uneven last chunks).
-  const bool uniform = (long long)max_kv_len * B == total_kv;
-  const long long target = (uniform ? 2LL : 4LL) * attn_device_cu_count();
+  const long long cus = attn_device_cu_count();
   long long c = 1;
   while (c < max_kv_len) c <<= 1;  // one split per request at most
-  // largest power-of-two chunk >= 256 whose estimated workgroup count reaches target
-  while (c > 256) {
-    const long long wgs = (long long)Hkv * ((total_kv + c - 1) / c + B / 2);
-    if (wgs >= target) break;
-    c >>= 1;
+  if (uniform_lengths(B, max_kv_len, total_kv)) {
+    // Equal lengths: workgroups of up to four KV heads, each wave streaming
+    // a whole chunk.  Largest power-of-two chunk >= 256 that gives every
+    // compute unit a workgroup.
+    const int hpw = Hkv >= 4 ? 4 : Hkv >= 2 ? 2 : 1;
+    const long long groups = (Hkv + hpw - 1) / hpw;
+    while (c > 256 && groups * B * ((max_kv_len + c - 1) / c) < cus) c >>= 1;
+  } else {
+    // Ragged lengths: one KV head per workgroup, four waves per chunk.  Aim
+    // for four (head, chunk) workgroups per compute unit, so that smaller
+    // chunks even out the uneven last chunks of the requests.
+    while (c > 256) {
+      const long long wgs = (long long)Hkv * ((total_kv + c - 1) / c + B / 2);
+      if (wgs >= 4 * cus) break;
+      c >>= 1;
+    }
   }
   long long s = (max_kv_len + c - 1) / c;
   if (s < 1) s = 1;
@@ -171,7 +184,8 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
   float* ws = static_cast<float*>(workspace);
   rattn::DecodeArgs a{q, k, v, kv_indptr, o, lse, ws, ws + size_t(s) * rows * D,
                       ws + size_t(s) * rows * D + size_t(s) * rows,
-                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype, 0};
+                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype, 0,
+                      uniform_lengths(B, max_kv_len, total_kv)};
   return hip_status(rattn::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
 }
 
@@ -187,7 +201,8 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
   if (!o_part || !m_part || !l_part) return fail(ATTN_EINVAL, "decode_partials: null output");
   const int chunk = max_kv_len > 0 ? (max_kv_len + num_splits - 1) / num_splits : 0;
   rattn::DecodeArgs a{q, k, v, kv_indptr, nullptr, nullptr, o_part, m_part, l_part,
-                      B, Hq, Hkv, D, Hq / Hkv, num_splits, chunk, scale * kLog2e, dtype, 1};
+                      B, Hq, Hkv, D, Hq / Hkv, num_splits, chunk, scale * kLog2e, dtype, 1,
+                      uniform_lengths(B, max_kv_len, total_kv)};
   return hip_status(rattn::launch_decode_partials(a, static_cast<hipStream_t>(hip_stream)),
                     "decode_partials launch");
 }

@@ -17,6 +17,7 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+
 namespace rattn {
 
 // Key range [lo, hi) (offsets inside request b) of split i with chunk c.
@@ -76,7 +77,7 @@ __device__ __forceinline__ void decode_load(DecodeTile<T, D>& t, const uint16_t*
     key = key < hi ? key : hi - 1;
     const uint16_t* p = kbase + int64_t(key) * row_stride + 8 * h4;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) t.k[a][u] = ldg128(p + 32 * u);
+    for (int u = 0; u < NU; ++u) t.k[a][u] = ldg128_nt(p + 32 * u);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -84,10 +85,10 @@ __device__ __forceinline__ void decode_load(DecodeTile<T, D>& t, const uint16_t*
     key = key < hi ? key : hi - 1;
     const uint16_t* p = vbase + int64_t(key) * row_stride + (D / 16) * c16;
     if constexpr (D == 128) {
-      u32x4 x = ldg128(p);
+      u32x4 x = ldg128_nt(p);
       t.v[i][0] = x[0]; t.v[i][1] = x[1]; t.v[i][2] = x[2]; t.v[i][3] = x[3];
     } else {
-      u32x2 x = *reinterpret_cast<const u32x2*>(p);
+      u32x2 x = ldg64_nt(p);
       t.v[i][0] = x[0]; t.v[i][1] = x[1];
     }
   }
@@ -153,43 +154,59 @@ __device__ __forceinline__ void decode_step(DecodeState<T, D>& st, const DecodeT
   }
 }
 
-template <class T, int D, int W>
-__global__ __launch_bounds__(64 * W, 3) void decode_partial_mfma(DecodeArgs args) {
-  // grid (Hkv, s, B): the KV heads of one chunk are consecutive workgroups,
-  // so the Hkv slices of each packed K/V row are streamed at about the same
-  // time rather than one head's 256-byte slice at a time per row.
-  const int g = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
+// Workgroup = HPW x WPH waves: wave w works on KV head blockIdx.x * HPW +
+// w % HPW and takes the 32-key steps w / HPW, w / HPW + WPH, ... of the
+// chunk.  Grid (ceil(Hkv / HPW), s, B).
+//
+// Two shapes are used.  HPW = 4, WPH = 1 (equal request lengths): the
+// waves side by side stream the four head slices of the same packed K/V
+// rows, so a workgroup reads 1 KB row segments rather than 256-byte pieces
+// 2 KB apart -- on MI355X that lifts a plain stream of the decode's reads
+// from 5.6 to 6.2 TB/s -- and each wave owns its head's whole chunk, so
+// its result needs no combining.  HPW = 1, WPH = 4 (ragged lengths): four
+// waves share a head's chunk, so that a chunk, and the tail of the launch
+// made of the last chunks, finish four times sooner; the waves' results
+// are combined through LDS.
+template <class T, int D, int HPW, int WPH>
+__global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_partial_mfma(DecodeArgs args) {
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int hs = w % HPW, ks = w / HPW;
+  const int g = blockIdx.x * HPW + hs, i = blockIdx.y, b = blockIdx.z;
+  const bool head_ok = g < args.Hkv;  // a last workgroup may hold idle head slots
   const int G = args.G, Hq = args.Hq;
+  const int lane = threadIdx.x & 63, c16 = lane & 15, h4 = lane >> 4;
   const int64_t rows = int64_t(args.B) * Hq;
   const SplitRange sr = split_range(args.kv_indptr, b, i, args.chunk);
   const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
-  if (sr.lo >= sr.hi) {  // split unused by this request
+  if (sr.lo >= sr.hi) {  // split unused by this request (uniform over the workgroup)
+    if (!head_ok || ks != 0) return;
     if (args.partials_only) {
-      if (threadIdx.x < G) {
-        args.m_part[int64_t(i) * rows + row0 + threadIdx.x] = -INFINITY;
-        args.l_part[int64_t(i) * rows + row0 + threadIdx.x] = 0.f;
+      if (lane < G) {
+        args.m_part[int64_t(i) * rows + row0 + lane] = -INFINITY;
+        args.l_part[int64_t(i) * rows + row0 + lane] = 0.f;
       }
     } else if (i == 0) {    // empty request: O = 0, LSE = -inf
       typename T::elem* o = static_cast<typename T::elem*>(args.o);
-      for (int e = threadIdx.x; e < G * D; e += 64 * W) o[row0 * D + e] = typename T::elem(0.f);
-      if (args.lse && threadIdx.x < G) args.lse[row0 + threadIdx.x] = -INFINITY;
+      for (int e = lane; e < G * D; e += 64) o[row0 * D + e] = typename T::elem(0.f);
+      if (args.lse && lane < G) args.lse[row0 + lane] = -INFINITY;
     }
     return;
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int c16 = lane & 15, h4 = lane >> 4;
+  if (WPH == 1 && !head_ok) return;  // no barrier in this shape
+  const int gg = head_ok ? g : 0;    // idle slots (WPH > 1) read head 0 and store nothing
   const int64_t row_stride = int64_t(args.Hkv) * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(args.k) + (sr.base + sr.lo) * row_stride +
-                          int64_t(g) * D;
+                          int64_t(gg) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(args.v) + (sr.base + sr.lo) * row_stride +
-                          int64_t(g) * D;
+                          int64_t(gg) * D;
   const int n = sr.hi - sr.lo;
 
   // Q^T operand: head c16 (zero past G), slab u -> dims 32u + 8*h4 .. +8
   u32x4 qb[D / 32];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(args.q) + (row0 + (c16 < G ? c16 : 0)) * D +
-                         8 * h4;
+    const int64_t qrow = int64_t(b) * Hq + int64_t(gg) * G + (c16 < G ? c16 : 0);
+    const uint16_t* qp = static_cast<const uint16_t*>(args.q) + qrow * D + 8 * h4;
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
       qb[u] = ldg128(qp + 32 * u);
@@ -203,18 +220,24 @@ __global__ __launch_bounds__(64 * W, 3) void decode_partial_mfma(DecodeArgs args
   st.m = -INFINITY;
   st.l = 0.f;
 
-  // wave w takes 32-key steps w, w + W, w + 2W, ...  Each step's loads are
-  // consumed in issue order; the latency of one wave's loads is covered by
-  // the other waves resident on the same SIMD (the kernel is sized for three
-  // workgroups per compute unit), not by a software prefetch, which would
-  // need a second register buffer and halve that occupancy.
+  // 32-key steps ks, ks + WPH, ...  Two register buffers: the loads of the
+  // next step are in flight while the current one is computed.  Loads are
+  // issued unconditionally (key indices are clamped into the request), so
+  // every path leaves the same number of loads outstanding and the waits
+  // stay exact.
   const int nsteps = (n + 31) / 32;
-  for (int s0 = w; s0 < nsteps; s0 += W) {
-    DecodeTile<T, D> t;
-    decode_load<T, D>(t, kbase, vbase, row_stride, 32 * s0, n, c16, h4);
-    // all sixteen 16-byte loads are issued before the first is consumed
-    __builtin_amdgcn_sched_barrier(0);
-    decode_step<T, D>(st, t, qb, 32 * s0, n, args.scale_log2, h4);
+  {
+    DecodeTile<T, D> t0, t1;
+    decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * ks, n, c16, h4);
+    for (int s0 = ks; s0 < nsteps; s0 += 2 * WPH) {
+      decode_load<T, D>(t1, kbase, vbase, row_stride, 32 * (s0 + WPH), n, c16, h4);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_step<T, D>(st, t0, qb, 32 * s0, n, args.scale_log2, h4);
+      if (s0 + WPH >= nsteps) break;
+      decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * (s0 + 2 * WPH), n, c16, h4);
+      __builtin_amdgcn_sched_barrier(0);
+      decode_step<T, D>(st, t1, qb, 32 * (s0 + WPH), n, args.scale_log2, h4);
+    }
   }
 
   // lane sums -> head sums (the four h4 lanes of head c16)
@@ -222,43 +245,14 @@ __global__ __launch_bounds__(64 * W, 3) void decode_partial_mfma(DecodeArgs args
   l += shfl_xor(l, 16);
   l += shfl_xor(l, 32);
 
-  // combine the W waves through LDS
-  __shared__ float red_m[W][16];
-  __shared__ float red_l[W][16];
-  __shared__ float red_o[W][16][D + 4];
-  if (c16 < G) {
-    if (h4 == 0) {
-      red_m[w][c16] = st.m;  // -inf for a wave that had no step
-      red_l[w][c16] = l;
-    }
-#pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red_o[w][c16][(D / 4) * h4 + (D / 16) * r + j] = st.o[j][r];
-  }
-  __syncthreads();
-
-  // This workgroup's result for its G heads: O (normalised), M (log2 units),
+  // This workgroup's result for its heads: O (normalised), M (log2 units),
   // L.  A request held by a single split is final here; otherwise this is
   // partial i, merged by decode_merge_kernel.
   const int n_b = int(args.kv_indptr[b + 1] - sr.base);
   const int splits_b = args.partials_only ? 0 : (n_b + args.chunk - 1) / args.chunk;
-  typename T::elem* out = static_cast<typename T::elem*>(args.o);
-  for (int e = threadIdx.x; e < G * D; e += 64 * W) {
-    const int h = e / D, d = e % D;
-    float M = red_m[0][h];
-#pragma unroll
-    for (int ww = 1; ww < W; ++ww) M = fmaxf(M, red_m[ww][h]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const float f = fexp2(red_m[ww][h] - M);
-      L += red_l[ww][h] * f;
-      O += red_o[ww][h][d] * f;
-    }
-    const int64_t row = row0 + h;
+  auto emit = [&](int64_t row, int d, float O, float M, float L) {
     if (splits_b == 1) {  // the whole request in one split: final output
-      out[row * D + d] = typename T::elem(O / L);
+      static_cast<typename T::elem*>(args.o)[row * D + d] = typename T::elem(O / L);
       if (d == 0 && args.lse) args.lse[row] = (M + flog2(L)) * kLn2;
     } else {
       args.o_part[(int64_t(i) * rows + row) * D + d] = O / L;
@@ -266,6 +260,49 @@ __global__ __launch_bounds__(64 * W, 3) void decode_partial_mfma(DecodeArgs args
         args.m_part[int64_t(i) * rows + row] = M * kLn2;
         args.l_part[int64_t(i) * rows + row] = L;
       }
+    }
+  };
+  if constexpr (WPH == 1) {
+    // lane (c16, h4) holds dims (D/4)*h4 + (D/16)*r + j of head c16 in o[j][r];
+    // st.m is finite (the chunk holds a key)
+    if (c16 >= G) return;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        const int d = (D / 4) * h4 + (D / 16) * r + j;
+        emit(row0 + c16, d, st.o[j][r], st.m, l);
+      }
+  } else {
+    // combine the WPH waves of each head through LDS
+    __shared__ float red_m[WPH][HPW][16];
+    __shared__ float red_l[WPH][HPW][16];
+    __shared__ float red_o[WPH][HPW][16][D + 4];
+    if (c16 < G) {
+      if (h4 == 0) {
+        red_m[ks][hs][c16] = st.m;  // -inf for a wave that had no step
+        red_l[ks][hs][c16] = l;
+      }
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red_o[ks][hs][c16][(D / 4) * h4 + (D / 16) * r + j] = st.o[j][r];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < HPW * G * D; e += 64 * HPW * WPH) {
+      const int slot = e / (G * D), h = (e / D) % G, d = e % D;
+      if (blockIdx.x * HPW + slot >= args.Hkv) continue;
+      float M = red_m[0][slot][h];
+#pragma unroll
+      for (int k2 = 1; k2 < WPH; ++k2) M = fmaxf(M, red_m[k2][slot][h]);
+      float L = 0.f, O = 0.f;
+#pragma unroll
+      for (int k2 = 0; k2 < WPH; ++k2) {
+        const float f = fexp2(red_m[k2][slot][h] - M);
+        L += red_l[k2][slot][h] * f;
+        O += red_o[k2][slot][h][d] * f;
+      }
+      emit(int64_t(b) * Hq + int64_t(blockIdx.x * HPW + slot) * G + h, d, O, M, L);
     }
   }
 }
@@ -510,9 +547,34 @@ __global__ void split_ranges_kernel(const int32_t* kv_indptr, int B, int s, int 
 
 // ---- launchers -----------------------------------------------------------
 
+// Workgroup shape: four waves side by side on four KV heads when every
+// request has the same length (the host passes uniform = 1), one KV head
+// with four waves splitting its chunk otherwise.  Heads per workgroup never
+// exceed Hkv.
+template <class T, int D>
+static void launch_partial_mfma_t(const DecodeArgs& a, hipStream_t st) {
+  const int hpw = a.uniform ? (a.Hkv >= 4 ? 4 : a.Hkv >= 2 ? 2 : 1) : 1;
+  const dim3 grid(unsigned((a.Hkv + hpw - 1) / hpw), unsigned(a.s), unsigned(a.B));
+  switch (hpw) {
+    case 4: hipLaunchKernelGGL((decode_partial_mfma<T, D, 4, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_partial_mfma<T, D, 2, 1>), grid, dim3(128), 0, st, a); break;
+    default:
+      if (a.uniform) hipLaunchKernelGGL((decode_partial_mfma<T, D, 1, 1>), grid, dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_partial_mfma<T, D, 1, 4>), grid, dim3(256), 0, st, a);
+      break;
+  }
+}
+
+static void launch_partial_mfma(const DecodeArgs& a, hipStream_t st) {
+  if (a.dtype == 1) {
+    if (a.D == 64) launch_partial_mfma_t<BF16, 64>(a, st); else launch_partial_mfma_t<BF16, 128>(a, st);
+  } else {
+    if (a.D == 64) launch_partial_mfma_t<F16, 64>(a, st); else launch_partial_mfma_t<F16, 128>(a, st);
+  }
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
-  const dim3 mgrid_mfma(a.Hkv, a.s, a.B);
   if (a.dtype == 0) {  // fp32: partial kernel, then the standalone merge
     if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
@@ -521,14 +583,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, a.B * a.Hq, a.D, a.o, 0, a.lse};
     return launch_merge(m, st);
   } else {  // 16-bit: MFMA partial kernel, then the merge of multi-split requests
-    constexpr int W = 4;
-    if (a.dtype == 1) {
-      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-      else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-    } else {
-      if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-      else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-    }
+    launch_partial_mfma(a, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.s == 1) return e;  // one split: every request is final
     const dim3 mgrid(unsigned((int64_t(a.B) * a.Hq + 3) / 4));
@@ -545,17 +600,11 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
-  const dim3 mgrid_mfma(a.Hkv, a.s, a.B);
-  constexpr int W = 4;
   if (a.dtype == 0) {
     if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
     else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
-  } else if (a.dtype == 1) {
-    if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<BF16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-    else hipLaunchKernelGGL((decode_partial_mfma<BF16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
   } else {
-    if (a.D == 64) hipLaunchKernelGGL((decode_partial_mfma<F16, 64, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
-    else hipLaunchKernelGGL((decode_partial_mfma<F16, 128, W>), mgrid_mfma, dim3(64 * W), 0, st, a);
+    launch_partial_mfma(a, st);
   }
   return hipGetLastError();
 }

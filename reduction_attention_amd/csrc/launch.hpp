@@ -26,6 +26,8 @@ struct DecodeArgs {
   int partials_only;  // 1: every used split writes a partial, unused splits
                       // write (m, l) = (-inf, 0); 0: single-split requests are
                       // written to o / lse directly
+  int uniform;        // 1: every request has max_kv_len keys (picks the
+                      // workgroup shape; results do not depend on it)
 };
 
 struct MergeArgs {

@@ -57,10 +57,14 @@ def test_workspace_formula(lib):
 
 
 def test_split_rule(lib):
-    # no device here: the CU count falls back to 256 -> 512 workgroups (uniform), 1024 (ragged)
+    # no device here: the CU count falls back to 256 -> 256 four-head workgroups
+    # (uniform), 1024 one-head workgroups (ragged)
     assert lib.attn_device_cu_count() == 256
-    # Llama-3-8B-shaped decode: 16 requests x 4096 keys, 8 KV heads -> c = 1024, s = 4
-    assert lib.attn_decode_choose_splits(16, 32, 8, 128, 16 * 4096, 4096) == 4
+    # Llama-3-8B-shaped decode: 16 requests x 4096 keys, 8 KV heads -> 2 head
+    # groups x 16 x 8 chunks = 256 workgroups at c = 512, s = 8
+    assert lib.attn_decode_choose_splits(16, 32, 8, 128, 16 * 4096, 4096) == 8
+    # equal lengths, 2 KV heads (two-head workgroups): 4 x 1024 keys -> c = 256, s = 4
+    assert lib.attn_decode_choose_splits(4, 8, 2, 128, 4 * 1024, 1024) == 4
     # ragged: 226896 keys over 64 requests, longest 27752 -> c = 2048, s = 14
     assert lib.attn_decode_choose_splits(64, 64, 8, 128, 226896, 27752) == 14
     assert lib.attn_decode_choose_splits(1, 4, 1, 64, 256, 256) == 1
