@@ -479,36 +479,63 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 template <int D, class OutT>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DL = (D + 63) / 64;
+  constexpr int SB = 16;  // splits whose loads are issued together
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.B) * a.Hq;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int b = int(row / a.Hq);
-  const int n_b = int(a.kv_indptr[b + 1] - a.kv_indptr[b]);
-  const int splits_b = a.chunk > 0 ? (n_b + a.chunk - 1) / a.chunk : 0;
-  if (splits_b <= 1) return;
+  // The request's split count, the first SB splits' (m, l) and their
+  // partial outputs are loaded at once (every address lies inside the
+  // workspace; values of splits the request does not use are discarded
+  // below, never multiplied), so the merge costs one memory round trip.
+  const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
+  const int s0n = a.s < SB ? a.s : SB;
   float mi = -INFINITY, li = 0.f;
-  if (lane < splits_b) {
+  if (lane < s0n) {
     mi = a.m_part[int64_t(lane) * rows + row];
     li = a.l_part[int64_t(lane) * rows + row];
   }
+  float ov[SB][DL];
+#pragma unroll
+  for (int j = 0; j < SB; ++j)
+#pragma unroll
+    for (int x = 0; x < DL; ++x)
+      ov[j][x] = (j < s0n && lane + 64 * x < D) ? a.o_part[(int64_t(j) * rows + row) * D + lane + 64 * x] : 0.f;
+  const int n_b = int(kb1 - kb0);
+  const int splits_b = a.chunk > 0 ? (n_b + a.chunk - 1) / a.chunk : 0;
+  if (splits_b <= 1) return;
+  if (lane >= splits_b) { mi = -INFINITY; li = 0.f; }
   float M = mi;
+  for (int i = SB + lane; i < splits_b; i += 64) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-  for (int i = 64 + lane; i < splits_b; i += 64) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
-  if (splits_b > 64) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-  }
   float acc[DL];
 #pragma unroll
   for (int x = 0; x < DL; ++x) acc[x] = 0.f;
   float wsum = 0.f;
-  for (int i0 = 0; i0 < splits_b; i0 += 64) {
+  {
+    // splits 0 .. SB-1 from the registers loaded above
+    const float wi = lane < splits_b ? li * fexp2((mi - M) * kLog2e) : 0.f;
+    float ws = wi;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ws += shfl_xor(ws, off);
+    wsum += ws;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const float wj = __shfl(wi, j, 64);
+      if (j < splits_b) {
+#pragma unroll
+        for (int x = 0; x < DL; ++x) acc[x] += wj * ov[j][x];
+      }
+    }
+  }
+  // splits SB .. splits_b-1, if any, in batches of 64
+  for (int i0 = SB; i0 < splits_b; i0 += 64) {
     float wi = 0.f;
     if (i0 + lane < splits_b) {
-      const float m2 = i0 == 0 ? mi : a.m_part[int64_t(i0 + lane) * rows + row];
-      const float l2 = i0 == 0 ? li : a.l_part[int64_t(i0 + lane) * rows + row];
+      const float m2 = a.m_part[int64_t(i0 + lane) * rows + row];
+      const float l2 = a.l_part[int64_t(i0 + lane) * rows + row];
       wi = l2 * fexp2((m2 - M) * kLog2e);
     }
     float ws = wi;

@@ -82,6 +82,21 @@ def test_small_ragged_shapes(dtype, D, G):
     assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[4]).all())
 
 
+@pytest.mark.parametrize("Hkv", [1, 2, 6])
+def test_equal_lengths_head_groups(Hkv):
+    """Equal request lengths take the multi-head workgroup shape (up to four KV
+    heads per workgroup; Hkv = 6 leaves idle head slots in the last one)."""
+    lengths = [300] * 5
+    G = 4
+    q, k, v, kv = synth.decode_inputs(len(lengths), G * Hkv, Hkv, 128, lengths, torch.bfloat16,
+                                      seed=40 + Hkv)
+    inp = dict(q=q, k=k, v=v, kv_indptr=kv)
+    o_ref, lse_ref = oracle_decode(inp, 128 ** -0.5)
+    for s in (0, 1, 2, 5, 19):
+        o, lse = run_decode(inp, max(lengths), s)
+        check(f"equal lengths Hkv={Hkv} s={s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
 def test_split_ranges_bit_exact():
     import reduction_attention_amd as r
     lengths = [1, 31, 32, 33, 0, 300, 4096, 517, 7]
