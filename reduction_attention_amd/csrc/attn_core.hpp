@@ -387,4 +387,162 @@ __device__ __forceinline__ void row_store(const RowState<D>& st, uint16_t* orow,
   if (lse_out && h == 0) *lse_out = l > 0.f ? (st.m + flog2(l)) * kLn2 : -INFINITY;
 }
 
+
+// ---------------------------------------------------------------------------
+// Natural-layout tiles written straight from global memory into LDS.
+//
+// K and V tiles of BK keys keep their global row layout ([key][D], D*2-byte
+// rows, no padding); a row's 16-byte chunks are stored at permuted slots,
+// slot = chunk ^ f(row), so that the LDS reads below hit distinct banks.
+// The tiles are filled by buffer loads that write LDS directly (each wave
+// instruction writes 64 lanes x 16 bytes = RPI whole rows, lane l taking
+// slot l % CPR of its row and fetching the chunk that belongs there), so no
+// registers stage the tile and no instruction re-packs it.  V is consumed
+// through LDS transpose reads (ds_read_b64_tr_b16), which hand each lane
+// four consecutive keys of one dimension -- the reduction run an MFMA
+// operand needs -- from the natural layout.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Swz {
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;     // rows per 64-lane instruction
+  static constexpr int RP = 16 / CPR;      // rows per 256 bytes (one pass over the 64 banks)
+  // K: the 16 rows one 16-lane read group touches land on distinct slots
+  static __device__ __forceinline__ int fk(int r) { return (r / RP) % CPR; }
+  // V: the four consecutive rows a transpose-read group touches land on
+  // disjoint 4-chunk blocks
+  static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RP) % (4 / RP)); }
+};
+
+// One BK-key tile (K if IS_V is false, else V) of a request with n_keys
+// keys, rows key0 .. key0+BK-1, into the LDS stage at dst; rows past the
+// request end arrive as zeros (the buffer resource ends there).  The NT
+// threads share the BK / RPI instructions.  Completion is tracked by vmcnt:
+// the caller waits for it before the barrier that publishes the stage.
+template <int D, int BK, int NT, bool IS_V>
+__device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, int row_stride,
+                                         int key0, int n_keys, int tid) {
+  typedef Swz<D> S;
+  constexpr int NI = BK / S::RPI, W = NT / 64;
+  static_assert(NI % W == 0, "tile instructions must split evenly over the waves");
+  // raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte count,
+  // 32-bit data format) over the request's rows from key0 on; rows past
+  // the request end read as zeros
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t addr = uint64_t(size_t(base + int64_t(key0) * row_stride));
+  const int64_t bytes = int64_t(n_keys - key0) * row_stride * 2;
+  const int64_t cap = 0x7fffffff;
+  i32x4 rsv;
+  rsv[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr)));
+  rsv[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
+  rsv[2] = __builtin_amdgcn_readfirstlane(int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  rsv[3] = 0x00020000;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst));
+#pragma unroll
+  for (int x = 0; x < NI / W; ++x) {
+    const int inst = w + W * x;
+    const int r = S::RPI * inst + lane / S::CPR;
+    const int slot = lane % S::CPR;
+    const int chunk = slot ^ (IS_V ? S::fv(r) : S::fk(r));
+    const int voff = (r * row_stride + 8 * chunk) * 2;
+    // Written as assembly so that the compiler, which cannot tell which
+    // LDS bytes a direct-to-LDS load writes, does not make every later LDS
+    // read wait for it: the tile goes to a stage no read of the same step
+    // touches, and the caller waits (vmcnt) before publishing it.
+    __asm__ volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(lds0 + inst * 1024), "v"(voff), "s"(rsv)
+        : "memory", "m0");
+  }
+}
+
+// One 32-key block of S^T over a swizzled K tile (as qk_block).
+template <class T, int D>
+__device__ __forceinline__ void qk_block_sw(f32x16& s, const uint16_t* klds, int kb,
+                                            const u32x4 (&qb)[D / 16], int lane) {
+  typedef typename T::vec8 vec8;
+  typedef Swz<D> S;
+  const int r = 32 * kb + (lane & 31), h = lane >> 5;
+  const uint16_t* row = klds + r * D;
+  const int f = S::fk(r);
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(row + 8 * ((2 * u + h) ^ f));
+    acc = T::mfma32(as<vec8>(a), as<vec8>(qb[u]), acc);
+  }
+  s = acc;
+}
+
+template <class T, int D, int BK, int RB>
+__device__ __forceinline__ void qk_tile_sw(f32x16 (&s)[RB][BK / 32], const uint16_t* klds,
+                                           const u32x4 (&qb)[RB][D / 16], int lane) {
+  typedef typename T::vec8 vec8;
+  typedef Swz<D> S;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < BK / 32; ++kb) {
+    const int r = 32 * kb + (lane & 31);
+    const uint16_t* row = klds + r * D;
+    const int f = S::fk(r);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[rb][kb][i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(row + 8 * ((2 * u + h) ^ f));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        s[rb][kb] = T::mfma32(as<vec8>(a), as<vec8>(qb[rb][u]), s[rb][kb]);
+    }
+  }
+}
+
+// Four consecutive keys k0 .. k0+3 of dimension dbase + (lane % 16) from a
+// swizzled V tile: lane q + 4e of the 16-lane group supplies row k0 + e,
+// dims dbase + 4q .. +4.
+template <int D>
+__device__ __forceinline__ u32x2 v_tr4(const uint16_t* vlds, int k0, int dbase, int lane) {
+  typedef Swz<D> S;
+  const int i = lane & 15, q = i & 3, e = i >> 2;
+  const int r = k0 + e, dim = dbase + 4 * q;
+  const uint16_t* p = vlds + r * D + 8 * ((dim >> 3) ^ S::fv(r)) + (dim & 7);
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// O^T += V^T P^T over a swizzled V tile.  For score block kb and half t, the
+// P operand of lane l (h = l / 32) holds keys 16t + 4h + {0..3} in k-slots
+// 0..3 and 16t + 4h + 8 + {0..3} in k-slots 4..7 (the order the S^T
+// accumulator hands them over in); two transpose reads give lane l the V
+// values of its dimension for exactly those keys.
+template <class T, int D, int BK, int RB>
+__device__ __forceinline__ void pv_tile_tr(RowState<D> (&st)[RB],
+                                           const typename T::vec8 (&pb)[RB][BK / 32][2],
+                                           const uint16_t* vlds, int lane) {
+  typedef typename T::vec8 vec8;
+  const int h = lane >> 5, g2 = (lane >> 4) & 1;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int kb = 0; kb < BK / 32; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int k0 = 32 * kb + 16 * t + 4 * h, dbase = 32 * db + 16 * g2;
+        const u32x2 lo = v_tr4<D>(vlds, k0, dbase, lane);
+        const u32x2 hi = v_tr4<D>(vlds, k0 + 8, dbase, lane);
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          st[rb].o[db] = T::mfma32(as<vec8>(a), pb[rb][kb][t], st[rb].o[db]);
+      }
+}
+
 }  // namespace rattn

@@ -1,9 +1,9 @@
 // prefill.hip -- fused prefill attention on gfx950: dense / causal over a
 // ragged batch, and block-sparse over STOF's two-level mask.
 //
-// Both kernels stream key/value tiles of 64 keys through a two-stage LDS
-// ring while the query tile stays in registers, and fuse QK^T, the row
-// max, the exp-sum and PV into one loop (attn_core.hpp).  The dense kernel
+// Both kernels stream key/value tiles of 64 keys through LDS while the query
+// tile stays in registers, and fuse QK^T, the row max, the exp-sum and PV
+// into one loop (attn_core.hpp).  The dense kernel
 // follows the iterative tiling and horizontal fusion of the Cleave article
 // (tip.co.jp, "複数リダクションのスケジューリング"), with dynamic batch and
 // sequence lengths read from indptr arrays at run time so one compiled
@@ -25,10 +25,12 @@ namespace rattn {
 // Keys arrive in tiles of BK.  In step j a wave computes the scores of tile
 // j + 1 and the value update of tile j (weights from the previous step),
 // then the weights of tile j + 1.  K therefore runs one tile ahead of V:
-// LDS holds two K stages and two V stages, and the loads issued at the top
-// of step j (K of tile j + 2, V of tile j + 1) land, at its end, in the
-// stages that step j - 1 released.  One barrier per step.  The ring takes
-// 70 KB at D = 128, so two workgroups share a compute unit and one's
+// LDS holds two K stages and two V stages (64 KB at D = 128), and the tiles
+// issued at the top of step j (K of tile j + 2, V of tile j + 1) stream
+// straight from memory into the stages step j - 1 released while the step
+// computes; one wait and one barrier end the step.  Tiles keep their
+// natural layout with swizzled 16-byte slots; V is read through transposing
+// LDS reads (attn_core.hpp).  Two workgroups share a compute unit, so one's
 // start-up (its query rows and first tiles coming in from memory) and
 // barriers overlap the other's matrix work.  Shape knobs (waves, row
 // blocks, occupancy) were swept on MI355X; the defaults won.
@@ -82,8 +84,13 @@ void prefill_kernel(PrefillArgs a) {
   constexpr int NT = 64 * kPrefillWaves, RB = kPrefillRB, BQ = kPrefillBQ, BK = kPrefillBK;
   typedef TileGeom<D, BK> Gm;
   typedef typename T::vec8 vec8;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * Gm::K_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * Gm::V_ELEMS];
+  constexpr int TE = BK * D;  // elements per natural-layout tile
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
+  uint16_t* const lds_k0 = lds_k;
+  uint16_t* const lds_k1 = lds_k + TE;
+  uint16_t* const lds_v0 = lds_v;
+  uint16_t* const lds_v1 = lds_v + TE;
 
   // grid (Hq, B, query tiles): workgroups are dispatched in linear order, so
   // with the query tile slowest every causal tile of one size goes out
@@ -131,15 +138,12 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
 
   // prologue: K of tiles 0 and 1, V of tile 0
-  TileRegs<D, BK, NT> rr;
   if (ntiles > 0) {
-    tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, 0, 0, n_kv, tid);
-    tile_store<D, BK, NT>(rr, lds_k, lds_v, tid);
+    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, 0, n_kv, tid);
+    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, 0, n_kv, tid);
   }
-  if (ntiles > 1) {
-    tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, BK, BK, n_kv, tid, true, false);
-    tile_store<D, BK, NT>(rr, lds_k + Gm::K_ELEMS, lds_v, tid, true, false);
-  }
+  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, BK, n_kv, tid);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
   // causal / ragged-tail masking of tile j's scores, needed on few tiles
@@ -179,29 +183,33 @@ void prefill_kernel(PrefillArgs a) {
   f32x16 sc[RB][Gm::NKB];
   vec8 pb[RB][Gm::NKB][2];
   if (wnt > 0) {
-    qk_tile_rb<T, D, BK, RB>(sc, lds_k, qb, lane);
+    qk_tile_sw<T, D, BK, RB>(sc, lds_k0, qb, lane);
     weights(sc, 0, pb);
   }
   // step 0 refills K stage 0, which every wave must have finished reading
   __syncthreads();
-  for (int j = 0; j < ntiles; ++j) {
-    const bool kmore = j + 2 < ntiles, vmore = j + 1 < ntiles;
-    if (vmore)
-      tile_load<D, BK, NT>(rr, kbase, vbase, row_stride, (j + 2) * BK, (j + 1) * BK, n_kv, tid,
-                           kmore, true);
+  // step j: K of tile j+2 and V of tile j+1 stream into the stages step
+  // j-1 freed (K stage j%2, V stage (j+1)%2) while the scores of tile j+1
+  // (K stage (j+1)%2) and the value update of tile j (V stage j%2) run.
+  // (The stage pointers are restrict-qualified: the tile a step streams in
+  // and the tiles it reads never overlap, and saying so keeps the compiler
+  // from making the reads wait for the stream.)
+  auto step = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill,
+                  const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
+    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, tid);
     if (j + 1 < wnt) {
-      qk_tile_rb<T, D, BK, RB>(sc, lds_k + ((j + 1) & 1) * Gm::K_ELEMS, qb, lane);
+      qk_tile_sw<T, D, BK, RB>(sc, kread, qb, lane);
       lds_pipeline<Gm::NKB * D / 16, RB>();
     }
-    if (j < wnt) {
-      pv_tile_rb<T, D, BK, RB>(st, pb, lds_v + (j & 1) * Gm::V_ELEMS, lane);
-      lds_pipeline<2 * Gm::NKB * D / 32, RB>();
-    }
+    if (j < wnt) pv_tile_tr<T, D, BK, RB>(st, pb, vread, lane);
     if (j + 1 < wnt) weights(sc, j + 1, pb);
-    if (vmore)
-      tile_store<D, BK, NT>(rr, lds_k + (j & 1) * Gm::K_ELEMS, lds_v + ((j + 1) & 1) * Gm::V_ELEMS,
-                            tid, kmore, true);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's tiles are in LDS
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    step(j, lds_k0, lds_v1, lds_k1, lds_v0);
+    if (j + 1 < ntiles) step(j + 1, lds_k1, lds_v0, lds_k0, lds_v1);
   }
 
 #pragma unroll
