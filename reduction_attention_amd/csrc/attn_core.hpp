@@ -221,7 +221,8 @@ __device__ __forceinline__ float tile_rowmax(const f32x16 (&s)[NKB], int xaddr) 
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = max3(mx, s[kb][r], s[kb][r + 1]);
-  return fmaxf(mx, swap_halves(mx, xaddr));
+  (void)xaddr;
+  return max_halves(mx);
 }
 
 // Step 2: raise the reference max to the tile max mx (raw score units; c =
@@ -362,7 +363,7 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const f32x16 (&s)[BK
 template <class T, int D>
 __device__ __forceinline__ void row_store(const RowState<D>& st, uint16_t* orow, float* lse_out,
                                           int lane) {
-  float l = st.l + swap_halves(st.l, (lane ^ 32) << 2);
+  float l = sum_halves(st.l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int h = lane >> 5;
   if (orow) {

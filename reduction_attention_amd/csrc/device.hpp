@@ -114,4 +114,19 @@ __device__ __forceinline__ float swap_halves(float x, int addr) {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
+// x combined with its partner lane l ^ 32, in every lane, through the
+// cross-half lane swap (a VALU op, no LDS round trip): swapping the upper
+// half of one copy of x with the lower half of another leaves, in each
+// lane, x of both partners.
+__device__ __forceinline__ float max_halves(float x) {
+  const int b = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const int b = __float_as_int(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
 }  // namespace rattn
