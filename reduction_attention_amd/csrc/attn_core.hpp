@@ -415,20 +415,37 @@ struct Swz {
   static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RP) % (4 / RP)); }
 };
 
-// One BK-key tile (K if IS_V is false, else V) of a request with n_keys
-// keys, rows key0 .. key0+BK-1, into the LDS stage at dst; rows past the
-// request end arrive as zeros (the buffer resource ends there).  The NT
-// threads share the BK / RPI instructions.  Completion is tracked by vmcnt:
-// the caller waits for it before the barrier that publishes the stage.
+// Per-lane byte offset of this thread's first 16-byte chunk in a tile
+// (K if IS_V is false, else V), for dma_tile.  The NT threads share the
+// BK / RPI instructions of a tile, wave w taking instructions w, w + W, ...;
+// those rows differ by multiples of RPI * W, which leave the swizzle of a
+// lane's row unchanged, so a lane's later chunks sit at fixed distances
+// from the first and one offset serves the whole loop.
 template <int D, int BK, int NT, bool IS_V>
+__device__ __forceinline__ int dma_lane_offset(int row_stride, int tid) {
+  typedef Swz<D> S;
+  constexpr int W = NT / 64, STEP = S::RPI * W;
+  static_assert((STEP / S::RP) % S::CPR == 0 && (STEP / S::RP) % (4 / S::RP) == 0,
+                "rows one wave loads must share their swizzle");
+  const int lane = tid & 63, w = tid >> 6;
+  const int r = S::RPI * w + lane / S::CPR;
+  const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
+  return (r * row_stride + 8 * chunk) * 2;
+}
+
+// One BK-key tile of a request with n_keys keys, rows key0 .. key0+BK-1,
+// into the LDS stage at dst; rows past the request end arrive as zeros (the
+// buffer resource ends there).  lane_off comes from dma_lane_offset.
+// Completion is tracked by vmcnt: the caller waits for it before the
+// barrier that publishes the stage.
+template <int D, int BK, int NT>
 __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, int row_stride,
-                                         int key0, int n_keys, int tid) {
+                                         int key0, int n_keys, int lane_off, int tid) {
   typedef Swz<D> S;
   constexpr int NI = BK / S::RPI, W = NT / 64;
   static_assert(NI % W == 0, "tile instructions must split evenly over the waves");
   // raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte count,
-  // 32-bit data format) over the request's rows from key0 on; rows past
-  // the request end read as zeros
+  // 32-bit data format) over the request's rows from key0 on
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const uint64_t addr = uint64_t(size_t(base + int64_t(key0) * row_stride));
   const int64_t bytes = int64_t(n_keys - key0) * row_stride * 2;
@@ -438,15 +455,11 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
   rsv[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
   rsv[2] = __builtin_amdgcn_readfirstlane(int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
   rsv[3] = 0x00020000;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst));
 #pragma unroll
   for (int x = 0; x < NI / W; ++x) {
     const int inst = w + W * x;
-    const int r = S::RPI * inst + lane / S::CPR;
-    const int slot = lane % S::CPR;
-    const int chunk = slot ^ (IS_V ? S::fv(r) : S::fk(r));
-    const int voff = (r * row_stride + 8 * chunk) * 2;
     // Written as assembly so that the compiler, which cannot tell which
     // LDS bytes a direct-to-LDS load writes, does not make every later LDS
     // read wait for it: the tile goes to a stage no read of the same step
@@ -455,7 +468,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(lds0 + inst * 1024), "v"(voff), "s"(rsv)
+        : "s"(lds0 + inst * 1024), "v"(lane_off + x * (S::RPI * W * row_stride * 2)), "s"(rsv)
         : "memory", "m0");
   }
 }

@@ -138,11 +138,13 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
 
   // prologue: K of tiles 0 and 1, V of tile 0
+  const int koff = dma_lane_offset<D, BK, NT, false>(row_stride, tid);
+  const int voff = dma_lane_offset<D, BK, NT, true>(row_stride, tid);
   if (ntiles > 0) {
-    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, 0, n_kv, tid);
-    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, 0, n_kv, tid);
+    dma_tile<D, BK, NT>(lds_k0, kbase, row_stride, 0, n_kv, koff, tid);
+    dma_tile<D, BK, NT>(lds_v0, vbase, row_stride, 0, n_kv, voff, tid);
   }
-  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, BK, n_kv, tid);
+  if (ntiles > 1) dma_tile<D, BK, NT>(lds_k1, kbase, row_stride, BK, n_kv, koff, tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
@@ -196,8 +198,8 @@ void prefill_kernel(PrefillArgs a) {
   // from making the reads wait for the stream.)
   auto step = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill,
                   const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
-    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, tid);
-    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, tid);
+    if (j + 2 < ntiles) dma_tile<D, BK, NT>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, koff, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, voff, tid);
     if (j + 1 < wnt) {
       qk_tile_sw<T, D, BK, RB>(sc, kread, qb, lane);
       lds_pipeline<Gm::NKB * D / 16, RB>();
