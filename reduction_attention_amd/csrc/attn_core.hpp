@@ -415,30 +415,22 @@ struct Swz {
   static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RP) % (4 / RP)); }
 };
 
-// Per-lane byte offset of this thread's first 16-byte chunk in a tile
-// (K if IS_V is false, else V), for dma_tile.  The NT threads share the
-// BK / RPI instructions of a tile, wave w taking instructions w, w + W, ...;
-// those rows differ by multiples of RPI * W, which leave the swizzle of a
-// lane's row unchanged, so a lane's later chunks sit at fixed distances
-// from the first and one offset serves the whole loop.
-template <int D, int BK, int NT, bool IS_V>
+// Byte offset of this lane's row within a tile instruction's RPI rows
+// (computed once per workgroup; dma_tile adds the rest with cheap ops).
+template <int D>
 __device__ __forceinline__ int dma_lane_offset(int row_stride, int tid) {
-  typedef Swz<D> S;
-  constexpr int W = NT / 64, STEP = S::RPI * W;
-  static_assert((STEP / S::RP) % S::CPR == 0 && (STEP / S::RP) % (4 / S::RP) == 0,
-                "rows one wave loads must share their swizzle");
-  const int lane = tid & 63, w = tid >> 6;
-  const int r = S::RPI * w + lane / S::CPR;
-  const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
-  return (r * row_stride + 8 * chunk) * 2;
+  return ((tid & 63) / Swz<D>::CPR) * row_stride * 2;
 }
 
-// One BK-key tile of a request with n_keys keys, rows key0 .. key0+BK-1,
-// into the LDS stage at dst; rows past the request end arrive as zeros (the
-// buffer resource ends there).  lane_off comes from dma_lane_offset.
+// One BK-key tile (K if IS_V is false, else V) of a request with n_keys
+// keys, rows key0 .. key0+BK-1, into the LDS stage at dst; rows past the
+// request end arrive as zeros (the buffer resource ends there).  The NT
+// threads share the BK / RPI instructions of the tile, wave w taking
+// instructions w, w + W, ...; lane l writes slot l % CPR of row
+// RPI * inst + l / CPR and fetches the chunk that belongs there.
 // Completion is tracked by vmcnt: the caller waits for it before the
 // barrier that publishes the stage.
-template <int D, int BK, int NT>
+template <int D, int BK, int NT, bool IS_V>
 __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, int row_stride,
                                          int key0, int n_keys, int lane_off, int tid) {
   typedef Swz<D> S;
@@ -455,11 +447,15 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
   rsv[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
   rsv[2] = __builtin_amdgcn_readfirstlane(int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
   rsv[3] = 0x00020000;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst));
 #pragma unroll
   for (int x = 0; x < NI / W; ++x) {
     const int inst = w + W * x;
+    const int r = S::RPI * inst + lane / S::CPR;
+    const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
+    const int rows_off = __builtin_amdgcn_readfirstlane(S::RPI * inst * row_stride * 2);
+    const int voff = lane_off + rows_off + 16 * chunk;
     // Written as assembly so that the compiler, which cannot tell which
     // LDS bytes a direct-to-LDS load writes, does not make every later LDS
     // read wait for it: the tile goes to a stage no read of the same step
@@ -468,7 +464,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(lds0 + inst * 1024), "v"(lane_off + x * (S::RPI * W * row_stride * 2)), "s"(rsv)
+        : "s"(lds0 + inst * 1024), "v"(voff), "s"(rsv)
         : "memory", "m0");
   }
 }

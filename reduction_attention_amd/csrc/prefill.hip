@@ -138,13 +138,12 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
 
   // prologue: K of tiles 0 and 1, V of tile 0
-  const int koff = dma_lane_offset<D, BK, NT, false>(row_stride, tid);
-  const int voff = dma_lane_offset<D, BK, NT, true>(row_stride, tid);
+  const int loff = dma_lane_offset<D>(row_stride, tid);
   if (ntiles > 0) {
-    dma_tile<D, BK, NT>(lds_k0, kbase, row_stride, 0, n_kv, koff, tid);
-    dma_tile<D, BK, NT>(lds_v0, vbase, row_stride, 0, n_kv, voff, tid);
+    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, 0, n_kv, loff, tid);
+    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, 0, n_kv, loff, tid);
   }
-  if (ntiles > 1) dma_tile<D, BK, NT>(lds_k1, kbase, row_stride, BK, n_kv, koff, tid);
+  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, BK, n_kv, loff, tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
@@ -194,20 +193,32 @@ void prefill_kernel(PrefillArgs a) {
   // j-1 freed (K stage j%2, V stage (j+1)%2) while the scores of tile j+1
   // (K stage (j+1)%2) and the value update of tile j (V stage j%2) run.
   // (The stage pointers are restrict-qualified: the tile a step streams in
-  // and the tiles it reads never overlap, and saying so keeps the compiler
-  // from making the reads wait for the stream.)
-  auto step = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill,
-                  const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
-    if (j + 2 < ntiles) dma_tile<D, BK, NT>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, koff, tid);
-    if (j + 1 < ntiles) dma_tile<D, BK, NT>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, voff, tid);
+  // and the tiles it reads never overlap.)
+  auto fill = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill) {
+    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, loff, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, loff, tid);
+  };
+  auto matrix = [&](int j, const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
+    // matrix phase at raised issue priority: of the two waves sharing a
+    // SIMD, the one feeding the matrix core is served first and the other's
+    // vector work fills the gaps
+    __builtin_amdgcn_s_setprio(3);
     if (j + 1 < wnt) {
       qk_tile_sw<T, D, BK, RB>(sc, kread, qb, lane);
       lds_pipeline<Gm::NKB * D / 16, RB>();
     }
     if (j < wnt) pv_tile_tr<T, D, BK, RB>(st, pb, vread, lane);
-    if (j + 1 < wnt) weights(sc, j + 1, pb);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto end_step = [&]() {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's tiles are in LDS
     __syncthreads();
+  };
+  auto step = [&](int j, uint16_t* kf, uint16_t* vf, const uint16_t* kr, const uint16_t* vr) {
+    fill(j, kf, vf);
+    matrix(j, kr, vr);
+    if (j + 1 < wnt) weights(sc, j + 1, pb);
+    end_step();
   };
   for (int j = 0; j < ntiles; j += 2) {
     step(j, lds_k0, lds_v1, lds_k1, lds_v0);
@@ -260,9 +271,12 @@ __device__ __forceinline__ void apply_part_mask(f32x16 (&x)[2], const uint8_t* b
 
 template <class T, int D>
 __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
-  constexpr int NT = 128, BK = 64;
-  typedef TileGeom<D, BK> Gm;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * Gm::STAGE];
+  constexpr int NT = 128, BK = 64, TE = BK * D;
+  typedef typename T::vec8 vec8;
+  // two stages of natural-layout K and V outer-tile columns, filled
+  // straight from memory (attn_core.hpp), plus the part tiles' bitmaps
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
   __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
   const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
@@ -275,48 +289,54 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   const int64_t L = a.L;
   const int my_q = qblk * 64 + 32 * w + (lane & 31);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
-  u32x4 qb[D / 16];
-  load_q<D>(qb, Q + ((int64_t(b) * L + my_q) * a.Hq + hq) * D, lane);
+  u32x4 qb[1][D / 16];
+  load_q<D>(qb[0], Q + ((int64_t(b) * L + my_q) * a.Hq + hq) * D, lane);
 
-  RowState<D> st;
-  row_state_init(st);
+  RowState<D> st[1];
+  row_state_init(st[0]);
 
   const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
+  const int loff = dma_lane_offset<D>(row_stride, tid);
 
-  TileRegs<D, BK, NT> tr;
+  // the key block of stored tile j (full tiles first, then part tiles) into
+  // the given stage, and its bitmap word if it is a part tile
   uint64_t word = 0;
-  auto fetch = [&](int j) {
+  auto fetch = [&](int j, uint16_t* kd, uint16_t* vd) {
     const bool part = j >= n_full;
     const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
-    tile_load<D, BK, NT>(tr, kbase, vbase, row_stride, kblk * 64, kblk * 64, int(L), tid);
     if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
+    dma_tile<D, BK, NT, false>(kd, kbase, row_stride, kblk * 64, int(L), loff, tid);
+    dma_tile<D, BK, NT, true>(vd, vbase, row_stride, kblk * 64, int(L), loff, tid);
   };
-  if (ntiles > 0) {
-    fetch(0);
-    tile_store<D, BK, NT>(tr, lds, lds + Gm::K_ELEMS, tid);
-    if (n_full == 0) bitmap_store(word, bm[0], tid);
-  }
+  if (ntiles > 0) fetch(0, lds_k, lds_v);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 is in LDS
+  if (ntiles > 0 && n_full == 0) bitmap_store(word, bm[0], tid);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) fetch(j + 1);
-    const uint16_t* cur = lds + (j & 1) * Gm::STAGE;
-    f32x16 s[2];
-    qk_tile<T, D, BK>(s, cur, qb, lane);
-    if (j >= n_full) apply_part_mask(s, bm[j & 1], w, lane);
-    softmax_pv<T, D, BK>(st, s, a.scale_log2, cur + Gm::K_ELEMS, lane);
-    if (j + 1 < ntiles) {
-      uint16_t* nxt = lds + ((j + 1) & 1) * Gm::STAGE;
-      tile_store<D, BK, NT>(tr, nxt, nxt + Gm::K_ELEMS, tid);
-      if (j + 1 >= n_full) bitmap_store(word, bm[(j + 1) & 1], tid);
-    }
+    const int cur = j & 1, nxt = cur ^ 1;
+    // tile j + 1 streams into the stage tile j - 1 released
+    if (j + 1 < ntiles) fetch(j + 1, lds_k + nxt * TE, lds_v + nxt * TE);
+    f32x16 s[1][2];
+    vec8 pb[1][2][2];
+    __builtin_amdgcn_s_setprio(3);
+    qk_tile_sw<T, D, BK, 1>(s, lds_k + cur * TE, qb, lane);
+    __builtin_amdgcn_s_setprio(0);
+    if (j >= n_full) apply_part_mask(s[0], bm[cur], w, lane);
+    const float mref = softmax_max<D, 2>(st[0], s[0], a.scale_log2, 0);
+    softmax_exp<T, D, 2>(st[0], s[0], a.scale_log2, mref, pb[0]);
+    __builtin_amdgcn_s_setprio(3);
+    pv_tile_tr<T, D, BK, 1>(st, pb, lds_v + cur * TE, lane);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 1 (and its word) arrived
+    if (j + 1 < ntiles && j + 1 >= n_full) bitmap_store(word, bm[nxt], tid);
     __syncthreads();
   }
 
   const int64_t orow_idx = (int64_t(b) * L + my_q) * a.Hq + hq;
   uint16_t* orow = static_cast<uint16_t*>(a.o) + orow_idx * D;
-  row_store<T, D>(st, orow, a.lse ? a.lse + orow_idx : nullptr, lane);
+  row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
 }
 
 // Dense expansion of the two-level mask with the kernel's own predicate:
