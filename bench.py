@@ -44,7 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
-    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "copy"], default=None,
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "append", "copy"],
+                   default=None,
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
@@ -170,6 +171,39 @@ def bench_prefill(torch, ra, synth, args, timer):
                 frac=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
 
 
+def append_flops(B, Hq, Lq, L, D):
+    # bottom-right causal: new token t of Lq sees L - Lq + t + 1 keys
+    pairs = sum(L - Lq + t + 1 for t in range(Lq))
+    return 4 * D * pairs * B * Hq
+
+
+def bench_append(torch, ra, synth, args, timer):
+    """Append / chunked prefill: the split-KV prefill at its automatic split
+    count, and the unsplit kernel on the same inputs for comparison."""
+    w = synth.workload("append_prefill_bf16")
+    inp = w.make("cuda:0")
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qo, kv = inp["qo_indptr"].to(dev), inp["kv_indptr"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], w.Hq), dtype=torch.float32, device=dev)
+    s = ra.attn_prefill_choose_splits(w.B, w.Hq, w.Hkv, w.D, w.Lq, w.L)
+    ws = torch.empty(max(ra.attn_prefill_workspace_bytes(q.shape[0], w.Hq, w.D, s), 256),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ms, _ = timer.run(lambda i: ra.attn_prefill_splitkv(q, k, v, qo, kv, w.Lq, w.L, causal=True,
+                                                        num_splits=s, o=o, lse=lse, workspace=ws,
+                                                        stream=stream), args.steps, args.warmup)
+    ms1, _ = timer.run(lambda i: ra.attn_prefill(q, k, v, qo, kv, w.Lq, w.L, causal=True, o=o,
+                                                 lse=lse, stream=stream), args.steps, args.warmup)
+    flops = append_flops(w.B, w.Hq, w.Lq, w.L, w.D)
+    t, t1 = median(ms), median(ms1)
+    return dict(workload=w.name, B=w.B, Lq=w.Lq, L=w.L, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
+                dtype="bf16", splits=s, ms=t, flops=flops, tflops=flops / t / 1e9,
+                frac=flops / t / 1e9 / MFMA_BF16_PEAK_TFS, ms_unsplit=t1,
+                tflops_unsplit=flops / t1 / 1e9)
+
+
 def bench_bsr(torch, ra, synth, args, timer):
     w = synth.workload("bsr_prefill_fp16")
     inp = w.make("cuda:0")
@@ -265,6 +299,7 @@ def main():
               "ragged": lambda: bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, 1),
               "prefill": lambda: bench_prefill(torch, ra, synth, args, timer),
               "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
+              "append": lambda: bench_append(torch, ra, synth, args, timer),
               "copy": lambda: bench_copy(torch, args, timer)}[args.only]
         r = fn()
         print(json.dumps({"only": args.only, **r}))
@@ -322,6 +357,11 @@ def main():
                                      gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
                                      total_kv=r["total_kv"], splits=r["splits"],
                                      kv_bytes=r["kv_bytes"])
+        ap = bench_append(torch, ra, synth, args, timer)
+        log(f"append prefill: {ap['ms']*1e3:.1f} us, {ap['tflops']:.1f} TFLOP/s, s={ap['splits']} "
+            f"(unsplit {ap['ms_unsplit']*1e3:.1f} us)")
+        also["append_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                  for k, v in ap.items()}
         b = bench_bsr(torch, ra, synth, args, timer)
         log(f"bsr: {b['ms']*1e3:.1f} us, {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
         also["bsr_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}

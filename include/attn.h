@@ -186,6 +186,47 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v,
                            int max_kv_len, float scale, int causal, int dtype,
                            void* hip_stream);
 
+/* Workspace bytes attn_prefill_splitkv needs for `num_splits` splits:
+ * num_splits * total_q * Hq * (D + 2) * 4 (fp32 partial outputs, maxima,
+ * sums), rounded up to 256 bytes; 0 for invalid arguments. */
+size_t attn_prefill_workspace_bytes(long long total_q, int Hq, int D, int num_splits);
+
+/* The split count attn_prefill_splitkv picks when num_splits = 0: 1 when the
+ * B * Hq * ceil(max_q_len / 128) query-tile workgroups already give two per
+ * compute unit; otherwise enough splits to reach two per compute unit,
+ * with chunks of at least 1024 keys, clamped to [1, 256].  [CA] leaves the
+ * concrete s to the scheduler; this is that scheduler's rule. */
+int attn_prefill_choose_splits(int B, int Hq, int Hkv, int D, int max_q_len, int max_kv_len);
+
+/*
+ * Prefill / append with the key dimension cut by the Split operator [CA
+ * "Split演算子によるSplit-Kの対応"]: the operation and the arguments of
+ * attn_prefill, for batches whose query tiles alone cannot fill the chip
+ * (a few new tokens against a long key/value history).  Split i covers key
+ * offsets [i*c, min((i+1)*c, n_kv)) of each request, c = ceil(max_kv_len /
+ * s); it computes, for every query row, the softmax-weighted output over
+ * its valid keys in that range (causal masking as in attn_prefill), and a
+ * merge combines the splits by log-sum-exp weights (as attn_merge_lse).
+ * total_q   qo_indptr[B] (sizes the workspace).
+ * num_splits  s in [1, 256], or 0 to use attn_prefill_choose_splits;
+ *   s = 1 is attn_prefill itself (no workspace needed).
+ * workspace  device memory of at least attn_prefill_workspace_bytes(total_q,
+ *   Hq, D, s) bytes, 16-byte aligned; contents on entry do not matter.
+ *   Layout: o_part [s, total_q*Hq, D], then m_part and l_part
+ *   [s, total_q*Hq], fp32 (row = query row * Hq + head); a split without
+ *   valid keys for a row leaves (m, l) = (-inf, 0) there.  Calls sharing one
+ *   workspace must not overlap in time.
+ * Two kernels are enqueued on hip_stream: the split partials, then the merge.
+ * Supported: as attn_prefill, with ceil(max_q_len / 128) * s <= 65535 and
+ * total_q * Hq <= 2^30 when s > 1.
+ */
+attn_status_t attn_prefill_splitkv(const void* q, const void* k, const void* v,
+                                   const int32_t* qo_indptr, const int32_t* kv_indptr, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int D, int max_q_len,
+                                   int max_kv_len, long long total_q, float scale, int causal,
+                                   int num_splits, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+
 /* ---- block-sparse prefill (BSR outer tiles + 8x8 bitmaps) -------------- */
 
 /*

@@ -16,6 +16,9 @@ from .api import (  # noqa: F401
     attn_merge_lse,
     attn_prefill,
     attn_prefill_bsr,
+    attn_prefill_choose_splits,
+    attn_prefill_splitkv,
+    attn_prefill_workspace_bytes,
     decode_workspace_views,
 )
 from ._lib import ATTN_BF16, ATTN_F16, ATTN_F32, AttnError  # noqa: F401

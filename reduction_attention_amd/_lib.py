@@ -37,6 +37,10 @@ SIGNATURES = {
     "attn_merge_lse": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                             _f32, _i32, _i32, _vp]),
+    "attn_prefill_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32]),
+    "attn_prefill_choose_splits": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "attn_prefill_splitkv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "attn_bsr_encode_host": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "attn_prefill_bsr": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _vp, _vp, _i32, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _vp]),

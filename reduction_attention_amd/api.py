@@ -148,6 +148,46 @@ def attn_prefill(q, k, v, qo_indptr, kv_indptr, max_q_len, max_kv_len, scale=Non
     return o, lse
 
 
+def attn_prefill_workspace_bytes(total_q, Hq, D, num_splits):
+    return load().attn_prefill_workspace_bytes(int(total_q), Hq, D, num_splits)
+
+
+def attn_prefill_choose_splits(B, Hq, Hkv, D, max_q_len, max_kv_len):
+    return load().attn_prefill_choose_splits(B, Hq, Hkv, D, int(max_q_len), int(max_kv_len))
+
+
+def attn_prefill_splitkv(q, k, v, qo_indptr, kv_indptr, max_q_len, max_kv_len, scale=None,
+                         causal=True, num_splits=0, o=None, lse=None, workspace=None,
+                         stream=None, want_lse=True):
+    """Prefill / append with the key dimension split in num_splits chunks (0 = auto).
+
+    Same tensors as attn_prefill; returns (o, lse).
+    """
+    _dev(q, k, v, qo_indptr, kv_indptr, o, lse, workspace)
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = qo_indptr.numel() - 1
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lib = load()
+    s = num_splits or lib.attn_prefill_choose_splits(B, Hq, Hkv, D, int(max_q_len),
+                                                     int(max_kv_len))
+    need = lib.attn_prefill_workspace_bytes(total_q, Hq, D, s) if s > 1 else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((total_q, Hq), dtype=torch.float32, device=q.device)
+    st = lib.attn_prefill_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(qo_indptr), _ptr(kv_indptr),
+                                  _ptr(o), _ptr(lse), B, Hq, Hkv, D, int(max_q_len),
+                                  int(max_kv_len), total_q, scale, int(bool(causal)), int(s),
+                                  _dtype_code(q), _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0,
+                                  _stream(stream))
+    check(st, "attn_prefill_splitkv")
+    return o, lse
+
+
 @dataclass
 class BsrMask:
     """Two-level mask: host arrays from the encoder, device copies for kernels."""

@@ -215,8 +215,9 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, const in
     return fail(ATTN_EINVAL, "prefill: null pointer");
   if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill: B, Hq, Hkv must be >= 1");
   if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill: B or Hq above 65535");
-  if ((long long)max_q_len > 128LL * 65535)
-    return fail(ATTN_EUNSUPPORTED, "prefill: max_q_len above %lld", 128LL * 65535);
+  if ((long long)max_q_len > (long long)rattn::prefill_rows_per_workgroup() * 65535)
+    return fail(ATTN_EUNSUPPORTED, "prefill: max_q_len above %lld",
+                (long long)rattn::prefill_rows_per_workgroup() * 65535);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill: Hq %d not a multiple of Hkv %d", Hq, Hkv);
   if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill: D = %d (supported: 64, 128)", D);
   if (dtype != ATTN_BF16 && dtype != ATTN_F16)
@@ -228,8 +229,84 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, const in
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(ATTN_EINVAL, "prefill: q, k, v, o must be 16-byte aligned");
   rattn::PrefillArgs a{q, k, v, qo_indptr, kv_indptr, o, lse, B, Hq, Hkv, D, Hq / Hkv,
-                       max_q_len, max_kv_len, scale * kLog2e, causal, dtype};
+                       max_q_len, max_kv_len, scale * kLog2e, causal, dtype,
+                       1, 0, nullptr, nullptr, nullptr, 0};
   return hip_status(rattn::launch_prefill(a, static_cast<hipStream_t>(hip_stream)), "prefill launch");
+}
+
+size_t attn_prefill_workspace_bytes(long long total_q, int Hq, int D, int num_splits) {
+  if (total_q < 0 || Hq < 1 || D < 1 || num_splits < 1) return 0;
+  const size_t raw = size_t(num_splits) * size_t(total_q) * size_t(Hq) * size_t(D + 2) * 4;
+  return (raw + 255) / 256 * 256;
+}
+
+int attn_prefill_choose_splits(int B, int Hq, int Hkv, int D, int max_q_len, int max_kv_len) {
+  (void)Hkv;
+  (void)D;
+  if (B <= 0 || Hq <= 0 || max_q_len <= 0 || max_kv_len <= 0) return 1;
+  // Two workgroups per compute unit fill the chip; split the keys only when
+  // the query tiles alone fall short, and keep chunks of at least 1024 keys.
+  const int bq = rattn::prefill_rows_per_workgroup();
+  const long long wgs = (long long)B * Hq * ((max_q_len + bq - 1) / bq);
+  const long long target = 2LL * attn_device_cu_count();
+  if (wgs >= target) return 1;
+  long long s = (target + wgs - 1) / wgs;
+  const long long s_max = (max_kv_len + 1023) / 1024;
+  if (s > s_max) s = s_max;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : int(s);
+}
+
+attn_status_t attn_prefill_splitkv(const void* q, const void* k, const void* v,
+                                   const int32_t* qo_indptr, const int32_t* kv_indptr, void* o,
+                                   float* lse, int B, int Hq, int Hkv, int D, int max_q_len,
+                                   int max_kv_len, long long total_q, float scale, int causal,
+                                   int num_splits, int dtype, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
+  if (!q || !k || !v || !qo_indptr || !kv_indptr || !o)
+    return fail(ATTN_EINVAL, "prefill_splitkv: null pointer");
+  if (B < 1 || Hq < 1 || Hkv < 1) return fail(ATTN_EINVAL, "prefill_splitkv: B, Hq, Hkv must be >= 1");
+  if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill_splitkv: B or Hq above 65535");
+  if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill_splitkv: Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  if (D != 64 && D != 128)
+    return fail(ATTN_EUNSUPPORTED, "prefill_splitkv: D = %d (supported: 64, 128)", D);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_EUNSUPPORTED, "prefill_splitkv: dtype %d (supported: bf16, f16)", dtype);
+  if (max_q_len < 0 || max_kv_len < 0 || total_q < 0)
+    return fail(ATTN_EINVAL, "prefill_splitkv: negative length");
+  if (causal != 0 && causal != 1) return fail(ATTN_EINVAL, "prefill_splitkv: causal must be 0 or 1");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "prefill_splitkv: scale must be finite and positive");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "prefill_splitkv: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_EINVAL, "prefill_splitkv: q, k, v, o must be 16-byte aligned");
+  const int s = num_splits ? num_splits
+                           : attn_prefill_choose_splits(B, Hq, Hkv, D, max_q_len, max_kv_len);
+  const int bq = rattn::prefill_rows_per_workgroup();
+  const long long qtiles = (max_q_len + bq - 1) / bq;
+  if (qtiles * s > 65535)
+    return fail(ATTN_EUNSUPPORTED, "prefill_splitkv: ceil(max_q_len / %d) * s = %lld above 65535",
+                bq, qtiles * s);
+  const long long rows = total_q * Hq;
+  if (s > 1 && rows > (1LL << 30)) return fail(ATTN_EUNSUPPORTED, "prefill_splitkv: rows above 2^30");
+  const size_t need = s > 1 ? attn_prefill_workspace_bytes(total_q, Hq, D, s) : 0;
+  if (s > 1 && (!workspace || workspace_bytes < need))
+    return fail(ATTN_EWORKSPACE, "prefill_splitkv: workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (s > 1 && !aligned16(workspace))
+    return fail(ATTN_EINVAL, "prefill_splitkv: workspace must be 16-byte aligned");
+  const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
+  float* ws = static_cast<float*>(workspace);
+  rattn::PrefillArgs a{q, k, v, qo_indptr, kv_indptr, o, lse, B, Hq, Hkv, D, Hq / Hkv,
+                       max_q_len, max_kv_len, scale * kLog2e, causal, dtype,
+                       s, chunk,
+                       s > 1 ? ws : nullptr,
+                       s > 1 ? ws + size_t(s) * size_t(rows) * D : nullptr,
+                       s > 1 ? ws + size_t(s) * size_t(rows) * (D + 1) : nullptr,
+                       rows};
+  return hip_status(rattn::launch_prefill(a, static_cast<hipStream_t>(hip_stream)),
+                    "prefill_splitkv launch");
 }
 
 attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_indptr,

@@ -389,6 +389,33 @@ __device__ __forceinline__ void row_store(const RowState<D>& st, uint16_t* orow,
 }
 
 
+// A split's partial result for the wave's 32 rows: O normalised by the
+// split's own sum (fp32), the reference max m in natural-log units and the
+// sum l relative to it; a row without valid keys gets O = 0, m = -inf,
+// l = 0.  orow points at dim 0 of the lane's row in the partial output (or
+// is nullptr when the row does not exist).
+template <int D>
+__device__ __forceinline__ void row_store_partial(const RowState<D>& st, float* orow, float* m_out,
+                                                  float* l_out, int lane) {
+  const float l = sum_halves(st.l);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int h = lane >> 5;
+  if (!orow) return;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = st.o[db][4 * g4 + e] * inv;
+      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g4 + 4 * h) = y;
+    }
+  if (h == 0) {
+    *m_out = l > 0.f ? st.m * kLn2 : -INFINITY;
+    *l_out = l;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Natural-layout tiles written straight from global memory into LDS.
 //

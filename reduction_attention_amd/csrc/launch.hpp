@@ -53,6 +53,16 @@ struct PrefillArgs {
   float scale_log2;
   int causal;
   int dtype;
+  // Split of the key dimension (Split operator): s chunks of `chunk` keys
+  // per request.  s = 1 writes o / lse; s > 1 writes, for every split i,
+  // the normalised partial output o_part[i, row, :] and its (m, l) (m in
+  // natural-log units; m = -inf, l = 0 for a split without valid keys),
+  // row = (qo_indptr[b] + query) * Hq + head, rows rows in all.
+  int s, chunk;
+  float* o_part;
+  float* m_part;
+  float* l_part;
+  int64_t rows;
 };
 
 struct BsrArgs {
@@ -77,6 +87,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
                                hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
+int prefill_rows_per_workgroup();  // query rows one prefill workgroup covers
 hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st);
 hipError_t launch_bsr_decode(const int32_t* full_indptr, const int32_t* full_kblock,
                              const int32_t* part_indptr, const int32_t* part_kblock,

@@ -92,34 +92,39 @@ void prefill_kernel(PrefillArgs a) {
   uint16_t* const lds_v0 = lds_v;
   uint16_t* const lds_v1 = lds_v + TE;
 
-  // grid (Hq, B, query tiles): workgroups are dispatched in linear order, so
-  // with the query tile slowest every causal tile of one size goes out
-  // before any smaller one (heaviest first) and the short ones fill the tail.
+  // grid (Hq, B, query tiles x splits): workgroups are dispatched in linear
+  // order, so with the query tile slowest every causal tile of one size
+  // goes out before any smaller one (heaviest first) and the short ones
+  // fill the tail.  Split si covers keys [si * chunk, (si + 1) * chunk).
   const int hq = xcd_head(blockIdx.x, a.Hq), b = blockIdx.y;
-  const int qt = CAUSAL ? int(gridDim.z) - 1 - int(blockIdx.z) : int(blockIdx.z);
+  const int nqt = int(gridDim.z) / a.s;
+  const int zq = int(blockIdx.z) / a.s, si = int(blockIdx.z) % a.s;
+  const int qt = CAUSAL ? nqt - 1 - zq : zq;
   const int64_t q_begin = a.qo_indptr[b];
   const int n_q = int(a.qo_indptr[b + 1] - q_begin);
   const int64_t k_begin = a.kv_indptr[b];
   const int n_kv = int(a.kv_indptr[b + 1] - k_begin);
   const int q_start = qt * BQ;
   if (q_start >= n_q) return;
+  const int k_lo = a.s > 1 ? si * a.chunk : 0;
+  const int k_hi = a.s > 1 ? (k_lo + a.chunk < n_kv ? k_lo + a.chunk : n_kv) : n_kv;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = hq / a.G;
   const int off = n_kv - n_q;  // causal: key j valid for query i iff j <= i + off
   const int q_last_wg = (q_start + BQ < n_q ? q_start + BQ : n_q) - 1;
-  int kv_end = n_kv;
-  if (CAUSAL) kv_end = q_last_wg + 1 + off < n_kv ? q_last_wg + 1 + off : n_kv;
-  const int ntiles = kv_end > 0 ? (kv_end + BK - 1) / BK : 0;
+  int kv_end = k_hi;
+  if (CAUSAL) kv_end = q_last_wg + 1 + off < k_hi ? q_last_wg + 1 + off : k_hi;
+  const int ntiles = kv_end > k_lo ? (kv_end - k_lo + BK - 1) / BK : 0;
 
   // this wave's rows (RB blocks of 32) and the tiles it takes part in
   const int q0w = q_start + 32 * RB * w;
   int wnt = 0;
   if (q0w < n_q) {
     const int wq_last = q0w + 32 * RB - 1 < n_q ? q0w + 32 * RB - 1 : n_q - 1;
-    int wkv_end = n_kv;
-    if (CAUSAL) wkv_end = wq_last + 1 + off < n_kv ? wq_last + 1 + off : n_kv;
-    wnt = wkv_end > 0 ? (wkv_end + BK - 1) / BK : 0;
+    int wkv_end = k_hi;
+    if (CAUSAL) wkv_end = wq_last + 1 + off < k_hi ? wq_last + 1 + off : k_hi;
+    wnt = wkv_end > k_lo ? (wkv_end - k_lo + BK - 1) / BK : 0;
   }
   wnt = __builtin_amdgcn_readfirstlane(wnt);
   const uint16_t* Q = static_cast<const uint16_t*>(a.q);
@@ -140,20 +145,20 @@ void prefill_kernel(PrefillArgs a) {
   // prologue: K of tiles 0 and 1, V of tile 0
   const int loff = dma_lane_offset<D>(row_stride, tid);
   if (ntiles > 0) {
-    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, 0, n_kv, loff, tid);
-    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, 0, n_kv, loff, tid);
+    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, k_lo, n_kv, loff, tid);
+    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, k_lo, n_kv, loff, tid);
   }
-  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, BK, n_kv, loff, tid);
+  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, k_lo + BK, n_kv, loff, tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
   // causal / ragged-tail masking of tile j's scores, needed on few tiles
   auto need_mask = [&](int j) {
-    const int k0 = j * BK;
-    return (k0 + BK > n_kv) || (CAUSAL && k0 + BK - 1 > q0w + off);
+    const int k0 = k_lo + j * BK;
+    return (k0 + BK > k_hi) || (CAUSAL && k0 + BK - 1 > q0w + off);
   };
   auto mask = [&](f32x16 (&s)[RB][Gm::NKB], int j) {
-    const int k0 = j * BK;
+    const int k0 = k_lo + j * BK;
     const int ln = lane, hh = ln >> 5;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -163,7 +168,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          bool ok = key < n_kv;
+          bool ok = key < k_hi;
           if (CAUSAL) ok = ok && key <= mq + off;
           if (!ok) s[rb][kb][r] = -INFINITY;
         }
@@ -195,8 +200,8 @@ void prefill_kernel(PrefillArgs a) {
   // (The stage pointers are restrict-qualified: the tile a step streams in
   // and the tiles it reads never overlap.)
   auto fill = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill) {
-    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, (j + 2) * BK, n_kv, loff, tid);
-    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, (j + 1) * BK, n_kv, loff, tid);
+    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, k_lo + (j + 2) * BK, n_kv, loff, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, k_lo + (j + 1) * BK, n_kv, loff, tid);
   };
   auto matrix = [&](int j, const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
     // matrix phase at raised issue priority: of the two waves sharing a
@@ -229,9 +234,16 @@ void prefill_kernel(PrefillArgs a) {
   for (int rb = 0; rb < RB; ++rb) {
     const int oq = q0w + 32 * rb + (lane & 31);
     const bool row_ok = oq < n_q;
-    uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + ((q_begin + oq) * a.Hq + hq) * D : nullptr;
-    float* lse = (row_ok && a.lse) ? a.lse + (q_begin + oq) * a.Hq + hq : nullptr;
-    row_store<T, D>(st[rb], orow, lse, lane);
+    const int64_t row = (q_begin + oq) * a.Hq + hq;
+    if (a.s == 1) {
+      uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + row * D : nullptr;
+      float* lse = (row_ok && a.lse) ? a.lse + row : nullptr;
+      row_store<T, D>(st[rb], orow, lse, lane);
+    } else {
+      const int64_t prow = int64_t(si) * a.rows + row;
+      row_store_partial<D>(st[rb], row_ok ? a.o_part + prow * D : nullptr, a.m_part + prow,
+                           a.l_part + prow, lane);
+    }
   }
 }
 
@@ -385,11 +397,13 @@ __global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_ind
 template <class T, int D>
 static void launch_prefill_t(const PrefillArgs& a, hipStream_t st) {
   constexpr int BQ = kPrefillBQ;
-  const dim3 grid(a.Hq, a.B, (a.max_q_len + BQ - 1) / BQ);
+  const dim3 grid(a.Hq, a.B, unsigned((a.max_q_len + BQ - 1) / BQ * a.s));
   const dim3 block(64 * kPrefillWaves);
   if (a.causal) hipLaunchKernelGGL((prefill_kernel<T, D, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((prefill_kernel<T, D, false>), grid, block, 0, st, a);
 }
+
+int prefill_rows_per_workgroup() { return kPrefillBQ; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.max_q_len <= 0) return hipSuccess;
@@ -398,7 +412,11 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   } else {
     if (a.D == 64) launch_prefill_t<F16, 64>(a, st); else launch_prefill_t<F16, 128>(a, st);
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.s == 1) return e;
+  // split partials -> o / lse by log-sum-exp weights (the decode merge)
+  MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, int(a.rows), a.D, a.o, a.dtype, a.lse};
+  return launch_merge(m, st);
 }
 
 hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st) {

@@ -120,14 +120,15 @@ def sparse_mask(L: int, g: torch.Generator, window: int = 256, block: int = 64,
 @dataclass
 class Workload:
     name: str
-    kind: str            # "decode", "prefill", "bsr"
+    kind: str            # "decode", "prefill", "append", "bsr"
     seed: int
     dtype: torch.dtype
     B: int
     Hq: int
     Hkv: int
     D: int
-    L: int = 0           # prefill / bsr sequence length, or uniform decode KV length
+    L: int = 0           # prefill / bsr sequence length, or uniform decode / append KV length
+    Lq: int = 0          # append: new query tokens per request
     ragged: tuple = ()   # (lo, hi) log-uniform decode lengths
     causal: bool = False
     splits: tuple = ()   # forced split counts to check (decode)
@@ -161,6 +162,12 @@ class Workload:
             v = rn((self.B * self.L, self.Hkv, self.D))
             ind = indptr([self.L] * self.B).to(device)
             return dict(q=q, k=k, v=v, qo_indptr=ind, kv_indptr=ind.clone())
+        if self.kind == "append":
+            q = rn((self.B * self.Lq, self.Hq, self.D))
+            k = rn((self.B * self.L, self.Hkv, self.D))
+            v = rn((self.B * self.L, self.Hkv, self.D))
+            return dict(q=q, k=k, v=v, qo_indptr=indptr([self.Lq] * self.B).to(device),
+                        kv_indptr=indptr([self.L] * self.B).to(device))
         if self.kind == "bsr":
             mask = self.mask(g_shape)
             q = rn((self.B, self.L, self.Hq, self.D))
@@ -185,6 +192,9 @@ WORKLOADS = {
                                     Hq=32, Hkv=8, D=128, L=4096, causal=True),
     "bsr_prefill_fp16": Workload("bsr_prefill_fp16", "bsr", 5, torch.float16, B=1, Hq=16,
                                  Hkv=16, D=64, L=4096),
+    # append / chunked prefill: 128 new tokens per request against a 16k history
+    "append_prefill_bf16": Workload("append_prefill_bf16", "append", 6, torch.bfloat16, B=4,
+                                    Hq=32, Hkv=8, D=128, L=16384, Lq=128, causal=True),
 }
 
 

@@ -114,6 +114,39 @@ def test_prefill_validation(lib, kw, status):
     assert prefill_call(lib, **kw) == status
 
 
+def splitkv_call(lib, **kw):
+    a = dict(q=P, k=P, v=P, qo=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, mq=64, mk=4096,
+             tq=128, scale=0.1, causal=1, s=4, dt=1, ws=P, wsb=1 << 30, st=None)
+    a.update(kw)
+    return lib.attn_prefill_splitkv(a["q"], a["k"], a["v"], a["qo"], a["kv"], a["o"], a["lse"],
+                                    a["B"], a["Hq"], a["Hkv"], a["D"], a["mq"], a["mk"], a["tq"],
+                                    a["scale"], a["causal"], a["s"], a["dt"], a["ws"], a["wsb"],
+                                    a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(o=None), 1), (dict(Hq=5, Hkv=2), 1), (dict(D=32), 2), (dict(dt=0), 2),
+    (dict(s=257), 1), (dict(s=-1), 1), (dict(tq=-1), 1), (dict(ws=None), 3), (dict(wsb=1024), 3),
+    (dict(ws=ctypes.c_void_p(24)), 1), (dict(mq=128 * 65535, s=2), 2), (dict(scale=0.0), 1),
+])
+def test_prefill_splitkv_validation(lib, kw, status):
+    assert splitkv_call(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
+def test_prefill_split_rule_and_workspace(lib):
+    for tq, Hq, D, s in [(128, 8, 128, 4), (4096, 32, 64, 1), (1, 1, 128, 256)]:
+        raw = s * tq * Hq * (D + 2) * 4
+        assert lib.attn_prefill_workspace_bytes(tq, Hq, D, s) == (raw + 255) // 256 * 256
+    assert lib.attn_prefill_workspace_bytes(16, 8, 128, 0) == 0
+    # 4 requests x 128 new tokens x 32 heads = 128 query-tile workgroups < 512
+    # -> s = 4; at most one split per 1024 keys; full-sized prefill -> 1
+    assert lib.attn_prefill_choose_splits(4, 32, 8, 128, 128, 16384) == 4
+    assert lib.attn_prefill_choose_splits(4, 32, 8, 128, 128, 2048) == 2
+    assert lib.attn_prefill_choose_splits(2, 32, 8, 128, 4096, 4096) == 1
+    assert lib.attn_prefill_choose_splits(1, 1, 1, 128, 1, 100000) == 98
+
+
 def test_merge_validation(lib):
     f = lib.attn_merge_lse
     assert f(None, P, P, 2, 4, 128, P, 1, None, None) == 1

@@ -107,3 +107,73 @@ def test_two_runs_bit_identical():
     o1, l1 = prefill(q, k, v, qo, kv, True)
     o2, l2 = prefill(q, k, v, qo, kv, True)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---- split-KV prefill / append ---------------------------------------------
+
+def prefill_split(q, k, v, qo, kv, causal, s, scale=None):
+    lq = (qo[1:] - qo[:-1]).max().item()
+    lk = (kv[1:] - kv[:-1]).max().item()
+    o, lse = ra().attn_prefill_splitkv(q.to(DEV), k.to(DEV), v.to(DEV), qo.to(DEV), kv.to(DEV),
+                                       lq, lk, scale=scale, causal=causal, num_splits=s)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float16, 64)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_splitkv_append_ragged(dtype, D, causal):
+    """Few new tokens against long, ragged key histories (bottom-right causal);
+    every split count agrees with the oracle, and with the others."""
+    lens_q = [1, 7, 64, 130, 0]
+    lens_k = [300, 1000, 2049, 5000, 70]
+    Hkv, G = 2, 4
+    qo, kv = synth.indptr(lens_q), synth.indptr(lens_k)
+    g = synth.gen(60 + D + causal)
+    q = synth.randn((sum(lens_q), G * Hkv, D), dtype, g)
+    k = synth.randn((sum(lens_k), Hkv, D), dtype, g)
+    v = synth.randn((sum(lens_k), Hkv, D), dtype, g)
+    mk = oracle.MASK_CAUSAL if causal else oracle.MASK_NONE
+    o_ref, lse_ref = oracle.attention(q, k, v, qo, kv, 1 / D ** 0.5, mk)
+    outs = []
+    for s in (0, 1, 2, 3, 7, 40):
+        o, lse = prefill_split(q, k, v, qo, kv, causal, s)
+        check(f"splitkv {dtype} D={D} causal={causal} s={s}", o, o_ref, lse, lse_ref, dtype)
+        outs.append(o.double().cpu())
+    for x in outs[1:]:
+        assert (x - outs[0]).abs().max().item() <= 2 * TOL_O[dtype]
+
+
+def test_splitkv_equals_prefill_when_one_split():
+    """s = 1 is attn_prefill itself: bit-identical output."""
+    lens = [200, 65]
+    qo, kv = synth.indptr(lens), synth.indptr(lens)
+    g = synth.gen(77)
+    q = synth.randn((sum(lens), 4, 128), torch.bfloat16, g)
+    k = synth.randn((sum(lens), 2, 128), torch.bfloat16, g)
+    v = synth.randn((sum(lens), 2, 128), torch.bfloat16, g)
+    o1, l1 = prefill(q, k, v, qo, kv, True)
+    o2, l2 = prefill_split(q, k, v, qo, kv, True, 1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_splitkv_append_workload_sampled():
+    """4 requests x 128 new tokens against 16,384 cached keys, 32/8 heads,
+    D 128, bf16, bottom-right causal, auto split count: sampled rows."""
+    w = synth.workload("append_prefill_bf16")
+    inp = w.make(DEV)
+    qo, kv = inp["qo_indptr"], inp["kv_indptr"]
+    lq = (qo[1:] - qo[:-1]).max().item()
+    lk = (kv[1:] - kv[:-1]).max().item()
+    s = ra().attn_prefill_choose_splits(w.B, w.Hq, w.Hkv, w.D, lq, lk)
+    assert s > 1
+    o, lse = prefill_split(inp["q"], inp["k"], inp["v"], qo, kv, True, 0)
+    g = synth.gen(98)
+    total_q = int(qo[-1])
+    rows = torch.stack([torch.randint(0, total_q, (1500,), generator=g),
+                        torch.randint(0, w.Hq, (1500,), generator=g)], 1)
+    o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], qo, kv, w.scale,
+                                      oracle.MASK_CAUSAL, rows=rows)
+    t, h = rows[:, 0].to(DEV), rows[:, 1].to(DEV)
+    check(f"append 4x128 vs 16384, s={s}, sampled", o[t, h], o_ref, lse[t, h], lse_ref,
+          torch.bfloat16)
