@@ -44,7 +44,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
-    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "append", "copy"],
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "bsr_heads", "append",
+                                      "copy"],
                    default=None,
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -204,8 +205,8 @@ def bench_append(torch, ra, synth, args, timer):
                 tflops_unsplit=flops / t1 / 1e9)
 
 
-def bench_bsr(torch, ra, synth, args, timer):
-    w = synth.workload("bsr_prefill_fp16")
+def bench_bsr(torch, ra, synth, args, timer, name="bsr_prefill_fp16"):
+    w = synth.workload(name)
     inp = w.make("cuda:0")
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
@@ -218,14 +219,16 @@ def bench_bsr(torch, ra, synth, args, timer):
     stream = torch.cuda.current_stream()
     ms, _ = timer.run(lambda i: ra.attn_prefill_bsr(q, k, v, md, o=o, lse=lse, stream=stream),
                       args.steps, args.warmup)
+    # every mask serves Hq / num_masks heads
+    hpm = w.Hq // m.num_masks
     n_ot = m.nnz_full + m.nnz_part
-    flops_ot = 4 * w.D * 64 * 64 * n_ot * w.Hq * w.B
+    flops_ot = 4 * w.D * 64 * 64 * n_ot * hpm * w.B
     valid = int(inp["mask"].to(torch.int64).sum())
-    flops_valid = 4 * w.D * valid * w.Hq * w.B
+    flops_valid = 4 * w.D * valid * hpm * w.B
     t = median(ms)
     return dict(workload=w.name, B=w.B, L=w.L, H=w.Hq, D=w.D, dtype="fp16", ms=t,
-                nnz_full=m.nnz_full, nnz_part=m.nnz_part,
-                density=valid / (w.L * w.L), flops_ot=flops_ot,
+                num_masks=m.num_masks, nnz_full=m.nnz_full, nnz_part=m.nnz_part,
+                density=valid / (w.L * w.L * m.num_masks), flops_ot=flops_ot,
                 tflops_ot=flops_ot / t / 1e9, tflops_valid=flops_valid / t / 1e9,
                 frac_ot=flops_ot / t / 1e9 / MFMA_BF16_PEAK_TFS, host_encode_s=enc_s)
 
@@ -299,6 +302,8 @@ def main():
               "ragged": lambda: bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, 1),
               "prefill": lambda: bench_prefill(torch, ra, synth, args, timer),
               "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
+              "bsr_heads": lambda: bench_bsr(torch, ra, synth, args, timer,
+                                             "bsr_heads_prefill_fp16"),
               "append": lambda: bench_append(torch, ra, synth, args, timer),
               "copy": lambda: bench_copy(torch, args, timer)}[args.only]
         r = fn()
@@ -365,6 +370,11 @@ def main():
         b = bench_bsr(torch, ra, synth, args, timer)
         log(f"bsr: {b['ms']*1e3:.1f} us, {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
         also["bsr_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}
+        bh = bench_bsr(torch, ra, synth, args, timer, "bsr_heads_prefill_fp16")
+        log(f"bsr per-head-group masks, L {bh['L']}: {bh['ms']*1e3:.1f} us, "
+            f"{bh['tflops_ot']:.1f} TFLOP/s at OT granularity")
+        also["bsr_heads_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                     for k, v in bh.items()}
         out["also"] = also
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -278,6 +278,32 @@ attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
                                int Hq, int Hkv, int D, float scale, int dtype,
                                void* hip_stream);
 
+/*
+ * Several masks stacked in one attn_bsr_mask, for per-head (or per head
+ * group) sparsity [ST "2 段階ストレージ形式"]: num_masks masks of the same
+ * L, mask m's indptr arrays at full_indptr + m*(num_blocks + 1) and
+ * part_indptr + m*(num_blocks + 1), with values indexing the concatenated
+ * kblock / bits arrays; nnz_full / nnz_part are totals.  Encoder: dense is
+ * uint8 [num_masks, L, L]; same two-pass protocol as attn_bsr_encode_host
+ * (which is this call with num_masks = 1); indptr outputs need
+ * num_masks * (L/64 + 1) entries.
+ */
+attn_status_t attn_bsr_encode_host_stacked(const uint8_t* dense, int num_masks, int L,
+                                           int32_t* full_indptr, int32_t* full_kblock,
+                                           int32_t* part_indptr, int32_t* part_kblock,
+                                           uint64_t* part_bits, int* nnz_full, int* nnz_part);
+
+/*
+ * attn_prefill_bsr with num_masks stacked masks (layout above): query head h
+ * uses mask h / (Hq / num_masks); num_masks must divide Hq (1: one mask for
+ * every head, Hq: one mask per head).  attn_prefill_bsr is this call with
+ * num_masks = 1.
+ */
+attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v,
+                                     const attn_bsr_mask* mask, int num_masks, void* o,
+                                     float* lse, int B, int L, int Hq, int Hkv, int D, float scale,
+                                     int dtype, void* hip_stream);
+
 /* ---- test exports ------------------------------------------------------ */
 
 /* Write, with the device code the decode kernels use, every split's key range

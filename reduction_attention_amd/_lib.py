@@ -42,6 +42,10 @@ SIGNATURES = {
     "attn_prefill_splitkv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _i64, _f32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "attn_bsr_encode_host": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "attn_bsr_encode_host_stacked": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                            _vp]),
+    "attn_prefill_bsr_heads": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _i32, _vp,
+                                      _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
     "attn_prefill_bsr": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _vp, _vp, _i32, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _vp]),
     "attn_debug_split_ranges": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),

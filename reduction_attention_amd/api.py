@@ -199,6 +199,7 @@ class BsrMask:
     part_indptr: torch.Tensor
     part_kblock: torch.Tensor
     part_bits: torch.Tensor  # int64 storage of the uint64 words
+    num_masks: int = 1  # stacked masks; indptr arrays hold num_masks * (num_blocks + 1)
 
     @property
     def num_blocks(self) -> int:
@@ -208,7 +209,7 @@ class BsrMask:
         mv = lambda t: t.to(device).contiguous()  # noqa: E731
         return BsrMask(self.seq_len, self.nnz_full, self.nnz_part, mv(self.full_indptr),
                        mv(self.full_kblock), mv(self.part_indptr), mv(self.part_kblock),
-                       mv(self.part_bits))
+                       mv(self.part_bits), self.num_masks)
 
     def struct(self) -> AttnBsrMask:
         return AttnBsrMask(self.seq_len, self.num_blocks, self.nnz_full, self.nnz_part,
@@ -218,29 +219,49 @@ class BsrMask:
 
 
 def attn_bsr_encode_host(dense: torch.Tensor) -> BsrMask:
-    """Encode a dense 0/1 mask (CPU uint8 [L,L], 1 = attend) on the host."""
+    """Encode dense 0/1 masks on the host (CPU uint8, 1 = attend).
+
+    [L, L] gives one mask; [M, L, L] gives M stacked masks (mask m serves
+    query heads m*Hq/M .. (m+1)*Hq/M - 1 in attn_prefill_bsr)."""
     dense = dense.to("cpu", torch.uint8).contiguous()
-    L = dense.shape[0]
-    if dense.dim() != 2 or dense.shape[1] != L:
-        raise ValueError("mask must be square [L, L]")
+    if dense.dim() == 2:
+        dense3, stacked = dense.unsqueeze(0), False
+    elif dense.dim() == 3:
+        dense3, stacked = dense, True
+    else:
+        raise ValueError("mask must be [L, L] or [M, L, L]")
+    M, L = dense3.shape[0], dense3.shape[1]
+    if dense3.shape[2] != L:
+        raise ValueError("mask must be square in its last two dimensions")
     lib = load()
     nf, np_ = ctypes.c_int(0), ctypes.c_int(0)
-    check(lib.attn_bsr_encode_host(_ptr(dense), L, None, None, None, None, None,
-                                   ctypes.byref(nf), ctypes.byref(np_)), "attn_bsr_encode_host")
+
+    def call(*outs):
+        if stacked:
+            st = lib.attn_bsr_encode_host_stacked(_ptr(dense3), M, L, *outs, ctypes.byref(nf),
+                                                  ctypes.byref(np_))
+            check(st, "attn_bsr_encode_host_stacked")
+        else:
+            st = lib.attn_bsr_encode_host(_ptr(dense3), L, *outs, ctypes.byref(nf),
+                                          ctypes.byref(np_))
+            check(st, "attn_bsr_encode_host")
+
+    call(None, None, None, None, None)
     nb = L // 64
-    fi = torch.zeros(nb + 1, dtype=torch.int32)
+    fi = torch.zeros(M * (nb + 1), dtype=torch.int32)
     fk = torch.zeros(max(nf.value, 1), dtype=torch.int32)
-    pi = torch.zeros(nb + 1, dtype=torch.int32)
+    pi = torch.zeros(M * (nb + 1), dtype=torch.int32)
     pk = torch.zeros(max(np_.value, 1), dtype=torch.int32)
     pb = torch.zeros(max(np_.value, 1) * 64, dtype=torch.int64)
-    check(lib.attn_bsr_encode_host(_ptr(dense), L, _ptr(fi), _ptr(fk), _ptr(pi), _ptr(pk), _ptr(pb),
-                                   ctypes.byref(nf), ctypes.byref(np_)), "attn_bsr_encode_host")
-    return BsrMask(L, nf.value, np_.value, fi, fk, pi, pk, pb)
+    call(_ptr(fi), _ptr(fk), _ptr(pi), _ptr(pk), _ptr(pb))
+    return BsrMask(L, nf.value, np_.value, fi, fk, pi, pk, pb, M)
 
 
 def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, stream=None,
                      want_lse=True):
-    """Block-sparse prefill.  q [B,L,Hq,D]; k, v [B,L,Hkv,D]; mask on q's device."""
+    """Block-sparse prefill.  q [B,L,Hq,D]; k, v [B,L,Hkv,D]; mask on q's device.
+
+    A mask of M stacked masks applies mask h // (Hq // M) to query head h."""
     _dev(q, k, v, o, lse)
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -250,9 +271,16 @@ def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, strea
     if lse is None and want_lse:
         lse = torch.empty((B, L, Hq), dtype=torch.float32, device=q.device)
     ms = mask.struct()
-    st = load().attn_prefill_bsr(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(ms), _ptr(o), _ptr(lse),
-                                 B, L, Hq, Hkv, D, scale, _dtype_code(q), _stream(stream))
-    check(st, "attn_prefill_bsr")
+    if mask.num_masks == 1:
+        st = load().attn_prefill_bsr(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(ms), _ptr(o),
+                                     _ptr(lse), B, L, Hq, Hkv, D, scale, _dtype_code(q),
+                                     _stream(stream))
+        check(st, "attn_prefill_bsr")
+    else:
+        st = load().attn_prefill_bsr_heads(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(ms),
+                                           mask.num_masks, _ptr(o), _ptr(lse), B, L, Hq, Hkv, D,
+                                           scale, _dtype_code(q), _stream(stream))
+        check(st, "attn_prefill_bsr_heads")
     return o, lse
 
 

@@ -309,21 +309,19 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* k, const void* v,
                     "prefill_splitkv launch");
 }
 
-attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_indptr,
-                                   int32_t* full_kblock, int32_t* part_indptr,
-                                   int32_t* part_kblock, uint64_t* part_bits, int* nnz_full,
-                                   int* nnz_part) {
-  if (!dense || !nnz_full || !nnz_part) return fail(ATTN_EINVAL, "bsr_encode: null pointer");
-  if (L <= 0 || L % 64) return fail(ATTN_EINVAL, "bsr_encode: L = %d is not a positive multiple of 64", L);
-  const bool fill = full_indptr || full_kblock || part_indptr || part_kblock || part_bits;
-  if (fill && !(full_indptr && part_indptr && part_bits && (full_kblock || *nnz_full == 0) &&
-                (part_kblock || *nnz_part == 0)))
-    return fail(ATTN_EINVAL, "bsr_encode: fill pass needs every output array");
+// One L x L mask into the two-level format, appended after f_base full and
+// p_base part tiles already written: indptr entries qb = 0 .. nb (values
+// global, i.e. offset by the bases), kblock / bits entries from the bases
+// on.  fill = false only counts.
+static attn_status_t encode_mask(const uint8_t* dense, int L, int f_base, int p_base,
+                                 int32_t* full_indptr, int32_t* full_kblock, int32_t* part_indptr,
+                                 int32_t* part_kblock, uint64_t* part_bits, bool fill, int f_cap,
+                                 int p_cap, int* nf_out, int* np_out) {
   const int nb = L / 64;
-  int nf = 0, np = 0;
+  int nf = f_base, np = p_base;
   if (fill) {
-    full_indptr[0] = 0;
-    part_indptr[0] = 0;
+    full_indptr[0] = nf;
+    part_indptr[0] = np;
   }
   for (int qb = 0; qb < nb; ++qb) {
     for (int kb = 0; kb < nb; ++kb) {
@@ -346,13 +344,13 @@ attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_in
       if (valid == 0) continue;  // empty OT: not stored
       if (valid == 64 * 64) {
         if (fill) {
-          if (nf >= *nnz_full) return fail(ATTN_EINVAL, "bsr_encode: nnz_full too small");
+          if (nf >= f_cap) return fail(ATTN_EINVAL, "bsr_encode: nnz_full too small");
           full_kblock[nf] = kb;
         }
         ++nf;
       } else {
         if (fill) {
-          if (np >= *nnz_part) return fail(ATTN_EINVAL, "bsr_encode: nnz_part too small");
+          if (np >= p_cap) return fail(ATTN_EINVAL, "bsr_encode: nnz_part too small");
           part_kblock[np] = kb;
           std::memcpy(part_bits + size_t(np) * 64, words, sizeof words);
         }
@@ -364,12 +362,45 @@ attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_in
       part_indptr[qb + 1] = np;
     }
   }
+  *nf_out = nf;
+  *np_out = np;
+  return ATTN_OK;
+}
+
+attn_status_t attn_bsr_encode_host_stacked(const uint8_t* dense, int num_masks, int L,
+                                           int32_t* full_indptr, int32_t* full_kblock,
+                                           int32_t* part_indptr, int32_t* part_kblock,
+                                           uint64_t* part_bits, int* nnz_full, int* nnz_part) {
+  if (!dense || !nnz_full || !nnz_part) return fail(ATTN_EINVAL, "bsr_encode: null pointer");
+  if (L <= 0 || L % 64) return fail(ATTN_EINVAL, "bsr_encode: L = %d is not a positive multiple of 64", L);
+  if (num_masks < 1) return fail(ATTN_EINVAL, "bsr_encode: num_masks %d < 1", num_masks);
+  const bool fill = full_indptr || full_kblock || part_indptr || part_kblock || part_bits;
+  if (fill && !(full_indptr && part_indptr && part_bits && (full_kblock || *nnz_full == 0) &&
+                (part_kblock || *nnz_part == 0)))
+    return fail(ATTN_EINVAL, "bsr_encode: fill pass needs every output array");
+  const int nb = L / 64;
+  int nf = 0, np = 0;
+  for (int m = 0; m < num_masks; ++m) {
+    const uint8_t* dm = dense + size_t(m) * size_t(L) * size_t(L);
+    attn_status_t st = encode_mask(dm, L, nf, np, fill ? full_indptr + size_t(m) * (nb + 1) : nullptr,
+                                   full_kblock, fill ? part_indptr + size_t(m) * (nb + 1) : nullptr,
+                                   part_kblock, part_bits, fill, *nnz_full, *nnz_part, &nf, &np);
+    if (st != ATTN_OK) return st;
+  }
   if (fill && (nf != *nnz_full || np != *nnz_part))
     return fail(ATTN_EINVAL, "bsr_encode: sizes differ from the mask (%d/%d full, %d/%d part)", nf,
                 *nnz_full, np, *nnz_part);
   *nnz_full = nf;
   *nnz_part = np;
   return ok();
+}
+
+attn_status_t attn_bsr_encode_host(const uint8_t* dense, int L, int32_t* full_indptr,
+                                   int32_t* full_kblock, int32_t* part_indptr,
+                                   int32_t* part_kblock, uint64_t* part_bits, int* nnz_full,
+                                   int* nnz_part) {
+  return attn_bsr_encode_host_stacked(dense, 1, L, full_indptr, full_kblock, part_indptr,
+                                      part_kblock, part_bits, nnz_full, nnz_part);
 }
 
 static attn_status_t check_mask(const attn_bsr_mask* m, const char* who) {
@@ -385,9 +416,10 @@ static attn_status_t check_mask(const attn_bsr_mask* m, const char* who) {
   return ATTN_OK;
 }
 
-attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
-                               const attn_bsr_mask* mask, void* o, float* lse, int B, int L, int Hq,
-                               int Hkv, int D, float scale, int dtype, void* hip_stream) {
+attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v,
+                                     const attn_bsr_mask* mask, int num_masks, void* o, float* lse,
+                                     int B, int L, int Hq, int Hkv, int D, float scale, int dtype,
+                                     void* hip_stream) {
   if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "prefill_bsr: null pointer");
   attn_status_t ms = check_mask(mask, "prefill_bsr");
   if (ms != ATTN_OK) return ms;
@@ -395,6 +427,8 @@ attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
   if (B > 65535 || Hq > 65535) return fail(ATTN_EUNSUPPORTED, "prefill_bsr: B or Hq above 65535");
   if (L != mask->seq_len) return fail(ATTN_EINVAL, "prefill_bsr: L %d != mask seq_len %d", L, mask->seq_len);
   if (Hq % Hkv) return fail(ATTN_EINVAL, "prefill_bsr: Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  if (num_masks < 1 || Hq % num_masks)
+    return fail(ATTN_EINVAL, "prefill_bsr: num_masks %d does not divide Hq %d", num_masks, Hq);
   if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "prefill_bsr: D = %d (supported: 64, 128)", D);
   if (dtype != ATTN_BF16 && dtype != ATTN_F16)
     return fail(ATTN_EUNSUPPORTED, "prefill_bsr: dtype %d (supported: f16, bf16)", dtype);
@@ -406,9 +440,16 @@ attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
     return fail(ATTN_EINVAL, "prefill_bsr: part_bits must be 8-byte aligned");
   rattn::BsrArgs a{q, k, v, mask->full_indptr, mask->full_kblock, mask->part_indptr,
                    mask->part_kblock, mask->part_bits, o, lse, B, L, Hq, Hkv, D, Hq / Hkv,
-                   mask->num_blocks, scale * kLog2e, dtype};
+                   mask->num_blocks, scale * kLog2e, dtype, Hq / num_masks};
   return hip_status(rattn::launch_prefill_bsr(a, static_cast<hipStream_t>(hip_stream)),
                     "prefill_bsr launch");
+}
+
+attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,
+                               const attn_bsr_mask* mask, void* o, float* lse, int B, int L, int Hq,
+                               int Hkv, int D, float scale, int dtype, void* hip_stream) {
+  return attn_prefill_bsr_heads(q, k, v, mask, 1, o, lse, B, L, Hq, Hkv, D, scale, dtype,
+                                hip_stream);
 }
 
 attn_status_t attn_debug_split_ranges(const int32_t* kv_indptr, int B, int max_kv_len,

@@ -79,6 +79,8 @@ struct BsrArgs {
   int B, L, Hq, Hkv, D, G, num_blocks;
   float scale_log2;
   int dtype;
+  int heads_per_mask;  // query head h uses mask h / heads_per_mask of the
+                       // stacked arrays (indptr entries (num_blocks + 1) per mask)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

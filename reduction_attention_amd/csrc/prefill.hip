@@ -294,8 +294,9 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = hq / a.G;
-  const int f0 = a.full_indptr[qblk], n_full = a.full_indptr[qblk + 1] - f0;
-  const int p0 = a.part_indptr[qblk], n_part = a.part_indptr[qblk + 1] - p0;
+  const int mrow = (hq / a.heads_per_mask) * (a.num_blocks + 1) + qblk;  // this head's mask
+  const int f0 = a.full_indptr[mrow], n_full = a.full_indptr[mrow + 1] - f0;
+  const int p0 = a.part_indptr[mrow], n_part = a.part_indptr[mrow + 1] - p0;
   const int ntiles = n_full + n_part;
 
   const int64_t L = a.L;

@@ -132,6 +132,7 @@ class Workload:
     ragged: tuple = ()   # (lo, hi) log-uniform decode lengths
     causal: bool = False
     splits: tuple = ()   # forced split counts to check (decode)
+    num_masks: int = 1   # bsr: masks stacked [M, L, L], mask m for query heads m*Hq/M ..
     extra: dict = field(default_factory=dict)
 
     @property
@@ -177,8 +178,12 @@ class Workload:
         raise ValueError(self.kind)
 
     def mask(self, g_shape=None) -> torch.Tensor:
-        """The workload's dense 0/1 mask (CPU uint8), drawn from the shape generator."""
-        return sparse_mask(self.L, g_shape if g_shape is not None else gen(self.seed), **self.extra)
+        """The workload's dense 0/1 mask (CPU uint8), drawn from the shape generator:
+        [L, L], or [num_masks, L, L] drawn one after another when num_masks > 1."""
+        g = g_shape if g_shape is not None else gen(self.seed)
+        if self.num_masks == 1:
+            return sparse_mask(self.L, g, **self.extra)
+        return torch.stack([sparse_mask(self.L, g, **self.extra) for _ in range(self.num_masks)])
 
 
 WORKLOADS = {
@@ -192,6 +197,9 @@ WORKLOADS = {
                                     Hq=32, Hkv=8, D=128, L=4096, causal=True),
     "bsr_prefill_fp16": Workload("bsr_prefill_fp16", "bsr", 5, torch.float16, B=1, Hq=16,
                                  Hkv=16, D=64, L=4096),
+    # longer sequence, one mask per group of 4 query heads
+    "bsr_heads_prefill_fp16": Workload("bsr_heads_prefill_fp16", "bsr", 7, torch.float16, B=1,
+                                       Hq=16, Hkv=16, D=64, L=8192, num_masks=4),
     # append / chunked prefill: 128 new tokens per request against a 16k history
     "append_prefill_bf16": Workload("append_prefill_bf16", "append", 6, torch.bfloat16, B=4,
                                     Hq=32, Hkv=8, D=128, L=16384, Lq=128, causal=True),

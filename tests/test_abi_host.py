@@ -237,6 +237,57 @@ def test_encoder_roundtrip(lib, kind):
         assert bm.nnz_full == 3 and bm.nnz_part == 3  # below diagonal full, diagonal part
 
 
+def test_encoder_stacked_equals_single(lib):
+    """Stacked encoding: mask m's rows at indptr[m*(nb+1):], values index the
+    concatenated arrays; each mask decodes to its own dense mask and matches
+    the one-mask encoding of that mask shifted by the running totals."""
+    import reduction_attention_amd as ra
+    L, nb = 256, 4
+    masks = [torch.ones(L, L, dtype=torch.uint8).tril(),
+             torch.zeros(L, L, dtype=torch.uint8),
+             synth.window_mask(L, 70),
+             (torch.rand(L, L, generator=synth.gen(9)) < 0.2).to(torch.uint8)]
+    dense = torch.stack(masks)
+    bm = ra.attn_bsr_encode_host(dense)
+    assert bm.num_masks == 4 and bm.full_indptr.numel() == 4 * (nb + 1)
+    f0 = p0 = 0
+    for m, d in enumerate(masks):
+        one = ra.attn_bsr_encode_host(d)
+        fi = bm.full_indptr[m * (nb + 1):(m + 1) * (nb + 1)]
+        pi = bm.part_indptr[m * (nb + 1):(m + 1) * (nb + 1)]
+        assert torch.equal(fi - f0, one.full_indptr) and torch.equal(pi - p0, one.part_indptr)
+        assert torch.equal(bm.full_kblock[f0:f0 + one.nnz_full], one.full_kblock[:one.nnz_full])
+        assert torch.equal(bm.part_kblock[p0:p0 + one.nnz_part], one.part_kblock[:one.nnz_part])
+        assert torch.equal(bm.part_bits[p0 * 64:(p0 + one.nnz_part) * 64],
+                           one.part_bits[:one.nnz_part * 64])
+        sub = ra.BsrMask(L, one.nnz_full, one.nnz_part, fi - f0,
+                         bm.full_kblock[f0:f0 + max(one.nnz_full, 1)], pi - p0,
+                         bm.part_kblock[p0:p0 + max(one.nnz_part, 1)],
+                         bm.part_bits[p0 * 64:(p0 + max(one.nnz_part, 1)) * 64])
+        assert torch.equal(decode_by_definition(sub, L), d)
+        f0 += one.nnz_full
+        p0 += one.nnz_part
+    assert bm.nnz_full == f0 and bm.nnz_part == p0
+
+
+def test_bsr_heads_validation(lib):
+    from reduction_attention_amd._lib import AttnBsrMask
+    m = AttnBsrMask(256, 4, 0, 0, 16, 0, 16, 0, 0)
+    f = lib.attn_prefill_bsr_heads
+    ok = (P, P, P, ctypes.byref(m))
+    assert f(*ok, 0, P, None, 1, 256, 4, 2, 64, 0.1, 2, None) == 1   # no masks
+    assert f(*ok, 3, P, None, 1, 256, 4, 2, 64, 0.1, 2, None) == 1   # 3 does not divide 4
+    assert f(*ok, 8, P, None, 1, 256, 4, 2, 64, 0.1, 2, None) == 1   # more masks than heads
+    assert f(*ok, 2, P, None, 1, 256, 4, 2, 64, 0.1, 0, None) == 2   # fp32
+    d = torch.ones(2, 100, 100, dtype=torch.uint8)
+    nf, np_ = ctypes.c_int(0), ctypes.c_int(0)
+    enc = lib.attn_bsr_encode_host_stacked
+    assert enc(ctypes.c_void_p(d.data_ptr()), 2, 100, None, None, None, None, None,
+               ctypes.byref(nf), ctypes.byref(np_)) == 1
+    assert enc(ctypes.c_void_p(d.data_ptr()), 0, 64, None, None, None, None, None,
+               ctypes.byref(nf), ctypes.byref(np_)) == 1
+
+
 def test_encoder_rejects_bad_sizes(lib):
     d = torch.ones(100, 100, dtype=torch.uint8)
     nf, np_ = ctypes.c_int(0), ctypes.c_int(0)

@@ -118,3 +118,73 @@ def test_device_decode_bit_exact(kind):
     m = ra().attn_bsr_encode_host(dense).to(DEV)
     got = ra().attn_debug_bsr_decode(m).cpu()
     assert torch.equal(got, dense)
+
+
+def oracle_bsr_heads(q, k, v, dense3, scale):
+    """Per-head masks through the one-mask oracle, one query head at a time:
+    head h takes mask h // (Hq / M) and KV head h // (Hq / Hkv)."""
+    B, L, Hq, _ = q.shape
+    M, g = dense3.shape[0], Hq // k.shape[2]
+    o = torch.zeros(q.shape, dtype=torch.float64)
+    lse = torch.zeros((B, L, Hq), dtype=torch.float64)
+    for h in range(Hq):
+        kh = h // g
+        oh, lh = oracle_bsr(q[:, :, h:h + 1], k[:, :, kh:kh + 1], v[:, :, kh:kh + 1],
+                            dense3[h // (Hq // M)], scale)
+        o[:, :, h:h + 1] = oh
+        lse[:, :, h:h + 1] = lh
+    return o, lse
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("num_masks", [2, 4])
+def test_per_head_masks(dtype, D, num_masks):
+    """Stacked masks: each head (group) sees only its own mask."""
+    L, B, Hq, Hkv = 320, 2, 4, 2
+    kinds = [synth.window_mask(L, 90),
+             synth.sparse_mask(L, synth.gen(61), window=64, block=64, globals_per_block=2,
+                               random_blocks=1),
+             torch.ones(L, L, dtype=torch.uint8).tril(),
+             (torch.rand(L, L, generator=synth.gen(62)) < 0.25).to(torch.uint8)]
+    dense3 = torch.stack(kinds[:num_masks])
+    q, k, v = qkv(B, L, Hq, Hkv, D, dtype, 63 + D)
+    o_ref, lse_ref = oracle_bsr_heads(q, k, v, dense3, 1 / D ** 0.5)
+    o, lse, m = bsr(q, k, v, dense3)
+    assert m.num_masks == num_masks
+    check(f"bsr heads M={num_masks} {dtype} D={D}", o, o_ref, lse, lse_ref, dtype)
+
+
+def test_per_head_masks_equal_separate_calls():
+    """Mask per head in one call == one single-mask call per head, bit for bit."""
+    L, Hq, D = 256, 4, 64
+    dense3 = torch.stack([synth.window_mask(L, 40 + 30 * h) for h in range(Hq)])
+    q, k, v = qkv(1, L, Hq, Hq, D, torch.float16, 64)
+    o, lse, _ = bsr(q, k, v, dense3)
+    for h in range(Hq):
+        oh, lh, _ = bsr(q[:, :, h:h + 1].contiguous(), k[:, :, h:h + 1].contiguous(),
+                        v[:, :, h:h + 1].contiguous(), dense3[h])
+        assert torch.equal(o[:, :, h:h + 1], oh) and torch.equal(lse[:, :, h:h + 1], lh)
+
+
+def test_heads_workload_sampled():
+    """B 1, L 8192, 16 heads, D 64, fp16; 4 masks (one per 4 heads) of the sparse recipe."""
+    w = synth.workload("bsr_heads_prefill_fp16")
+    inp = w.make(DEV)
+    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"])
+    print(f"masks={m.num_masks} full={m.nnz_full} part={m.nnz_part}", flush=True)
+    g = synth.gen(78)
+    n = 1000
+    hpm = w.Hq // w.num_masks
+    q, k, v = (inp[x][0].cpu() for x in ("q", "k", "v"))
+    for mi in range(w.num_masks):
+        t = torch.randint(0, w.L, (n,), generator=g)
+        hl = torch.randint(0, hpm, (n,), generator=g)
+        hs = slice(mi * hpm, (mi + 1) * hpm)
+        o_ref, lse_ref = oracle.attention(q[:, hs], k[:, hs], v[:, hs], [0, w.L], [0, w.L],
+                                          w.scale, oracle.MASK_DENSE, inp["mask"][mi],
+                                          rows=torch.stack([t, hl], 1))
+        h = hl + mi * hpm
+        check(f"bsr heads 8192 sampled mask {mi}", o[0][t.to(DEV), h.to(DEV)], o_ref,
+              lse[0][t.to(DEV), h.to(DEV)], lse_ref, torch.float16)
+    assert bool(torch.isfinite(o).all())

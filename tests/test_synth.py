@@ -40,3 +40,11 @@ def test_window_mask_definition():
                            [0, 0, 1, 1, 0, 0], [0, 0, 0, 1, 1, 0], [0, 0, 0, 0, 1, 1]],
                           dtype=torch.uint8)
     assert torch.equal(m, expect)
+
+
+def test_stacked_workload_masks_differ():
+    w = synth.workload("bsr_heads_prefill_fp16")
+    m = w.mask()
+    assert m.shape == (w.num_masks, w.L, w.L) and w.Hq % w.num_masks == 0
+    assert not torch.equal(m[0], m[1])  # random blocks drawn per mask
+    assert torch.equal(m, w.mask())     # deterministic
