@@ -442,27 +442,39 @@ struct Swz {
   static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RP) % (4 / RP)); }
 };
 
-// Byte offset of this lane's row within a tile instruction's RPI rows
-// (computed once per workgroup; dma_tile adds the rest with cheap ops).
-template <int D>
-__device__ __forceinline__ int dma_lane_offset(int row_stride, int tid) {
-  return ((tid & 63) / Swz<D>::CPR) * row_stride * 2;
-}
+// This lane's byte offsets (row within the tile, swizzled 16-byte chunk)
+// for every tile instruction its wave issues: the NT threads share the
+// BK / RPI instructions of a tile, wave w taking instructions w, w + W, ...;
+// lane l writes slot l % CPR of row RPI * inst + l / CPR and fetches the
+// chunk that belongs there.  Computed once per workgroup, so a tile load
+// costs only its scalar setup and the loads themselves.
+template <int D, int BK, int NT, bool IS_V>
+struct DmaLane {
+  typedef Swz<D> S;
+  static constexpr int NI = BK / S::RPI, W = NT / 64, PER = NI / W;
+  static_assert(NI % W == 0, "tile instructions must split evenly over the waves");
+  int off[PER];
+  __device__ __forceinline__ DmaLane(int row_stride, int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int r = S::RPI * (w + W * x) + lane / S::CPR;
+      const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
+      off[x] = r * row_stride * 2 + 16 * chunk;
+    }
+  }
+};
 
 // One BK-key tile (K if IS_V is false, else V) of a request with n_keys
 // keys, rows key0 .. key0+BK-1, into the LDS stage at dst; rows past the
-// request end arrive as zeros (the buffer resource ends there).  The NT
-// threads share the BK / RPI instructions of the tile, wave w taking
-// instructions w, w + W, ...; lane l writes slot l % CPR of row
-// RPI * inst + l / CPR and fetches the chunk that belongs there.
+// request end arrive as zeros (the buffer resource ends there).
 // Completion is tracked by vmcnt: the caller waits for it before the
 // barrier that publishes the stage.
 template <int D, int BK, int NT, bool IS_V>
 __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, int row_stride,
-                                         int key0, int n_keys, int lane_off, int tid) {
-  typedef Swz<D> S;
-  constexpr int NI = BK / S::RPI, W = NT / 64;
-  static_assert(NI % W == 0, "tile instructions must split evenly over the waves");
+                                         int key0, int n_keys, const DmaLane<D, BK, NT, IS_V>& dl,
+                                         int tid) {
+  typedef DmaLane<D, BK, NT, IS_V> DL;
   // raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte count,
   // 32-bit data format) over the request's rows from key0 on
   typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -474,15 +486,11 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
   rsv[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
   rsv[2] = __builtin_amdgcn_readfirstlane(int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
   rsv[3] = 0x00020000;
-  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst));
 #pragma unroll
-  for (int x = 0; x < NI / W; ++x) {
-    const int inst = w + W * x;
-    const int r = S::RPI * inst + lane / S::CPR;
-    const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
-    const int rows_off = __builtin_amdgcn_readfirstlane(S::RPI * inst * row_stride * 2);
-    const int voff = lane_off + rows_off + 16 * chunk;
+  for (int x = 0; x < DL::PER; ++x) {
+    const int inst = w + DL::W * x;
     // Written as assembly so that the compiler, which cannot tell which
     // LDS bytes a direct-to-LDS load writes, does not make every later LDS
     // read wait for it: the tile goes to a stage no read of the same step
@@ -491,7 +499,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, in
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %2, 0 offen lds"
         :
-        : "s"(lds0 + inst * 1024), "v"(voff), "s"(rsv)
+        : "s"(lds0 + inst * 1024), "v"(dl.off[x]), "s"(rsv)
         : "memory", "m0");
   }
 }

@@ -143,12 +143,13 @@ void prefill_kernel(PrefillArgs a) {
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
 
   // prologue: K of tiles 0 and 1, V of tile 0
-  const int loff = dma_lane_offset<D>(row_stride, tid);
+  const DmaLane<D, BK, NT, false> dk(row_stride, tid);
+  const DmaLane<D, BK, NT, true> dv(row_stride, tid);
   if (ntiles > 0) {
-    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, k_lo, n_kv, loff, tid);
-    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, k_lo, n_kv, loff, tid);
+    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, k_lo, n_kv, dk, tid);
+    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, k_lo, n_kv, dv, tid);
   }
-  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, k_lo + BK, n_kv, loff, tid);
+  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, k_lo + BK, n_kv, dk, tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
@@ -200,8 +201,8 @@ void prefill_kernel(PrefillArgs a) {
   // (The stage pointers are restrict-qualified: the tile a step streams in
   // and the tiles it reads never overlap.)
   auto fill = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill) {
-    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, k_lo + (j + 2) * BK, n_kv, loff, tid);
-    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, k_lo + (j + 1) * BK, n_kv, loff, tid);
+    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, k_lo + (j + 2) * BK, n_kv, dk, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, k_lo + (j + 1) * BK, n_kv, dv, tid);
   };
   auto matrix = [&](int j, const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
     // matrix phase at raised issue priority: of the two waves sharing a
@@ -311,7 +312,8 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
-  const int loff = dma_lane_offset<D>(row_stride, tid);
+  const DmaLane<D, BK, NT, false> dk(row_stride, tid);
+  const DmaLane<D, BK, NT, true> dv(row_stride, tid);
 
   // the key block of stored tile j (full tiles first, then part tiles) into
   // the given stage, and its bitmap word if it is a part tile
@@ -320,8 +322,8 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
     const bool part = j >= n_full;
     const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
     if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
-    dma_tile<D, BK, NT, false>(kd, kbase, row_stride, kblk * 64, int(L), loff, tid);
-    dma_tile<D, BK, NT, true>(vd, vbase, row_stride, kblk * 64, int(L), loff, tid);
+    dma_tile<D, BK, NT, false>(kd, kbase, row_stride, kblk * 64, int(L), dk, tid);
+    dma_tile<D, BK, NT, true>(vd, vbase, row_stride, kblk * 64, int(L), dv, tid);
   };
   if (ntiles > 0) fetch(0, lds_k, lds_v);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 is in LDS
