@@ -61,6 +61,23 @@ __device__ __forceinline__ int xcd_head(int x, int hq_count) {
   return (x & 7) * (hq_count >> 3) + (x >> 3);
 }
 
+// The value update's schedule: N matrix ops (times RB), each fed by two
+// transposing LDS reads, with PV_DEPTH reads kept in flight ahead of them.
+#ifndef RATTN_PREFILL_PV_DEPTH
+#define RATTN_PREFILL_PV_DEPTH 8
+#endif
+template <int N, int RB>
+__device__ __forceinline__ void lds_pipeline_pv() {
+#if RATTN_PREFILL_PV_DEPTH
+  __builtin_amdgcn_sched_group_barrier(0x100, RATTN_PREFILL_PV_DEPTH, 1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 1);
+    if (i < N - RATTN_PREFILL_PV_DEPTH / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+  }
+#endif
+}
+
 // Schedule of a block of N operand reads from LDS, each feeding RB matrix
 // ops: keep DEPTH reads in flight ahead of the matrix ops.
 #ifndef RATTN_PREFILL_DEPTH
@@ -213,7 +230,10 @@ void prefill_kernel(PrefillArgs a) {
       qk_tile_sw<T, D, BK, RB>(sc, kread, qb, lane);
       lds_pipeline<Gm::NKB * D / 16, RB>();
     }
-    if (j < wnt) pv_tile_tr<T, D, BK, RB>(st, pb, vread, lane);
+    if (j < wnt) {
+      pv_tile_tr<T, D, BK, RB>(st, pb, vread, lane);
+      lds_pipeline_pv<D / 32 * Gm::NKB * 2, RB>();
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   auto end_step = [&]() {
