@@ -444,65 +444,109 @@ struct Swz {
   static __device__ __forceinline__ int fv(int r) { return 4 * ((r / RP) % (4 / RP)); }
 };
 
-// This lane's byte offsets (row within the tile, swizzled 16-byte chunk)
-// for every tile instruction its wave issues: the NT threads share the
-// BK / RPI instructions of a tile, wave w taking instructions w, w + W, ...;
-// lane l writes slot l % CPR of row RPI * inst + l / CPR and fetches the
-// chunk that belongs there.  Computed once per workgroup, so a tile load
-// costs only its scalar setup and the loads themselves.
+// This lane's byte offsets (row within the tile, swizzled 16-byte chunk) in
+// the tile instructions its wave issues, computed once per workgroup: the
+// NT threads share the BK / RPI instructions of a tile, wave w taking
+// instructions w, w + W, ...; lane l writes slot l % CPR of row
+// RPI * inst + l / CPR and fetches the chunk that belongs there.  When a
+// wave's instructions are a whole number of swizzle periods (16 rows)
+// apart they share the chunk, and one offset serves them all (the
+// instruction's first row goes into its buffer resource).
 template <int D, int BK, int NT, bool IS_V>
 struct DmaLane {
   typedef Swz<D> S;
   static constexpr int NI = BK / S::RPI, W = NT / 64, PER = NI / W;
   static_assert(NI % W == 0, "tile instructions must split evenly over the waves");
-  int off[PER];
+  static constexpr bool SHARED = (S::RPI * W) % 16 == 0;
+  int off[SHARED ? 1 : PER];  // relative to the instruction's first row
   __device__ __forceinline__ DmaLane(int row_stride, int tid) {
     const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
-    for (int x = 0; x < PER; ++x) {
+    for (int x = 0; x < (SHARED ? 1 : PER); ++x) {
       const int r = S::RPI * (w + W * x) + lane / S::CPR;
       const int chunk = (lane % S::CPR) ^ (IS_V ? S::fv(r) : S::fk(r));
-      off[x] = r * row_stride * 2 + 16 * chunk;
+      off[x] = (lane / S::CPR) * row_stride * 2 + 16 * chunk;
     }
   }
+  __device__ __forceinline__ int get(int x) const { return off[SHARED ? 0 : x]; }
 };
 
-// One BK-key tile (K if IS_V is false, else V) of a request with n_keys
-// keys, rows key0 .. key0+BK-1, into the LDS stage at dst; rows past the
-// request end arrive as zeros (the buffer resource ends there).
+// min(max(x, 0), HI) of a uniform x on the scalar unit.  (Written out: the
+// compiler otherwise fuses the pair into a vector median instruction and
+// then has to move the result back to a scalar register.)
+template <int HI>
+__device__ __forceinline__ int sclamp_rows(int x) {
+  int r;
+  __asm__("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(x), "n"(HI));
+  return r;
+}
+
+// Where a request's K or V rows live: base address, bytes per row, row
+// count -- uniform values, held in scalar registers.
+struct DmaSrc {
+  uint32_t lo, hi;
+  int row_bytes, n_keys;
+};
+
+__device__ __forceinline__ DmaSrc dma_src(const uint16_t* base, int row_stride, int n_keys) {
+  const uint64_t a = uint64_t(size_t(base));
+  return {uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a)))),
+          uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(a >> 32)))),
+          __builtin_amdgcn_readfirstlane(row_stride * 2), __builtin_amdgcn_readfirstlane(n_keys)};
+}
+
+// One BK-key tile (K if IS_V is false, else V), rows key0 .. key0+BK-1 of
+// the request at src, into the LDS stage at dst; rows past the request end
+// arrive as zeros.  A tile inside the request takes one raw buffer resource
+// (gfx9 layout: 48-bit base, stride 0, byte count, 32-bit data format) at
+// the wave's first row and a scalar offset per instruction: a handful of
+// scalar instructions per tile.  The request's last tile gives each
+// instruction a resource of its own over just its rows, cut short at the
+// request end, since only the vector offset is range-checked.
 // Completion is tracked by vmcnt: the caller waits for it before the
 // barrier that publishes the stage.
 template <int D, int BK, int NT, bool IS_V>
-__device__ __forceinline__ void dma_tile(uint16_t* dst, const uint16_t* base, int row_stride,
-                                         int key0, int n_keys, const DmaLane<D, BK, NT, IS_V>& dl,
-                                         int tid) {
+__device__ __forceinline__ void dma_tile(uint16_t* dst, const DmaSrc& src, int key0,
+                                         const DmaLane<D, BK, NT, IS_V>& dl, int tid) {
   typedef DmaLane<D, BK, NT, IS_V> DL;
-  // raw buffer resource (gfx9 layout: 48-bit base, stride 0, byte count,
-  // 32-bit data format) over the request's rows from key0 on
+  typedef Swz<D> S;
   typedef int i32x4 __attribute__((ext_vector_type(4)));
-  const uint64_t addr = uint64_t(size_t(base + int64_t(key0) * row_stride));
-  const int64_t bytes = int64_t(n_keys - key0) * row_stride * 2;
-  const int64_t cap = 0x7fffffff;
-  i32x4 rsv;
-  rsv[0] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr)));
-  rsv[1] = __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu));
-  rsv[2] = __builtin_amdgcn_readfirstlane(int(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
-  rsv[3] = 0x00020000;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst));
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)dst)) + w * 1024;
+  const uint64_t base = (uint64_t(src.hi) << 32) | src.lo;
+  const int row0 = key0 + S::RPI * w;  // the wave's first row
+  // Written as assembly so that the compiler, which cannot tell which LDS
+  // bytes a direct-to-LDS load writes, does not make every later LDS read
+  // wait for it: the tile goes to a stage no read of the same step
+  // touches, and the caller waits (vmcnt) before publishing it.
+  if (key0 + BK <= src.n_keys) {
+    const uint64_t addr = base + uint64_t(uint32_t(row0)) * uint32_t(src.row_bytes);
+    const i32x4 rsv = {int(uint32_t(addr)), int(uint32_t(addr >> 32) & 0xffffu), 0x7fffffff,
+                       0x00020000};
 #pragma unroll
-  for (int x = 0; x < DL::PER; ++x) {
-    const int inst = w + DL::W * x;
-    // Written as assembly so that the compiler, which cannot tell which
-    // LDS bytes a direct-to-LDS load writes, does not make every later LDS
-    // read wait for it: the tile goes to a stage no read of the same step
-    // touches, and the caller waits (vmcnt) before publishing it.
-    __asm__ volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
-        : "s"(lds0 + inst * 1024), "v"(dl.off[x]), "s"(rsv)
-        : "memory", "m0");
+    for (int x = 0; x < DL::PER; ++x) {
+      const int soff = S::RPI * DL::W * x * src.row_bytes;
+      __asm__ volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, %3 offen lds"
+          :
+          : "s"(lds0 + x * DL::W * 1024), "v"(dl.get(x)), "s"(rsv), "s"(soff)
+          : "memory", "m0");
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < DL::PER; ++x) {
+      const int rowx = row0 + S::RPI * DL::W * x;  // the instruction's first row
+      const uint64_t addr = base + uint64_t(uint32_t(rowx)) * uint32_t(src.row_bytes);
+      const i32x4 rsv = {int(uint32_t(addr)), int(uint32_t(addr >> 32) & 0xffffu),
+                         sclamp_rows<S::RPI>(src.n_keys - rowx) * src.row_bytes, 0x00020000};
+      __asm__ volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(lds0 + x * DL::W * 1024), "v"(dl.get(x)), "s"(rsv)
+          : "memory", "m0");
+    }
   }
 }
 
@@ -551,16 +595,25 @@ __device__ __forceinline__ void qk_tile_sw(f32x16 (&s)[RB][BK / 32], const uint1
   }
 }
 
-// Four consecutive keys k0 .. k0+3 of dimension dbase + (lane % 16) from a
-// swizzled V tile: lane q + 4e of the 16-lane group supplies row k0 + e,
-// dims dbase + 4q .. +4.
+// Transposing reads of a swizzled V tile.  Lane q + 4e of each 16-lane group
+// supplies the address of row k0 + e, dims dbase + 4q .. +4, and receives
+// the four consecutive keys k0 .. k0+3 of dimension dbase + (lane % 16).
+// The swizzle of a row repeats every four rows, and every k0 a lane uses is
+// 4h plus a multiple of 8, so the address is a per-lane base for each
+// 32-dimension block plus a constant: the reads of a tile take D / 32
+// address registers and immediate offsets.
 template <int D>
-__device__ __forceinline__ u32x2 v_tr4(const uint16_t* vlds, int k0, int dbase, int lane) {
+__device__ __forceinline__ int vtr_base(int db, int lane) {
   typedef Swz<D> S;
-  const int i = lane & 15, q = i & 3, e = i >> 2;
-  const int r = k0 + e, dim = dbase + 4 * q;
-  const uint16_t* p = vlds + r * D + 8 * ((dim >> 3) ^ S::fv(r)) + (dim & 7);
+  static_assert(S::RP * (4 / S::RP) == 4, "the V swizzle must repeat every four rows");
+  const int i = lane & 15, q = i & 3, e = i >> 2, h = lane >> 5, g2 = (lane >> 4) & 1;
+  const int r = 4 * h + e, dim = 32 * db + 16 * g2 + 4 * q;
+  return 2 * (r * D + 8 * ((dim >> 3) ^ S::fv(r)) + (dim & 7));
+}
+
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* vlds, int byte_off) {
   typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const char* p = reinterpret_cast<const char*>(vlds) + byte_off;
   const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
   return __builtin_bit_cast(u32x2, x);
 }
@@ -575,21 +628,22 @@ __device__ __forceinline__ void pv_tile_tr(RowState<D> (&st)[RB],
                                            const typename T::vec8 (&pb)[RB][BK / 32][2],
                                            const uint16_t* vlds, int lane) {
   typedef typename T::vec8 vec8;
-  const int h = lane >> 5, g2 = (lane >> 4) & 1;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db) {
+    const int base = vtr_base<D>(db, lane);
 #pragma unroll
     for (int kb = 0; kb < BK / 32; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int k0 = 32 * kb + 16 * t + 4 * h, dbase = 32 * db + 16 * g2;
-        const u32x2 lo = v_tr4<D>(vlds, k0, dbase, lane);
-        const u32x2 hi = v_tr4<D>(vlds, k0 + 8, dbase, lane);
+        const int k0 = 32 * kb + 16 * t;  // plus 4h, inside base
+        const u32x2 lo = lds_tr4(vlds, base + 2 * k0 * D);
+        const u32x2 hi = lds_tr4(vlds, base + 2 * (k0 + 8) * D);
         const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           st[rb].o[db] = T::mfma32(as<vec8>(a), pb[rb][kb][t], st[rb].o[db]);
       }
+  }
 }
 
 }  // namespace rattn

@@ -126,7 +126,8 @@ void prefill_kernel(PrefillArgs a) {
   const int k_lo = a.s > 1 ? si * a.chunk : 0;
   const int k_hi = a.s > 1 ? (k_lo + a.chunk < n_kv ? k_lo + a.chunk : n_kv) : n_kv;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g = hq / a.G;
   const int off = n_kv - n_q;  // causal: key j valid for query i iff j <= i + off
   const int q_last_wg = (q_start + BQ < n_q ? q_start + BQ : n_q) - 1;
@@ -158,15 +159,16 @@ void prefill_kernel(PrefillArgs a) {
   const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + k_begin * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + k_begin * row_stride + int64_t(g) * D;
+  const DmaSrc ksrc = dma_src(kbase, row_stride, n_kv), vsrc = dma_src(vbase, row_stride, n_kv);
 
   // prologue: K of tiles 0 and 1, V of tile 0
   const DmaLane<D, BK, NT, false> dk(row_stride, tid);
   const DmaLane<D, BK, NT, true> dv(row_stride, tid);
   if (ntiles > 0) {
-    dma_tile<D, BK, NT, false>(lds_k0, kbase, row_stride, k_lo, n_kv, dk, tid);
-    dma_tile<D, BK, NT, true>(lds_v0, vbase, row_stride, k_lo, n_kv, dv, tid);
+    dma_tile<D, BK, NT, false>(lds_k0, ksrc, k_lo, dk, tid);
+    dma_tile<D, BK, NT, true>(lds_v0, vsrc, k_lo, dv, tid);
   }
-  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, kbase, row_stride, k_lo + BK, n_kv, dk, tid);
+  if (ntiles > 1) dma_tile<D, BK, NT, false>(lds_k1, ksrc, k_lo + BK, dk, tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tiles are in LDS
   __syncthreads();
 
@@ -205,7 +207,7 @@ void prefill_kernel(PrefillArgs a) {
   };
 
   f32x16 sc[RB][Gm::NKB];
-  vec8 pb[RB][Gm::NKB][2];
+  vec8 pb[RB][Gm::NKB][2];  // weights of the tile whose value update is next
   if (wnt > 0) {
     qk_tile_sw<T, D, BK, RB>(sc, lds_k0, qb, lane);
     weights(sc, 0, pb);
@@ -218,13 +220,16 @@ void prefill_kernel(PrefillArgs a) {
   // (The stage pointers are restrict-qualified: the tile a step streams in
   // and the tiles it reads never overlap.)
   auto fill = [&](int j, uint16_t* __restrict__ kfill, uint16_t* __restrict__ vfill) {
-    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, kbase, row_stride, k_lo + (j + 2) * BK, n_kv, dk, tid);
-    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vbase, row_stride, k_lo + (j + 1) * BK, n_kv, dv, tid);
+    if (j + 2 < ntiles) dma_tile<D, BK, NT, false>(kfill, ksrc, k_lo + (j + 2) * BK, dk, tid);
+    if (j + 1 < ntiles) dma_tile<D, BK, NT, true>(vfill, vsrc, k_lo + (j + 1) * BK, dv, tid);
   };
-  auto matrix = [&](int j, const uint16_t* __restrict__ kread, const uint16_t* __restrict__ vread) {
-    // matrix phase at raised issue priority: of the two waves sharing a
-    // SIMD, the one feeding the matrix core is served first and the other's
-    // vector work fills the gaps
+  // The scores and the value update run at raised issue priority: of the
+  // two waves sharing a SIMD, the one feeding the matrix core is served
+  // first and the other's vector work fills the gaps.  The step's tile
+  // loads are issued after them (their issue stalls while the load queue
+  // drains the other waves' tiles), then come the weights of tile j + 1.
+  auto step = [&](int j, uint16_t* kf, uint16_t* vf, const uint16_t* __restrict__ kread,
+                  const uint16_t* __restrict__ vread) {
     __builtin_amdgcn_s_setprio(3);
     if (j + 1 < wnt) {
       qk_tile_sw<T, D, BK, RB>(sc, kread, qb, lane);
@@ -234,17 +239,11 @@ void prefill_kernel(PrefillArgs a) {
       pv_tile_tr<T, D, BK, RB>(st, pb, vread, lane);
       lds_pipeline_pv<D / 32 * Gm::NKB * 2, RB>();
     }
+    fill(j, kf, vf);
     __builtin_amdgcn_s_setprio(0);
-  };
-  auto end_step = [&]() {
+    if (j + 1 < wnt) weights(sc, j + 1, pb);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this step's tiles are in LDS
     __syncthreads();
-  };
-  auto step = [&](int j, uint16_t* kf, uint16_t* vf, const uint16_t* kr, const uint16_t* vr) {
-    fill(j, kf, vf);
-    matrix(j, kr, vr);
-    if (j + 1 < wnt) weights(sc, j + 1, pb);
-    end_step();
   };
   for (int j = 0; j < ntiles; j += 2) {
     step(j, lds_k0, lds_v1, lds_k1, lds_v0);
@@ -313,7 +312,8 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
   const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g = hq / a.G;
   const int mrow = (hq / a.heads_per_mask) * (a.num_blocks + 1) + qblk;  // this head's mask
   const int f0 = a.full_indptr[mrow], n_full = a.full_indptr[mrow + 1] - f0;
@@ -332,6 +332,7 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   const int row_stride = a.Hkv * D;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
+  const DmaSrc ksrc = dma_src(kbase, row_stride, int(L)), vsrc = dma_src(vbase, row_stride, int(L));
   const DmaLane<D, BK, NT, false> dk(row_stride, tid);
   const DmaLane<D, BK, NT, true> dv(row_stride, tid);
 
@@ -342,8 +343,8 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
     const bool part = j >= n_full;
     const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
     if (part && tid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + tid];
-    dma_tile<D, BK, NT, false>(kd, kbase, row_stride, kblk * 64, int(L), dk, tid);
-    dma_tile<D, BK, NT, true>(vd, vbase, row_stride, kblk * 64, int(L), dv, tid);
+    dma_tile<D, BK, NT, false>(kd, ksrc, kblk * 64, dk, tid);
+    dma_tile<D, BK, NT, true>(vd, vsrc, kblk * 64, dv, tid);
   };
   if (ntiles > 0) fetch(0, lds_k, lds_v);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 is in LDS
