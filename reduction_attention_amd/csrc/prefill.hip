@@ -49,7 +49,10 @@ namespace rattn {
 #endif
 constexpr int kPrefillWaves = RATTN_PREFILL_WAVES;
 constexpr int kPrefillRB = RATTN_PREFILL_RB;
-constexpr int kPrefillBK = 64;
+#ifndef RATTN_PREFILL_BK
+#define RATTN_PREFILL_BK 64
+#endif
+constexpr int kPrefillBK = RATTN_PREFILL_BK;
 constexpr int kPrefillBQ = 32 * kPrefillRB * kPrefillWaves;  // query rows per workgroup
 
 // Workgroups are dealt to the eight XCDs round robin by linear index, and
