@@ -217,20 +217,33 @@ def bench_bsr(torch, ra, synth, args, timer, name="bsr_prefill_fp16"):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.L, w.Hq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    ms, _ = timer.run(lambda i: ra.attn_prefill_bsr(q, k, v, md, o=o, lse=lse, stream=stream),
-                      args.steps, args.warmup)
+    t0 = time.perf_counter()
+    plan = m.plan(w.D, w.Hq, w.B)
+    plan_s = time.perf_counter() - t0
+    times = {}
+    for kern in ("block", "row"):
+        ms, _ = timer.run(lambda i: ra.attn_prefill_bsr(q, k, v, md, o=o, lse=lse, stream=stream,
+                                                        kernel=kern), args.steps, args.warmup)
+        times[kern] = median(ms)
     # every mask serves Hq / num_masks heads
     hpm = w.Hq // m.num_masks
     n_ot = m.nnz_full + m.nnz_part
     flops_ot = 4 * w.D * 64 * 64 * n_ot * hpm * w.B
+    flops_rows = 4 * w.D * 16 * 16 * plan["row_blocks"] * hpm * w.B
     valid = int(inp["mask"].to(torch.int64).sum())
     flops_valid = 4 * w.D * valid * hpm * w.B
-    t = median(ms)
+    t = times[plan["kernel"]]  # what kernel="auto" runs
     return dict(workload=w.name, B=w.B, L=w.L, H=w.Hq, D=w.D, dtype="fp16", ms=t,
+                kernel=plan["kernel"], ms_block=times["block"], ms_row=times["row"],
                 num_masks=m.num_masks, nnz_full=m.nnz_full, nnz_part=m.nnz_part,
+                row_blocks=plan["row_blocks"], model_block_us=plan["block_cost"],
+                model_row_us=plan["row_cost"],
                 density=valid / (w.L * w.L * m.num_masks), flops_ot=flops_ot,
-                tflops_ot=flops_ot / t / 1e9, tflops_valid=flops_valid / t / 1e9,
-                frac_ot=flops_ot / t / 1e9 / MFMA_BF16_PEAK_TFS, host_encode_s=enc_s)
+                tflops_ot=flops_ot / times["block"] / 1e9,
+                tflops_rows=flops_rows / times["row"] / 1e9,
+                tflops_valid=flops_valid / t / 1e9,
+                frac_ot=flops_ot / times["block"] / 1e9 / MFMA_BF16_PEAK_TFS,
+                host_encode_s=enc_s, host_plan_s=plan_s)
 
 
 def bench_copy(torch, args, timer):
@@ -368,11 +381,12 @@ def main():
         also["append_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in ap.items()}
         b = bench_bsr(torch, ra, synth, args, timer)
-        log(f"bsr: {b['ms']*1e3:.1f} us, {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
+        log(f"bsr: {b['ms']*1e3:.1f} us ({b['kernel']}-wise; block {b['ms_block']*1e3:.1f}, "
+            f"row {b['ms_row']*1e3:.1f}), {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
         also["bsr_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}
         bh = bench_bsr(torch, ra, synth, args, timer, "bsr_heads_prefill_fp16")
-        log(f"bsr per-head-group masks, L {bh['L']}: {bh['ms']*1e3:.1f} us, "
-            f"{bh['tflops_ot']:.1f} TFLOP/s at OT granularity")
+        log(f"bsr per-head-group masks, L {bh['L']}: {bh['ms']*1e3:.1f} us ({bh['kernel']}-wise; "
+            f"block {bh['ms_block']*1e3:.1f}, row {bh['ms_row']*1e3:.1f})")
         also["bsr_heads_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                      for k, v in bh.items()}
         out["also"] = also

@@ -304,6 +304,45 @@ attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v
                                      float* lse, int B, int L, int Hq, int Hkv, int D, float scale,
                                      int dtype, void* hip_stream);
 
+/*
+ * Block-sparse prefill, row-wise kernel [ST "デュアルカーネル戦略"]: the same
+ * operation, arguments, layouts and errors as attn_prefill_bsr_heads.  Each
+ * wave takes 16 query rows of one head on its own (no workgroup barrier) and
+ * visits only the 16-key blocks of its outer-tile row in which those rows
+ * hold a valid element, so masks whose part tiles are sparse inside cost less
+ * than with the block-wise kernel, which computes every stored 64x64 tile.
+ */
+attn_status_t attn_prefill_bsr_rows(const void* q, const void* k, const void* v,
+                                    const attn_bsr_mask* mask, int num_masks, void* o,
+                                    float* lse, int B, int L, int Hq, int Hkv, int D, float scale,
+                                    int dtype, void* hip_stream);
+
+/*
+ * Kernel choice [ST "デュアルカーネル戦略", カーネル選択]: an analytical model
+ * over the mask's sparsity and the sequence length picks the row-wise or the
+ * block-wise kernel.  Inputs are the host arrays of the encoder (num_masks
+ * stacked masks of length L; part_bits may be null when no part tile is
+ * stored) and the call's shape (Hq query heads, B batch entries, head dim D
+ * 64 or 128).  The model counts the stored outer tiles (block-wise work) and
+ * the (16-row slab, 16-key block) pairs holding a valid element (row-wise
+ * work), and prices each kernel as a launch floor plus a per-unit time over
+ * all heads and batch entries, fitted on MI355X; plan->kernel is the
+ * cheaper.  Host only; fails with ATTN_EINVAL on null pointers, L not a
+ * positive multiple of 64, num_masks not dividing Hq, or indptr not
+ * monotone, and ATTN_EUNSUPPORTED on another D.
+ */
+enum { ATTN_BSR_BLOCKWISE = 0, ATTN_BSR_ROWWISE = 1 };
+typedef struct {
+  long long stored_ots; /* full + part outer tiles over all masks */
+  long long row_blocks; /* (16-row slab, 16-key block) pairs with a valid element */
+  double block_cost;    /* modelled time of the block-wise kernel, us */
+  double row_cost;      /* modelled time of the row-wise kernel, us */
+  int kernel;           /* ATTN_BSR_BLOCKWISE or ATTN_BSR_ROWWISE */
+} attn_bsr_plan;
+attn_status_t attn_bsr_plan_host(const int32_t* full_indptr, const int32_t* part_indptr,
+                                 const uint64_t* part_bits, int num_masks, int L, int Hq, int B,
+                                 int D, attn_bsr_plan* plan);
+
 /* ---- test exports ------------------------------------------------------ */
 
 /* Write, with the device code the decode kernels use, every split's key range

@@ -6,6 +6,7 @@ package is its thin Python binding; see ``api`` for the entry points.
 from .api import (  # noqa: F401
     BsrMask,
     attn_bsr_encode_host,
+    attn_bsr_plan,
     attn_debug_bsr_decode,
     attn_debug_split_ranges,
     attn_decode_choose_splits,

@@ -24,6 +24,15 @@ class AttnBsrMask(ctypes.Structure):
     ]
 
 
+class AttnBsrPlan(ctypes.Structure):
+    """Mirror of attn_bsr_plan."""
+    _fields_ = [
+        ("stored_ots", ctypes.c_longlong), ("row_blocks", ctypes.c_longlong),
+        ("block_cost", ctypes.c_double), ("row_cost", ctypes.c_double),
+        ("kernel", ctypes.c_int),
+    ]
+
+
 SIGNATURES = {
     "attn_status_string": (ctypes.c_char_p, [_i32]),
     "attn_last_error": (ctypes.c_char_p, []),
@@ -46,6 +55,10 @@ SIGNATURES = {
                                             _vp]),
     "attn_prefill_bsr_heads": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _i32, _vp,
                                       _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "attn_prefill_bsr_rows": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _i32, _vp,
+                                     _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "attn_bsr_plan_host": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                  ctypes.POINTER(AttnBsrPlan)]),
     "attn_prefill_bsr": (_i32, [_vp, _vp, _vp, ctypes.POINTER(AttnBsrMask), _vp, _vp, _i32, _i32,
                                 _i32, _i32, _i32, _f32, _i32, _vp]),
     "attn_debug_split_ranges": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp]),

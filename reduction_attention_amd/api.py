@@ -16,7 +16,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import ATTN_BF16, ATTN_F16, ATTN_F32, AttnBsrMask, check, load
+from ._lib import ATTN_BF16, ATTN_F16, ATTN_F32, AttnBsrMask, AttnBsrPlan, check, load
 
 _DT = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16, torch.float16: ATTN_F16}
 
@@ -207,9 +207,27 @@ class BsrMask:
 
     def to(self, device) -> "BsrMask":
         mv = lambda t: t.to(device).contiguous()  # noqa: E731
-        return BsrMask(self.seq_len, self.nnz_full, self.nnz_part, mv(self.full_indptr),
-                       mv(self.full_kblock), mv(self.part_indptr), mv(self.part_kblock),
-                       mv(self.part_bits), self.num_masks)
+        out = BsrMask(self.seq_len, self.nnz_full, self.nnz_part, mv(self.full_indptr),
+                      mv(self.full_kblock), mv(self.part_indptr), mv(self.part_kblock),
+                      mv(self.part_bits), self.num_masks)
+        out._host = self._host_mask()
+        return out
+
+    def _host_mask(self) -> "BsrMask":
+        if self.full_indptr.device.type == "cpu":
+            return self
+        host = getattr(self, "_host", None)
+        return host if host is not None else self.to("cpu")
+
+    def plan(self, D: int, Hq: int = None, B: int = 1) -> dict:
+        """The kernel selector's counts, modelled costs (us) and choice for head
+        dim D, Hq query heads (default: one per mask) and B batch entries."""
+        Hq = self.num_masks if Hq is None else Hq
+        cache = self.__dict__.setdefault("_plans", {})
+        key = (D, Hq, B)
+        if key not in cache:
+            cache[key] = attn_bsr_plan(self._host_mask(), D, Hq, B)
+        return cache[key]
 
     def struct(self) -> AttnBsrMask:
         return AttnBsrMask(self.seq_len, self.num_blocks, self.nnz_full, self.nnz_part,
@@ -257,11 +275,28 @@ def attn_bsr_encode_host(dense: torch.Tensor) -> BsrMask:
     return BsrMask(L, nf.value, np_.value, fi, fk, pi, pk, pb, M)
 
 
+def attn_bsr_plan(mask: BsrMask, D: int, Hq: int = None, B: int = 1) -> dict:
+    """Run the host-side kernel selector on a CPU-resident mask."""
+    Hq = mask.num_masks if Hq is None else Hq
+    plan = AttnBsrPlan()
+    check(load().attn_bsr_plan_host(_ptr(mask.full_indptr), _ptr(mask.part_indptr),
+                                    _ptr(mask.part_bits) if mask.nnz_part else None,
+                                    mask.num_masks, mask.seq_len, Hq, B, D, ctypes.byref(plan)),
+          "attn_bsr_plan_host")
+    return dict(stored_ots=plan.stored_ots, row_blocks=plan.row_blocks,
+                block_cost=plan.block_cost, row_cost=plan.row_cost,
+                kernel="row" if plan.kernel == 1 else "block")
+
+
 def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, stream=None,
-                     want_lse=True):
+                     want_lse=True, kernel="auto"):
     """Block-sparse prefill.  q [B,L,Hq,D]; k, v [B,L,Hkv,D]; mask on q's device.
 
-    A mask of M stacked masks applies mask h // (Hq // M) to query head h."""
+    A mask of M stacked masks applies mask h // (Hq // M) to query head h.
+    kernel: "block" (block-wise), "row" (row-wise) or "auto" (the selector's
+    choice for this mask and head dim)."""
+    if kernel not in ("auto", "block", "row"):
+        raise ValueError(f"kernel must be auto, block or row, not {kernel!r}")
     _dev(q, k, v, o, lse)
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
@@ -271,7 +306,14 @@ def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, strea
     if lse is None and want_lse:
         lse = torch.empty((B, L, Hq), dtype=torch.float32, device=q.device)
     ms = mask.struct()
-    if mask.num_masks == 1:
+    if kernel == "auto":
+        kernel = mask.plan(D, Hq, B)["kernel"]
+    if kernel == "row":
+        st = load().attn_prefill_bsr_rows(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(ms),
+                                          mask.num_masks, _ptr(o), _ptr(lse), B, L, Hq, Hkv, D,
+                                          scale, _dtype_code(q), _stream(stream))
+        check(st, "attn_prefill_bsr_rows")
+    elif mask.num_masks == 1:
         st = load().attn_prefill_bsr(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(ms), _ptr(o),
                                      _ptr(lse), B, L, Hq, Hkv, D, scale, _dtype_code(q),
                                      _stream(stream))

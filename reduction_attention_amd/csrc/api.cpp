@@ -416,10 +416,11 @@ static attn_status_t check_mask(const attn_bsr_mask* m, const char* who) {
   return ATTN_OK;
 }
 
-attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v,
-                                     const attn_bsr_mask* mask, int num_masks, void* o, float* lse,
-                                     int B, int L, int Hq, int Hkv, int D, float scale, int dtype,
-                                     void* hip_stream) {
+// Shared validation of the block-sparse prefill entry points; fills a.
+static attn_status_t bsr_args(const void* q, const void* k, const void* v,
+                              const attn_bsr_mask* mask, int num_masks, void* o, float* lse, int B,
+                              int L, int Hq, int Hkv, int D, float scale, int dtype,
+                              rattn::BsrArgs* a) {
   if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "prefill_bsr: null pointer");
   attn_status_t ms = check_mask(mask, "prefill_bsr");
   if (ms != ATTN_OK) return ms;
@@ -438,11 +439,83 @@ attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v
     return fail(ATTN_EINVAL, "prefill_bsr: q, k, v, o must be 16-byte aligned");
   if (mask->nnz_part && (reinterpret_cast<uintptr_t>(mask->part_bits) & 7u))
     return fail(ATTN_EINVAL, "prefill_bsr: part_bits must be 8-byte aligned");
-  rattn::BsrArgs a{q, k, v, mask->full_indptr, mask->full_kblock, mask->part_indptr,
-                   mask->part_kblock, mask->part_bits, o, lse, B, L, Hq, Hkv, D, Hq / Hkv,
-                   mask->num_blocks, scale * kLog2e, dtype, Hq / num_masks};
+  *a = rattn::BsrArgs{q, k, v, mask->full_indptr, mask->full_kblock, mask->part_indptr,
+                      mask->part_kblock, mask->part_bits, o, lse, B, L, Hq, Hkv, D, Hq / Hkv,
+                      mask->num_blocks, scale * kLog2e, dtype, Hq / num_masks};
+  return ATTN_OK;
+}
+
+attn_status_t attn_prefill_bsr_heads(const void* q, const void* k, const void* v,
+                                     const attn_bsr_mask* mask, int num_masks, void* o, float* lse,
+                                     int B, int L, int Hq, int Hkv, int D, float scale, int dtype,
+                                     void* hip_stream) {
+  rattn::BsrArgs a;
+  attn_status_t st = bsr_args(q, k, v, mask, num_masks, o, lse, B, L, Hq, Hkv, D, scale, dtype, &a);
+  if (st != ATTN_OK) return st;
   return hip_status(rattn::launch_prefill_bsr(a, static_cast<hipStream_t>(hip_stream)),
                     "prefill_bsr launch");
+}
+
+attn_status_t attn_prefill_bsr_rows(const void* q, const void* k, const void* v,
+                                    const attn_bsr_mask* mask, int num_masks, void* o, float* lse,
+                                    int B, int L, int Hq, int Hkv, int D, float scale, int dtype,
+                                    void* hip_stream) {
+  rattn::BsrArgs a;
+  attn_status_t st = bsr_args(q, k, v, mask, num_masks, o, lse, B, L, Hq, Hkv, D, scale, dtype, &a);
+  if (st != ATTN_OK) return st;
+  return hip_status(rattn::launch_prefill_bsr_rows(a, static_cast<hipStream_t>(hip_stream)),
+                    "prefill_bsr_rows launch");
+}
+
+// Modelled time of the two block-sparse kernels on MI355X, in us: a launch
+// floor plus a cost per unit of work summed over heads and batch entries
+// (per stored outer tile for the block-wise kernel, per (16-row slab,
+// 16-key block) for the row-wise one).  Fitted to a sweep of both kernels
+// over nine mask families at L 1024 and 4096, D 64 and 128 (fp16, 16
+// heads), where the model picks the faster kernel in every case.
+struct BsrCost { double b0, b1, r0, r1; };
+static BsrCost bsr_cost(int D) {
+  return D == 64 ? BsrCost{11.0, 2.18e-3, 8.0, 0.37e-3} : BsrCost{18.0, 4.7e-3, 10.0, 0.62e-3};
+}
+
+attn_status_t attn_bsr_plan_host(const int32_t* full_indptr, const int32_t* part_indptr,
+                                 const uint64_t* part_bits, int num_masks, int L, int Hq, int B,
+                                 int D, attn_bsr_plan* plan) {
+  if (!full_indptr || !part_indptr || !plan) return fail(ATTN_EINVAL, "bsr_plan: null pointer");
+  if (L <= 0 || L % 64) return fail(ATTN_EINVAL, "bsr_plan: L = %d is not a positive multiple of 64", L);
+  if (num_masks < 1 || Hq < 1 || B < 1 || Hq % num_masks)
+    return fail(ATTN_EINVAL, "bsr_plan: need num_masks >= 1 dividing Hq >= 1, B >= 1");
+  if (D != 64 && D != 128) return fail(ATTN_EUNSUPPORTED, "bsr_plan: D = %d (supported: 64, 128)", D);
+  const int nb = L / 64;
+  long long ots = 0, units = 0;
+  for (int m = 0; m < num_masks; ++m) {
+    const int32_t* fi = full_indptr + size_t(m) * (nb + 1);
+    const int32_t* pi = part_indptr + size_t(m) * (nb + 1);
+    for (int qb = 0; qb < nb; ++qb) {
+      const long long nf = fi[qb + 1] - fi[qb], np = pi[qb + 1] - pi[qb];
+      if (nf < 0 || np < 0) return fail(ATTN_EINVAL, "bsr_plan: indptr not monotone");
+      if (np && !part_bits) return fail(ATTN_EINVAL, "bsr_plan: null part_bits");
+      ots += nf + np;
+      units += 16 * nf;  // a full tile: 4 slabs x 4 key blocks
+      for (int p = pi[qb]; p < pi[qb + 1]; ++p) {
+        const uint64_t* wd = part_bits + size_t(p) * 64;
+        for (int slab = 0; slab < 4; ++slab)
+          for (int kb = 0; kb < 4; ++kb) {
+            const int r0 = 2 * slab * 8, r1 = (2 * slab + 1) * 8;
+            if (wd[r0 + 2 * kb] | wd[r0 + 2 * kb + 1] | wd[r1 + 2 * kb] | wd[r1 + 2 * kb + 1]) ++units;
+          }
+      }
+    }
+  }
+  // each mask serves Hq / num_masks heads of every batch entry
+  const double reps = double(Hq / num_masks) * B;
+  const BsrCost c = bsr_cost(D);
+  plan->stored_ots = ots;
+  plan->row_blocks = units;
+  plan->block_cost = c.b0 + c.b1 * double(ots) * reps;
+  plan->row_cost = c.r0 + c.r1 * double(units) * reps;
+  plan->kernel = plan->row_cost < plan->block_cost ? ATTN_BSR_ROWWISE : ATTN_BSR_BLOCKWISE;
+  return ok();
 }
 
 attn_status_t attn_prefill_bsr(const void* q, const void* k, const void* v,

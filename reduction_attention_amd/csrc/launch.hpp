@@ -91,6 +91,7 @@ hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 int prefill_rows_per_workgroup();  // query rows one prefill workgroup covers
 hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st);
+hipError_t launch_prefill_bsr_rows(const BsrArgs& a, hipStream_t st);
 hipError_t launch_bsr_decode(const int32_t* full_indptr, const int32_t* full_kblock,
                              const int32_t* part_indptr, const int32_t* part_kblock,
                              const uint64_t* part_bits, int num_blocks, uint8_t* dense,

@@ -304,3 +304,75 @@ def test_workload_mask_statistics(lib):
     density = mask.float().mean().item()
     assert 0.15 < density < 0.25
     assert bm.nnz_full + bm.nnz_part == 64 * 64  # every outer tile holds a global token
+
+
+# ---- block-sparse kernel selector --------------------------------------------
+
+def plan_by_definition(dense3):
+    """Stored outer tiles and (16-row slab, 16-key block) pairs with a valid
+    element, counted on the dense masks."""
+    M, L, _ = dense3.shape
+    b = dense3.bool()
+    ots = int(b.view(M, L // 64, 64, L // 64, 64).any(4).any(2).sum())
+    units = int(b.view(M, L // 16, 16, L // 16, 16).any(4).any(2).sum())
+    return ots, units
+
+
+@pytest.mark.parametrize("kind", ["sparse", "window", "random", "stacked", "empty"])
+def test_bsr_plan_counts(lib, kind):
+    import reduction_attention_amd as ra
+    L = 256
+    if kind == "sparse":
+        dense = synth.sparse_mask(L, synth.gen(71), window=64, block=64, globals_per_block=2,
+                                  random_blocks=1)
+    elif kind == "window":
+        dense = synth.window_mask(L, 40)
+    elif kind == "random":
+        dense = (torch.rand(L, L, generator=synth.gen(72)) < 0.02).to(torch.uint8)
+    elif kind == "stacked":
+        dense = torch.stack([synth.window_mask(L, 20), torch.ones(L, L, dtype=torch.uint8),
+                             (torch.rand(L, L, generator=synth.gen(73)) < 0.05).to(torch.uint8)])
+    else:
+        dense = torch.zeros(L, L, dtype=torch.uint8)
+    bm = ra.attn_bsr_encode_host(dense)
+    d3 = dense if dense.dim() == 3 else dense.unsqueeze(0)
+    ots, units = plan_by_definition(d3)
+    for D in (64, 128):
+        p = ra.attn_bsr_plan(bm, D, Hq=6, B=2)
+        assert p["stored_ots"] == ots and p["row_blocks"] == units
+        assert p["kernel"] == ("row" if p["row_cost"] < p["block_cost"] else "block")
+        assert p["block_cost"] >= 0 and p["row_cost"] >= 0
+
+
+def test_bsr_plan_prefers_rows_when_part_tiles_are_sparse(lib):
+    """Columns-only globals: every tile is stored, few of its 16-key blocks
+    hold valid elements -> row-wise; a dense causal mask -> block-wise
+    (16 heads, D 64)."""
+    import reduction_attention_amd as ra
+    L = 1024
+    cols = torch.zeros(L, L, dtype=torch.uint8)
+    cols[:, ::64] = 1
+    assert ra.attn_bsr_plan(ra.attn_bsr_encode_host(cols), 64, 16)["kernel"] == "row"
+    causal = torch.ones(L, L, dtype=torch.uint8).tril()
+    assert ra.attn_bsr_plan(ra.attn_bsr_encode_host(causal), 64, 16)["kernel"] == "block"
+
+
+def test_bsr_plan_validation(lib):
+    from reduction_attention_amd._lib import AttnBsrPlan
+    f = lib.attn_bsr_plan_host
+    ind = torch.zeros(5, dtype=torch.int32)
+    bad = torch.tensor([0, 2, 1, 1, 1], dtype=torch.int32)
+    plan = AttnBsrPlan()
+    p = ctypes.c_void_p(ind.data_ptr())
+    assert f(p, p, None, 1, 256, 4, 1, 64, ctypes.byref(plan)) == 0
+    assert plan.stored_ots == 0 and plan.row_blocks == 0
+    assert f(None, p, None, 1, 256, 4, 1, 64, ctypes.byref(plan)) == 1
+    assert f(p, p, None, 1, 250, 4, 1, 64, ctypes.byref(plan)) == 1
+    assert f(p, p, None, 0, 256, 4, 1, 64, ctypes.byref(plan)) == 1
+    assert f(p, p, None, 3, 256, 4, 1, 64, ctypes.byref(plan)) == 1  # 3 masks, 4 heads
+    assert f(p, p, None, 1, 256, 4, 0, 64, ctypes.byref(plan)) == 1
+    assert f(p, p, None, 1, 256, 4, 1, 80, ctypes.byref(plan)) == 2
+    assert f(ctypes.c_void_p(bad.data_ptr()), p, None, 1, 256, 4, 1, 64,
+             ctypes.byref(plan)) == 1
+    assert lib.attn_prefill_bsr_rows(P, P, P, None, 1, P, None, 1, 256, 2, 2, 64, 0.1, 2,
+                                     None) == 1

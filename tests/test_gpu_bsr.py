@@ -14,9 +14,9 @@ def ra():
     return reduction_attention_amd
 
 
-def bsr(q, k, v, dense):
+def bsr(q, k, v, dense, kernel="block"):
     m = ra().attn_bsr_encode_host(dense).to(DEV)
-    o, lse = ra().attn_prefill_bsr(q.to(DEV), k.to(DEV), v.to(DEV), m)
+    o, lse = ra().attn_prefill_bsr(q.to(DEV), k.to(DEV), v.to(DEV), m, kernel=kernel)
     torch.cuda.synchronize()
     return o, lse, m
 
@@ -188,3 +188,105 @@ def test_heads_workload_sampled():
         check(f"bsr heads 8192 sampled mask {mi}", o[0][t.to(DEV), h.to(DEV)], o_ref,
               lse[0][t.to(DEV), h.to(DEV)], lse_ref, torch.float16)
     assert bool(torch.isfinite(o).all())
+
+
+# ---- row-wise kernel -----------------------------------------------------------
+
+def small_mask(kind, L, seed):
+    if kind == "sparse":
+        return synth.sparse_mask(L, synth.gen(seed), window=96, block=64, globals_per_block=2,
+                                 random_blocks=1)
+    if kind == "window":
+        return synth.window_mask(L, 100)
+    if kind == "cols":  # columns-only globals plus a narrow window: sparse part tiles
+        d = synth.window_mask(L, 8)
+        d[:, ::64] = 1
+        d[:, 1::64] = 1
+        return d
+    if kind == "random":
+        d = (torch.rand(L, L, generator=synth.gen(seed)) < 0.05).to(torch.uint8)
+        d[70] = 0  # a query row with no valid key
+        d[:, 128:192] = 0
+        return d
+    return torch.ones(L, L, dtype=torch.uint8).tril()
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("kind", ["sparse", "window", "cols", "random", "causal"])
+def test_rows_small_masks(dtype, D, kind):
+    L, B, Hq, Hkv = 320, 2, 4, 2
+    dense = small_mask(kind, L, 81)
+    q, k, v = qkv(B, L, Hq, Hkv, D, dtype, 83 + D)
+    o_ref, lse_ref = oracle_bsr(q, k, v, dense, 1 / D ** 0.5)
+    o, lse, _ = bsr(q, k, v, dense, kernel="row")
+    check(f"bsr rows {dtype} D={D} {kind}", o, o_ref, lse, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rows_per_head_masks(D):
+    L, B, Hq, Hkv = 256, 1, 4, 4
+    dense3 = torch.stack([small_mask(kd, L, 90 + n)
+                          for n, kd in enumerate(["cols", "random", "window", "sparse"])])
+    q, k, v = qkv(B, L, Hq, Hkv, D, torch.bfloat16, 95)
+    o_ref, lse_ref = oracle_bsr_heads(q, k, v, dense3, 1 / D ** 0.5)
+    o, lse, m = bsr(q, k, v, dense3, kernel="row")
+    check(f"bsr rows heads D={D}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+def test_rows_unread_blocks_never_read():
+    """NaN in K/V of a 16-key block in which no query row holds a valid
+    element (keys 48..63, inside stored outer tiles) leaves the row-wise
+    output bit-identical: the kernel never loads such a block."""
+    L, D = 256, 64
+    dense = small_mask("cols", L, 0)
+    dense[:, 48:64] = 0
+    q, k, v = qkv(1, L, 2, 2, D, torch.float16, 96)
+    o1, l1, m = bsr(q, k, v, dense, kernel="row")
+    assert m.nnz_full + m.nnz_part == 16  # every outer tile stays stored
+    k2, v2 = k.clone(), v.clone()
+    k2[:, 48:64] = float("nan")
+    v2[:, 48:64] = float("nan")
+    o2, l2, _ = bsr(q, k2, v2, dense, kernel="row")
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", ["bsr_prefill_fp16", "bsr_heads_prefill_fp16"])
+def test_rows_workload_sampled(name):
+    """The sparse workloads through the row-wise kernel, sampled rows vs the oracle."""
+    w = synth.workload(name)
+    inp = w.make(DEV)
+    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"], kernel="row")
+    g = synth.gen(79)
+    M = m.num_masks
+    hpm = w.Hq // M
+    q, k, v = (inp[x][0].cpu() for x in ("q", "k", "v"))
+    masks = inp["mask"] if M > 1 else inp["mask"].unsqueeze(0)
+    for mi in range(M):
+        n = 2000 // M
+        t = torch.randint(0, w.L, (n,), generator=g)
+        hl = torch.randint(0, hpm, (n,), generator=g)
+        hs = slice(mi * hpm, (mi + 1) * hpm)
+        o_ref, lse_ref = oracle.attention(q[:, hs], k[:, hs], v[:, hs], [0, w.L], [0, w.L],
+                                          w.scale, oracle.MASK_DENSE, masks[mi],
+                                          rows=torch.stack([t, hl], 1))
+        h = hl + mi * hpm
+        check(f"bsr rows {name} sampled mask {mi}", o[0][t.to(DEV), h.to(DEV)], o_ref,
+              lse[0][t.to(DEV), h.to(DEV)], lse_ref, torch.float16)
+    assert bool(torch.isfinite(o).all())
+
+
+def test_auto_kernel_matches_choice():
+    """kernel="auto" runs the selector's choice: bit-identical to that kernel."""
+    L, D = 512, 64
+    dense = small_mask("cols", L, 0)
+    q, k, v = qkv(1, L, 2, 2, D, torch.float16, 97)
+    m = ra().attn_bsr_encode_host(dense)
+    choice = m.plan(D, 2, 1)["kernel"]
+    md = m.to(DEV)
+    assert md.plan(D, 2, 1)["kernel"] == choice
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    oa, la = ra().attn_prefill_bsr(qd, kd, vd, md, kernel="auto")
+    oc, lc = ra().attn_prefill_bsr(qd, kd, vd, md, kernel=choice)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, oc) and torch.equal(la, lc)
