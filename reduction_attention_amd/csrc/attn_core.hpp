@@ -521,11 +521,14 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const DmaSrc& src, int k
   // touches, and the caller waits (vmcnt) before publishing it.
   if (key0 + BK <= src.n_keys) {
     const uint64_t addr = base + uint64_t(uint32_t(row0)) * uint32_t(src.row_bytes);
-    const i32x4 rsv = {int(uint32_t(addr)), int(uint32_t(addr >> 32) & 0xffffu), 0x7fffffff,
-                       0x00020000};
+    // (readfirstlane: the operands must sit in scalar registers; free when
+    // the compiler already keeps them there)
+    const i32x4 rsv = {__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
+                       __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
+                       0x7fffffff, 0x00020000};
 #pragma unroll
     for (int x = 0; x < DL::PER; ++x) {
-      const int soff = S::RPI * DL::W * x * src.row_bytes;
+      const int soff = __builtin_amdgcn_readfirstlane(S::RPI * DL::W * x * src.row_bytes);
       __asm__ volatile(
           "s_mov_b32 m0, %0\n\t"
           "buffer_load_dwordx4 %1, %2, %3 offen lds"
@@ -538,8 +541,12 @@ __device__ __forceinline__ void dma_tile(uint16_t* dst, const DmaSrc& src, int k
     for (int x = 0; x < DL::PER; ++x) {
       const int rowx = row0 + S::RPI * DL::W * x;  // the instruction's first row
       const uint64_t addr = base + uint64_t(uint32_t(rowx)) * uint32_t(src.row_bytes);
-      const i32x4 rsv = {int(uint32_t(addr)), int(uint32_t(addr >> 32) & 0xffffu),
-                         sclamp_rows<S::RPI>(src.n_keys - rowx) * src.row_bytes, 0x00020000};
+      const i32x4 rsv = {__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
+                         __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
+                         __builtin_amdgcn_readfirstlane(
+                             sclamp_rows<S::RPI>(__builtin_amdgcn_readfirstlane(src.n_keys - rowx)) *
+                             src.row_bytes),
+                         0x00020000};
       __asm__ volatile(
           "s_mov_b32 m0, %0\n\t"
           "buffer_load_dwordx4 %1, %2, 0 offen lds"
