@@ -51,6 +51,11 @@ def bind(path: str):
                                      ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                      ctypes.c_int, vp, ctypes.c_int64, i64p, ctypes.c_int64,
                                      dp, dp, ctypes.c_int]
+    lib.oracle_attention_dv.restype = ctypes.c_int
+    lib.oracle_attention_dv.argtypes = [vp, vp, vp, ctypes.c_int, i64p, i64p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_double, ctypes.c_int, vp, ctypes.c_int64, i64p,
+                                        ctypes.c_int64, dp, dp, ctypes.c_int]
     lib.oracle_split_ranges.restype = ctypes.c_int
     lib.oracle_split_ranges.argtypes = [i64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int, i64p]
     lib.oracle_chunk_len.restype = ctypes.c_int64
@@ -127,19 +132,21 @@ def attention(q, k, v, qo_indptr, kv_indptr, scale, mask_kind=MASK_NONE, mask=No
               rows=None, nthreads=0):
     """Masked softmax attention by its definition, fp64, two passes.
 
-    q: [total_q, Hq, D]; k, v: [total_kv, Hkv, D]; request b owns query tokens
+    q: [total_q, Hq, D]; k: [total_kv, Hkv, D]; v: [total_kv, Hkv, Dv] (Dv = D,
+    or MLA's latent width); request b owns query tokens
     qo_indptr[b]:qo_indptr[b+1] and keys kv_indptr[b]:kv_indptr[b+1].
     mask_kind: MASK_NONE, MASK_CAUSAL (j <= i + n_kv - n_q) or MASK_DENSE with
     ``mask`` a uint8 [n_q, n_kv] (1 = attend) shared by every request and head.
     rows: optional int64 [n, 2] of (packed query token, head); then returns
-    o [n, D] and lse [n] for those pairs only.  Otherwise o [total_q, Hq, D]
+    o [n, Dv] and lse [n] for those pairs only.  Otherwise o [total_q, Hq, Dv]
     and lse [total_q, Hq].  Returns float64 CPU tensors.
     """
     q, k, v = _host(q), _host(k), _host(v)
     dt = _common_dtype(q, k, v)
     total_q, Hq, D = q.shape
     _, Hkv, Dk = k.shape
-    assert Dk == D and v.shape == k.shape
+    Dv = v.shape[2]  # the value head dim may differ (MLA: the latent part only)
+    assert Dk == D and v.shape[:2] == k.shape[:2]
     qo = _indptr(qo_indptr)
     kv = _indptr(kv_indptr)
     B = qo.numel() - 1
@@ -152,17 +159,17 @@ def attention(q, k, v, qo_indptr, kv_indptr, scale, mask_kind=MASK_NONE, mask=No
     if rows is not None:
         rows = _host(torch.as_tensor(rows)).to(torch.int64).reshape(-1, 2).contiguous()
         n = rows.shape[0]
-        o = torch.empty((n, D), dtype=torch.float64)
+        o = torch.empty((n, Dv), dtype=torch.float64)
         lse = torch.empty((n,), dtype=torch.float64)
         r_ptr = _ptr(rows)
     else:
         n = 0
-        o = torch.empty((total_q, Hq, D), dtype=torch.float64)
+        o = torch.empty((total_q, Hq, Dv), dtype=torch.float64)
         lse = torch.empty((total_q, Hq), dtype=torch.float64)
         r_ptr = None
-    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(qo), _ptr(kv), B, Hq, Hkv, D,
-                                  float(scale), int(mask_kind), m_ptr, ld, r_ptr, n, _ptr(o),
-                                  _ptr(lse), int(nthreads))
+    rc = _load().oracle_attention_dv(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(qo), _ptr(kv), B, Hq,
+                                     Hkv, D, Dv, float(scale), int(mask_kind), m_ptr, ld, r_ptr,
+                                     n, _ptr(o), _ptr(lse), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
     return o, lse

@@ -105,11 +105,14 @@ static int key_valid(int mask_kind, const uint8_t* mask, int64_t mask_ld,
   return mask[i * mask_ld + j] != 0;
 }
 
-/* One (query row, head): two passes over the valid keys in fp64.
+/* One (query row, head): two passes over the valid keys in fp64.  Queries
+ * and keys have D elements per head, values Dv (Dv = D for ordinary
+ * attention; MLA's absorbed form scores over the latent plus the decoupled
+ * rotary dims and averages the latent part only).
  * scores[] is caller scratch of at least n_kv doubles. */
 static void attend_row(const void* q, const void* k, const void* v, int dtype,
                        int64_t tq, int h, int64_t kv0, int64_t n_q, int64_t n_kv,
-                       int64_t i_local, int Hq, int Hkv, int D, double scale,
+                       int64_t i_local, int Hq, int Hkv, int D, int Dv, double scale,
                        int mask_kind, const uint8_t* mask, int64_t mask_ld,
                        double* scores, double* o_row, double* lse_out) {
   const int G = Hq / Hkv;
@@ -130,7 +133,7 @@ static void attend_row(const void* q, const void* k, const void* v, int dtype,
     if (scores[j] > m) m = scores[j];
     ++count;
   }
-  for (int d = 0; d < D; ++d) o_row[d] = 0.0;
+  for (int d = 0; d < Dv; ++d) o_row[d] = 0.0;
   if (count == 0) { /* no valid key: O = 0, LSE = -inf */
     *lse_out = -INFINITY;
     return;
@@ -140,10 +143,10 @@ static void attend_row(const void* q, const void* k, const void* v, int dtype,
     if (!key_valid(mask_kind, mask, mask_ld, i_local, j, n_q, n_kv)) continue;
     const double p = exp(scores[j] - m);
     l += p;
-    const int64_t v_off = ((kv0 + j) * Hkv + g) * (int64_t)D;
-    for (int d = 0; d < D; ++d) o_row[d] += p * load_elem(v, dtype, v_off + d);
+    const int64_t v_off = ((kv0 + j) * Hkv + g) * (int64_t)Dv;
+    for (int d = 0; d < Dv; ++d) o_row[d] += p * load_elem(v, dtype, v_off + d);
   }
-  for (int d = 0; d < D; ++d) o_row[d] /= l;
+  for (int d = 0; d < Dv; ++d) o_row[d] /= l;
   *lse_out = m + log(l);
 }
 
@@ -169,13 +172,13 @@ static int owner_of(const int64_t* indptr, int B, int64_t t) {
  *   and lse nrows values, in list order.
  * Returns 0, or -1 on bad arguments.
  */
-int oracle_attention(const void* q, const void* k, const void* v, int dtype,
-                     const int64_t* qo_indptr, const int64_t* kv_indptr, int B,
-                     int Hq, int Hkv, int D, double scale, int mask_kind,
-                     const uint8_t* mask, int64_t mask_ld,
-                     const int64_t* rows, int64_t nrows, double* o, double* lse,
-                     int nthreads) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv) return -1;
+int oracle_attention_dv(const void* q, const void* k, const void* v, int dtype,
+                        const int64_t* qo_indptr, const int64_t* kv_indptr, int B,
+                        int Hq, int Hkv, int D, int Dv, double scale, int mask_kind,
+                        const uint8_t* mask, int64_t mask_ld,
+                        const int64_t* rows, int64_t nrows, double* o, double* lse,
+                        int nthreads) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Dv <= 0 || Hq % Hkv) return -1;
   if (mask_kind == OR_MASK_DENSE && !mask) return -1;
   int64_t max_kv = 0;
   for (int b = 0; b < B; ++b) {
@@ -206,13 +209,24 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
         const int64_t n_kv = kv_indptr[b + 1] - kv_indptr[b];
         const int64_t out = rows ? p : tq * Hq + h;
         attend_row(q, k, v, dtype, tq, h, kv_indptr[b], n_q, n_kv,
-                   tq - qo_indptr[b], Hq, Hkv, D, scale, mask_kind, mask,
-                   mask_ld, scores, o + out * D, lse + out);
+                   tq - qo_indptr[b], Hq, Hkv, D, Dv, scale, mask_kind, mask,
+                   mask_ld, scores, o + out * Dv, lse + out);
       }
       free(scores);
     }
   }
   return err ? -1 : 0;
+}
+
+/* Ordinary attention: values have the keys' head dim. */
+int oracle_attention(const void* q, const void* k, const void* v, int dtype,
+                     const int64_t* qo_indptr, const int64_t* kv_indptr, int B,
+                     int Hq, int Hkv, int D, double scale, int mask_kind,
+                     const uint8_t* mask, int64_t mask_ld,
+                     const int64_t* rows, int64_t nrows, double* o, double* lse,
+                     int nthreads) {
+  return oracle_attention_dv(q, k, v, dtype, qo_indptr, kv_indptr, B, Hq, Hkv, D, D, scale,
+                             mask_kind, mask, mask_ld, rows, nrows, o, lse, nthreads);
 }
 
 /* ---- the Split operator: split ranges, partials and their merge -------- */
@@ -328,7 +342,7 @@ int oracle_split_decode(const void* q, const void* k, const void* v, int dtype,
          * keys [kv_indptr[b] + lo, kv_indptr[b] + hi), no mask. */
         double lse_i;
         attend_row(q, k, v, dtype, b, h, kv_indptr[b] + rg[0], 1, rg[1] - rg[0], 0,
-                   Hq, Hkv, D, scale, OR_MASK_NONE, NULL, 0, scores, op, &lse_i);
+                   Hq, Hkv, D, D, scale, OR_MASK_NONE, NULL, 0, scores, op, &lse_i);
         /* Recover (m, l) of the partial from its own scores: the two-pass
          * max and sum of exp(score - max). */
         double m = -INFINITY;

@@ -331,3 +331,53 @@ def test_merge_properties():
     o6, lse6 = oracle.merge(op[:2], mp[:2], lp[:2])
     expect = torch.logaddexp(mp[0] + lp[0].log(), mp[1] + lp[1].log())
     assert torch.allclose(lse6, expect, atol=1e-13)
+
+
+# ---- values narrower than keys (MLA's absorbed form) -----------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_value_width_differs_matches_sdpa(causal):
+    """Keys/queries of D elements, values of Dv: fp64 torch SDPA takes the
+    value width from V, so it pins the separate value head dim."""
+    lens_q, lens_k, D, Dv = [2, 5], [6, 5], 12, 5
+    qo, kv = synth.indptr(lens_q), synth.indptr(lens_k)
+    q = rand((sum(lens_q), 4, D), 31)
+    k = rand((sum(lens_k), 2, D), 32)
+    v = rand((sum(lens_k), 2, Dv), 33)
+    mk = oracle.MASK_CAUSAL if causal else oracle.MASK_NONE
+    o, lse = oracle.attention(q, k, v, qo, kv, 0.45, mk)
+    o_ref, lse_ref = sdpa_reference(q, k, v, qo, kv, 0.45, mk)
+    assert o.shape == (sum(lens_q), 4, Dv)
+    assert torch.allclose(o, o_ref, atol=1e-12, rtol=0)
+    assert torch.allclose(lse, lse_ref, atol=1e-12, rtol=0)
+
+
+def test_mla_absorbed_decode_by_loops():
+    """MLA decode in its absorbed form, written out with plain loops: every
+    head scores the whole cache row (latent + rotary part), the output
+    averages the latent part of the rows."""
+    H, T, Dc, Dr, scale = 3, 7, 6, 2, 0.37
+    q = rand((1, H, Dc + Dr), 34)
+    cache = rand((T, 1, Dc + Dr), 35)
+    o, lse = oracle.attention(q, cache, cache[:, :, :Dc].contiguous(), [0, 1], [0, T], scale)
+    for h in range(H):
+        s = [scale * sum(float(q[0, h, d]) * float(cache[t, 0, d]) for d in range(Dc + Dr))
+             for t in range(T)]
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = sum(w)
+        for d in range(Dc):
+            want = sum(w[t] * float(cache[t, 0, d]) for t in range(T)) / z
+            assert abs(float(o[0, h, d]) - want) < 1e-13
+        assert abs(float(lse[0, h]) - (m + math.log(z))) < 1e-13
+
+
+def test_constant_keys_mean_of_narrow_values():
+    L, Hq, D, Dv = 7, 2, 9, 4
+    q = rand((1, Hq, D), 36)
+    k = rand((1, 1, D), 37).expand(L, 1, D).contiguous()
+    v = rand((L, 1, Dv), 38)
+    o, lse = oracle.attention(q, k, v, [0, 1], [0, L], 0.6)
+    for h in range(Hq):
+        assert torch.allclose(o[0, h], v[:, 0].mean(0), atol=1e-13)
+        assert abs(float(lse[0, h]) - (0.6 * float((q[0, h] * k[0, 0]).sum()) + math.log(L))) < 1e-12
