@@ -67,6 +67,18 @@ def bind(path: str):
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         ctypes.c_int64, ctypes.c_double, ctypes.c_int,
                                         dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_split_decode_ranges.restype = ctypes.c_int
+    lib.oracle_split_decode_ranges.argtypes = [vp, vp, vp, ctypes.c_int, i64p, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int64, ctypes.c_double, ctypes.c_int,
+                                               i64p, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_flat_piece_len.restype = ctypes.c_int64
+    lib.oracle_flat_piece_len.argtypes = [ctypes.c_int64, ctypes.c_int]
+    lib.oracle_flat_max_splits.restype = ctypes.c_int
+    lib.oracle_flat_max_splits.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_flat_ranges.restype = ctypes.c_int
+    lib.oracle_flat_ranges.argtypes = [i64p, ctypes.c_int, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_int, i64p]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_version.restype = ctypes.c_char_p
     return lib
@@ -190,6 +202,34 @@ def split_ranges(kv_indptr, max_kv_len: int, s: int) -> torch.Tensor:
     return out
 
 
+def flat_piece_len(total_kv: int, P: int) -> int:
+    """Flat plan: c = ceil(total_kv / P) packed key rows per piece."""
+    return int(_load().oracle_flat_piece_len(int(total_kv), int(P)))
+
+
+def flat_max_splits(total_kv: int, max_kv_len: int, P: int) -> int:
+    """Flat plan: most pieces one request of at most max_kv_len keys overlaps."""
+    return int(_load().oracle_flat_max_splits(int(total_kv), int(max_kv_len), int(P)))
+
+
+def flat_ranges(kv_indptr, total_kv: int, P: int, s: int = 0) -> torch.Tensor:
+    """Flat plan: [B, s, 2] int64 key-offset ranges per split, -1 if unused.
+
+    The packed key rows [0, total_kv) are cut into P pieces of
+    ceil(total_kv / P) rows; split i of request b is the request's
+    intersection with the i-th piece it overlaps.  s defaults to
+    flat_max_splits(total_kv, max length, P)."""
+    kv = _indptr(kv_indptr)
+    B = kv.numel() - 1
+    if not s:
+        n = (kv[1:] - kv[:-1]).max().item() if B > 0 else 0
+        s = flat_max_splits(total_kv, n, P)
+    out = torch.empty((B, s, 2), dtype=torch.int64)
+    if _load().oracle_flat_ranges(_ptr(kv), B, int(total_kv), int(P), int(s), _ptr(out)) != 0:
+        raise ValueError("oracle_flat_ranges rejected its arguments")
+    return out
+
+
 def merge(o_part, m_part, l_part):
     """LSE-weighted merge of s partials.  o_part [s, rows, D], m/l [s, rows]."""
     o_part = _host(o_part).to(torch.float64).contiguous()
@@ -203,11 +243,13 @@ def merge(o_part, m_part, l_part):
     return o, lse
 
 
-def split_decode(q, k, v, kv_indptr, max_kv_len, scale, s, nthreads=0):
+def split_decode(q, k, v, kv_indptr, max_kv_len, scale, s, nthreads=0, ranges=None):
     """Split-KV decode by definition: per-split fp64 attention, then merge.
 
     q [B, Hq, D]; k, v [total_kv, Hkv, D].  Returns (o [B,Hq,D], lse [B,Hq],
     o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) as float64.
+    The splits are the chunk plan's (split_ranges) unless ``ranges`` [B, s, 2]
+    gives them (e.g. flat_ranges); s is then ranges.shape[1].
     """
     q, k, v = _host(q), _host(k), _host(v)
     dt = _common_dtype(q, k, v)
@@ -216,14 +258,24 @@ def split_decode(q, k, v, kv_indptr, max_kv_len, scale, s, nthreads=0):
     kv = _indptr(kv_indptr)
     assert kv.numel() == B + 1
     rows = B * Hq
+    if ranges is not None:
+        s = int(torch.as_tensor(ranges).shape[1])
     o = torch.empty((B, Hq, D), dtype=torch.float64)
     lse = torch.empty((B, Hq), dtype=torch.float64)
     op = torch.empty((s, rows, D), dtype=torch.float64)
     mp = torch.empty((s, rows), dtype=torch.float64)
     lp = torch.empty((s, rows), dtype=torch.float64)
-    rc = _load().oracle_split_decode(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv), B, Hq, Hkv, D,
-                                     int(max_kv_len), float(scale), int(s), _ptr(o), _ptr(lse),
-                                     _ptr(op), _ptr(mp), _ptr(lp), int(nthreads))
+    if ranges is None:
+        rc = _load().oracle_split_decode(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv), B, Hq, Hkv, D,
+                                         int(max_kv_len), float(scale), int(s), _ptr(o),
+                                         _ptr(lse), _ptr(op), _ptr(mp), _ptr(lp), int(nthreads))
+    else:
+        rg = torch.as_tensor(ranges).to(torch.int64).contiguous()
+        assert rg.shape == (B, s, 2)
+        rc = _load().oracle_split_decode_ranges(_ptr(q), _ptr(k), _ptr(v), dt, _ptr(kv), B, Hq,
+                                                Hkv, D, int(max_kv_len), float(scale), int(s),
+                                                _ptr(rg), _ptr(o), _ptr(lse), _ptr(op), _ptr(mp),
+                                                _ptr(lp), int(nthreads))
     if rc != 0:
         raise ValueError("oracle_split_decode rejected its arguments")
     return o, lse, op, mp, lp

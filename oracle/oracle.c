@@ -33,6 +33,10 @@
  *   - Split ranges: c = ceil(max_kv_len / s); request b uses ceil(n_b / c)
  *     non-empty chunks of c keys; the merge of partials is the
  *     log-sum-exp-weighted average (the only exact recombination).
+ *   - Flat split ranges (the Split operator applied to the packed key
+ *     array as one reduction dimension): P pieces of c = ceil(total_kv / P)
+ *     consecutive key rows; split i of request b is its intersection with
+ *     the i-th piece it touches.
  *
  * Inputs arrive as raw element arrays of type f64, f32, bf16 or f16 and are
  * widened to double exactly, element by element.  Every accumulation is in
@@ -261,6 +265,50 @@ int oracle_split_ranges(const int64_t* kv_indptr, int B, int64_t max_kv_len,
   return 0;
 }
 
+/* Flat split plan.  The packed key rows [0, total_kv) are cut into P
+ * pieces of c = ceil(total_kv / P) rows, piece p = [p*c, (p+1)*c).  Request
+ * b (rows [kv_indptr[b], kv_indptr[b+1])) is split where the piece
+ * boundaries fall inside it: its split i is the request's intersection
+ * with the i-th piece it overlaps, written as key offsets within the
+ * request.  Empty requests have no split. */
+int64_t oracle_flat_piece_len(int64_t total_kv, int P) {
+  if (P <= 0 || total_kv < 0) return -1;
+  return total_kv > 0 ? (total_kv + P - 1) / P : 0;
+}
+
+/* Most splits one request of at most max_kv_len keys can have: it overlaps
+ * ceil((n - 1) / c) + 1 pieces at worst, and never more than P. */
+int oracle_flat_max_splits(int64_t total_kv, int64_t max_kv_len, int P) {
+  const int64_t c = oracle_flat_piece_len(total_kv, P);
+  if (c < 0) return -1;
+  if (c == 0 || max_kv_len <= 0) return 1;
+  int64_t s = (max_kv_len - 1 + c - 1) / c + 1;
+  return (int)(s < P ? s : P);
+}
+
+/* ranges[(b*s + i)*2 + {0,1}] as in oracle_split_ranges, for the flat plan
+ * with s slots per request (fails if a request needs more). */
+int oracle_flat_ranges(const int64_t* kv_indptr, int B, int64_t total_kv, int P, int s,
+                       int64_t* ranges) {
+  const int64_t c = oracle_flat_piece_len(total_kv, P);
+  if (c < 0 || s <= 0) return -1;
+  for (int64_t e = 0; e < (int64_t)B * s * 2; ++e) ranges[e] = -1;
+  for (int b = 0; b < B; ++b) {
+    const int64_t r0 = kv_indptr[b], r1 = kv_indptr[b + 1];
+    if (r1 < r0 || r0 < 0 || r1 > total_kv) return -1;
+    int i = 0;
+    for (int64_t pos = r0; pos < r1; ++i) {
+      const int64_t piece_end = (pos / c + 1) * c;  /* end of the piece holding pos */
+      const int64_t end = piece_end < r1 ? piece_end : r1;
+      if (i >= s) return -1;
+      ranges[((int64_t)b * s + i) * 2] = pos - r0;
+      ranges[((int64_t)b * s + i) * 2 + 1] = end - r0;
+      pos = end;
+    }
+  }
+  return 0;
+}
+
 /*
  * Merge s partial results of one row.  Partial i is a normalised attention
  * output o_i over its key subset with max score m_i and sum
@@ -307,20 +355,47 @@ int oracle_merge(const double* o_part, const double* m_part, const double* l_par
  * o_part [s, B*Hq, D], m_part / l_part [s, B*Hq] (any may be NULL except o
  * and lse).
  */
+int oracle_split_decode_ranges(const void* q, const void* k, const void* v, int dtype,
+                               const int64_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                               int64_t max_kv_len, double scale, int s,
+                               const int64_t* ranges_in, double* o, double* lse,
+                               double* o_part_out, double* m_part_out, double* l_part_out,
+                               int nthreads);
+
 int oracle_split_decode(const void* q, const void* k, const void* v, int dtype,
                         const int64_t* kv_indptr, int B, int Hq, int Hkv, int D,
                         int64_t max_kv_len, double scale, int s, double* o,
                         double* lse, double* o_part_out, double* m_part_out,
                         double* l_part_out, int nthreads) {
+  if (B <= 0 || s <= 0) return -1;
+  int64_t* ranges = (int64_t*)malloc(sizeof(int64_t) * 2 * (size_t)B * s);
+  int rc = -1;
+  if (ranges && !oracle_split_ranges(kv_indptr, B, max_kv_len, s, ranges))
+    rc = oracle_split_decode_ranges(q, k, v, dtype, kv_indptr, B, Hq, Hkv, D, max_kv_len, scale,
+                                    s, ranges, o, lse, o_part_out, m_part_out, l_part_out,
+                                    nthreads);
+  free(ranges);
+  return rc;
+}
+
+/* The same with the split ranges given ([B, s, 2] key offsets within each
+ * request, -1 for unused slots; any plan, e.g. oracle_flat_ranges). */
+int oracle_split_decode_ranges(const void* q, const void* k, const void* v, int dtype,
+                               const int64_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                               int64_t max_kv_len, double scale, int s,
+                               const int64_t* ranges_in, double* o, double* lse,
+                               double* o_part_out, double* m_part_out, double* l_part_out,
+                               int nthreads) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv || s <= 0) return -1;
   const int64_t rows = (int64_t)B * Hq;
-  int64_t* ranges = (int64_t*)malloc(sizeof(int64_t) * 2 * (size_t)B * s);
+  const int64_t* ranges = ranges_in;
   double* o_part = (double*)calloc((size_t)(s * rows * D), sizeof(double));
   double* m_part = (double*)malloc(sizeof(double) * (size_t)(s * rows));
   double* l_part = (double*)calloc((size_t)(s * rows), sizeof(double));
   int rc = -1;
-  if (!ranges || !o_part || !m_part || !l_part) goto done;
-  if (oracle_split_ranges(kv_indptr, B, max_kv_len, s, ranges)) goto done;
+  if (!o_part || !m_part || !l_part) goto done;
+  for (int64_t e = 0; e < (int64_t)B * s; ++e)
+    if (ranges[2 * e] >= 0 && (ranges[2 * e + 1] - ranges[2 * e] > max_kv_len)) goto done;
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -360,7 +435,6 @@ int oracle_split_decode(const void* q, const void* k, const void* v, int dtype,
   if (m_part_out) memcpy(m_part_out, m_part, sizeof(double) * (size_t)(s * rows));
   if (l_part_out) memcpy(l_part_out, l_part, sizeof(double) * (size_t)(s * rows));
 done:
-  free(ranges);
   free(o_part);
   free(m_part);
   free(l_part);

@@ -30,6 +30,10 @@ MUTANTS = {
     "f16_exponent_bias": ("mag = ldexp((double)(f + 1024), e - 25);",
                           "mag = ldexp((double)(f + 1024), e - 24);"),
     "empty_row_lse": ("*lse_out = -INFINITY;\n    return;", "*lse_out = 0.0;\n    return;"),
+    "flat_piece_end": ("const int64_t piece_end = (pos / c + 1) * c;",
+                       "const int64_t piece_end = pos + c;"),
+    "flat_bound_loose": ("int64_t s = (max_kv_len - 1 + c - 1) / c + 1;",
+                         "int64_t s = (max_kv_len + c - 1) / c;"),
     "value_index_dropped": ("o_row[d] += p * load_elem(v, dtype, v_off + d);",
                             "o_row[d] += p * load_elem(v, dtype, v_off);"),
 }

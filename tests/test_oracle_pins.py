@@ -286,6 +286,87 @@ def test_split_ranges_partition_each_request(lengths, s):
         assert all(x == [-1, -1] for x in r[b].tolist()[len(used):])
 
 
+def flat_ranges_brute(lengths, total, P, s):
+    """The flat plan by enumeration: walk every packed key row, tag it with
+    (request, piece) and cut a request's rows wherever the tag changes."""
+    c = -(-total // P) if total else 0
+    owner = {}
+    pos = 0
+    for b, n in enumerate(lengths):
+        for j in range(n):
+            owner[pos + j] = (b, j)
+        pos += n
+    out = [[[-1, -1] for _ in range(s)] for _ in lengths]
+    last = {}
+    for t in range(total):
+        if t not in owner:
+            continue
+        b, j = owner[t]
+        key = (b, t // c)
+        if b not in last or last[b][0] != key:
+            i = 0 if b not in last else last[b][1] + 1
+            out[b][i] = [j, j + 1]
+            last[b] = (key, i)
+        else:
+            out[b][last[b][1]][1] = j + 1
+    return torch.tensor(out, dtype=torch.int64).reshape(len(lengths), s, 2)
+
+
+@pytest.mark.parametrize("lengths", [[256], [7, 64, 1, 33], [1000, 3], [0, 5, 0, 9, 0],
+                                     [13] * 9])
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8, 64])
+def test_flat_ranges_match_enumeration(lengths, P):
+    total = sum(lengths)
+    n = max(lengths)
+    s = oracle.flat_max_splits(total, n, P)
+    c = oracle.flat_piece_len(total, P)
+    assert c == (-(-total // P) if total else 0)
+    r = oracle.flat_ranges(synth.indptr(lengths), total, P, s)
+    assert torch.equal(r, flat_ranges_brute(lengths, total, P, s))
+    # every request is partitioned in order; no request needs more slots than
+    # the bound, and the bound is reached by some placement of a request of
+    # length n (checked on the worst offset below)
+    for b, nb in enumerate(lengths):
+        used = [tuple(x) for x in r[b].tolist() if x[0] >= 0]
+        cov = []
+        for lo, hi in used:
+            assert 0 < hi - lo <= c
+            cov.extend(range(lo, hi))
+        assert cov == list(range(nb))
+
+
+def test_flat_max_splits_is_tight():
+    # pieces of 4 rows; request 1 holds rows [3, 12): one row before the
+    # first boundary, so its 9 keys touch pieces 0, 1 and 2
+    lengths = [3, 9, 4]
+    assert oracle.flat_piece_len(16, 4) == 4
+    assert oracle.flat_max_splits(16, 9, 4) == 3
+    r = oracle.flat_ranges(synth.indptr(lengths), 16, 4, 3)
+    assert r[1].tolist() == [[0, 1], [1, 5], [5, 9]]
+    assert r[0].tolist() == [[0, 3], [-1, -1], [-1, -1]]
+    assert r[2].tolist() == [[0, 4], [-1, -1], [-1, -1]]
+    assert oracle.flat_max_splits(16, 9, 2) == 2  # never more than P
+
+
+def test_flat_ranges_reject_too_few_slots():
+    with pytest.raises(ValueError):
+        oracle.flat_ranges(synth.indptr([10, 10]), 20, 4, 1)
+
+
+@pytest.mark.parametrize("P", [1, 3, 7, 50])
+def test_split_decode_flat_plan_equals_attention(P):
+    lengths = [256, 37, 0, 1, 129]
+    B, Hq, Hkv, D = len(lengths), 8, 2, 16
+    q, k, v, kv = synth.decode_inputs(B, Hq, Hkv, D, lengths, torch.bfloat16, seed=41)
+    o_ref, lse_ref = oracle.attention(q, k, v, list(range(B + 1)), kv, 0.25)
+    rg = oracle.flat_ranges(kv, sum(lengths), P)
+    o, lse, op, mp, lp = oracle.split_decode(q, k, v, kv, max(lengths), 0.25, 0, ranges=rg)
+    assert torch.allclose(o, o_ref, atol=1e-12, rtol=0)
+    assert torch.equal(lse[2], torch.full((Hq,), -math.inf, dtype=torch.float64))
+    ok = torch.isfinite(lse_ref)
+    assert torch.allclose(lse[ok], lse_ref[ok], atol=1e-12, rtol=0)
+
+
 @pytest.mark.parametrize("dtype", [torch.float64, torch.bfloat16])
 def test_split_decode_is_invariant_to_s(dtype):
     lengths = [256, 37, 1, 129]
