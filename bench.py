@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
-    p.add_argument("--only", choices=["decode", "prefill", "ragged", "bsr", "bsr_heads", "append",
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "bsr", "bsr_heads", "append",
                                       "copy"],
                    default=None,
                    help="time one workload only (for profiler runs)")
@@ -147,6 +147,31 @@ def bench_decode(torch, ra, synth, wname, args, timer, rotate=3):
                 kv_bytes=kvb, gbs=step_bytes / step_ms / 1e6, kernel_ms=kernel_ms,
                 kernel_bytes=kernel_bytes, kernel_gbs=kernel_bytes / kernel_ms / 1e6,
                 wall_s=wall, kv_copies_rotated=rotate)
+
+
+def bench_decode_flat(torch, ra, synth, wname, args, timer):
+    """Split-KV decode with the flat plan (packed key rows cut into equal
+    pieces), whole step: pieces kernel + merge."""
+    w = synth.workload(wname)
+    inp = w.make("cuda:0")
+    dev = torch.device("cuda:0")
+    lengths = inp["lengths"]
+    max_len, total = max(lengths), sum(lengths)
+    q, k, v = inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev)
+    kvp = inp["kv_indptr"].to(dev)
+    P = ra.attn_decode_flat_pieces(w.B, w.Hq, w.Hkv, w.D, k.shape[0])
+    ws = torch.empty(max(ra.attn_decode_flat_workspace_bytes(w.B, w.Hq, w.D, max_len, k.shape[0], P),
+                         256), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ms, _ = timer.run(lambda i: ra.attn_decode_splitkv_flat(q, k, v, kvp, max_len, num_pieces=P,
+                                                            o=o, lse=lse, workspace=ws,
+                                                            stream=stream), args.steps, args.warmup)
+    kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, total, q.element_size())
+    t = median(ms)
+    return dict(workload=wname, pieces=P, piece_len=-(-k.shape[0] // P), step_ms=t,
+                gbs=(kvb + qb + ob + lb + ib) / t / 1e6)
 
 
 def causal_flops(B, Hq, L, D):
@@ -313,6 +338,8 @@ def main():
     if args.only:
         fn = {"decode": lambda: bench_decode(torch, ra, synth, "llama3_8b_decode_bf16", args, timer),
               "ragged": lambda: bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, 1),
+              "ragged_flat": lambda: bench_decode_flat(torch, ra, synth, "ragged_decode_bf16",
+                                                       args, timer),
               "prefill": lambda: bench_prefill(torch, ra, synth, args, timer),
               "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
               "bsr_heads": lambda: bench_bsr(torch, ra, synth, args, timer,
@@ -370,11 +397,17 @@ def main():
                                                     frac=round(p["frac"], 4),
                                                     algorithmic_flops=p["flops"]))
         r = bench_decode(torch, ra, synth, "ragged_decode_bf16", args, timer, rotate=1)
-        log(f"ragged decode: {r['step_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, s={r['splits']}")
-        also["ragged_decode"] = dict(workload=r["workload"], ms=round(r["step_ms"], 4),
-                                     gbs=round(r["gbs"], 1), frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
-                                     total_kv=r["total_kv"], splits=r["splits"],
-                                     kv_bytes=r["kv_bytes"])
+        rf = bench_decode_flat(torch, ra, synth, "ragged_decode_bf16", args, timer)
+        log(f"ragged decode: flat plan {rf['step_ms']*1e3:.1f} us, {rf['gbs']:.0f} GB/s, "
+            f"P={rf['pieces']}; chunk plan {r['step_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, "
+            f"s={r['splits']}")
+        also["ragged_decode"] = dict(workload=r["workload"], plan="flat", ms=round(rf["step_ms"], 4),
+                                     gbs=round(rf["gbs"], 1),
+                                     frac=round(rf["gbs"] / HBM_PEAK_GBS, 4),
+                                     total_kv=r["total_kv"], pieces=rf["pieces"],
+                                     piece_len=rf["piece_len"], kv_bytes=r["kv_bytes"],
+                                     chunk_plan=dict(ms=round(r["step_ms"], 4),
+                                                     gbs=round(r["gbs"], 1), splits=r["splits"]))
         ap = bench_append(torch, ra, synth, args, timer)
         log(f"append prefill: {ap['ms']*1e3:.1f} us, {ap['tflops']:.1f} TFLOP/s, s={ap['splits']} "
             f"(unsplit {ap['ms_unsplit']*1e3:.1f} us)")

@@ -145,6 +145,55 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
                                    int dtype, float* o_part, float* m_part, float* l_part,
                                    void* hip_stream);
 
+/* ---- split-KV decode over the packed key array (flat plan) -------------- */
+
+/* Piece count P the library picks for attn_decode_splitkv_flat when
+ * num_pieces = 0: enough pieces for four waves per compute unit, with
+ * workgroups of up to four KV heads (P = ceil(4 * CUs / (ceil(Hkv / hpw) *
+ * hpw)), hpw = 4, 2 or 1, at most Hkv), capped so that no piece is shorter
+ * than 256 keys, within [1, 65535].  Fitted to a sweep on MI355X. */
+int attn_decode_flat_pieces(int B, int Hq, int Hkv, int D, long long total_kv);
+
+/* Most splits one request can have under the flat plan with P pieces of
+ * c = ceil(total_kv / P) rows: ceil((max_kv_len - 1) / c) + 1, at most P
+ * (1 when total_kv or max_kv_len is 0; 0 for invalid arguments). */
+int attn_decode_flat_max_splits(int max_kv_len, long long total_kv, int num_pieces);
+
+/* Workspace bytes of attn_decode_splitkv_flat: s * B * Hq * (D + 2) * 4 with
+ * s = attn_decode_flat_max_splits(...), rounded up to 256 (0 if invalid). */
+size_t attn_decode_flat_workspace_bytes(int B, int Hq, int D, int max_kv_len, long long total_kv,
+                                        int num_pieces);
+
+/*
+ * Split-KV decode with the Split operator applied to the packed key array
+ * of the whole batch as one reduction dimension [CA "Split演算子による
+ * Split-Kの対応": the split is a symbol the scheduler fixes later; AB]: the
+ * rows [0, total_kv) of k / v are cut into P pieces of c = ceil(total_kv /
+ * P) rows, and split i of request b is the request's intersection with the
+ * i-th piece it overlaps.  Every piece holds the same number of keys
+ * whatever the length mix, so a ragged batch keeps all compute units busy
+ * to the end; one workgroup reduces one piece for up to four KV heads (the
+ * request segments inside it one after another, online softmax over key
+ * tiles [CA "複数リダクションのスケジューリング"]).  The merge
+ * (log-sum-exp weights, as attn_merge_lse) then combines the pieces of each
+ * request and writes O = 0, LSE = -inf for empty requests.
+ *
+ * Arguments as attn_decode_splitkv, except:
+ * num_pieces  P in [1, 65535], or 0 for attn_decode_flat_pieces.
+ * total_kv    the row count of k and v (<= 2^31 - 1); every kv_indptr entry
+ *   must lie in [0, total_kv].  Rows outside every request are not read.
+ * workspace   at least attn_decode_flat_workspace_bytes(B, Hq, D, max_kv_len,
+ *   total_kv, P) bytes; layout o_part [s, B*Hq, D], m_part [s, B*Hq],
+ *   l_part [s, B*Hq] fp32, s = attn_decode_flat_max_splits(...), split i of
+ *   request b in slot i.  Calls that share one workspace must not overlap.
+ * Supported: dtype ATTN_BF16 or ATTN_F16; D in {64, 128}; 1 <= G <= 16.
+ */
+attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void* v,
+                                       const int32_t* kv_indptr, void* o, float* lse, int B,
+                                       int Hq, int Hkv, int D, int max_kv_len, long long total_kv,
+                                       float scale, int num_pieces, int dtype, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream);
+
 /*
  * Merge of Split partials [CA "Split演算子によるSplit-Kの対応"]: for each row r,
  *   M = max_i m_i over partials with l_i > 0;  w_i = l_i exp(m_i - M);
@@ -351,6 +400,15 @@ attn_status_t attn_bsr_plan_host(const int32_t* full_indptr, const int32_t* part
  * Synchronises the stream before returning. */
 attn_status_t attn_debug_split_ranges(const int32_t* kv_indptr, int B, int max_kv_len,
                                       int num_splits, int32_t* ranges, void* hip_stream);
+
+/* Write, with the device code attn_decode_splitkv_flat uses, the flat
+ * plan's split ranges: ranges [B, s, 2] int32 on the device (s =
+ * attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces)), slot i of
+ * request b = [begin, end) as key offsets within the request, -1, -1 for
+ * slots the request does not use.  Synchronises the stream. */
+attn_status_t attn_debug_flat_ranges(const int32_t* kv_indptr, int B, int max_kv_len,
+                                     long long total_kv, int num_pieces, int32_t* ranges,
+                                     void* hip_stream);
 
 /* Expand a two-level mask to dense uint8 [L, L] (device) with the predicate
  * the block-sparse kernel applies.  Synchronises the stream. */

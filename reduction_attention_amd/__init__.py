@@ -8,10 +8,15 @@ from .api import (  # noqa: F401
     attn_bsr_encode_host,
     attn_bsr_plan,
     attn_debug_bsr_decode,
+    attn_debug_flat_ranges,
     attn_debug_split_ranges,
     attn_decode_choose_splits,
+    attn_decode_flat_max_splits,
+    attn_decode_flat_pieces,
+    attn_decode_flat_workspace_bytes,
     attn_decode_partials,
     attn_decode_splitkv,
+    attn_decode_splitkv_flat,
     attn_decode_workspace_bytes,
     attn_device_cu_count,
     attn_merge_lse,

@@ -43,6 +43,12 @@ SIGNATURES = {
                                    _i64, _f32, _i32, _i32, _vp, _sz, _vp]),
     "attn_decode_partials": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                     _i32, _i32, _vp, _vp, _vp, _vp]),
+    "attn_decode_flat_pieces": (_i32, [_i32, _i32, _i32, _i32, _i64]),
+    "attn_decode_flat_max_splits": (_i32, [_i32, _i64, _i32]),
+    "attn_decode_flat_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32]),
+    "attn_decode_splitkv_flat": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                        _i32, _i64, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "attn_debug_flat_ranges": (_i32, [_vp, _i32, _i32, _i64, _i32, _vp, _vp]),
     "attn_merge_lse": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                             _f32, _i32, _i32, _vp]),

@@ -83,6 +83,49 @@ def attn_decode_splitkv(q, k, v, kv_indptr, max_kv_len, scale=None, num_splits=0
     return o, lse
 
 
+def attn_decode_flat_pieces(B, Hq, Hkv, D, total_kv) -> int:
+    return int(load().attn_decode_flat_pieces(B, Hq, Hkv, D, int(total_kv)))
+
+
+def attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces) -> int:
+    return int(load().attn_decode_flat_max_splits(int(max_kv_len), int(total_kv), int(num_pieces)))
+
+
+def attn_decode_flat_workspace_bytes(B, Hq, D, max_kv_len, total_kv, num_pieces) -> int:
+    return int(load().attn_decode_flat_workspace_bytes(B, Hq, D, int(max_kv_len), int(total_kv),
+                                                       int(num_pieces)))
+
+
+def attn_decode_splitkv_flat(q, k, v, kv_indptr, max_kv_len, scale=None, num_pieces=0, o=None,
+                             lse=None, workspace=None, stream=None, want_lse=True):
+    """Split-KV decode with the packed key rows cut into equal pieces.
+
+    q [B,Hq,D]; k, v [total_kv,Hkv,D] (total_kv = k.shape[0]); kv_indptr int32
+    [B+1].  Returns (o [B,Hq,D] in q's dtype, lse [B,Hq] fp32 or None).
+    """
+    _dev(q, k, v, kv_indptr, o, lse, workspace)
+    B, Hq, D = q.shape
+    Hkv, total = k.shape[1], k.shape[0]
+    if kv_indptr.dtype != torch.int32:
+        raise TypeError("kv_indptr must be int32")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    lib = load()
+    P = num_pieces or lib.attn_decode_flat_pieces(B, Hq, Hkv, D, total)
+    need = lib.attn_decode_flat_workspace_bytes(B, Hq, D, int(max_kv_len), total, P)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_splitkv_flat(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(o),
+                                      _ptr(lse), B, Hq, Hkv, D, int(max_kv_len), total, scale,
+                                      int(P), _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                      _stream(stream))
+    check(st, "attn_decode_splitkv_flat")
+    return o, lse
+
+
 def attn_decode_partials(q, k, v, kv_indptr, max_kv_len, num_splits, scale=None, o_part=None,
                          m_part=None, l_part=None, stream=None):
     """Split partials only: (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) fp32."""
@@ -332,6 +375,17 @@ def attn_debug_split_ranges(kv_indptr, max_kv_len, num_splits, stream=None) -> t
     out = torch.empty((B, num_splits, 2), dtype=torch.int32, device=kv_indptr.device)
     check(load().attn_debug_split_ranges(_ptr(kv_indptr), B, int(max_kv_len), int(num_splits),
                                          _ptr(out), _stream(stream)), "attn_debug_split_ranges")
+    return out
+
+
+def attn_debug_flat_ranges(kv_indptr, max_kv_len, total_kv, num_pieces, stream=None):
+    _dev(kv_indptr)
+    B = kv_indptr.numel() - 1
+    s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces)
+    out = torch.empty((B, s, 2), dtype=torch.int32, device=kv_indptr.device)
+    check(load().attn_debug_flat_ranges(_ptr(kv_indptr), B, int(max_kv_len), int(total_kv),
+                                        int(num_pieces), _ptr(out), _stream(stream)),
+          "attn_debug_flat_ranges")
     return out
 
 

@@ -46,6 +46,7 @@ bool valid_dtype(int dt) { return dt == ATTN_F32 || dt == ATTN_BF16 || dt == ATT
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxPieces = 65535;
 
 }  // namespace
 
@@ -205,6 +206,118 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
                       uniform_lengths(B, max_kv_len, total_kv)};
   return hip_status(rattn::launch_decode_partials(a, static_cast<hipStream_t>(hip_stream)),
                     "decode_partials launch");
+}
+
+// ---- flat split plan -------------------------------------------------------
+
+static long long flat_piece_len(long long total_kv, int P) {
+  return total_kv > 0 ? (total_kv + P - 1) / P : 0;
+}
+
+int attn_decode_flat_pieces(int B, int Hq, int Hkv, int D, long long total_kv) {
+  (void)B;
+  (void)Hq;
+  (void)D;
+  if (Hkv <= 0 || total_kv <= 0) return 1;
+  // Workgroups of up to four KV heads side by side; enough pieces for four
+  // waves per compute unit, all resident at once (a sweep on MI355X over
+  // 128..384 pieces and 1..8 heads per workgroup peaked there), and no
+  // piece shorter than 256 keys.
+  const int hpw = Hkv >= 4 ? 4 : Hkv >= 2 ? 2 : 1;
+  const long long groups = (Hkv + hpw - 1) / hpw;
+  long long P = (4LL * attn_device_cu_count() + groups * hpw - 1) / (groups * hpw);
+  const long long cap = (total_kv + 255) / 256;
+  if (P > cap) P = cap;
+  if (P < 1) P = 1;
+  if (P > kMaxPieces) P = kMaxPieces;
+  return int(P);
+}
+
+int attn_decode_flat_max_splits(int max_kv_len, long long total_kv, int num_pieces) {
+  if (num_pieces < 1 || total_kv < 0 || max_kv_len < 0) return 0;
+  const long long c = flat_piece_len(total_kv, num_pieces);
+  if (c == 0 || max_kv_len == 0) return 1;
+  const long long s = (max_kv_len - 1 + c - 1) / c + 1;
+  return int(s < num_pieces ? s : num_pieces);
+}
+
+size_t attn_decode_flat_workspace_bytes(int B, int Hq, int D, int max_kv_len, long long total_kv,
+                                        int num_pieces) {
+  const int s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces);
+  if (B <= 0 || Hq <= 0 || D <= 0 || s <= 0) return 0;
+  const size_t bytes = size_t(s) * size_t(B) * size_t(Hq) * (size_t(D) + 2) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+static attn_status_t flat_args(const void* q, const void* k, const void* v,
+                               const int32_t* kv_indptr, int B, int Hq, int Hkv, int D,
+                               int max_kv_len, long long total_kv, float scale, int num_pieces,
+                               int dtype, const char* who, rattn::DecodeArgs* a) {
+  attn_status_t cs = check_decode(q, k, v, kv_indptr, B, Hq, Hkv, D, max_kv_len, total_kv, scale,
+                                  0, dtype);
+  if (cs != ATTN_OK) return cs;
+  if (dtype == ATTN_F32) return fail(ATTN_EUNSUPPORTED, "%s: 16-bit inputs only", who);
+  if (num_pieces < 0 || num_pieces > kMaxPieces)
+    return fail(ATTN_EINVAL, "%s: num_pieces %d outside [0, %d]", who, num_pieces, kMaxPieces);
+  if (total_kv > 0x7fffffffLL) return fail(ATTN_EUNSUPPORTED, "%s: total_kv above 2^31 - 1", who);
+  const int P = num_pieces ? num_pieces : attn_decode_flat_pieces(B, Hq, Hkv, D, total_kv);
+  *a = rattn::DecodeArgs{q, k, v, kv_indptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         B, Hq, Hkv, D, Hq / Hkv, attn_decode_flat_max_splits(max_kv_len, total_kv, P),
+                         int(flat_piece_len(total_kv, P)), scale * kLog2e, dtype, 0, 0};
+  a->flat = 1;
+  a->pieces = P;
+  a->total_kv = total_kv;
+  return ATTN_OK;
+}
+
+attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void* v,
+                                       const int32_t* kv_indptr, void* o, float* lse, int B,
+                                       int Hq, int Hkv, int D, int max_kv_len, long long total_kv,
+                                       float scale, int num_pieces, int dtype, void* workspace,
+                                       size_t workspace_bytes, void* hip_stream) {
+  rattn::DecodeArgs a;
+  attn_status_t cs = flat_args(q, k, v, kv_indptr, B, Hq, Hkv, D, max_kv_len, total_kv, scale,
+                               num_pieces, dtype, "decode_flat", &a);
+  if (cs != ATTN_OK) return cs;
+  if (!o) return fail(ATTN_EINVAL, "decode_flat: null output");
+  if (!aligned16(o)) return fail(ATTN_EINVAL, "decode_flat: o must be 16-byte aligned");
+  const size_t need = attn_decode_flat_workspace_bytes(B, Hq, D, max_kv_len, total_kv, a.pieces);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_EWORKSPACE, "decode_flat: workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned16(workspace))
+    return fail(ATTN_EINVAL, "decode_flat: workspace must be 16-byte aligned");
+  const size_t rows = size_t(B) * Hq;
+  float* ws = static_cast<float*>(workspace);
+  a.o = o;
+  a.lse = lse;
+  a.o_part = ws;
+  a.m_part = ws + size_t(a.s) * rows * D;
+  a.l_part = a.m_part + size_t(a.s) * rows;
+  return hip_status(rattn::launch_decode_flat(a, static_cast<hipStream_t>(hip_stream)),
+                    "decode_flat launch");
+}
+
+attn_status_t attn_debug_flat_ranges(const int32_t* kv_indptr, int B, int max_kv_len,
+                                     long long total_kv, int num_pieces, int32_t* ranges,
+                                     void* hip_stream) {
+  if (!kv_indptr || !ranges) return fail(ATTN_EINVAL, "flat_ranges: null pointer");
+  if (B < 1 || max_kv_len < 0 || total_kv < 0 || total_kv > 0x7fffffffLL)
+    return fail(ATTN_EINVAL, "flat_ranges: bad B, max_kv_len or total_kv");
+  if (num_pieces < 1 || num_pieces > kMaxPieces)
+    return fail(ATTN_EINVAL, "flat_ranges: num_pieces %d outside [1, %d]", num_pieces, kMaxPieces);
+  rattn::DecodeArgs a{};
+  a.kv_indptr = kv_indptr;
+  a.B = B;
+  a.s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces);
+  a.chunk = int(flat_piece_len(total_kv, num_pieces));
+  a.flat = 1;
+  a.pieces = num_pieces;
+  a.total_kv = total_kv;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e = rattn::launch_flat_ranges(a, ranges, st);
+  if (e != hipSuccess) return hip_status(e, "flat_ranges launch");
+  return hip_status(hipStreamSynchronize(st), "flat_ranges sync");
 }
 
 attn_status_t attn_prefill(const void* q, const void* k, const void* v, const int32_t* qo_indptr,

@@ -154,6 +154,49 @@ __device__ __forceinline__ void decode_step(DecodeState<T, D>& st, const DecodeT
   }
 }
 
+// Q^T operand of the query heads row0 .. row0 + G - 1 sharing one KV head:
+// head c16 (zero past G), slab u -> dims 32u + 8*h4 .. +8.
+template <int D>
+__device__ __forceinline__ void decode_load_q(u32x4 (&qb)[D / 32], const uint16_t* q, int64_t row0,
+                                              int G, int c16, int h4) {
+  const uint16_t* qp = q + (row0 + (c16 < G ? c16 : 0)) * D + 8 * h4;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    qb[u] = ldg128(qp + 32 * u);
+    if (c16 >= G) qb[u] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// The online softmax of one wave over keys 0 .. n-1 of a key range (n >= 1)
+// starting at kbase / vbase: 32-key steps ks, ks + WPH, ...  Two register
+// buffers: the loads of the next step are in flight while the current one
+// is computed.  Loads are issued unconditionally (key indices are clamped
+// into the range), so every path leaves the same number of loads
+// outstanding and the waits stay exact.  A wave with no step leaves
+// st.m = -inf, st.l = 0.
+template <class T, int D, int WPH>
+__device__ __forceinline__ void decode_range(DecodeState<T, D>& st, const uint16_t* kbase,
+                                             const uint16_t* vbase, int64_t row_stride, int n,
+                                             int ks, const u32x4 (&qb)[D / 32], float sl2,
+                                             int c16, int h4) {
+#pragma unroll
+  for (int j = 0; j < D / 16; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  const int nsteps = (n + 31) / 32;
+  DecodeTile<T, D> t0, t1;
+  decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * ks, n, c16, h4);
+  for (int s0 = ks; s0 < nsteps; s0 += 2 * WPH) {
+    decode_load<T, D>(t1, kbase, vbase, row_stride, 32 * (s0 + WPH), n, c16, h4);
+    __builtin_amdgcn_sched_barrier(0);
+    decode_step<T, D>(st, t0, qb, 32 * s0, n, sl2, h4);
+    if (s0 + WPH >= nsteps) break;
+    decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * (s0 + 2 * WPH), n, c16, h4);
+    __builtin_amdgcn_sched_barrier(0);
+    decode_step<T, D>(st, t1, qb, 32 * (s0 + WPH), n, sl2, h4);
+  }
+}
+
 // Workgroup = HPW x WPH waves: wave w works on KV head blockIdx.x * HPW +
 // w % HPW and takes the 32-key steps w / HPW, w / HPW + WPH, ... of the
 // chunk.  Grid (ceil(Hkv / HPW), s, B).
@@ -202,43 +245,11 @@ void decode_partial_mfma(DecodeArgs args) {
                           int64_t(gg) * D;
   const int n = sr.hi - sr.lo;
 
-  // Q^T operand: head c16 (zero past G), slab u -> dims 32u + 8*h4 .. +8
   u32x4 qb[D / 32];
-  {
-    const int64_t qrow = int64_t(b) * Hq + int64_t(gg) * G + (c16 < G ? c16 : 0);
-    const uint16_t* qp = static_cast<const uint16_t*>(args.q) + qrow * D + 8 * h4;
-#pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      qb[u] = ldg128(qp + 32 * u);
-      if (c16 >= G) qb[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
+  decode_load_q<D>(qb, static_cast<const uint16_t*>(args.q), int64_t(b) * Hq + int64_t(gg) * G,
+                   G, c16, h4);
   DecodeState<T, D> st;
-#pragma unroll
-  for (int j = 0; j < D / 16; ++j) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = -INFINITY;
-  st.l = 0.f;
-
-  // 32-key steps ks, ks + WPH, ...  Two register buffers: the loads of the
-  // next step are in flight while the current one is computed.  Loads are
-  // issued unconditionally (key indices are clamped into the request), so
-  // every path leaves the same number of loads outstanding and the waits
-  // stay exact.
-  const int nsteps = (n + 31) / 32;
-  {
-    DecodeTile<T, D> t0, t1;
-    decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * ks, n, c16, h4);
-    for (int s0 = ks; s0 < nsteps; s0 += 2 * WPH) {
-      decode_load<T, D>(t1, kbase, vbase, row_stride, 32 * (s0 + WPH), n, c16, h4);
-      __builtin_amdgcn_sched_barrier(0);
-      decode_step<T, D>(st, t0, qb, 32 * s0, n, args.scale_log2, h4);
-      if (s0 + WPH >= nsteps) break;
-      decode_load<T, D>(t0, kbase, vbase, row_stride, 32 * (s0 + 2 * WPH), n, c16, h4);
-      __builtin_amdgcn_sched_barrier(0);
-      decode_step<T, D>(st, t1, qb, 32 * (s0 + WPH), n, args.scale_log2, h4);
-    }
-  }
+  decode_range<T, D, WPH>(st, kbase, vbase, row_stride, n, ks, qb, args.scale_log2, c16, h4);
 
   // lane sums -> head sums (the four h4 lanes of head c16)
   float l = st.l;
@@ -305,6 +316,125 @@ void decode_partial_mfma(DecodeArgs args) {
       emit(int64_t(b) * Hq + int64_t(blockIdx.x * HPW + slot) * G + h, d, O, M, L);
     }
   }
+}
+
+// -------------------------------------------------------------------------
+// Flat split plan, for ragged batches.  The Split operator cuts the packed
+// key array of the whole batch as one reduction dimension: P pieces of
+// c = ceil(total_kv / P) rows, so every workgroup streams the same number of
+// key rows whatever the length mix (cutting each request into chunks of
+// ceil(max_kv_len / s) keys leaves a launch of unequal last chunks).  Split
+// i of request b is its intersection with the i-th piece it overlaps.
+//
+// Workgroup (x, p) = HPW waves on KV heads x*HPW .. x*HPW + HPW - 1 over
+// piece p: side by side the waves read HPW contiguous head slices of each
+// packed row (HPW = 4: 1 KB of a 2 KB row of K or V).  A wave walks the
+// request segments of its
+// piece one after the other with the decode step above; a request lying in
+// one piece is final here, the others leave partial i for the merge.
+// -------------------------------------------------------------------------
+struct FlatSeg {
+  int64_t lo, hi;  // packed key rows [lo, hi)
+};
+
+// Request rows [r0, r1) inside piece p of c rows.
+__device__ __forceinline__ FlatSeg flat_segment(int64_t r0, int64_t r1, int64_t p, int64_t c) {
+  const int64_t a = p * c, e = a + c;
+  return {r0 > a ? r0 : a, r1 < e ? r1 : e};
+}
+
+// Pieces a request of rows [r0, r1) overlaps (0 for an empty request); its
+// split i lies in piece r0 / c + i.
+__device__ __forceinline__ int flat_splits(int64_t r0, int64_t r1, int64_t c) {
+  return r1 > r0 ? int((r1 - 1) / c - r0 / c) + 1 : 0;
+}
+
+template <class T, int D, int HPW>
+__global__ __launch_bounds__(64 * HPW) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_flat_kernel(DecodeArgs args) {
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int g = blockIdx.x * HPW + w;
+  if (g >= args.Hkv) return;  // idle head slot (no barriers in this kernel)
+  const int lane = threadIdx.x & 63, c16 = lane & 15, h4 = lane >> 4;
+  const int G = args.G, Hq = args.Hq, B = args.B;
+  const int64_t rows = int64_t(B) * Hq, c = args.chunk, p = blockIdx.y;
+  const int64_t pos0 = p * c;
+  const int64_t pos1 = pos0 + c < args.total_kv ? pos0 + c : args.total_kv;
+  if (pos0 >= pos1) return;
+  // first request that may hold row pos0: (indptr entries <= pos0) - 1,
+  // counted 64 entries per step across the lanes
+  int cnt = 0;
+  for (int j0 = 0; j0 <= B; j0 += 64) {
+    const int j = j0 + lane;
+    cnt += __popcll(__ballot(j <= B && int64_t(args.kv_indptr[j <= B ? j : B]) <= pos0));
+  }
+  int b = __builtin_amdgcn_readfirstlane(cnt > 0 ? cnt - 1 : 0);
+  const int64_t row_stride = int64_t(args.Hkv) * D;
+  for (; b < B; ++b) {
+    const int64_t r0 = args.kv_indptr[b], r1 = args.kv_indptr[b + 1];
+    if (r0 >= pos1) break;
+    const FlatSeg sg = flat_segment(r0, r1, p, c);
+    if (sg.lo >= sg.hi) continue;  // empty request, or one that ends before pos0
+    const int splits_b = flat_splits(r0, r1, c);
+    const int i = int(p - r0 / c);
+    // (with a consistent indptr 0 <= i < s always holds; otherwise nothing
+    // is written outside the workspace)
+    if (splits_b > 1 && (i < 0 || i >= args.s)) continue;
+    const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
+    u32x4 qb[D / 32];
+    decode_load_q<D>(qb, static_cast<const uint16_t*>(args.q), row0, G, c16, h4);
+    const int64_t off = sg.lo * row_stride + int64_t(g) * D;
+    DecodeState<T, D> st;
+    decode_range<T, D, 1>(st, static_cast<const uint16_t*>(args.k) + off,
+                          static_cast<const uint16_t*>(args.v) + off, row_stride,
+                          int(sg.hi - sg.lo), 0, qb, args.scale_log2, c16, h4);
+    float l = st.l;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    // lane (c16, h4) holds dims (D/4)*h4 + (D/16)*r + j of head c16 in
+    // o[j][r]; st.m is finite (the segment holds a key)
+    if (c16 < G) {
+      const int64_t row = row0 + c16;
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) {
+          const int d = (D / 4) * h4 + (D / 16) * r + j;
+          if (splits_b == 1)
+            static_cast<typename T::elem*>(args.o)[row * D + d] = typename T::elem(st.o[j][r] * inv);
+          else
+            args.o_part[(int64_t(i) * rows + row) * D + d] = st.o[j][r] * inv;
+        }
+      if (h4 == 0) {
+        if (splits_b == 1) {
+          if (args.lse) args.lse[row] = (st.m + flog2(l)) * kLn2;
+        } else {
+          args.m_part[int64_t(i) * rows + row] = st.m * kLn2;
+          args.l_part[int64_t(i) * rows + row] = l;
+        }
+      }
+    }
+  }
+}
+
+// The flat plan's split ranges, [B, s, 2] key offsets within each request
+// (-1 for slots a request does not use), from the same segment arithmetic
+// as decode_flat_kernel.
+__global__ void flat_ranges_kernel(DecodeArgs a, int32_t* ranges) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.B * a.s) return;
+  const int b = e / a.s, i = e % a.s;
+  const int64_t r0 = a.kv_indptr[b], r1 = a.kv_indptr[b + 1];
+  const int64_t c = a.chunk;
+  int32_t lo = -1, hi = -1;
+  if (c > 0 && i < flat_splits(r0, r1, c)) {
+    const FlatSeg sg = flat_segment(r0, r1, r0 / c + i, c);
+    lo = int32_t(sg.lo - r0);
+    hi = int32_t(sg.hi - r0);
+  }
+  ranges[2 * e] = lo;
+  ranges[2 * e + 1] = hi;
 }
 
 // -------------------------------------------------------------------------
@@ -476,34 +606,61 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 // rows of requests held by one split (already final) and unused splits are
 // never touched; (m, l) of the splits are loaded side by side across lanes.
 // -------------------------------------------------------------------------
-template <int D, class OutT>
+template <int D, class OutT, int SB>  // SB: splits whose loads are issued together
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DL = (D + 63) / 64;
-  constexpr int SB = 16;  // splits whose loads are issued together
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.B) * a.Hq;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int b = int(row / a.Hq);
-  // The request's split count, the first SB splits' (m, l) and their
-  // partial outputs are loaded at once (every address lies inside the
-  // workspace; values of splits the request does not use are discarded
-  // below, never multiplied), so the merge costs one memory round trip.
+  // The request's split count from kv_indptr and the chunk or piece
+  // length (an inconsistent indptr is capped at the slot count, so no read
+  // leaves the workspace); an empty request of the flat plan is written
+  // here (O = 0, LSE = -inf) and yields 0.
   const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
-  const int s0n = a.s < SB ? a.s : SB;
+  auto split_count = [&]() -> int {
+    int n;
+    if (a.flat) {
+      n = a.chunk > 0 ? flat_splits(kb0, kb1, a.chunk) : 0;
+      n = n < a.s ? n : a.s;
+      if (n == 0) {
+        OutT* o = static_cast<OutT*>(a.o) + row * D;
+#pragma unroll
+        for (int x = 0; x < DL; ++x)
+          if (lane + 64 * x < D) o[lane + 64 * x] = OutT(0.f);
+        if (a.lse && lane == 0) a.lse[row] = -INFINITY;
+      }
+    } else {
+      n = a.chunk > 0 ? int((kb1 - kb0 + a.chunk - 1) / a.chunk) : 0;
+    }
+    return n;
+  };
+  // The first n splits' (m, l) and partial outputs, loaded at once.
   float mi = -INFINITY, li = 0.f;
-  if (lane < s0n) {
-    mi = a.m_part[int64_t(lane) * rows + row];
-    li = a.l_part[int64_t(lane) * rows + row];
-  }
   float ov[SB][DL];
+  auto load_batch = [&](int n) {
+    if (lane < n) {
+      mi = a.m_part[int64_t(lane) * rows + row];
+      li = a.l_part[int64_t(lane) * rows + row];
+    }
 #pragma unroll
-  for (int j = 0; j < SB; ++j)
+    for (int j = 0; j < SB; ++j)
 #pragma unroll
-    for (int x = 0; x < DL; ++x)
-      ov[j][x] = (j < s0n && lane + 64 * x < D) ? a.o_part[(int64_t(j) * rows + row) * D + lane + 64 * x] : 0.f;
-  const int n_b = int(kb1 - kb0);
-  const int splits_b = a.chunk > 0 ? (n_b + a.chunk - 1) / a.chunk : 0;
+      for (int x = 0; x < DL; ++x)
+        ov[j][x] = (j < n && lane + 64 * x < D) ? a.o_part[(int64_t(j) * rows + row) * D + lane + 64 * x] : 0.f;
+  };
+  int splits_b;
+  if (a.uniform) {
+    // equal lengths: every request uses min(s, SB) of the first slots, so
+    // the loads go out together with the indptr reads (one round trip)
+    load_batch(a.s < SB ? a.s : SB);
+    splits_b = split_count();
+  } else {
+    // ragged: only the request's own splits are loaded
+    splits_b = split_count();
+    if (splits_b > 1) load_batch(splits_b < SB ? splits_b : SB);
+  }
   if (splits_b <= 1) return;
   if (lane >= splits_b) { mi = -INFINITY; li = 0.f; }
   float M = mi;
@@ -613,15 +770,51 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     launch_partial_mfma(a, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.s == 1) return e;  // one split: every request is final
+    // equal lengths: every request has s splits, a batch of 16 covers the
+    // usual split counts; ragged: up to 32 of a request's own splits
     const dim3 mgrid(unsigned((int64_t(a.B) * a.Hq + 3) / 4));
+#define RATTN_MERGE(DD, TT)                                                                  \
+  if (a.uniform) hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 16>), mgrid, dim3(256), 0, st, a); \
+  else hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 32>), mgrid, dim3(256), 0, st, a)
     if (a.dtype == 1) {
-      if (a.D == 64) hipLaunchKernelGGL((decode_merge_kernel<64, __bf16>), mgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((decode_merge_kernel<128, __bf16>), mgrid, dim3(256), 0, st, a);
+      if (a.D == 64) { RATTN_MERGE(64, __bf16); } else { RATTN_MERGE(128, __bf16); }
     } else {
-      if (a.D == 64) hipLaunchKernelGGL((decode_merge_kernel<64, _Float16>), mgrid, dim3(256), 0, st, a);
-      else hipLaunchKernelGGL((decode_merge_kernel<128, _Float16>), mgrid, dim3(256), 0, st, a);
+      if (a.D == 64) { RATTN_MERGE(64, _Float16); } else { RATTN_MERGE(128, _Float16); }
     }
+#undef RATTN_MERGE
   }
+  return hipGetLastError();
+}
+
+// Up to four KV heads per workgroup: on MI355X a piece streamed by four
+// waves side by side (1 KB of each 2 KB packed row) at one workgroup per
+// compute unit sustained more than eight waves on whole rows, or two.
+template <class T, int D>
+static void launch_flat_t(const DecodeArgs& a, hipStream_t st) {
+  const int hpw = a.Hkv >= 4 ? 4 : a.Hkv >= 2 ? 2 : 1;
+  const dim3 grid(unsigned((a.Hkv + hpw - 1) / hpw), unsigned(a.pieces));
+  if (a.pieces > 0 && a.total_kv > 0) switch (hpw) {
+    case 4: hipLaunchKernelGGL((decode_flat_kernel<T, D, 4>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((decode_flat_kernel<T, D, 2>), grid, dim3(128), 0, st, a); break;
+    default: hipLaunchKernelGGL((decode_flat_kernel<T, D, 1>), grid, dim3(64), 0, st, a); break;
+  }
+  const dim3 mgrid(unsigned((int64_t(a.B) * a.Hq + 3) / 4));
+  hipLaunchKernelGGL((decode_merge_kernel<D, typename T::elem, 32>), mgrid, dim3(256), 0, st, a);
+}
+
+hipError_t launch_decode_flat(const DecodeArgs& a, hipStream_t st) {
+  if (a.dtype == 1) {
+    if (a.D == 64) launch_flat_t<BF16, 64>(a, st); else launch_flat_t<BF16, 128>(a, st);
+  } else {
+    if (a.D == 64) launch_flat_t<F16, 64>(a, st); else launch_flat_t<F16, 128>(a, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t st) {
+  const int n = a.B * a.s;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(flat_ranges_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a, ranges);
   return hipGetLastError();
 }
 

@@ -28,6 +28,12 @@ struct DecodeArgs {
                       // written to o / lse directly
   int uniform;        // 1: every request has max_kv_len keys (picks the
                       // workgroup shape; results do not depend on it)
+  // Flat plan: the packed key rows [0, total_kv) are cut into `pieces`
+  // pieces of `chunk` rows; split i of a request is its i-th piece, and s
+  // bounds the splits of any request (the partial slots per row).
+  int flat = 0;
+  int pieces = 0;
+  int64_t total_kv = 0;
 };
 
 struct MergeArgs {
@@ -85,6 +91,8 @@ struct BsrArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_flat(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
                                hipStream_t st);

@@ -96,6 +96,52 @@ def test_decode_validation(lib, kw, status):
     assert lib.attn_last_error().decode() != ""
 
 
+def test_flat_plan_host_rules(lib):
+    # no device here: 256 CUs; four KV heads per workgroup, four waves per
+    # CU -> 8 KV heads: 128 pieces (two workgroups each)
+    assert lib.attn_decode_flat_pieces(64, 64, 8, 128, 226896) == 128
+    # four KV heads -> 256 pieces of one four-wave workgroup each
+    assert lib.attn_decode_flat_pieces(4, 16, 4, 128, 1 << 20) == 256
+    # one KV head -> 1024 one-wave workgroups
+    assert lib.attn_decode_flat_pieces(4, 16, 1, 128, 1 << 20) == 1024
+    # no piece below 256 keys
+    assert lib.attn_decode_flat_pieces(2, 16, 8, 128, 1000) == 4
+    assert lib.attn_decode_flat_pieces(2, 16, 8, 128, 0) == 1
+    # worst-case splits per request: ceil((n - 1) / c) + 1, at most P
+    c = -(-226896 // 256)
+    assert lib.attn_decode_flat_max_splits(27752, 226896, 256) == -(-(27752 - 1) // c) + 1
+    assert lib.attn_decode_flat_max_splits(16, 16, 4) == 4
+    assert lib.attn_decode_flat_max_splits(9, 16, 4) == 3
+    assert lib.attn_decode_flat_max_splits(0, 0, 4) == 1
+    assert lib.attn_decode_flat_max_splits(5, 16, 0) == 0
+    s = lib.attn_decode_flat_max_splits(27752, 226896, 256)
+    raw = s * 64 * 64 * 130 * 4
+    assert lib.attn_decode_flat_workspace_bytes(64, 64, 128, 27752, 226896, 256) == \
+        (raw + 255) // 256 * 256
+    assert lib.attn_decode_flat_workspace_bytes(64, 64, 128, 27752, 226896, 0) == 0
+
+
+def flat_call(lib, **kw):
+    a = dict(q=P, k=P, v=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, maxlen=100,
+             total=150, scale=0.1, n=3, dt=1, ws=P, wsb=1 << 20, st=None)
+    a.update(kw)
+    return lib.attn_decode_splitkv_flat(a["q"], a["k"], a["v"], a["kv"], a["o"], a["lse"], a["B"],
+                                        a["Hq"], a["Hkv"], a["D"], a["maxlen"], a["total"],
+                                        a["scale"], a["n"], a["dt"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(Hq=6, Hkv=4), 1),
+    (dict(Hq=34, Hkv=2), 2), (dict(D=96), 2), (dict(dt=0), 2), (dict(maxlen=200, total=150), 1),
+    (dict(n=-1), 1), (dict(n=65536), 1), (dict(ws=None), 3), (dict(wsb=100), 3),
+    (dict(total=1 << 31, maxlen=5), 2), (dict(o=ctypes.c_void_p(18)), 1),
+])
+def test_flat_validation(lib, kw, status):
+    assert flat_call(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+    assert lib.attn_debug_flat_ranges(P, 2, 10, 20, 0, P, None) == 1
+
+
 def prefill_call(lib, **kw):
     a = dict(q=P, k=P, v=P, qo=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, mq=64, mk=64,
              scale=0.1, causal=1, dt=1, st=None)

@@ -197,3 +197,102 @@ def test_partials_match_oracle_split(s):
     torch.cuda.synchronize()
     check(f"partials+merge s={s}", o.view(len(lengths), 8, 128), o_ref, lse.view(len(lengths), 8),
           lse_ref, torch.bfloat16)
+
+
+# ---- flat split plan (packed key array cut into equal pieces) -------------
+
+def run_flat(inp, max_len, P, **kw):
+    q, k, v, kv = (inp[x].to(DEV) for x in ("q", "k", "v", "kv_indptr"))
+    o, lse = ra().attn_decode_splitkv_flat(q, k, v, kv, max_len, num_pieces=P, **kw)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_flat_ranges_bit_exact():
+    lengths = [1, 31, 32, 33, 0, 300, 4096, 517, 7, 0]
+    kv = synth.indptr(lengths)
+    total = sum(lengths)
+    for P in (1, 2, 3, 7, 64, 256, 5117):
+        got = ra().attn_debug_flat_ranges(kv.to(DEV), max(lengths), total, P).cpu().to(torch.int64)
+        want = oracle.flat_ranges(kv, total, P, got.shape[1])
+        assert got.shape[1] == oracle.flat_max_splits(total, max(lengths), P)
+        assert torch.equal(got, want), P
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Hkv,G", [(1, 8), (2, 16), (3, 4), (8, 8), (12, 1)])
+def test_flat_small_ragged(dtype, D, Hkv, G):
+    """Pieces spanning several requests, requests spanning several pieces,
+    empty requests, and head groups that leave idle wave slots (Hkv 3, 12)."""
+    lengths = [1, 31, 32, 33, 0, 300, 64, 517, 0]
+    q, k, v, kv = synth.decode_inputs(len(lengths), G * Hkv, Hkv, D, lengths, dtype,
+                                      seed=D + G + Hkv)
+    inp = dict(q=q, k=k, v=v, kv_indptr=kv)
+    o_ref, lse_ref = oracle_decode(inp, 1.0 / D ** 0.5)
+    for P in (0, 1, 2, 5, 31, 978):
+        o, lse = run_flat(inp, max(lengths), P)
+        check(f"flat {dtype} D={D} Hkv={Hkv} G={G} P={P}", o, o_ref, lse, lse_ref, dtype)
+    assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[8]).all())
+
+
+def test_flat_all_requests_empty():
+    lengths = [0, 0, 0]
+    q, k, v, kv = synth.decode_inputs(3, 8, 2, 128, lengths, torch.bfloat16, seed=3)
+    k = torch.zeros((16, 2, 128), dtype=torch.bfloat16)  # rows no request owns
+    v = k.clone()
+    o = torch.full((3, 8, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+    o, lse = ra().attn_decode_splitkv_flat(q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV), 0, o=o)
+    torch.cuda.synchronize()
+    assert bool((o == 0).all()) and bool(torch.isinf(lse).all()) and bool((lse < 0).all())
+
+
+def test_flat_ragged_serving_full_parity():
+    """The ragged serving-like workload through the flat plan, every row."""
+    w = synth.workload("ragged_decode_bf16")
+    inp = w.make(DEV)
+    L = inp["lengths"]
+    P = ra().attn_decode_flat_pieces(w.B, w.Hq, w.Hkv, w.D, sum(L))
+    print(f"flat plan: P={P} piece={-(-sum(L) // P)} "
+          f"slots={ra().attn_decode_flat_max_splits(max(L), sum(L), P)}", flush=True)
+    o_ref, lse_ref = oracle_decode(inp, w.scale)
+    o, lse = run_flat(inp, max(L), 0)
+    check("ragged decode, flat plan", o, o_ref, lse, lse_ref, torch.bfloat16)
+    o2, lse2 = run_flat(inp, max(L), 0)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_flat_equals_oracle_split_partials():
+    """The flat plan's merged result against the oracle's split decode over
+    the same ranges, and the Llama-shaped batch (equal lengths)."""
+    lengths = [700, 1, 64, 0, 513, 2048]
+    q, k, v, kv = synth.decode_inputs(len(lengths), 8, 2, 128, lengths, torch.bfloat16, seed=9)
+    P = 6
+    rg = oracle.flat_ranges(kv, sum(lengths), P)
+    o_ref, lse_ref, *_ = oracle.split_decode(q, k, v, kv, max(lengths), 1 / 128 ** 0.5, 0,
+                                             ranges=rg)
+    o, lse = run_flat(dict(q=q, k=k, v=v, kv_indptr=kv), max(lengths), P)
+    check("flat P=6 vs oracle split decode", o, o_ref, lse, lse_ref, torch.bfloat16)
+    w = synth.workload("llama3_8b_decode_bf16")
+    inp = w.make(DEV)
+    o_ref, lse_ref = oracle_decode(inp, w.scale)
+    o, lse = run_flat(inp, w.L, 0)
+    check("llama3-8b decode, flat plan", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+def test_flat_rows_outside_requests_not_read():
+    """Key rows before kv_indptr[0] and after kv_indptr[B] hold NaN; the
+    flat plan's pieces cover them but no request owns them, so they are
+    never read."""
+    q, k, v, _ = synth.decode_inputs(2, 8, 2, 128, [300, 200], torch.bfloat16, seed=21)
+    kk = torch.full((700, 2, 128), float("nan"), dtype=torch.bfloat16)
+    vv = kk.clone()
+    kk[50:550], vv[50:550] = k, v
+    kv = torch.tensor([50, 350, 550], dtype=torch.int32)
+    o_ref, lse_ref = oracle.attention(q, kk, vv, [0, 1, 2], kv, 1 / 128 ** 0.5)
+    assert torch.isfinite(o_ref).all()
+    for P in (1, 3, 7, 700):
+        o, lse = ra().attn_decode_splitkv_flat(q.to(DEV), kk.to(DEV), vv.to(DEV), kv.to(DEV),
+                                               300, num_pieces=P)
+        torch.cuda.synchronize()
+        check(f"flat outside rows P={P}", o, o_ref, lse, lse_ref, torch.bfloat16)
