@@ -12,8 +12,11 @@ not hit the 256 MB Infinity Cache (one copy of K + V is 268 MB).
 Also measured in the same run (reported under "also"): causal prefill
 (B 2, L 4096, 32/8 heads, D 128, bf16) in TFLOP/s of the lower triangle,
 ragged serving-like decode (64 requests, 64/8 heads, lengths log-uniform in
-[128, 32768]) in GB/s, and block-sparse prefill (B 1, L 4096, 16 heads,
-D 64, fp16) in TFLOP/s at outer-tile granularity.
+[128, 32768]; flat split plan, chunk plan for comparison) in GB/s, append
+prefill, MLA decode (absorbed form, 576-element cache rows; 16 heads x 32
+requests x 4096 tokens, and 128 heads with ragged lengths) in GB/s, and
+block-sparse prefill (B 1, L 4096, 16 heads, D 64, fp16) in TFLOP/s at
+outer-tile granularity.
 
 Prints one JSON line on stdout (progress goes to stderr).
 """
@@ -44,7 +47,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
-    p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "bsr", "bsr_heads", "append",
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "mla", "mla_ragged", "bsr", "bsr_heads", "append",
                                       "copy"],
                    default=None,
                    help="time one workload only (for profiler runs)")
@@ -172,6 +175,32 @@ def bench_decode_flat(torch, ra, synth, wname, args, timer):
     t = median(ms)
     return dict(workload=wname, pieces=P, piece_len=-(-k.shape[0] // P), step_ms=t,
                 gbs=(kvb + qb + ob + lb + ib) / t / 1e6)
+
+
+def bench_mla(torch, ra, synth, wname, args, timer):
+    """MLA decode (absorbed form), whole step: chunk kernel + merge.  Bytes:
+    cache rows (576 x 2 B per token, read once for keys and values), q,
+    o (512 wide), lse, indptr."""
+    w = synth.workload(wname)
+    inp = w.make("cuda:0")
+    q, kv, kvp = inp["q"], inp["kv"], inp["kv_indptr"]
+    L = inp["lengths"]
+    max_len, total = max(L), sum(L)
+    s = ra.attn_mla_decode_choose_splits(w.B, w.Hq, total, max_len)
+    ws = torch.empty(max(ra.attn_mla_decode_workspace_bytes(w.B, w.Hq, s), 256), dtype=torch.uint8,
+                     device=q.device)
+    o = torch.empty((w.B, w.Hq, 512), dtype=q.dtype, device=q.device)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    ms, _ = timer.run(lambda i: ra.attn_mla_decode(q, kv, kvp, max_len, w.scale, num_splits=s, o=o,
+                                                   lse=lse, workspace=ws, stream=stream),
+                      args.steps, args.warmup)
+    t = median(ms)
+    byt = total * 576 * 2 + w.B * w.Hq * (576 * 2 + 512 * 2 + 4) + 4 * (w.B + 1)
+    flops = 2 * w.Hq * total * (576 + 512)
+    return dict(workload=wname, B=w.B, H=w.Hq, total_kv=total, max_kv_len=max_len, splits=s,
+                ms=t, bytes=byt, gbs=byt / t / 1e6, frac=byt / t / 1e6 / HBM_PEAK_GBS,
+                tflops=flops / t / 1e9)
 
 
 def causal_flops(B, Hq, L, D):
@@ -345,6 +374,9 @@ def main():
               "bsr_heads": lambda: bench_bsr(torch, ra, synth, args, timer,
                                              "bsr_heads_prefill_fp16"),
               "append": lambda: bench_append(torch, ra, synth, args, timer),
+              "mla": lambda: bench_mla(torch, ra, synth, "mla_decode_bf16", args, timer),
+              "mla_ragged": lambda: bench_mla(torch, ra, synth, "mla_ragged_decode_bf16", args,
+                                              timer),
               "copy": lambda: bench_copy(torch, args, timer)}[args.only]
         r = fn()
         print(json.dumps({"only": args.only, **r}))
@@ -413,6 +445,12 @@ def main():
             f"(unsplit {ap['ms_unsplit']*1e3:.1f} us)")
         also["append_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in ap.items()}
+        for name, key in (("mla_decode_bf16", "mla_decode"),
+                          ("mla_ragged_decode_bf16", "mla_ragged_decode")):
+            m = bench_mla(torch, ra, synth, name, args, timer)
+            log(f"{name}: {m['ms']*1e3:.1f} us, {m['gbs']:.0f} GB/s, s={m['splits']}, "
+                f"{m['tflops']:.1f} TFLOP/s")
+            also[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}
         b = bench_bsr(torch, ra, synth, args, timer)
         log(f"bsr: {b['ms']*1e3:.1f} us ({b['kernel']}-wise; block {b['ms_block']*1e3:.1f}, "
             f"row {b['ms_row']*1e3:.1f}), {b['tflops_ot']:.1f} TFLOP/s at OT granularity")

@@ -194,6 +194,54 @@ attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void*
                                        float scale, int num_pieces, int dtype, void* workspace,
                                        size_t workspace_bytes, void* hip_stream);
 
+/* ---- multi-head latent attention (MLA) decode, absorbed form ----------- */
+
+/* Workspace bytes of attn_mla_decode with s splits: s * B * H * (512 + 2) * 4
+ * (fp32 partial outputs of the 512-wide latent part, maxima, sums), rounded
+ * up to 256; 0 for invalid arguments. */
+size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
+
+/* The split count attn_mla_decode picks when num_splits = 0: s = ceil(max_kv_len
+ * / c) with c the largest power of two >= 256 keys such that ceil(H / 16) *
+ * chunks reaches one workgroup per compute unit for equal lengths (chunks =
+ * B * ceil(max_kv_len / c)), two otherwise (chunks = total_kv / c + B / 2,
+ * and s made odd so that the splits of the requests spread over the eight
+ * XCDs); within [1, 256].  Fitted to sweeps on MI355X. */
+int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len);
+
+/*
+ * Multi-head latent attention decode in its absorbed form ([AB] lists MLA
+ * among the attention subgraphs; the shapes are not on the pages, so the
+ * widths below are those of the published DeepSeek-V2/V3 models): every
+ * query head attends to one cache row per token shared by all heads, a
+ * latent vector of Dc = 512 elements followed by a rotary key part of
+ * Dr = 64.  The score of head h and token j is scale * q_h . kv_j over all
+ * 576 elements; the output is the softmax-weighted sum of the latent parts
+ * kv_j[0 .. 511].  The Split operator cuts each request's keys into chunks
+ * of c = ceil(max_kv_len / s) keys [CA "Split演算子によるSplit-Kの対応"],
+ * exactly as attn_decode_splitkv; each chunk is reduced with an online
+ * softmax over LDS-staged key tiles [CA "複数リダクションのスケジューリング"]
+ * and the chunks are merged with log-sum-exp weights.
+ *
+ * q         [B, H, 576]           element type `dtype` (latent part first)
+ * kv        [total_kv, 576]       request b owns rows kv_indptr[b] .. kv_indptr[b+1]-1
+ * kv_indptr [B + 1] int32, device
+ * o         [B, H, 512]           element type `dtype`
+ * lse       [B, H] fp32 (natural log), or NULL
+ * Dc, Dr      512 and 64 (other widths: ATTN_EUNSUPPORTED)
+ * num_splits  s in [1, 256], or 0 for attn_mla_decode_choose_splits; s = 1
+ *   needs no workspace (may be NULL).
+ * workspace   at least attn_mla_decode_workspace_bytes(B, H, s) bytes when
+ *   s > 1; layout o_part [s, B*H, 512], m_part [s, B*H], l_part [s, B*H] fp32.
+ *   Calls that share one workspace must not overlap in time.
+ * A request with no key yields O = 0, LSE = -inf.  One workgroup serves 16
+ * heads; any H >= 1 is accepted.  Supported: ATTN_BF16, ATTN_F16.
+ */
+attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_indptr, void* o,
+                              float* lse, int B, int H, int Dc, int Dr, int max_kv_len,
+                              long long total_kv, float scale, int num_splits, int dtype,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /*
  * Merge of Split partials [CA "Split演算子によるSplit-Kの対応"]: for each row r,
  *   M = max_i m_i over partials with l_i > 0;  w_i = l_i exp(m_i - M);

@@ -20,6 +20,9 @@ from .api import (  # noqa: F401
     attn_decode_workspace_bytes,
     attn_device_cu_count,
     attn_merge_lse,
+    attn_mla_decode,
+    attn_mla_decode_choose_splits,
+    attn_mla_decode_workspace_bytes,
     attn_prefill,
     attn_prefill_bsr,
     attn_prefill_choose_splits,

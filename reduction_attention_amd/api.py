@@ -126,6 +126,44 @@ def attn_decode_splitkv_flat(q, k, v, kv_indptr, max_kv_len, scale=None, num_pie
     return o, lse
 
 
+def attn_mla_decode_workspace_bytes(B, H, num_splits) -> int:
+    return int(load().attn_mla_decode_workspace_bytes(B, H, num_splits))
+
+
+def attn_mla_decode_choose_splits(B, H, total_kv, max_kv_len) -> int:
+    return int(load().attn_mla_decode_choose_splits(B, H, int(total_kv), int(max_kv_len)))
+
+
+def attn_mla_decode(q, kv, kv_indptr, max_kv_len, scale, num_splits=0, o=None, lse=None,
+                    workspace=None, stream=None, want_lse=True):
+    """MLA decode, absorbed form.  q [B,H,576]; kv [total_kv,576] (or
+    [total_kv,1,576]); kv_indptr int32 [B+1].  Returns (o [B,H,512], lse [B,H]).
+    """
+    _dev(q, kv, kv_indptr, o, lse, workspace)
+    B, H, Dq = q.shape
+    if kv.dim() == 3:
+        kv = kv.view(kv.shape[0], kv.shape[1] * kv.shape[2])
+    if Dq != 576 or kv.shape[1] != 576:
+        raise ValueError("MLA decode expects 576-element query and cache rows (512 + 64)")
+    if kv_indptr.dtype != torch.int32:
+        raise TypeError("kv_indptr must be int32")
+    lib = load()
+    s = num_splits or lib.attn_mla_decode_choose_splits(B, H, kv.shape[0], int(max_kv_len))
+    if workspace is None and s > 1:
+        need = lib.attn_mla_decode_workspace_bytes(B, H, s)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((B, H, 512), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = lib.attn_mla_decode(_ptr(q), _ptr(kv), _ptr(kv_indptr), _ptr(o), _ptr(lse), B, H, 512, 64,
+                             int(max_kv_len), int(kv.shape[0]), float(scale), int(s),
+                             _dtype_code(q), _ptr(workspace),
+                             0 if workspace is None else workspace.numel(), _stream(stream))
+    check(st, "attn_mla_decode")
+    return o, lse
+
+
 def attn_decode_partials(q, k, v, kv_indptr, max_kv_len, num_splits, scale=None, o_part=None,
                          m_part=None, l_part=None, stream=None):
     """Split partials only: (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) fp32."""

@@ -208,6 +208,79 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
                     "decode_partials launch");
 }
 
+// ---- multi-head latent attention decode ---------------------------------------
+
+size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
+  if (B <= 0 || H <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
+  const size_t bytes = size_t(num_splits) * size_t(B) * size_t(H) * (512 + 2) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len) {
+  if (B <= 0 || H <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
+  // Workgroups of 16 heads over one chunk, one per compute unit at a time.
+  // Equal lengths: the largest power-of-two chunk >= 256 keys that gives
+  // every compute unit a workgroup.  Ragged: chunks counted as total/c +
+  // B/2, two workgroups per compute unit, and an odd s: workgroups are
+  // dealt to the eight XCDs round robin, and with s a multiple of eight the
+  // first splits (present in every request) would all land on the same
+  // XCDs while the last ones (mostly empty) land on the others.
+  const long long cus = attn_device_cu_count();
+  const long long hg = (H + 15) / 16;
+  const bool uniform = (long long)max_kv_len * B == total_kv;
+  long long c = 1;
+  while (c < max_kv_len) c <<= 1;
+  while (c > 256) {
+    const long long chunks = uniform ? B * ((max_kv_len + c - 1) / c) : (total_kv + c - 1) / c + B / 2;
+    if (hg * chunks >= (uniform ? 1 : 2) * cus) break;
+    c >>= 1;
+  }
+  long long s = (max_kv_len + c - 1) / c;
+  if (!uniform && s > 1 && s % 2 == 0) s += 1;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return int(s);
+}
+
+attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_indptr, void* o,
+                              float* lse, int B, int H, int Dc, int Dr, int max_kv_len,
+                              long long total_kv, float scale, int num_splits, int dtype,
+                              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!q || !kv || !kv_indptr || !o) return fail(ATTN_EINVAL, "mla_decode: null pointer");
+  if (B < 1 || H < 1) return fail(ATTN_EINVAL, "mla_decode: B and H must be >= 1");
+  if ((long long)B * H > (1LL << 30)) return fail(ATTN_EUNSUPPORTED, "mla_decode: B * H above 2^30");
+  if (Dc != 512 || Dr != 64)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode: latent/rotary widths %d/%d (supported: 512/64)", Dc,
+                Dr);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode: dtype %d (16-bit only)", dtype);
+  if (max_kv_len < 0 || total_kv < 0) return fail(ATTN_EINVAL, "mla_decode: negative length");
+  if ((long long)max_kv_len > total_kv)
+    return fail(ATTN_EINVAL, "mla_decode: max_kv_len %d exceeds total_kv %lld", max_kv_len, total_kv);
+  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "mla_decode: scale is not finite");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(ATTN_EINVAL, "mla_decode: num_splits %d outside [0, %d]", num_splits, kMaxSplits);
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o))
+    return fail(ATTN_EINVAL, "mla_decode: q, kv, o must be 16-byte aligned");
+  const int s = num_splits ? num_splits : attn_mla_decode_choose_splits(B, H, total_kv, max_kv_len);
+  if ((long long)s * B > (1LL << 27)) return fail(ATTN_EUNSUPPORTED, "mla_decode: s * B too large");
+  const size_t need = attn_mla_decode_workspace_bytes(B, H, s);
+  if (s > 1 && (!workspace || workspace_bytes < need))
+    return fail(ATTN_EWORKSPACE, "mla_decode: workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (s > 1 && !aligned16(workspace))
+    return fail(ATTN_EINVAL, "mla_decode: workspace must be 16-byte aligned");
+  const size_t rows = size_t(B) * H;
+  float* ws = static_cast<float*>(workspace);
+  rattn::MlaArgs a{q, kv, kv_indptr, o, lse,
+                   s > 1 ? ws : nullptr, s > 1 ? ws + size_t(s) * rows * 512 : nullptr,
+                   s > 1 ? ws + size_t(s) * rows * 513 : nullptr,
+                   B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
+                   uniform_lengths(B, max_kv_len, total_kv)};
+  return hip_status(rattn::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)),
+                    "mla_decode launch");
+}
+
 // ---- flat split plan -------------------------------------------------------
 
 static long long flat_piece_len(long long total_kv, int P) {

@@ -606,12 +606,17 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 // rows of requests held by one split (already final) and unused splits are
 // never touched; (m, l) of the splits are loaded side by side across lanes.
 // -------------------------------------------------------------------------
+// D: row width; a wave merges DW = min(D, 128) dims of a row (wider rows,
+// such as MLA's 512 latent dims, take D / DW waves).
 template <int D, class OutT, int SB>  // SB: splits whose loads are issued together
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int DL = (D + 63) / 64;
+  constexpr int DW = D < 128 ? D : 128, NSL = D / DW;
+  constexpr int DL = (DW + 63) / 64;
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.B) * a.Hq;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t gw = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t row = gw / NSL;
+  const int d0 = int(gw % NSL) * DW;  // this wave's first dim
   if (row >= rows) return;
   const int b = int(row / a.Hq);
   // The request's split count from kv_indptr and the chunk or piece
@@ -625,11 +630,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       n = a.chunk > 0 ? flat_splits(kb0, kb1, a.chunk) : 0;
       n = n < a.s ? n : a.s;
       if (n == 0) {
-        OutT* o = static_cast<OutT*>(a.o) + row * D;
+        OutT* o = static_cast<OutT*>(a.o) + row * D + d0;
 #pragma unroll
         for (int x = 0; x < DL; ++x)
-          if (lane + 64 * x < D) o[lane + 64 * x] = OutT(0.f);
-        if (a.lse && lane == 0) a.lse[row] = -INFINITY;
+          if (lane + 64 * x < DW) o[lane + 64 * x] = OutT(0.f);
+        if (a.lse && lane == 0 && d0 == 0) a.lse[row] = -INFINITY;
       }
     } else {
       n = a.chunk > 0 ? int((kb1 - kb0 + a.chunk - 1) / a.chunk) : 0;
@@ -648,7 +653,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     for (int j = 0; j < SB; ++j)
 #pragma unroll
       for (int x = 0; x < DL; ++x)
-        ov[j][x] = (j < n && lane + 64 * x < D) ? a.o_part[(int64_t(j) * rows + row) * D + lane + 64 * x] : 0.f;
+        ov[j][x] = (j < n && lane + 64 * x < DW) ? a.o_part[(int64_t(j) * rows + row) * D + d0 + lane + 64 * x] : 0.f;
   };
   int splits_b;
   if (a.uniform) {
@@ -700,23 +705,23 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     for (int off = 32; off >= 1; off >>= 1) ws += shfl_xor(ws, off);
     wsum += ws;
     const int n = splits_b - i0 < 64 ? splits_b - i0 : 64;
-    const float* op = a.o_part + (int64_t(i0) * rows + row) * D + lane;
+    const float* op = a.o_part + (int64_t(i0) * rows + row) * D + d0 + lane;
 #pragma unroll 4
     for (int j = 0; j < n; ++j) {
       const float wj = __shfl(wi, j, 64);
 #pragma unroll
       for (int x = 0; x < DL; ++x)
-        if (lane + 64 * x < D) acc[x] += wj * op[int64_t(j) * rows * D + 64 * x];
+        if (lane + 64 * x < DW) acc[x] += wj * op[int64_t(j) * rows * D + 64 * x];
     }
   }
   const float inv = 1.f / wsum;
-  OutT* o = static_cast<OutT*>(a.o) + row * D;
+  OutT* o = static_cast<OutT*>(a.o) + row * D + d0;
 #pragma unroll
   for (int x = 0; x < DL; ++x) {
     const int d = lane + 64 * x;
-    if (d < D) o[d] = OutT(acc[x] * inv);
+    if (d < DW) o[d] = OutT(acc[x] * inv);
   }
-  if (a.lse && lane == 0) a.lse[row] = M + flog2(wsum) * kLn2;
+  if (a.lse && lane == 0 && d0 == 0) a.lse[row] = M + flog2(wsum) * kLn2;
 }
 
 __global__ void split_ranges_kernel(const int32_t* kv_indptr, int B, int s, int chunk,
@@ -815,6 +820,32 @@ hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t 
   const int n = a.B * a.s;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(flat_ranges_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a, ranges);
+  return hipGetLastError();
+}
+
+// The decode merge for MLA's 512-wide latent outputs (chunk plan).
+hipError_t launch_decode_merge_dv(const MlaArgs& m, hipStream_t st) {
+  DecodeArgs a{};
+  a.kv_indptr = m.kv_indptr;
+  a.o = m.o;
+  a.lse = m.lse;
+  a.o_part = m.o_part;
+  a.m_part = m.m_part;
+  a.l_part = m.l_part;
+  a.B = m.B;
+  a.Hq = m.H;
+  a.D = 512;
+  a.s = m.s;
+  a.chunk = m.chunk;
+  a.dtype = m.dtype;
+  a.uniform = m.uniform;
+  // four waves (128 dims each) per row
+  const dim3 grid(unsigned(int64_t(a.B) * a.Hq));
+#define RATTN_MERGE(TT)                                                                       \
+  if (a.uniform) hipLaunchKernelGGL((decode_merge_kernel<512, TT, 16>), grid, dim3(256), 0, st, a); \
+  else hipLaunchKernelGGL((decode_merge_kernel<512, TT, 32>), grid, dim3(256), 0, st, a)
+  if (a.dtype == 1) { RATTN_MERGE(__bf16); } else { RATTN_MERGE(_Float16); }
+#undef RATTN_MERGE
   return hipGetLastError();
 }
 

@@ -36,6 +36,25 @@ struct DecodeArgs {
   int64_t total_kv = 0;
 };
 
+// Multi-head latent attention decode (absorbed form): q [B, H, 576]; kv
+// [total_kv, 576] (latent 512 + rotary 64 per token, shared by all heads);
+// o [B, H, 512]; chunk plan of the Split operator (s chunks of `chunk` keys).
+struct MlaArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* kv_indptr;
+  void* o;
+  float* lse;
+  float* o_part;  // [s, B*H, 512]
+  float* m_part;  // [s, B*H]
+  float* l_part;  // [s, B*H]
+  int B, H;
+  int s, chunk;
+  float scale_log2;
+  int dtype;
+  int uniform;
+};
+
 struct MergeArgs {
   const float* o_part;
   const float* m_part;
@@ -94,6 +113,8 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_flat(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st);
+hipError_t launch_decode_merge_dv(const MlaArgs& a, hipStream_t st);  // value width 512
 hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
                                hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);

@@ -1,0 +1,317 @@
+// mla.hip -- multi-head latent attention (MLA) decode on gfx950, absorbed form.
+//
+// The Cleave arXiv abstract lists MLA among the attention subgraphs the
+// method handles.  In its absorbed decode form every query head attends to
+// one shared cache row per token: a latent vector of Dc = 512 elements
+// followed by a rotary key part of Dr = 64, 576 elements in all.  The score
+// of head h against token j is scale * q_h . row_j over all 576 elements;
+// the output of head h is the softmax-weighted sum of the latent parts
+// (the first 512 elements) of the rows.  So K is the whole row and V is its
+// first 512 elements: the same bytes, read once for both.
+//
+// Decomposition: the Split operator cuts each request's keys into chunks of
+// c = ceil(max_kv_len / s) (Cleave article on tip.co.jp, "Split演算子による
+// Split-Kの対応"), one workgroup per (16 query heads, chunk, request); the
+// partials are merged with log-sum-exp weights by the decode merge kernel.
+// Inside a chunk, 32-key tiles of cache rows are staged in LDS and each tile
+// feeds the score, the online max/sum and the value update in one pass
+// ("複数リダクションのスケジューリング": iterative tiling, horizontal fusion).
+//
+// Workgroup = 8 waves, two per SIMD.  The scores of a 32-key tile for the
+// 16 heads (S^T = K Q^T on 16x16x32 MFMAs, K from LDS) are split eight
+// ways: wave w takes the 16 keys 16 * (w / 4) .. and a quarter of the 576
+// dims (5, 4, 5 or 4 slabs of 32), and the partial sums meet in LDS; every
+// wave then adds the same partials in the same order, runs the same online
+// softmax, and updates output dims 64w .. 64w + 63 (O^T += V^T P^T, V^T
+// from transposing LDS reads).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace rattn {
+
+constexpr int kMlaDc = 512, kMlaDr = 64, kMlaD = kMlaDc + kMlaDr;  // cache row: 576 elements
+constexpr int kMlaBK = 32;                      // keys per tile
+constexpr int kMlaChunks = kMlaD / 8;           // 16-byte chunks per cache row (72)
+constexpr int kMlaLdsRow = kMlaChunks + 1;      // LDS row: one pad chunk (rows 36 banks apart)
+constexpr int kMlaWaves = 8;
+constexpr int kMlaThreads = 64 * kMlaWaves;
+// A tile goes from HBM straight into an LDS stage: 64-lane x 16-byte load
+// instructions, each filling 1 KB of the stage (37 per tile, the last one
+// partly padding), four stages in a ring.
+constexpr int kMlaInstr = (kMlaBK * kMlaLdsRow + 63) / 64;  // 37
+constexpr int kMlaPerWave = (kMlaInstr + kMlaWaves - 1) / kMlaWaves;  // 5 (waves 0-4) or 4
+constexpr int kMlaStageBytes = kMlaInstr * 1024;
+constexpr int kMlaStage = kMlaStageBytes / 2;  // 16-bit elements per stage
+constexpr int kMlaStages = 4;
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
+// lgkmcnt fields at their no-wait maximum): two tiles of loads may stay in
+// flight (the waves that issue one load more per tile only wait a little
+// earlier)
+constexpr int kVmTwoTiles = 2 * (kMlaInstr / kMlaWaves);
+constexpr int kVmcntTwoTiles = 0x0F70 | (kVmTwoTiles & 15) | ((kVmTwoTiles >> 4) << 14);
+
+// Work unit of workgroup L of the 1-D grid.  Workgroups are dealt to the
+// eight XCDs round robin by linear index and each XCD has its own L2, so
+// the head groups of one (chunk, request) unit are given consecutive
+// indices on the same XCD: unit = 8 * (r / HG) + L % 8, head group r % HG,
+// r = L / 8.  Returns false for the padding past the last unit.
+__device__ __forceinline__ bool mla_unit(int L, int HG, int units, int& hg, int& unit) {
+  const int r = L >> 3;
+  hg = r % HG;
+  unit = (r / HG) * 8 + (L & 7);
+  return unit < units;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) at a byte offset from base: see
+// the lane layout at its use below.
+__device__ __forceinline__ u32x2 mla_tr_read(const uint16_t* base, int byte_off) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const char* p = reinterpret_cast<const char*>(base) + byte_off;
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+template <class T>
+__global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
+  typedef typename T::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kMlaStages * kMlaStage];
+  const int HG = (a.H + 15) / 16;
+  int hg, unit;
+  if (!mla_unit(blockIdx.x, HG, a.s * a.B, hg, unit)) return;
+  const int b = unit / a.s, i = unit % a.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, h4 = lane >> 4;
+  const int H = a.H;
+  const int64_t rows = int64_t(a.B) * H;
+  const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
+  const int n_b = int(kb1 - kb0);
+  const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
+  const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
+  const int64_t row0 = int64_t(b) * H + 16 * hg;  // this workgroup's first query head row
+  const int nh = H - 16 * hg < 16 ? H - 16 * hg : 16;  // heads in this group
+  const int splits_b = (n_b + a.chunk - 1) / a.chunk;
+  if (lo >= hi) {  // split unused by this request
+    if (i == 0) {  // empty request: O = 0, LSE = -inf
+      typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
+      for (int e = tid; e < nh * kMlaDc; e += kMlaThreads) o[e] = typename T::elem(0.f);
+      if (a.lse && tid < nh) a.lse[row0 + tid] = -INFINITY;
+    }
+    return;
+  }
+  const int n = hi - lo;
+  const int ntiles = (n + kMlaBK - 1) / kMlaBK;
+
+  // The wave's share of the scores: key tile kt = w / 4 (keys 16 kt ..
+  // 16 kt + 15 of each 32-key tile), slabs u0 .. u0 + ns - 1 of the 18
+  // (dims 32 u0 ..; quarters of 5, 4, 5, 4 slabs).  Q^T operand: head c16
+  // of the group (zero past the last head), slab u0 + u -> dims
+  // 32 (u0 + u) + 8 h4 .. +8.
+  constexpr int NS = 5;  // slabs of the larger quarters
+  const int kt = w >> 2, dq = w & 3;
+  const int u0 = 9 * (dq >> 1) + 5 * (dq & 1), ns = (dq & 1) ? 4 : 5;
+  u32x4 qb[NS];  // loaded at start-up, after tile 0's loads are issued
+  // partial score tiles of the eight waves: sx[w][lane] = lane's four
+  // scores (head c16, keys 16 kt + 4 h4 + r) over the wave's slabs
+  __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][64];
+
+  // Direct-to-LDS tile loads.  Instruction x (wave x % 8 issues it) fills
+  // stage chunks 64x .. 64x + 63; lane l's chunk q = 64x + l is row q / 73,
+  // slot q % 73 of the padded stage, fetched from chunk 72 * row + slot of
+  // the tile's rows; the pad slot 72 and chunks past the 32 rows fetch
+  // from an offset outside every resource and receive zeros.  The offsets
+  // are the same for every tile, so they are computed once.  A tile's
+  // resource ends at the chunk's last key: keys past it arrive as zeros
+  // (their scores are masked, and zero values add nothing); a tile wholly
+  // past it reads no memory.
+  const int nwi = __builtin_amdgcn_readfirstlane((kMlaInstr - w + kMlaWaves - 1) / kMlaWaves);
+  int voff[kMlaPerWave];
+#pragma unroll
+  for (int k = 0; k < kMlaPerWave; ++k) {
+    const int q = 64 * (w + kMlaWaves * k) + lane;
+    const int r = q / kMlaLdsRow, c = q % kMlaLdsRow;
+    voff[k] = (c < kMlaChunks && r < kMlaBK) ? (r * kMlaChunks + c) * 16 : 0x40000000;
+  }
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t cbase = uint64_t(size_t(static_cast<const uint16_t*>(a.kv) + (kb0 + lo) * kMlaD));
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)lds)) + w * 1024;
+  auto dma = [&](int tile) {
+    const int key0 = tile * kMlaBK;
+    int left = n - key0;
+    left = left < 0 ? 0 : (left > kMlaBK ? kMlaBK : left);
+    const uint64_t addr = cbase + uint64_t(uint32_t(key0)) * (2 * kMlaD);
+    const i32x4 rsv = {__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
+                       __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
+                       __builtin_amdgcn_readfirstlane(left * 2 * kMlaD), 0x00020000};
+    const uint32_t st = lds0 + uint32_t(tile % kMlaStages) * kMlaStageBytes;
+#pragma unroll
+    for (int k = 0; k < kMlaPerWave; ++k)
+      if (k < nwi)
+        __asm__ volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "buffer_load_dwordx4 %1, %2, 0 offen lds"
+            :
+            : "s"(__builtin_amdgcn_readfirstlane(st + k * 1024 * kMlaWaves)), "v"(voff[k]), "s"(rsv)
+            : "memory", "m0");
+  };
+
+  // running state of head c16: m (log2 units, same in the four h4 lanes),
+  // this lane's share of the sum, O^T accumulators of the wave's 64 dims:
+  // o[blk][r] = dim 64w + 16 blk + 4 h4 + r
+  constexpr int NB = kMlaDc / 16 / kMlaWaves;  // 16-dim blocks per wave (4)
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // transposing-read addresses (bytes, within a stage): lane q + 4e of its
+  // 16-lane group points at row k0 + e, dims dbase + 4q; the group h4 reads
+  // rows 4*h4 + e (keys of its P slots 0..3) and 16 + 4*h4 + e (slots 4..7)
+  const int tq = lane & 3, te = (lane >> 2) & 3;
+  const int tr0 = 2 * ((4 * h4 + te) * kMlaLdsRow * 8 + 16 * NB * w + 4 * tq);
+  const int tr1 = tr0 + 2 * 16 * kMlaLdsRow * 8;
+
+  // Step j: the load of tile j + 3 goes into the stage tile j - 1 used
+  // (free since the barrier that ended step j - 1), tile j is computed,
+  // and the step ends once tile j + 1 is in LDS: each wave waits for its
+  // own loads of it (at most two tiles of 9 loads may stay in flight;
+  // wave 0's tenth load only makes it wait a little earlier), then the
+  // barrier publishes them.  Tiles past the chunk are issued too (they
+  // read nothing), so the count of loads in flight never depends on the
+  // path.
+  auto step = [&](int j) {
+    dma(j + 3);
+    const uint16_t* cur = lds + (j % kMlaStages) * kMlaStage;
+    // this wave's partial S^T tile (16 keys x 16 heads: lane (c16, h4) gets
+    // head c16, keys 16 kt + 4 h4 + r), operands read from LDS in one batch
+    {
+      const uint16_t* kp = cur + ((16 * kt + c16) * kMlaLdsRow + 4 * u0 + h4) * 8;
+      u32x4 ka[NS];
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (u < ns) ka[u] = *reinterpret_cast<const u32x4*>(kp + 32 * u);
+      f32x4 sp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NS; ++u)
+        if (u < ns) sp = T::mfma16(as<vec8>(ka[u]), as<vec8>(qb[u]), sp);
+      sx[w][lane] = sp;
+    }
+    __syncthreads();
+    // the whole tile's scores, summed the same way in every wave
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      s[t] = (sx[4 * t][lane] + sx[4 * t + 1][lane]) + (sx[4 * t + 2][lane] + sx[4 * t + 3][lane]);
+    float x[8];
+    const int key0 = j * kMlaBK;
+    const bool tail = key0 + kMlaBK > n;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float y = s[t][r] * a.scale_log2;
+        if (tail && key0 + 16 * t + 4 * h4 + r >= n) y = -INFINITY;
+        x[4 * t + r] = y;
+      }
+    float mx = max3(x[0], x[1], max3(x[2], x[3], max3(x[4], x[5], fmaxf(x[6], x[7]))));
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    // every tile holds at least one valid key, so mx and m_new are finite
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fexp2(m - m_new);
+    m = m_new;
+    f32x8 p;
+    float psum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      p[k] = fexp2(x[k] - m_new);
+      psum += p[k];
+    }
+    l = l * alpha + psum;
+    const vec8 pb = T::cvt8(p);
+    u32x2 v0[NB], v1[NB];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      v0[blk] = mla_tr_read(cur, tr0 + 32 * blk);
+      v1[blk] = mla_tr_read(cur, tr1 + 32 * blk);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const u32x4 av = {v0[blk][0], v0[blk][1], v1[blk][0], v1[blk][1]};
+      o[blk] *= alpha;
+      o[blk] = T::mfma16(as<vec8>(av), pb, o[blk]);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcntTwoTiles);  // tile j + 1 has arrived
+    __syncthreads();
+  };
+  // Start-up: tile 0 and the query operand come in together (the wait
+  // for the query below also covers tile 0, issued before it), then
+  // tiles 1 and 2 are issued.
+  dma(0);
+  {
+    const bool ok = c16 < nh;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row0 + (ok ? c16 : 0)) * kMlaD +
+                         32 * u0 + 8 * h4;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      qb[u] = (ok && u < ns) ? ldg128(qp + 32 * u) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // consume the loads now: the tile loads below are invisible to the
+    // compiler's wait counting, so no later wait may be left to it
+#pragma unroll
+    for (int u = 0; u < NS; ++u) __asm__ volatile("" ::"v"(qb[u]));
+  }
+  dma(1);
+  dma(2);
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) step(j);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the workgroup
+
+  // head sums over the four h4 lanes; lane (c16, h4) writes dims
+  // 64w + 16blk + 4h4 .. +4 of head c16
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (c16 >= nh) return;
+  const int64_t row = row0 + c16;
+  const float inv = 1.f / l;
+  if (splits_b == 1) {
+    typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 16 * NB * w + 4 * h4;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x8 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[r] = o[blk][r] * inv;
+        y[4 + r] = 0.f;
+      }
+      const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+      *reinterpret_cast<u32x2*>(orow + 16 * blk) = u32x2{bits[0], bits[1]};
+    }
+    if (a.lse && w == 0 && h4 == 0) a.lse[row] = (m + flog2(l)) * kLn2;
+  } else {
+    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) *reinterpret_cast<f32x4*>(prow + 16 * blk) = o[blk] * inv;
+    if (w == 0 && h4 == 0) {
+      a.m_part[int64_t(i) * rows + row] = m * kLn2;
+      a.l_part[int64_t(i) * rows + row] = l;
+    }
+  }
+}
+
+template <class T>
+static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
+  const int HG = (a.H + 15) / 16;
+  const int64_t units = int64_t(a.s) * a.B;
+  const int64_t nwg = 8 * HG * ((units + 7) / 8);
+  hipLaunchKernelGGL((mla_decode_kernel<T>), dim3(unsigned(nwg)), dim3(kMlaThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.s == 1) return e;
+  return launch_decode_merge_dv(a, st);
+}
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
+  return a.dtype == 1 ? launch_mla_t<BF16>(a, st) : launch_mla_t<F16>(a, st);
+}
+
+}  // namespace rattn

@@ -120,7 +120,7 @@ def sparse_mask(L: int, g: torch.Generator, window: int = 256, block: int = 64,
 @dataclass
 class Workload:
     name: str
-    kind: str            # "decode", "prefill", "append", "bsr"
+    kind: str            # "decode", "prefill", "append", "bsr", "mla"
     seed: int
     dtype: torch.dtype
     B: int
@@ -137,7 +137,7 @@ class Workload:
 
     @property
     def scale(self) -> float:
-        return 1.0 / math.sqrt(self.D)
+        return 1.0 / math.sqrt(self.extra.get("scale_dim", self.D))
 
     def make(self, device="cpu"):
         """Draw this workload's inputs (deterministic for its seed and device)."""
@@ -157,6 +157,14 @@ class Workload:
             k = rn((total, self.Hkv, self.D))
             v = rn((total, self.Hkv, self.D))
             return dict(q=q, k=k, v=v, kv_indptr=indptr(lengths).to(device), lengths=lengths)
+        if self.kind == "mla":
+            # one cache row per token shared by every head: D elements, the
+            # first extra["dv"] of which are the values
+            lengths = (loguniform_lengths(self.B, *self.ragged, g_shape) if self.ragged
+                       else [self.L] * self.B)
+            q = rn((self.B, self.Hq, self.D))
+            kv = rn((sum(lengths), 1, self.D))
+            return dict(q=q, kv=kv, kv_indptr=indptr(lengths).to(device), lengths=lengths)
         if self.kind == "prefill":
             q = rn((self.B * self.L, self.Hq, self.D))
             k = rn((self.B * self.L, self.Hkv, self.D))
@@ -203,6 +211,15 @@ WORKLOADS = {
     # append / chunked prefill: 128 new tokens per request against a 16k history
     "append_prefill_bf16": Workload("append_prefill_bf16", "append", 6, torch.bfloat16, B=4,
                                     Hq=32, Hkv=8, D=128, L=16384, Lq=128, causal=True),
+    # MLA decode, absorbed form: DeepSeek-V3-like latent 512 + rotary 64 per
+    # cached token, 16 query heads (its 128 heads over 8 tensor-parallel
+    # shards), softmax scale of the 192-wide un-absorbed query-key head
+    "mla_decode_bf16": Workload("mla_decode_bf16", "mla", 8, torch.bfloat16, B=32, Hq=16,
+                                Hkv=1, D=576, L=4096, extra=dict(dv=512, scale_dim=192)),
+    # the same with all 128 heads on one device and ragged serving-like lengths
+    "mla_ragged_decode_bf16": Workload("mla_ragged_decode_bf16", "mla", 9, torch.bfloat16, B=32,
+                                       Hq=128, Hkv=1, D=576, ragged=(128, 16384),
+                                       extra=dict(dv=512, scale_dim=192)),
 }
 
 

@@ -142,6 +142,41 @@ def test_flat_validation(lib, kw, status):
     assert lib.attn_debug_flat_ranges(P, 2, 10, 20, 0, P, None) == 1
 
 
+def test_mla_host_rules(lib):
+    for B, H, s in [(32, 16, 16), (1, 128, 3)]:
+        raw = s * B * H * (512 + 2) * 4
+        assert lib.attn_mla_decode_workspace_bytes(B, H, s) == (raw + 255) // 256 * 256
+    assert lib.attn_mla_decode_workspace_bytes(1, 16, 0) == 0
+    # 32 x 4096 tokens, one 16-head group: c = 512 gives 256 workgroups (one per CU)
+    assert lib.attn_mla_decode_choose_splits(32, 16, 32 * 4096, 4096) == 8
+    # 128 heads: eight groups, c = 4096 already gives 8 * 32 = 256 workgroups
+    assert lib.attn_mla_decode_choose_splits(32, 128, 32 * 4096, 4096) == 1
+    # ragged: 100000 keys, longest 16000, 128 heads: c = 2048 gives
+    # 8 * (49 + 16) >= 512 workgroups; s = ceil(16000 / 2048) = 8, made odd
+    assert lib.attn_mla_decode_choose_splits(32, 128, 100000, 16000) == 9
+    assert lib.attn_mla_decode_choose_splits(4, 16, 400, 100) == 1
+
+
+def mla_call(lib, **kw):
+    a = dict(q=P, kv=P, kvp=P, o=P, lse=None, B=2, H=16, Dc=512, Dr=64, maxlen=100, total=150,
+             scale=0.1, s=2, dt=1, ws=P, wsb=1 << 20, st=None)
+    a.update(kw)
+    return lib.attn_mla_decode(a["q"], a["kv"], a["kvp"], a["o"], a["lse"], a["B"], a["H"],
+                               a["Dc"], a["Dr"], a["maxlen"], a["total"], a["scale"], a["s"],
+                               a["dt"], a["ws"], a["wsb"], a["st"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(kv=None), 1), (dict(o=None), 1), (dict(B=0), 1), (dict(H=0), 1),
+    (dict(Dc=256), 2), (dict(Dr=0), 2), (dict(dt=0), 2), (dict(maxlen=-1), 1),
+    (dict(maxlen=200, total=150), 1), (dict(scale=float("nan")), 1), (dict(s=257), 1),
+    (dict(ws=None), 3), (dict(wsb=100), 3), (dict(kv=ctypes.c_void_p(20)), 1),
+])
+def test_mla_validation(lib, kw, status):
+    assert mla_call(lib, **kw) == status
+    assert lib.attn_last_error().decode() != ""
+
+
 def prefill_call(lib, **kw):
     a = dict(q=P, k=P, v=P, qo=P, kv=P, o=P, lse=None, B=2, Hq=8, Hkv=2, D=128, mq=64, mk=64,
              scale=0.1, causal=1, dt=1, st=None)

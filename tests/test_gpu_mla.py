@@ -1,0 +1,107 @@
+"""GPU parity of multi-head latent attention decode (absorbed form) against
+the fp64 oracle: keys are the whole 576-element cache rows, values their
+first 512 elements (oracle.attention with a narrower V)."""
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, TOL_O, check
+
+pytestmark = pytest.mark.gpu
+
+DC, DR = 512, 64
+
+
+def ra():
+    import reduction_attention_amd
+    return reduction_attention_amd
+
+
+def oracle_mla(q, kv, kv_indptr, scale, rows=None):
+    B = q.shape[0]
+    kv3 = kv.view(kv.shape[0], 1, DC + DR)
+    return oracle.attention(q, kv3, kv3[:, :, :DC].contiguous(), list(range(B + 1)), kv_indptr,
+                            scale, rows=rows)
+
+
+def mla_inputs(lengths, H, dtype, seed):
+    g = synth.gen(seed)
+    q = synth.randn((len(lengths), H, DC + DR), dtype, g)
+    kv = synth.randn((sum(lengths), DC + DR), dtype, g)
+    return q, kv, synth.indptr(lengths)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("H", [1, 16, 20, 128])
+def test_mla_small_ragged(dtype, H):
+    """Ragged lengths (tails inside a tile, an empty request), head counts
+    that fill, split and pad the 16-head groups."""
+    lengths = [1, 31, 32, 33, 0, 300, 64, 517]
+    q, kv, kvp = mla_inputs(lengths, H, dtype, seed=H)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    for s in (0, 1, 3, 8, 40):
+        o, lse = ra().attn_mla_decode(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                      num_splits=s)
+        torch.cuda.synchronize()
+        check(f"mla {dtype} H={H} s={s}", o, o_ref, lse, lse_ref, dtype)
+    assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[4]).all())
+
+
+def test_mla_workload_full_parity():
+    """32 requests x 4096 cached tokens, 16 heads, bf16: every row."""
+    w = synth.workload("mla_decode_bf16")
+    inp = w.make(DEV)
+    s = ra().attn_mla_decode_choose_splits(w.B, w.Hq, w.B * w.L, w.L)
+    print(f"mla automatic s={s}", flush=True)
+    o_ref, lse_ref = oracle_mla(inp["q"], inp["kv"], inp["kv_indptr"], w.scale)
+    for ns in (0, 1):
+        o, lse = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], w.L, w.scale,
+                                      num_splits=ns)
+        torch.cuda.synchronize()
+        check(f"mla workload s={ns or s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+def test_mla_ragged_128_heads_sampled():
+    """128 heads on one device, ragged lengths in [128, 16384]: a seeded
+    sample of rows (first and last head of every request included)."""
+    w = synth.workload("mla_ragged_decode_bf16")
+    inp = w.make(DEV)
+    L = inp["lengths"]
+    g = synth.gen(99)
+    pick = [(b, h) for b in range(w.B) for h in (0, w.Hq - 1)]
+    pick += [(int(b), int(h)) for b, h in zip(torch.randint(0, w.B, (448,), generator=g),
+                                              torch.randint(0, w.Hq, (448,), generator=g))]
+    rows = torch.tensor(pick, dtype=torch.int64)
+    o_ref, lse_ref = oracle_mla(inp["q"], inp["kv"], inp["kv_indptr"], w.scale, rows=rows)
+    o, lse = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], max(L), w.scale)
+    torch.cuda.synchronize()
+    oc, lc = o.cpu(), lse.cpu()
+    check("mla ragged 128 heads (sampled)", oc[rows[:, 0], rows[:, 1]], o_ref,
+          lc[rows[:, 0], rows[:, 1]], lse_ref, torch.bfloat16)
+    assert bool(torch.isfinite(o).all())
+
+
+def test_mla_equal_scores_give_mean_of_latents():
+    """Zero queries score every key equally: O is the mean of the latent
+    parts and LSE = ln(n)."""
+    lengths = [200, 1000]
+    q, kv, kvp = mla_inputs(lengths, 16, torch.bfloat16, seed=5)
+    q0 = torch.zeros_like(q)
+    o, lse = ra().attn_mla_decode(q0.to(DEV), kv.to(DEV), kvp.to(DEV), 1000, 0.1, num_splits=4)
+    torch.cuda.synchronize()
+    for b, (lo, hi) in enumerate([(0, 200), (200, 1200)]):
+        want = kv[lo:hi, :DC].double().mean(0)
+        assert (o[b].double().cpu() - want).abs().max().item() <= TOL_O[torch.bfloat16]
+        ln_n = torch.log(torch.tensor(float(hi - lo), dtype=torch.float64))
+        assert (lse[b].double().cpu() - ln_n).abs().max().item() <= 1e-4
+
+
+def test_mla_bit_identical_reruns():
+    w = synth.workload("mla_decode_bf16")
+    inp = w.make(DEV)
+    a = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], w.L, w.scale)
+    b = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], w.L, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
