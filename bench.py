@@ -53,6 +53,8 @@ def parse():
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-also", action="store_true", help="skip the secondary workloads")
+    p.add_argument("--warm-seconds", type=float, default=0.3,
+                   help="untimed run time of each workload before its timed steps (GPU clock warm-up)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_partial_traffic.json"))
@@ -60,23 +62,34 @@ def parse():
 
 
 class Timer:
-    """HIP events recorded on the stream the library launches on."""
+    """HIP events recorded on the stream the library launches on.
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream = torch, stream
+    Before the timed steps: the W warm-up steps, then more untimed steps of
+    the same work until ``warm_s`` seconds have passed, so that the GPU has
+    reached its working clock (a few milliseconds of steps do not; a fresh
+    process measured the causal prefill 10% slower without this)."""
+
+    def __init__(self, torch, stream, warm_s=0.3):
+        self.torch, self.stream, self.warm_s = torch, stream, warm_s
 
     def run(self, fn, steps, warmup):
         torch = self.torch
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
+        t0, i = time.perf_counter(), warmup
+        while time.perf_counter() - t0 < self.warm_s:
+            for _ in range(8):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         t0 = time.perf_counter()
-        for i in range(steps):
-            ev[i][0].record(self.stream)
-            fn(warmup + i)
-            ev[i][1].record(self.stream)
+        for k in range(steps):
+            ev[k][0].record(self.stream)
+            fn(i + k)
+            ev[k][1].record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         ms = [a.elapsed_time(b) for a, b in ev]
@@ -361,7 +374,7 @@ def main():
     import synth
     ra._lib.load()
     stream = torch.cuda.current_stream()
-    timer = Timer(torch, stream)
+    timer = Timer(torch, stream, args.warm_seconds)
     log(f"device: {torch.cuda.get_device_name(0)}, CUs: {ra.attn_device_cu_count()}")
 
     if args.only:
