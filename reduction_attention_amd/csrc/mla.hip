@@ -17,13 +17,14 @@
 // feeds the score, the online max/sum and the value update in one pass
 // ("複数リダクションのスケジューリング": iterative tiling, horizontal fusion).
 //
-// Workgroup = 8 waves, two per SIMD.  The scores of a 32-key tile for the
-// 16 heads (S^T = K Q^T on 16x16x32 MFMAs, K from LDS) are split eight
-// ways: wave w takes the 16 keys 16 * (w / 4) .. and a quarter of the 576
-// dims (5, 4, 5 or 4 slabs of 32), and the partial sums meet in LDS; every
-// wave then adds the same partials in the same order, runs the same online
-// softmax, and updates output dims 64w .. 64w + 63 (O^T += V^T P^T, V^T
-// from transposing LDS reads).
+// Workgroup = W waves (4 by default; two workgroups share a compute unit,
+// so one's barriers and LDS latencies overlap the other's work).  The
+// scores of a 32-key tile for the 16 heads (S^T = K Q^T on 16x16x32 MFMAs,
+// K from LDS) are split W ways: wave w takes the 16 keys 16 * (w / (W/2))
+// .. and a 1 / (W/2) share of the 576 dims, and the partial sums meet in
+// LDS; every wave then adds the same partials in the same order, runs the
+// same online softmax, and updates its 512 / W output dims (O^T += V^T
+// P^T, V^T from transposing LDS reads).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -33,22 +34,29 @@ constexpr int kMlaDc = 512, kMlaDr = 64, kMlaD = kMlaDc + kMlaDr;  // cache row:
 constexpr int kMlaBK = 32;                      // keys per tile
 constexpr int kMlaChunks = kMlaD / 8;           // 16-byte chunks per cache row (72)
 constexpr int kMlaLdsRow = kMlaChunks + 1;      // LDS row: one pad chunk (rows 36 banks apart)
-constexpr int kMlaWaves = 8;
+#ifndef RATTN_MLA_WAVES
+#define RATTN_MLA_WAVES 4
+#endif
+#ifndef RATTN_MLA_STAGES
+#define RATTN_MLA_STAGES 2
+#endif
+constexpr int kMlaWaves = RATTN_MLA_WAVES;
 constexpr int kMlaThreads = 64 * kMlaWaves;
 // A tile goes from HBM straight into an LDS stage: 64-lane x 16-byte load
 // instructions, each filling 1 KB of the stage (37 per tile, the last one
-// partly padding), four stages in a ring.
+// partly padding), kMlaStages stages in a ring (2 by default: 80 KB with
+// the score exchange, two workgroups per compute unit).
 constexpr int kMlaInstr = (kMlaBK * kMlaLdsRow + 63) / 64;  // 37
-constexpr int kMlaPerWave = (kMlaInstr + kMlaWaves - 1) / kMlaWaves;  // 5 (waves 0-4) or 4
+constexpr int kMlaPerWave = (kMlaInstr + kMlaWaves - 1) / kMlaWaves;  // loads per wave and tile (at most)
 constexpr int kMlaStageBytes = kMlaInstr * 1024;
 constexpr int kMlaStage = kMlaStageBytes / 2;  // 16-bit elements per stage
-constexpr int kMlaStages = 4;
+constexpr int kMlaStages = RATTN_MLA_STAGES;
 // s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
-// lgkmcnt fields at their no-wait maximum): two tiles of loads may stay in
-// flight (the waves that issue one load more per tile only wait a little
-// earlier)
-constexpr int kVmTwoTiles = 2 * (kMlaInstr / kMlaWaves);
-constexpr int kVmcntTwoTiles = 0x0F70 | (kVmTwoTiles & 15) | ((kVmTwoTiles >> 4) << 14);
+// lgkmcnt fields at their no-wait maximum) that lets the loads of all
+// stages but two stay in flight: the tile the next step reads has arrived
+// (waves that issue one load more per tile only wait a little earlier)
+constexpr int kVmAhead = (kMlaStages - 2) * (kMlaInstr / kMlaWaves);
+constexpr int kVmcntNext = 0x0F70 | (kVmAhead & 15) | ((kVmAhead >> 4) << 14);
 
 // Work unit of workgroup L of the 1-D grid.  Workgroups are dealt to the
 // eight XCDs round robin by linear index and each XCD has its own L2, so
@@ -72,7 +80,7 @@ __device__ __forceinline__ u32x2 mla_tr_read(const uint16_t* base, int byte_off)
 }
 
 template <class T>
-__global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
+__global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kMlaStages * kMlaStage];
   const int HG = (a.H + 15) / 16;
@@ -102,16 +110,17 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
   const int n = hi - lo;
   const int ntiles = (n + kMlaBK - 1) / kMlaBK;
 
-  // The wave's share of the scores: key tile kt = w / 4 (keys 16 kt ..
+  // The wave's share of the scores: key tile kt = w / (W/2) (keys 16 kt ..
   // 16 kt + 15 of each 32-key tile), slabs u0 .. u0 + ns - 1 of the 18
-  // (dims 32 u0 ..; quarters of 5, 4, 5, 4 slabs).  Q^T operand: head c16
-  // of the group (zero past the last head), slab u0 + u -> dims
-  // 32 (u0 + u) + 8 h4 .. +8.
-  constexpr int NS = 5;  // slabs of the larger quarters
-  const int kt = w >> 2, dq = w & 3;
-  const int u0 = 9 * (dq >> 1) + 5 * (dq & 1), ns = (dq & 1) ? 4 : 5;
+  // (dims 32 u0 ..; W = 4: halves of 9 slabs, W = 8: 4, 5, 4, 5).  Q^T
+  // operand: head c16 of the group (zero past the last head), slab u0 + u
+  // -> dims 32 (u0 + u) + 8 h4 .. +8.
+  constexpr int DQ = kMlaWaves / 2;             // parts of the dims
+  constexpr int NS = (kMlaD / 32 + DQ - 1) / DQ;  // slabs of the larger parts
+  const int kt = w / DQ, dq = w % DQ;
+  const int u0 = (kMlaD / 32) * dq / DQ, ns = (kMlaD / 32) * (dq + 1) / DQ - u0;
   u32x4 qb[NS];  // loaded at start-up, after tile 0's loads are issued
-  // partial score tiles of the eight waves: sx[w][lane] = lane's four
+  // partial score tiles of the waves: sx[w][lane] = lane's four
   // scores (head c16, keys 16 kt + 4 h4 + r) over the wave's slabs
   __shared__ __attribute__((aligned(16))) f32x4 sx[kMlaWaves][64];
 
@@ -156,9 +165,9 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
   };
 
   // running state of head c16: m (log2 units, same in the four h4 lanes),
-  // this lane's share of the sum, O^T accumulators of the wave's 64 dims:
-  // o[blk][r] = dim 64w + 16 blk + 4 h4 + r
-  constexpr int NB = kMlaDc / 16 / kMlaWaves;  // 16-dim blocks per wave (4)
+  // this lane's share of the sum, O^T accumulators of the wave's 512 / W
+  // dims: o[blk][r] = dim (512 / W) w + 16 blk + 4 h4 + r
+  constexpr int NB = kMlaDc / 16 / kMlaWaves;  // 16-dim blocks per wave
   float m = -INFINITY, l = 0.f;
   f32x4 o[NB];
 #pragma unroll
@@ -171,16 +180,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
   const int tr0 = 2 * ((4 * h4 + te) * kMlaLdsRow * 8 + 16 * NB * w + 4 * tq);
   const int tr1 = tr0 + 2 * 16 * kMlaLdsRow * 8;
 
-  // Step j: the load of tile j + 3 goes into the stage tile j - 1 used
-  // (free since the barrier that ended step j - 1), tile j is computed,
-  // and the step ends once tile j + 1 is in LDS: each wave waits for its
-  // own loads of it (at most two tiles of 9 loads may stay in flight;
-  // wave 0's tenth load only makes it wait a little earlier), then the
-  // barrier publishes them.  Tiles past the chunk are issued too (they
+  // Step j: the load of tile j + S - 1 (S stages) goes into the stage tile
+  // j - 1 used (free since the barrier that ended step j - 1), tile j is
+  // computed, and the step ends once tile j + 1 is in LDS: each wave waits
+  // for its own loads of it, then the barrier publishes them.  Tiles past the chunk are issued too (they
   // read nothing), so the count of loads in flight never depends on the
   // path.
   auto step = [&](int j) {
-    dma(j + 3);
+    dma(j + kMlaStages - 1);
     const uint16_t* cur = lds + (j % kMlaStages) * kMlaStage;
     // this wave's partial S^T tile (16 keys x 16 heads: lane (c16, h4) gets
     // head c16, keys 16 kt + 4 h4 + r), operands read from LDS in one batch
@@ -200,8 +207,11 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
     // the whole tile's scores, summed the same way in every wave
     f32x4 s[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      s[t] = (sx[4 * t][lane] + sx[4 * t + 1][lane]) + (sx[4 * t + 2][lane] + sx[4 * t + 3][lane]);
+    for (int t = 0; t < 2; ++t) {
+      s[t] = sx[DQ * t][lane];
+#pragma unroll
+      for (int q = 1; q < DQ; ++q) s[t] += sx[DQ * t + q][lane];
+    }
     float x[8];
     const int key0 = j * kMlaBK;
     const bool tail = key0 + kMlaBK > n;
@@ -241,12 +251,12 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
       o[blk] *= alpha;
       o[blk] = T::mfma16(as<vec8>(av), pb, o[blk]);
     }
-    __builtin_amdgcn_s_waitcnt(kVmcntTwoTiles);  // tile j + 1 has arrived
+    __builtin_amdgcn_s_waitcnt(kVmcntNext);  // tile j + 1 has arrived
     __syncthreads();
   };
   // Start-up: tile 0 and the query operand come in together (the wait
-  // for the query below also covers tile 0, issued before it), then
-  // tiles 1 and 2 are issued.
+  // for the query below also covers tile 0, issued before it), then the
+  // tiles of the other stages but one are issued.
   dma(0);
   {
     const bool ok = c16 < nh;
@@ -261,14 +271,14 @@ __global__ __launch_bounds__(kMlaThreads, 1) void mla_decode_kernel(MlaArgs a) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) __asm__ volatile("" ::"v"(qb[u]));
   }
-  dma(1);
-  dma(2);
+#pragma unroll
+  for (int t = 1; t < kMlaStages - 1; ++t) dma(t);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) step(j);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the workgroup
 
   // head sums over the four h4 lanes; lane (c16, h4) writes dims
-  // 64w + 16blk + 4h4 .. +4 of head c16
+  // (512 / W) w + 16blk + 4h4 .. +4 of head c16
   l += shfl_xor(l, 16);
   l += shfl_xor(l, 32);
   if (c16 >= nh) return;
