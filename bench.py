@@ -150,6 +150,27 @@ def bench_decode(torch, ra, synth, wname, args, timer, rotate=3):
                                 stream=stream)
 
     ms_k, _ = timer.run(partials, args.steps, args.warmup)
+    # the same step captured ten at a time in a HIP graph (one graph per
+    # K/V copy order), as a serving loop would launch it: per-step time
+    graph_ms = None
+    if rotate > 1:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graphs = []
+        with torch.cuda.stream(side):
+            for c in range(rotate):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for t in range(10):
+                        k, v = sets[(c + t) % rotate]
+                        ra.attn_decode_splitkv(q, k, v, kvp, max_len, num_splits=s, o=o, lse=lse,
+                                               workspace=ws, stream=torch.cuda.current_stream())
+                graphs.append(g)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        ms_g, _ = timer.run(lambda i: graphs[i % rotate].replay(), max(args.steps // 10, 3),
+                            max(args.warmup // 10, 1))
+        graph_ms = median(ms_g) / 10
     elem = q.element_size()
     kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, total, elem)
     step_ms = median(ms)
@@ -162,7 +183,7 @@ def bench_decode(torch, ra, synth, wname, args, timer, rotate=3):
                 step_ms_p90=sorted(ms)[(9 * len(ms)) // 10], step_bytes=step_bytes,
                 kv_bytes=kvb, gbs=step_bytes / step_ms / 1e6, kernel_ms=kernel_ms,
                 kernel_bytes=kernel_bytes, kernel_gbs=kernel_bytes / kernel_ms / 1e6,
-                wall_s=wall, kv_copies_rotated=rotate)
+                wall_s=wall, kv_copies_rotated=rotate, graph_step_ms=graph_ms)
 
 
 def bench_decode_flat(torch, ra, synth, wname, args, timer):
@@ -431,6 +452,12 @@ def main():
         "roofline": roofline,
         "frac_of_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
     }
+    if d["graph_step_ms"]:
+        gb = d["step_bytes"] / d["graph_step_ms"] / 1e6
+        out["graph_replay"] = dict(ms_per_step=round(d["graph_step_ms"], 5), gbs=round(gb, 1),
+                                   frac=round(gb / HBM_PEAK_GBS, 4),
+                                   note="the same step, ten per HIP graph replay")
+        log(f"decode in HIP graphs: {d['graph_step_ms']*1e3:.1f} us/step, {gb:.0f} GB/s")
     if not args.no_also:
         also = {}
         p = bench_prefill(torch, ra, synth, args, timer)
