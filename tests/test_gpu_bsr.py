@@ -59,6 +59,35 @@ def test_small_masks(dtype, D, kind):
     check(f"bsr {dtype} D={D} {kind}", o, o_ref, lse, lse_ref, dtype)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("D", [64, 128])
+def test_part_tiles_by_quadrant(dtype, D):
+    """Part tiles whose valid elements sit in chosen 32x32 quadrants: every
+    subset of the four (query half, key half) quadrants occurs once, so each
+    wave meets tiles where both, one or neither of its 32-key halves hold a
+    valid element."""
+    L, B, Hq, Hkv = 256, 2, 4, 2
+    g = synth.gen(41)
+    dense = torch.zeros(L, L, dtype=torch.uint8)
+    for qb in range(4):
+        for kb in range(4):
+            combo = 4 * qb + kb
+            for quad in range(4):
+                if not (combo >> quad) & 1:
+                    continue
+                w, kh = quad >> 1, quad & 1
+                r0, c0 = 64 * qb + 32 * w, 64 * kb + 32 * kh
+                bits = (torch.rand(32, 32, generator=g) < 0.3).to(torch.uint8)
+                bits[int(torch.randint(0, 32, (1,), generator=g))][
+                    int(torch.randint(0, 32, (1,), generator=g))] = 1
+                dense[r0:r0 + 32, c0:c0 + 32] = bits
+    q, k, v = qkv(B, L, Hq, Hkv, D, dtype, 43 + D)
+    o_ref, lse_ref = oracle_bsr(q, k, v, dense, 1 / D ** 0.5)
+    o, lse, m = bsr(q, k, v, dense)
+    assert m.nnz_full == 0 and m.nnz_part == 15
+    check(f"bsr quadrants {dtype} D={D}", o, o_ref, lse, lse_ref, dtype)
+
+
 def test_workload_sampled():
     """B 1, L 4096, 16 heads, D 64, fp16; window 256 + 2 globals/64 + 6 random blocks."""
     w = synth.workload("bsr_prefill_fp16")
