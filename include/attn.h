@@ -202,11 +202,14 @@ attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void*
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
 
 /* The split count attn_mla_decode picks when num_splits = 0: s = ceil(max_kv_len
- * / c) with c the largest power of two >= 256 keys such that ceil(H / 16) *
- * chunks reaches one workgroup per compute unit for equal lengths (chunks =
- * B * ceil(max_kv_len / c)), two otherwise (chunks = total_kv / c + B / 2,
- * and s made odd so that the splits of the requests spread over the eight
- * XCDs); within [1, 256].  Fitted to sweeps on MI355X. */
+ * / c) with c the largest power of two >= 256 keys such that hg * chunks
+ * reaches one workgroup per compute unit for equal lengths (chunks =
+ * B * ceil(max_kv_len / c)); for ragged lengths (chunks = total_kv / c +
+ * B / 2, and s made odd so that the splits of the requests spread over the
+ * eight XCDs) two per compute unit with 16-head workgroups, one per two
+ * compute units with 64-head ones.  hg = H / 64 when H is a multiple of 64
+ * (the many-head kernel), else ceil(H / 16).  Within [1, 256].  Fitted to
+ * sweeps on MI355X. */
 int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len);
 
 /*
@@ -234,8 +237,12 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
  * workspace   at least attn_mla_decode_workspace_bytes(B, H, s) bytes when
  *   s > 1; layout o_part [s, B*H, 512], m_part [s, B*H], l_part [s, B*H] fp32.
  *   Calls that share one workspace must not overlap in time.
- * A request with no key yields O = 0, LSE = -inf.  One workgroup serves 16
- * heads; any H >= 1 is accepted.  Supported: ATTN_BF16, ATTN_F16.
+ * A request with no key yields O = 0, LSE = -inf.  A workgroup serves 64
+ * heads when H is a multiple of 64, else 16; any H >= 1 is accepted.  The
+ * 64-head kernel weighs a chunk's keys against the row max of its first
+ * 32 keys and, should a later key's weight exceed 2^64 (2^15 for
+ * ATTN_F16), reduces the chunk a second time against its true row max, so
+ * results do not depend on the path.  Supported: ATTN_BF16, ATTN_F16.
  */
 attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_indptr, void* o,
                               float* lse, int B, int H, int Dc, int Dr, int max_kv_len,

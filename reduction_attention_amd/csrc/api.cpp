@@ -218,21 +218,25 @@ size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
 
 int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len) {
   if (B <= 0 || H <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
-  // Workgroups of 16 heads over one chunk, one per compute unit at a time.
+  // Workgroups of 16 heads (64 for the many-head kernel) over one chunk.
   // Equal lengths: the largest power-of-two chunk >= 256 keys that gives
   // every compute unit a workgroup.  Ragged: chunks counted as total/c +
-  // B/2, two workgroups per compute unit, and an odd s: workgroups are
-  // dealt to the eight XCDs round robin, and with s a multiple of eight the
-  // first splits (present in every request) would all land on the same
-  // XCDs while the last ones (mostly empty) land on the others.
+  // B/2, two 16-head workgroups per compute unit; many-head workgroups
+  // for half the units (their partials are 2 KB per head, so more,
+  // shorter chunks cost more in the merge than they gain in balance); and
+  // an odd s: workgroups are dealt to the eight XCDs round robin, and with
+  // s a multiple of eight the first splits (present in every request)
+  // would all land on the same XCDs while the last ones (mostly empty)
+  // land on the others.
   const long long cus = attn_device_cu_count();
-  const long long hg = (H + 15) / 16;
+  const bool wide = rattn::mla_wide(H);
+  const long long hg = wide ? H / 64 : (H + 15) / 16;
   const bool uniform = (long long)max_kv_len * B == total_kv;
   long long c = 1;
   while (c < max_kv_len) c <<= 1;
   while (c > 256) {
     const long long chunks = uniform ? B * ((max_kv_len + c - 1) / c) : (total_kv + c - 1) / c + B / 2;
-    if (hg * chunks >= (uniform ? 1 : 2) * cus) break;
+    if (2 * hg * chunks >= (uniform ? 2 : wide ? 1 : 4) * cus) break;
     c >>= 1;
   }
   long long s = (max_kv_len + c - 1) / c;

@@ -309,12 +309,303 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Many heads (H a multiple of 64): the heads are the rows of the score
+// matrix, so the tile feeds 32x32x16 MFMAs with K and V from LDS as in
+// prefill.  Workgroup = 4 waves over 64 heads of one (chunk, request):
+// wave w takes head block hb = w / 2 (32 heads) and half dh = w % 2, i.e.
+// the dims 288 dh .. 288 dh + 287 of the score contraction and the output
+// dims 256 dh .. 256 dh + 255.  The two waves of a head block add their
+// partial scores through LDS (a + b = b + a exactly, so both hold the same
+// scores) and run the same softmax.
+//
+// Softmax reference: the row max of the chunk's first tile, kept for the
+// whole chunk, so the value accumulators (in AGPRs) are never rescaled.  A
+// later weight above 2^64 (2^15 for fp16 operands) sets a flag; the
+// workgroup then runs the chunk again against the chunk's true row max
+// (found on the first pass), which no score exceeds.  Keys far below the reference only lose
+// weights that are negligible against the reference key's weight of 1.
+//
+// LDS: three stages of 32 cache rows in natural layout, 72 chunks of 16
+// bytes per row with the chunk index XOR-ed by f(row) = 2 (row % 4) +
+// (row / 4) % 2, so that both the 16-byte K reads (eight consecutive rows,
+// one chunk) and the transposing V reads (four consecutive rows, two
+// chunks) hit distinct banks; plus the score exchange (16 KB).
+// ---------------------------------------------------------------------------
+constexpr int kMwBK = 32;
+constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 KB per tile
+constexpr int kMwPerWave = kMwInstr / 4;           // 9
+constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
+#ifndef RATTN_MLAW_STAGES
+#define RATTN_MLAW_STAGES 3
+#endif
+constexpr int kMwStages = RATTN_MLAW_STAGES;
+// A weight above 2^mw_overflow forces the exact pass: 2^64 for bf16 (its
+// range is fp32's, and sums of such weights stay far from overflow), 2^15
+// for fp16, whose largest finite value is just below 2^16.
+__device__ __forceinline__ constexpr float mw_overflow(BF16) { return 64.f; }
+__device__ __forceinline__ constexpr float mw_overflow(F16) { return 15.f; }
+// vmcnt(n): the loads of the newest kMwStages - 2 tiles (kMwPerWave per
+// wave and tile) may stay in flight
+constexpr int kMwAhead = (kMwStages - 2) * kMwPerWave;
+constexpr int kMwVmNext = 0x0F70 | (kMwAhead & 15) | ((kMwAhead >> 4) << 14);
+
+__device__ __forceinline__ int mw_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+typedef __attribute__((address_space(3))) const char lds_cchar;
+__device__ __forceinline__ u32x4 mw_read128(lds_cchar* p) {
+  return *reinterpret_cast<__attribute__((address_space(3))) const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 mw_read_tr(lds_cchar* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+template <class T>
+__global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
+  typedef typename T::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kMwStages * kMwStageBytes / 2];
+  // score exchange, quarter-major so a wave's 16-byte accesses are
+  // consecutive across lanes: sx[w][k][lane] = lane's scores 4k .. 4k + 3
+  __shared__ __attribute__((aligned(16))) f32x4 sx[4][4][64];
+  const int HG = a.H / 64;
+  int hg, unit;
+  if (!mla_unit(blockIdx.x, HG, a.s * a.B, hg, unit)) return;
+  const int b = unit / a.s, i = unit % a.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hb = w >> 1, dh = w & 1, h = lane >> 5, l32 = lane & 31;
+  const int H = a.H;
+  const int64_t rows = int64_t(a.B) * H;
+  const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
+  const int n_b = int(kb1 - kb0);
+  const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
+  const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
+  const int64_t row0 = int64_t(b) * H + 64 * hg;  // the workgroup's first head row
+  const int splits_b = (n_b + a.chunk - 1) / a.chunk;
+  if (lo >= hi) {  // split unused by this request
+    if (i == 0) {  // empty request: O = 0, LSE = -inf
+      typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
+      for (int e = tid; e < 64 * kMlaDc; e += 256) o[e] = typename T::elem(0.f);
+      if (a.lse && tid < 64) a.lse[row0 + tid] = -INFINITY;
+    }
+    return;
+  }
+  const int n = hi - lo;
+  const int ntiles = (n + kMwBK - 1) / kMwBK;
+  const int64_t row = row0 + 32 * hb + l32;  // this lane's head row
+
+  // Q^T operand of the wave's 18 contraction steps: head l32, dims
+  // 16 (18 dh + u) + 8 h .. +8
+  u32x4 qb[18];
+  {
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * kMlaD + 288 * dh + 8 * h;
+#pragma unroll
+    for (int u = 0; u < 18; ++u) qb[u] = ldg128(qp + 16 * u);
+#pragma unroll
+    for (int u = 0; u < 18; ++u) __asm__ volatile("" ::"v"(qb[u]));
+  }
+
+  // direct-to-LDS loads: instruction x = w + 4k fills stage chunks
+  // 64x .. 64x + 63; lane chunk q = 64x + lane is row q / 72, slot q % 72,
+  // holding chunk slot ^ f(row) of the row
+  int voff[kMwPerWave];
+#pragma unroll
+  for (int k = 0; k < kMwPerWave; ++k) {
+    const int q = 64 * (w + 4 * k) + lane;
+    const int r = q / kMlaChunks, c = q % kMlaChunks;
+    voff[k] = (r * kMlaChunks + (c ^ mw_swz(r))) * 16;
+  }
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t cbase = uint64_t(size_t(static_cast<const uint16_t*>(a.kv) + (kb0 + lo) * kMlaD));
+  const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)lds)) + w * 1024;
+  auto dma = [&](int tile) {
+    const int key0 = tile * kMwBK;
+    int left = n - key0;
+    left = left < 0 ? 0 : (left > kMwBK ? kMwBK : left);
+    const uint64_t addr = cbase + uint64_t(uint32_t(key0)) * (2 * kMlaD);
+    const i32x4 rsv = {__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
+                       __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
+                       __builtin_amdgcn_readfirstlane(left * 2 * kMlaD), 0x00020000};
+    const uint32_t st = lds0 + uint32_t(tile % kMwStages) * kMwStageBytes;
+#pragma unroll
+    for (int k = 0; k < kMwPerWave; ++k)
+      __asm__ volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(__builtin_amdgcn_readfirstlane(st + k * 4096)), "v"(voff[k]), "s"(rsv)
+          : "memory", "m0");
+  };
+
+  // K operand reads (byte offsets in a stage): lane l32 reads key row l32,
+  // chunk ch = 2 (18 dh + u) + h, stored at slot ch ^ f(l32).  Chunks
+  // u and u + 4 are 8 apart and f only touches the low three bits, so four
+  // per-lane offsets and immediates cover the 18 reads.
+  int kofs[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    kofs[u] = 2 * (l32 * kMlaD + 8 * ((2 * (18 * dh + u) + h) ^ mw_swz(l32)));
+  // V^T operand (transposing reads): lane q + 4e of its 16-lane group
+  // points at key row k0 + e (k0 = 16 t + 4 h, then + 8) and dims
+  // 256 dh + 32 db + 16 g2 + 4 q; those rows have f = 2 e + h, and blocks
+  // db and db + 2 are 8 chunks apart: two per-lane offsets (db even, odd)
+  const int tq = lane & 3, te = (lane >> 2) & 3, g2 = (lane >> 4) & 1;
+  int vofs[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int dim = 256 * dh + 32 * d + 16 * g2 + 4 * tq;
+    vofs[d] = 2 * ((4 * h + te) * kMlaD + 8 * ((dim >> 3) ^ (2 * te + h)) + (dim & 7));
+  }
+
+  f32x16 o[8];  // O^T: head l32, dims 256 dh + 32 db + 8 (r / 4) + 4 h + r % 4
+  float l = 0.f, mref = 0.f, mrun = -INFINITY;
+  int flag = 0;
+  const float c = a.scale_log2;
+
+  // one pass over the chunk; exact = 1: reference fixed to mref from the start
+  auto run = [&](bool exact) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+    l = 0.f;
+    int stage = 0;
+#pragma unroll
+    for (int t = 0; t < kMwStages - 1; ++t) dma(t);
+    __builtin_amdgcn_s_waitcnt(kMwVmNext);  // tile 0 is in
+    __syncthreads();
+    for (int j = 0; j < ntiles; ++j) {
+      dma(j + kMwStages - 1);
+      lds_cchar* cur = (lds_cchar*)(lds) + stage * kMwStageBytes;
+      stage = stage == kMwStages - 1 ? 0 : stage + 1;
+      f32x16 sp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sp[r] = 0.f;
+      lds_cchar* kp[4] = {cur + kofs[0], cur + kofs[1], cur + kofs[2], cur + kofs[3]};
+#pragma unroll
+      for (int u = 0; u < 18; ++u) {
+        const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
+        sp = T::mfma32(as<vec8>(ka), as<vec8>(qb[u]), sp);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        sx[w][k][lane] = f32x4{sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
+      __syncthreads();
+      f32x16 s;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 other = sx[w ^ 1][k][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * k + e] = sp[4 * k + e] + other[e];
+      }
+      // scores in log2 units; keys of this lane: 32 j + 8 (r / 4) + 4 h + r % 4
+      float x[16];
+      const int key0 = j * kMwBK;
+      const bool tail = key0 + kMwBK > n;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = s[r] * c;
+      if (tail) {  // the chunk's last tile: keys past its end
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) x[r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      if (!exact) {
+        mrun = fmaxf(mrun, mx);
+        if (j == 0) {
+          mref = max_halves(mx);  // tile 0 holds a valid key: finite
+        } else if (mx > mref + mw_overflow(T{})) {
+          flag = 1;
+        }
+      }
+      vec8 pb[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x8 p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fexp2(x[8 * t + e] - mref);
+          psum += p[e];
+        }
+        pb[t] = T::cvt8(p);
+      }
+      l += psum;
+      lds_cchar* vp[2] = {cur + vofs[0], cur + vofs[1]};
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          lds_cchar* p = vp[db & 1] + 128 * (db >> 1) + 2 * 16 * t * kMlaD;
+          const u32x2 v0 = mw_read_tr(p);
+          const u32x2 v1 = mw_read_tr(p + 2 * 8 * kMlaD);
+          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+          o[db] = T::mfma32(as<vec8>(av), pb[t], o[db]);
+        }
+      __builtin_amdgcn_s_waitcnt(kMwVmNext);  // tile j + 1 has arrived
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the pass
+  };
+  run(false);
+  if (__syncthreads_or(flag)) {  // a score far above the first tile's max
+    mref = max_halves(mrun);
+    __syncthreads();
+    run(true);
+  }
+
+  l = sum_halves(l);
+  const float inv = 1.f / l;
+  if (splits_b == 1) {
+    typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 256 * dh + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x8 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          y[e] = o[db][4 * g4 + e] * inv;
+          y[4 + e] = 0.f;
+        }
+        const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
+      }
+    if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
+  } else {
+    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 256 * dh + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = o[db][4 * g4 + e] * inv;
+        *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * g4) = y;
+      }
+    if (dh == 0 && h == 0) {
+      a.m_part[int64_t(i) * rows + row] = mref * kLn2;
+      a.l_part[int64_t(i) * rows + row] = l;
+    }
+  }
+}
+
 template <class T>
 static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
-  const int HG = (a.H + 15) / 16;
   const int64_t units = int64_t(a.s) * a.B;
-  const int64_t nwg = 8 * HG * ((units + 7) / 8);
-  hipLaunchKernelGGL((mla_decode_kernel<T>), dim3(unsigned(nwg)), dim3(kMlaThreads), 0, st, a);
+  if (mla_wide(a.H)) {
+    const int64_t nwg = 8 * (a.H / 64) * ((units + 7) / 8);
+    hipLaunchKernelGGL((mla_wide_kernel<T>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
+  } else {
+    const int HG = (a.H + 15) / 16;
+    const int64_t nwg = 8 * HG * ((units + 7) / 8);
+    hipLaunchKernelGGL((mla_decode_kernel<T>), dim3(unsigned(nwg)), dim3(kMlaThreads), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.s == 1) return e;
   return launch_decode_merge_dv(a, st);

@@ -149,11 +149,16 @@ def test_mla_host_rules(lib):
     assert lib.attn_mla_decode_workspace_bytes(1, 16, 0) == 0
     # 32 x 4096 tokens, one 16-head group: c = 512 gives 256 workgroups (one per CU)
     assert lib.attn_mla_decode_choose_splits(32, 16, 32 * 4096, 4096) == 8
-    # 128 heads: eight groups, c = 4096 already gives 8 * 32 = 256 workgroups
-    assert lib.attn_mla_decode_choose_splits(32, 128, 32 * 4096, 4096) == 1
+    # 128 heads: the many-head kernel, two 64-head groups per chunk;
+    # c = 1024 is the first to give 2 * 32 * 4 = 256 workgroups
+    assert lib.attn_mla_decode_choose_splits(32, 128, 32 * 4096, 4096) == 4
     # ragged: 100000 keys, longest 16000, 128 heads: c = 2048 gives
-    # 8 * (49 + 16) >= 512 workgroups; s = ceil(16000 / 2048) = 8, made odd
+    # 2 * (49 + 16) >= 128 workgroups (half the CUs); s = ceil(16000 / 2048)
+    # = 8, made odd
     assert lib.attn_mla_decode_choose_splits(32, 128, 100000, 16000) == 9
+    # the same batch at 16 heads (one 16-head group): two workgroups per CU
+    # would need c < 256, so c stops at 256: s = ceil(16000 / 256) = 63
+    assert lib.attn_mla_decode_choose_splits(32, 16, 100000, 16000) == 63
     assert lib.attn_mla_decode_choose_splits(4, 16, 400, 100) == 1
 
 

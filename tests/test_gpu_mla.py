@@ -33,10 +33,11 @@ def mla_inputs(lengths, H, dtype, seed):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
-@pytest.mark.parametrize("H", [1, 16, 20, 128])
+@pytest.mark.parametrize("H", [1, 16, 20, 64, 128, 256])
 def test_mla_small_ragged(dtype, H):
     """Ragged lengths (tails inside a tile, an empty request), head counts
-    that fill, split and pad the 16-head groups."""
+    that fill, split and pad the 16-head groups, and multiples of 64 (the
+    many-head kernel, one to four workgroups per chunk)."""
     lengths = [1, 31, 32, 33, 0, 300, 64, 517]
     q, kv, kvp = mla_inputs(lengths, H, dtype, seed=H)
     scale = 192 ** -0.5
@@ -83,11 +84,39 @@ def test_mla_ragged_128_heads_sampled():
     assert bool(torch.isfinite(o).all())
 
 
-def test_mla_equal_scores_give_mean_of_latents():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("s", [0, 1, 3])
+def test_mla_many_heads_far_above_first_tile(dtype, s):
+    """Keys whose scores lie far above the first tile's (2^70 and more in
+    weight): the many-head kernel, which weighs against the first tile's
+    max, must take its exact second pass and still match the oracle."""
+    lengths = [300, 700, 33]
+    H = 64
+    g = synth.gen(61)
+    B = len(lengths)
+    base = torch.where(torch.rand(B, 1, DC + DR, generator=g) < 0.5, -1.0, 1.0)
+    q = (base + 0.25 * torch.randn(B, H, DC + DR, generator=g)).to(dtype)
+    kv = (0.5 * torch.randn(sum(lengths), DC + DR, generator=g)).to(dtype)
+    start = 0
+    for b, n in enumerate(lengths):
+        hot = [start + j for j in (40, 41, 250) if j < n]  # past the first 32-key tile
+        kv[hot] = (2.0 * base[b, 0]).to(dtype)
+        start += n
+    kvp = synth.indptr(lengths)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    o, lse = ra().attn_mla_decode(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                  num_splits=s)
+    torch.cuda.synchronize()
+    check(f"mla far-above {dtype} s={s}", o, o_ref, lse, lse_ref, dtype)
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_mla_equal_scores_give_mean_of_latents(H):
     """Zero queries score every key equally: O is the mean of the latent
     parts and LSE = ln(n)."""
     lengths = [200, 1000]
-    q, kv, kvp = mla_inputs(lengths, 16, torch.bfloat16, seed=5)
+    q, kv, kvp = mla_inputs(lengths, H, torch.bfloat16, seed=5)
     q0 = torch.zeros_like(q)
     o, lse = ra().attn_mla_decode(q0.to(DEV), kv.to(DEV), kvp.to(DEV), 1000, 0.1, num_splits=4)
     torch.cuda.synchronize()
