@@ -389,6 +389,123 @@ __global__ __launch_bounds__(128, ST == 1 ? 4 : 2) void bsr_kernel(BsrArgs a) {
   row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
 }
 
+// Two halves of a row's stored tiles in one workgroup (D = 64): wave w
+// takes query rows 32 (w % 2) .. +31 of the block row and the tiles of
+// half kh = w / 2 of the row's list (full tiles, then part tiles, cut at
+// ceil(n / 2)), each half with its own one-stage K/V and bitmap slot;
+// after the last tile the second half's (O, m, l) meet the first's in LDS
+// and combine with log-sum-exp weights.  A grid of one workgroup per block
+// row and head that only fills the CUs at four per CU (C5: 1,024) thereby
+// runs four waves per SIMD, as the one-stage form does on larger grids.
+template <class T>
+__global__ __launch_bounds__(256, 4) void bsr_kernel_halves(BsrArgs a) {
+  constexpr int D = 64, NT = 128, BK = 64, TE = BK * D;
+  typedef typename T::vec8 vec8;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
+
+  const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rw = w & 1, kh = w >> 1, htid = tid & 127;  // row half, tile half, thread in half
+  const int g = hq / a.G;
+  const int mrow = (hq / a.heads_per_mask) * (a.num_blocks + 1) + qblk;
+  const int f0 = a.full_indptr[mrow], n_full = a.full_indptr[mrow + 1] - f0;
+  const int p0 = a.part_indptr[mrow], n_part = a.part_indptr[mrow + 1] - p0;
+  const int ntiles = n_full + n_part;
+  const int nh = (ntiles + 1) / 2;                     // steps: tiles of the longer half
+  const int j0 = kh * nh, j1 = kh ? ntiles : nh;       // this half's tiles [j0, j1)
+
+  const int64_t L = a.L;
+  const int my_q = qblk * 64 + 32 * rw + (lane & 31);
+  const uint16_t* Q = static_cast<const uint16_t*>(a.q);
+  u32x4 qb[1][D / 16];
+  load_q<D>(qb[0], Q + ((int64_t(b) * L + my_q) * a.Hq + hq) * D, lane);
+  RowState<D> st[1];
+  row_state_init(st[0]);
+
+  const int row_stride = a.Hkv * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(a.k) + int64_t(b) * L * row_stride + int64_t(g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(a.v) + int64_t(b) * L * row_stride + int64_t(g) * D;
+  const DmaSrc ksrc = dma_src(kbase, row_stride, int(L)), vsrc = dma_src(vbase, row_stride, int(L));
+  const DmaLane<D, BK, NT, false> dk(row_stride, htid);
+  const DmaLane<D, BK, NT, true> dv(row_stride, htid);
+  uint16_t* const kst = lds_k + kh * TE;
+  uint16_t* const vst = lds_v + kh * TE;
+  uint8_t* const bmh = bm[kh];
+
+  // tile j of the row into this half's slot (its two waves load it), with
+  // its bitmap word if it is a part tile (lanes of the half's first wave)
+  uint64_t word = 0;
+  auto fetch = [&](int j) {
+    const bool part = j >= n_full;
+    const int kblk = part ? a.part_kblock[p0 + j - n_full] : a.full_kblock[f0 + j];
+    if (part && htid < 64) word = a.part_bits[int64_t(p0 + j - n_full) * 64 + htid];
+    dma_tile<D, BK, NT, false>(kst, ksrc, kblk * 64, dk, htid);
+    dma_tile<D, BK, NT, true>(vst, vsrc, kblk * 64, dv, htid);
+  };
+  if (j0 < j1) fetch(j0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (j0 < j1 && j0 >= n_full) bitmap_store(word, bmh, htid);
+  __syncthreads();
+  for (int t = 0; t < nh; ++t) {
+    const int j = j0 + t;
+    if (j < j1) {
+      f32x16 s[1][2];
+      vec8 pb[1][2][2];
+      __builtin_amdgcn_s_setprio(3);
+      qk_tile_sw<T, D, BK, 1>(s, kst, qb, lane);
+      __builtin_amdgcn_s_setprio(0);
+      if (j >= n_full) apply_part_mask(s[0], bmh, rw, lane);
+      const float mref = softmax_max<D, 2>(st[0], s[0], a.scale_log2, 0);
+      softmax_exp<T, D, 2>(st[0], s[0], a.scale_log2, mref, pb[0]);
+      __builtin_amdgcn_s_setprio(3);
+      pv_tile_tr<T, D, BK, 1>(st, pb, vst, lane);
+      __builtin_amdgcn_s_setprio(0);
+    }
+    __syncthreads();  // both halves are done with their slots
+    if (j + 1 < j1) fetch(j + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    if (j + 1 < j1 && j + 1 >= n_full) bitmap_store(word, bmh, htid);
+    __syncthreads();
+  }
+
+  // second half -> LDS, reusing the slots: O^T in the K slots (2 waves x
+  // D / 2 floats x 64 lanes = 16 KB, float r of lane l at r * 64 + l), m
+  // and l in the V slots
+  float* xo = reinterpret_cast<float*>(lds_k) + rw * (D / 2) * 64 + lane;
+  float* xm = reinterpret_cast<float*>(lds_v) + rw * 128 + lane;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(16 * db + r) * 64] = st[0].o[db][r];
+    xm[0] = st[0].m;
+    xm[64] = st[0].l;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float* p = xo;
+    const float m2 = xm[0], l2 = xm[64];
+    const float m1 = st[0].m;
+    const float M = fmaxf(m1, m2);
+    // m = -inf marks a half with no valid key so far: weight 0
+    const float a1 = m1 == -INFINITY ? 0.f : fexp2(m1 - M);
+    const float a2 = m2 == -INFINITY ? 0.f : fexp2(m2 - M);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[0].o[db][r] = st[0].o[db][r] * a1 + p[(16 * db + r) * 64] * a2;
+    st[0].l = st[0].l * a1 + l2 * a2;
+    st[0].m = M;
+  }
+  const int64_t orow_idx = (int64_t(b) * L + my_q) * a.Hq + hq;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + orow_idx * D;
+  row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
+}
+
 // Dense expansion of the two-level mask with the kernel's own predicate:
 // workgroup = 2 waves = one query block row, lanes laid out as in bsr_kernel.
 __global__ __launch_bounds__(128) void bsr_decode_kernel(const int32_t* full_indptr,
@@ -459,7 +576,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st) {
   const dim3 grid(a.num_blocks, a.Hq, a.B);
-  const bool one = a.single_stage && a.D == 64;
+  const bool one = a.single_stage == 1 && a.D == 64;
+  if (a.single_stage == 2 && a.D == 64) {
+    if (a.dtype == 1) hipLaunchKernelGGL((bsr_kernel_halves<BF16>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((bsr_kernel_halves<F16>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (a.dtype == 1) {
     if (one) hipLaunchKernelGGL((bsr_kernel<BF16, 64, 1>), grid, dim3(128), 0, st, a);
     else if (a.D == 64) hipLaunchKernelGGL((bsr_kernel<BF16, 64, 2>), grid, dim3(128), 0, st, a);
