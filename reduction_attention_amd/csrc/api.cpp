@@ -632,11 +632,6 @@ static attn_status_t bsr_args(const void* q, const void* k, const void* v,
   *a = rattn::BsrArgs{q, k, v, mask->full_indptr, mask->full_kblock, mask->part_indptr,
                       mask->part_kblock, mask->part_bits, o, lse, B, L, Hq, Hkv, D, Hq / Hkv,
                       mask->num_blocks, scale * kLog2e, dtype, Hq / num_masks};
-  // D = 64: two-stage workgroups fit four to a compute unit (LDS); a grid
-  // larger than that takes the one-stage form (eight to a unit), a smaller
-  // one the form that splits each row's tiles over two wave pairs.
-  if (D == 64)
-    a->single_stage = (long long)mask->num_blocks * Hq * B > 4LL * attn_device_cu_count() ? 1 : 2;
   return ATTN_OK;
 }
 

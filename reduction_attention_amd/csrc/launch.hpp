@@ -106,9 +106,6 @@ struct BsrArgs {
   int dtype;
   int heads_per_mask;  // query head h uses mask h / heads_per_mask of the
                        // stacked arrays (indptr entries (num_blocks + 1) per mask)
-  int single_stage = 0;  // D = 64 only.  1: one K/V stage, eight two-wave
-                         // workgroups per CU (grids larger than four per CU);
-                         // 2: four waves, each row's tiles in two halves
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

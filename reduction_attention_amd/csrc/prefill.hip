@@ -304,22 +304,15 @@ __device__ __forceinline__ void apply_part_mask(f32x16 (&x)[2], const uint8_t* b
     }
 }
 
-// ST = 2: two stages, the next stored tile streaming in while the current
-// one is computed, two workgroups per SIMD pair (LDS: 33 KB at D = 64).
-// ST = 1: one stage, loaded after the current tile is done, so a
-// workgroup waits for every tile, but at 17 KB and 128 registers eight
-// workgroups share a compute unit and hide each other's waits; used at
-// D = 64 when the grid holds more workgroups than the two-stage form fits
-// at once (a key-column tile of 8192 keys ran 574 -> 411 us).
-template <class T, int D, int ST>
-__global__ __launch_bounds__(128, ST == 1 ? 4 : 2) void bsr_kernel(BsrArgs a) {
+template <class T, int D>
+__global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   constexpr int NT = 128, BK = 64, TE = BK * D;
   typedef typename T::vec8 vec8;
-  // ST stages of natural-layout K and V outer-tile columns, filled
+  // two stages of natural-layout K and V outer-tile columns, filled
   // straight from memory (attn_core.hpp), plus the part tiles' bitmaps
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[ST * TE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[ST * TE];
-  __shared__ __attribute__((aligned(16))) uint8_t bm[ST][512];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
+  __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
   const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -361,9 +354,9 @@ __global__ __launch_bounds__(128, ST == 1 ? 4 : 2) void bsr_kernel(BsrArgs a) {
   if (ntiles > 0 && n_full == 0) bitmap_store(word, bm[0], tid);
   __syncthreads();
   for (int j = 0; j < ntiles; ++j) {
-    const int cur = ST == 2 ? (j & 1) : 0, nxt = ST == 2 ? (cur ^ 1) : 0;
-    // two stages: tile j + 1 streams into the stage tile j - 1 released
-    if (ST == 2 && j + 1 < ntiles) fetch(j + 1, lds_k + nxt * TE, lds_v + nxt * TE);
+    const int cur = j & 1, nxt = cur ^ 1;
+    // tile j + 1 streams into the stage tile j - 1 released
+    if (j + 1 < ntiles) fetch(j + 1, lds_k + nxt * TE, lds_v + nxt * TE);
     f32x16 s[1][2];
     vec8 pb[1][2][2];
     __builtin_amdgcn_s_setprio(3);
@@ -375,10 +368,6 @@ __global__ __launch_bounds__(128, ST == 1 ? 4 : 2) void bsr_kernel(BsrArgs a) {
     __builtin_amdgcn_s_setprio(3);
     pv_tile_tr<T, D, BK, 1>(st, pb, lds_v + cur * TE, lane);
     __builtin_amdgcn_s_setprio(0);
-    if (ST == 1) {  // one stage: tile j + 1 once every wave is done with tile j
-      __syncthreads();
-      if (j + 1 < ntiles) fetch(j + 1, lds_k, lds_v);
-    }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 1 (and its word) arrived
     if (j + 1 < ntiles && j + 1 >= n_full) bitmap_store(word, bm[nxt], tid);
     __syncthreads();
@@ -389,14 +378,16 @@ __global__ __launch_bounds__(128, ST == 1 ? 4 : 2) void bsr_kernel(BsrArgs a) {
   row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
 }
 
-// Two halves of a row's stored tiles in one workgroup (D = 64): wave w
-// takes query rows 32 (w % 2) .. +31 of the block row and the tiles of
-// half kh = w / 2 of the row's list (full tiles, then part tiles, cut at
-// ceil(n / 2)), each half with its own one-stage K/V and bitmap slot;
-// after the last tile the second half's (O, m, l) meet the first's in LDS
-// and combine with log-sum-exp weights.  A grid of one workgroup per block
-// row and head that only fills the CUs at four per CU (C5: 1,024) thereby
-// runs four waves per SIMD, as the one-stage form does on larger grids.
+// The D = 64 form: two halves of a row's stored tiles in one workgroup.
+// Wave w takes query rows 32 (w % 2) .. +31 of the block row and the tiles
+// of half kh = w / 2 of the row's list (full tiles, then part tiles, cut
+// at ceil(n / 2)), each half with its own one-stage K/V and bitmap slot
+// (a half waits for each of its tiles); after the last tile the second
+// half's (O, m, l) meet the first's in LDS and combine with log-sum-exp
+// weights.  At 17 KB per half and 120 registers, four such workgroups
+// share a compute unit: four waves per SIMD hide each other's waits, and
+// a row's tiles take half as long (C5: 122 -> 109 us against the
+// two-stage two-wave form; key-column tiles of 8192 keys 575 -> 393 us).
 template <class T>
 __global__ __launch_bounds__(256, 4) void bsr_kernel_halves(BsrArgs a) {
   constexpr int D = 64, NT = 128, BK = 64, TE = BK * D;
@@ -576,20 +567,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
 
 hipError_t launch_prefill_bsr(const BsrArgs& a, hipStream_t st) {
   const dim3 grid(a.num_blocks, a.Hq, a.B);
-  const bool one = a.single_stage == 1 && a.D == 64;
-  if (a.single_stage == 2 && a.D == 64) {
+  if (a.D == 64) {  // two-halves form
     if (a.dtype == 1) hipLaunchKernelGGL((bsr_kernel_halves<BF16>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((bsr_kernel_halves<F16>), grid, dim3(256), 0, st, a);
-    return hipGetLastError();
-  }
-  if (a.dtype == 1) {
-    if (one) hipLaunchKernelGGL((bsr_kernel<BF16, 64, 1>), grid, dim3(128), 0, st, a);
-    else if (a.D == 64) hipLaunchKernelGGL((bsr_kernel<BF16, 64, 2>), grid, dim3(128), 0, st, a);
-    else hipLaunchKernelGGL((bsr_kernel<BF16, 128, 2>), grid, dim3(128), 0, st, a);
   } else {
-    if (one) hipLaunchKernelGGL((bsr_kernel<F16, 64, 1>), grid, dim3(128), 0, st, a);
-    else if (a.D == 64) hipLaunchKernelGGL((bsr_kernel<F16, 64, 2>), grid, dim3(128), 0, st, a);
-    else hipLaunchKernelGGL((bsr_kernel<F16, 128, 2>), grid, dim3(128), 0, st, a);
+    if (a.dtype == 1) hipLaunchKernelGGL((bsr_kernel<BF16, 128>), grid, dim3(128), 0, st, a);
+    else hipLaunchKernelGGL((bsr_kernel<F16, 128>), grid, dim3(128), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -89,16 +89,16 @@ def test_part_tiles_by_quadrant(dtype, D):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
-def test_large_grid_one_stage(dtype):
-    """D 64 with more workgroups than the two-stage form fits at once
-    (16 block rows x 64 heads x 2 = 2048 > 4 per CU): the one-stage kernel."""
+def test_large_grid(dtype):
+    """D 64 on a grid of more workgroups than fit at once (16 block rows x
+    64 heads x 2 = 2048), rows with up to 16 stored tiles split in halves."""
     L, B, Hq, Hkv, D = 1024, 2, 64, 8, 64
     dense = synth.sparse_mask(L, synth.gen(51), window=128, block=64, globals_per_block=2,
                               random_blocks=2)
     q, k, v = qkv(B, L, Hq, Hkv, D, dtype, 53)
     o_ref, lse_ref = oracle_bsr(q, k, v, dense, 1 / D ** 0.5)
     o, lse, _ = bsr(q, k, v, dense)
-    check(f"bsr one-stage {dtype}", o, o_ref, lse, lse_ref, dtype)
+    check(f"bsr large grid {dtype}", o, o_ref, lse, lse_ref, dtype)
 
 
 def test_workload_sampled():
