@@ -665,7 +665,7 @@ attn_status_t attn_prefill_bsr_rows(const void* q, const void* k, const void* v,
 // heads), where the model picks the faster kernel in every case.
 struct BsrCost { double b0, b1, r0, r1; };
 static BsrCost bsr_cost(int D) {
-  return D == 64 ? BsrCost{11.0, 2.18e-3, 8.0, 0.37e-3} : BsrCost{18.0, 4.7e-3, 10.0, 0.62e-3};
+  return D == 64 ? BsrCost{9.0, 1.6e-3, 8.0, 0.37e-3} : BsrCost{18.0, 4.7e-3, 10.0, 0.62e-3};
 }
 
 attn_status_t attn_bsr_plan_host(const int32_t* full_indptr, const int32_t* part_indptr,
