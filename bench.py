@@ -232,9 +232,12 @@ def bench_mla(torch, ra, synth, wname, args, timer):
     t = median(ms)
     byt = total * 576 * 2 + w.B * w.Hq * (576 * 2 + 512 * 2 + 4) + 4 * (w.B + 1)
     flops = 2 * w.Hq * total * (576 + 512)
+    # the library runs its 64-head kernel when H is a multiple of 64
+    kernel = "mla_wide_kernel" if w.Hq >= 64 and w.Hq % 64 == 0 else "mla_decode_kernel"
     return dict(workload=wname, B=w.B, H=w.Hq, total_kv=total, max_kv_len=max_len, splits=s,
-                ms=t, bytes=byt, gbs=byt / t / 1e6, frac=byt / t / 1e6 / HBM_PEAK_GBS,
-                tflops=flops / t / 1e9)
+                kernel=kernel, ms=t, bytes=byt, gbs=byt / t / 1e6,
+                frac=byt / t / 1e6 / HBM_PEAK_GBS, tflops=flops / t / 1e9,
+                frac_mfma=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
 
 
 def causal_flops(B, Hq, L, D):
