@@ -775,13 +775,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     launch_partial_mfma(a, st);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.s == 1) return e;  // one split: every request is final
-    // equal lengths: every request has s splits, a batch of 16 covers the
-    // usual split counts; ragged: up to 32 of a request's own splits
+    // equal lengths: every request has s splits, loaded in one batch of 8
+    // (s <= 8) or 16; ragged: up to 32 of a request's own splits
     // two rows (waves) per workgroup: on MI355X the step ran 0.7-0.9 us
     // shorter than with four
     const dim3 mgrid(unsigned((int64_t(a.B) * a.Hq + 1) / 2));
 #define RATTN_MERGE(DD, TT)                                                                  \
-  if (a.uniform) hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 16>), mgrid, dim3(128), 0, st, a); \
+  if (a.uniform && a.s <= 8) hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 8>), mgrid, dim3(128), 0, st, a); \
+  else if (a.uniform) hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 16>), mgrid, dim3(128), 0, st, a); \
   else hipLaunchKernelGGL((decode_merge_kernel<DD, TT, 32>), mgrid, dim3(128), 0, st, a)
     if (a.dtype == 1) {
       if (a.D == 64) { RATTN_MERGE(64, __bf16); } else { RATTN_MERGE(128, __bf16); }
