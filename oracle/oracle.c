@@ -78,12 +78,27 @@ static double bf16_bits_to_double(uint16_t b) {
   return (double)x;
 }
 
+/* The two functions above evaluated once for all 65536 bit patterns, so
+ * that a 16-bit element is widened by a lookup: the same exact values,
+ * memoized.  Filled before any parallel region (widen_tables_init). */
+static double g_widen_f16[65536], g_widen_bf16[65536];
+static int g_widen_ready = 0;
+
+static void widen_tables_init(void) {
+  if (g_widen_ready) return;
+  for (uint32_t b = 0; b < 65536u; ++b) {
+    g_widen_f16[b] = f16_bits_to_double((uint16_t)b);
+    g_widen_bf16[b] = bf16_bits_to_double((uint16_t)b);
+  }
+  g_widen_ready = 1;
+}
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
   switch (dtype) {
     case OR_F64: return ((const double*)base)[idx];
     case OR_F32: return (double)((const float*)base)[idx];
-    case OR_BF16: return bf16_bits_to_double(((const uint16_t*)base)[idx]);
-    case OR_F16: return f16_bits_to_double(((const uint16_t*)base)[idx]);
+    case OR_BF16: return g_widen_bf16[((const uint16_t*)base)[idx]];
+    case OR_F16: return g_widen_f16[((const uint16_t*)base)[idx]];
   }
   return NAN;
 }
@@ -113,15 +128,17 @@ static int key_valid(int mask_kind, const uint8_t* mask, int64_t mask_ld,
  * and keys have D elements per head, values Dv (Dv = D for ordinary
  * attention; MLA's absorbed form scores over the latent plus the decoupled
  * rotary dims and averages the latent part only).
- * scores[] is caller scratch of at least n_kv doubles. */
+ * scores[] is caller scratch of at least n_kv doubles, q_row[] of D doubles
+ * (the query row, widened once). */
 static void attend_row(const void* q, const void* k, const void* v, int dtype,
                        int64_t tq, int h, int64_t kv0, int64_t n_q, int64_t n_kv,
                        int64_t i_local, int Hq, int Hkv, int D, int Dv, double scale,
                        int mask_kind, const uint8_t* mask, int64_t mask_ld,
-                       double* scores, double* o_row, double* lse_out) {
+                       double* scores, double* q_row, double* o_row, double* lse_out) {
   const int G = Hq / Hkv;
   const int g = h / G; /* contiguous head groups */
   const int64_t q_off = (tq * Hq + h) * (int64_t)D;
+  for (int d = 0; d < D; ++d) q_row[d] = load_elem(q, dtype, q_off + d);
   double m = -INFINITY;
   int64_t count = 0;
   for (int64_t j = 0; j < n_kv; ++j) {
@@ -131,8 +148,7 @@ static void attend_row(const void* q, const void* k, const void* v, int dtype,
     }
     const int64_t k_off = ((kv0 + j) * Hkv + g) * (int64_t)D;
     double dot = 0.0;
-    for (int d = 0; d < D; ++d)
-      dot += load_elem(q, dtype, q_off + d) * load_elem(k, dtype, k_off + d);
+    for (int d = 0; d < D; ++d) dot += q_row[d] * load_elem(k, dtype, k_off + d);
     scores[j] = scale * dot;
     if (scores[j] > m) m = scores[j];
     ++count;
@@ -197,9 +213,10 @@ int oracle_attention_dv(const void* q, const void* k, const void* v, int dtype,
   (void)nthreads;
 #endif
   int err = 0;
+  widen_tables_init();
 #pragma omp parallel
   {
-    double* scores = (double*)malloc(sizeof(double) * (size_t)(max_kv > 0 ? max_kv : 1));
+    double* scores = (double*)malloc(sizeof(double) * (size_t)((max_kv > 0 ? max_kv : 1) + D));
     if (!scores) {
 #pragma omp atomic write
       err = 1;
@@ -214,7 +231,8 @@ int oracle_attention_dv(const void* q, const void* k, const void* v, int dtype,
         const int64_t out = rows ? p : tq * Hq + h;
         attend_row(q, k, v, dtype, tq, h, kv_indptr[b], n_q, n_kv,
                    tq - qo_indptr[b], Hq, Hkv, D, Dv, scale, mask_kind, mask,
-                   mask_ld, scores, o + out * Dv, lse + out);
+                   mask_ld, scores, scores + (max_kv > 0 ? max_kv : 1), o + out * Dv,
+                   lse + out);
       }
       free(scores);
     }
@@ -401,9 +419,11 @@ int oracle_split_decode_ranges(const void* q, const void* k, const void* v, int 
 #else
   (void)nthreads;
 #endif
+  widen_tables_init();
 #pragma omp parallel
   {
-    double* scores = (double*)malloc(sizeof(double) * (size_t)(max_kv_len > 0 ? max_kv_len : 1));
+    const int64_t nsc = max_kv_len > 0 ? max_kv_len : 1;
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(nsc + D));
 #pragma omp for collapse(2) schedule(dynamic, 4)
     for (int64_t r = 0; r < rows; ++r)
       for (int i = 0; i < s; ++i) {
@@ -417,7 +437,8 @@ int oracle_split_decode_ranges(const void* q, const void* k, const void* v, int 
          * keys [kv_indptr[b] + lo, kv_indptr[b] + hi), no mask. */
         double lse_i;
         attend_row(q, k, v, dtype, b, h, kv_indptr[b] + rg[0], 1, rg[1] - rg[0], 0,
-                   Hq, Hkv, D, D, scale, OR_MASK_NONE, NULL, 0, scores, op, &lse_i);
+                   Hq, Hkv, D, D, scale, OR_MASK_NONE, NULL, 0, scores, scores + nsc, op,
+                   &lse_i);
         /* Recover (m, l) of the partial from its own scores: the two-pass
          * max and sum of exp(score - max). */
         double m = -INFINITY;

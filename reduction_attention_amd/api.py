@@ -27,10 +27,57 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DT[t.dtype]
 
 
-def _dev(*ts):
-    for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("tensors must be contiguous and on the GPU")
+def _placed(ref, **named):
+    """Every named tensor (None skipped) is contiguous and on ``ref``'s
+    device, and that device is a GPU.  Called after the shape and dtype
+    checks, before any pointer reaches the library."""
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not ref.is_cuda:
+        raise ValueError(f"tensors must be on the GPU, not {ref.device}")
+
+
+def _dims(name, t, ndim):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, has shape {tuple(t.shape)}")
+
+
+def _shape(name, t, shape, dtype=None):
+    """Check a caller-provided tensor (None skipped) against shape and dtype."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _same_dtype(ref, **named):
+    for name, t in named.items():
+        if t.dtype != ref.dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, q has {ref.dtype}")
+
+
+def _indptr(name, t, B):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, not {t.dtype}")
+    if t.dim() != 1 or t.numel() != B + 1:
+        raise ValueError(f"{name} must hold B + 1 = {B + 1} entries, has shape {tuple(t.shape)}")
+
+
+def _workspace(t, need):
+    """A caller's workspace must hold ``need`` bytes; returns its byte size."""
+    if t is None:
+        return 0
+    nbytes = t.numel() * t.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, needs {need}")
+    return nbytes
 
 
 def _ptr(t):
@@ -54,21 +101,37 @@ def attn_decode_choose_splits(B, Hq, Hkv, D, total_kv, max_kv_len) -> int:
     return int(load().attn_decode_choose_splits(B, Hq, Hkv, D, int(total_kv), int(max_kv_len)))
 
 
+def _decode_shapes(q, k, v, kv_indptr, o, lse):
+    """Shapes and dtypes of a decode call: q [B,Hq,D]; k, v [total_kv,Hkv,D]
+    of q's dtype; kv_indptr int32 [B+1]; o [B,Hq,D] of q's dtype and lse
+    [B,Hq] fp32 when given.  Returns (B, Hq, D, Hkv)."""
+    _dims("q", q, 3)
+    _dims("k", k, 3)
+    B, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != D:
+        raise ValueError(f"k has head dim {k.shape[2]}, q has {D}")
+    _shape("v", v, k.shape)
+    _same_dtype(q, k=k, v=v)
+    _indptr("kv_indptr", kv_indptr, B)
+    _shape("o", o, q.shape, q.dtype)
+    _shape("lse", lse, (B, Hq), torch.float32)
+    return B, Hq, D, Hkv
+
+
 def attn_decode_splitkv(q, k, v, kv_indptr, max_kv_len, scale=None, num_splits=0, o=None,
                         lse=None, workspace=None, stream=None, want_lse=True):
     """Split-KV decode.  q [B,Hq,D]; k, v [total_kv,Hkv,D]; kv_indptr int32 [B+1].
 
     Returns (o [B,Hq,D] in q's dtype, lse [B,Hq] fp32 or None).
     """
-    _dev(q, k, v, kv_indptr, o, lse, workspace)
-    B, Hq, D = q.shape
-    Hkv = k.shape[1]
-    if kv_indptr.dtype != torch.int32:
-        raise TypeError("kv_indptr must be int32")
+    B, Hq, D, Hkv = _decode_shapes(q, k, v, kv_indptr, o, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     lib = load()
     s = num_splits or lib.attn_decode_choose_splits(B, Hq, Hkv, D, k.shape[0], int(max_kv_len))
     need = lib.attn_decode_workspace_bytes(B, Hq, D, s)
+    _workspace(workspace, need)
+    _placed(q, k=k, v=v, kv_indptr=kv_indptr, o=o, lse=lse, workspace=workspace)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if o is None:
@@ -77,7 +140,7 @@ def attn_decode_splitkv(q, k, v, kv_indptr, max_kv_len, scale=None, num_splits=0
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     st = lib.attn_decode_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(o), _ptr(lse),
                                  B, Hq, Hkv, D, int(max_kv_len), int(k.shape[0]), scale, int(s),
-                                 _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                 _dtype_code(q), _ptr(workspace), _workspace(workspace, need),
                                  _stream(stream))
     check(st, "attn_decode_splitkv")
     return o, lse
@@ -103,15 +166,14 @@ def attn_decode_splitkv_flat(q, k, v, kv_indptr, max_kv_len, scale=None, num_pie
     q [B,Hq,D]; k, v [total_kv,Hkv,D] (total_kv = k.shape[0]); kv_indptr int32
     [B+1].  Returns (o [B,Hq,D] in q's dtype, lse [B,Hq] fp32 or None).
     """
-    _dev(q, k, v, kv_indptr, o, lse, workspace)
-    B, Hq, D = q.shape
-    Hkv, total = k.shape[1], k.shape[0]
-    if kv_indptr.dtype != torch.int32:
-        raise TypeError("kv_indptr must be int32")
+    B, Hq, D, Hkv = _decode_shapes(q, k, v, kv_indptr, o, lse)
+    total = k.shape[0]
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     lib = load()
     P = num_pieces or lib.attn_decode_flat_pieces(B, Hq, Hkv, D, total)
     need = lib.attn_decode_flat_workspace_bytes(B, Hq, D, int(max_kv_len), total, P)
+    _workspace(workspace, need)
+    _placed(q, k=k, v=v, kv_indptr=kv_indptr, o=o, lse=lse, workspace=workspace)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if o is None:
@@ -120,7 +182,8 @@ def attn_decode_splitkv_flat(q, k, v, kv_indptr, max_kv_len, scale=None, num_pie
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     st = lib.attn_decode_splitkv_flat(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(o),
                                       _ptr(lse), B, Hq, Hkv, D, int(max_kv_len), total, scale,
-                                      int(P), _dtype_code(q), _ptr(workspace), workspace.numel(),
+                                      int(P), _dtype_code(q), _ptr(workspace),
+                                      _workspace(workspace, need),
                                       _stream(stream))
     check(st, "attn_decode_splitkv_flat")
     return o, lse
@@ -139,18 +202,25 @@ def attn_mla_decode(q, kv, kv_indptr, max_kv_len, scale, num_splits=0, o=None, l
     """MLA decode, absorbed form.  q [B,H,576]; kv [total_kv,576] (or
     [total_kv,1,576]); kv_indptr int32 [B+1].  Returns (o [B,H,512], lse [B,H]).
     """
-    _dev(q, kv, kv_indptr, o, lse, workspace)
+    _dims("q", q, 3)
     B, H, Dq = q.shape
     if kv.dim() == 3:
-        kv = kv.view(kv.shape[0], kv.shape[1] * kv.shape[2])
+        if kv.shape[1] != 1:
+            raise ValueError(f"kv must be [total_kv, 576] or [total_kv, 1, 576], not {tuple(kv.shape)}")
+        kv = kv.view(kv.shape[0], kv.shape[2])
+    _dims("kv", kv, 2)
     if Dq != 576 or kv.shape[1] != 576:
         raise ValueError("MLA decode expects 576-element query and cache rows (512 + 64)")
-    if kv_indptr.dtype != torch.int32:
-        raise TypeError("kv_indptr must be int32")
+    _same_dtype(q, kv=kv)
+    _indptr("kv_indptr", kv_indptr, B)
+    _shape("o", o, (B, H, 512), q.dtype)
+    _shape("lse", lse, (B, H), torch.float32)
     lib = load()
     s = num_splits or lib.attn_mla_decode_choose_splits(B, H, kv.shape[0], int(max_kv_len))
+    need = lib.attn_mla_decode_workspace_bytes(B, H, s) if s > 1 else 0
+    _workspace(workspace, need)
+    _placed(q, kv=kv, kv_indptr=kv_indptr, o=o, lse=lse, workspace=workspace)
     if workspace is None and s > 1:
-        need = lib.attn_mla_decode_workspace_bytes(B, H, s)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     if o is None:
         o = torch.empty((B, H, 512), dtype=q.dtype, device=q.device)
@@ -158,8 +228,8 @@ def attn_mla_decode(q, kv, kv_indptr, max_kv_len, scale, num_splits=0, o=None, l
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
     st = lib.attn_mla_decode(_ptr(q), _ptr(kv), _ptr(kv_indptr), _ptr(o), _ptr(lse), B, H, 512, 64,
                              int(max_kv_len), int(kv.shape[0]), float(scale), int(s),
-                             _dtype_code(q), _ptr(workspace),
-                             0 if workspace is None else workspace.numel(), _stream(stream))
+                             _dtype_code(q), _ptr(workspace), _workspace(workspace, need),
+                             _stream(stream))
     check(st, "attn_mla_decode")
     return o, lse
 
@@ -167,10 +237,12 @@ def attn_mla_decode(q, kv, kv_indptr, max_kv_len, scale, num_splits=0, o=None, l
 def attn_decode_partials(q, k, v, kv_indptr, max_kv_len, num_splits, scale=None, o_part=None,
                          m_part=None, l_part=None, stream=None):
     """Split partials only: (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) fp32."""
-    _dev(q, k, v, kv_indptr, o_part, m_part, l_part)
-    B, Hq, D = q.shape
-    Hkv = k.shape[1]
+    B, Hq, D, Hkv = _decode_shapes(q, k, v, kv_indptr, None, None)
     s = int(num_splits)
+    _shape("o_part", o_part, (s, B * Hq, D), torch.float32)
+    _shape("m_part", m_part, (s, B * Hq), torch.float32)
+    _shape("l_part", l_part, (s, B * Hq), torch.float32)
+    _placed(q, k=k, v=v, kv_indptr=kv_indptr, o_part=o_part, m_part=m_part, l_part=l_part)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     f32 = dict(dtype=torch.float32, device=q.device)
     o_part = torch.empty((s, B * Hq, D), **f32) if o_part is None else o_part
@@ -195,11 +267,17 @@ def decode_workspace_views(workspace: torch.Tensor, B: int, Hq: int, D: int, s: 
 
 def attn_merge_lse(o_part, m_part, l_part, o_dtype=torch.float32, o=None, lse=None, stream=None):
     """LSE merge of split partials.  o_part [s,rows,D] fp32; m_part, l_part [s,rows] fp32."""
-    _dev(o_part, m_part, l_part, o, lse)
+    _dims("o_part", o_part, 3)
     s, rows, D = o_part.shape
-    for t in (o_part, m_part, l_part):
-        if t.dtype != torch.float32:
-            raise TypeError("partials must be float32")
+    if o_part.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    _shape("m_part", m_part, (s, rows), torch.float32)
+    _shape("l_part", l_part, (s, rows), torch.float32)
+    if o is not None:
+        _dtype_code(o)
+    _shape("o", o, (rows, D))
+    _shape("lse", lse, (rows,), torch.float32)
+    _placed(o_part, m_part=m_part, l_part=l_part, o=o, lse=lse)
     if o is None:
         o = torch.empty((rows, D), dtype=o_dtype, device=o_part.device)
     if lse is None:
@@ -210,13 +288,34 @@ def attn_merge_lse(o_part, m_part, l_part, o_dtype=torch.float32, o=None, lse=No
     return o, lse
 
 
+def _prefill_shapes(q, k, v, qo_indptr, kv_indptr, o, lse):
+    """Shapes and dtypes of a prefill call: q [total_q,Hq,D]; k, v
+    [total_kv,Hkv,D] of q's dtype; qo_indptr, kv_indptr int32 [B+1] (B from
+    qo_indptr); o like q and lse [total_q,Hq] fp32 when given.
+    Returns (B, total_q, Hq, D, Hkv)."""
+    _dims("q", q, 3)
+    _dims("k", k, 3)
+    total_q, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != D:
+        raise ValueError(f"k has head dim {k.shape[2]}, q has {D}")
+    _shape("v", v, k.shape)
+    _same_dtype(q, k=k, v=v)
+    if qo_indptr.dim() != 1 or qo_indptr.numel() < 2:
+        raise ValueError("qo_indptr must hold B + 1 >= 2 entries")
+    B = qo_indptr.numel() - 1
+    _indptr("qo_indptr", qo_indptr, B)
+    _indptr("kv_indptr", kv_indptr, B)
+    _shape("o", o, q.shape, q.dtype)
+    _shape("lse", lse, (total_q, Hq), torch.float32)
+    return B, total_q, Hq, D, Hkv
+
+
 def attn_prefill(q, k, v, qo_indptr, kv_indptr, max_q_len, max_kv_len, scale=None, causal=True,
                  o=None, lse=None, stream=None, want_lse=True):
     """Prefill.  q [total_q,Hq,D]; k, v [total_kv,Hkv,D]; indptr int32 [B+1]."""
-    _dev(q, k, v, qo_indptr, kv_indptr, o, lse)
-    total_q, Hq, D = q.shape
-    Hkv = k.shape[1]
-    B = qo_indptr.numel() - 1
+    B, total_q, Hq, D, Hkv = _prefill_shapes(q, k, v, qo_indptr, kv_indptr, o, lse)
+    _placed(q, k=k, v=v, qo_indptr=qo_indptr, kv_indptr=kv_indptr, o=o, lse=lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if o is None:
         o = torch.empty_like(q)
@@ -244,15 +343,15 @@ def attn_prefill_splitkv(q, k, v, qo_indptr, kv_indptr, max_q_len, max_kv_len, s
 
     Same tensors as attn_prefill; returns (o, lse).
     """
-    _dev(q, k, v, qo_indptr, kv_indptr, o, lse, workspace)
-    total_q, Hq, D = q.shape
-    Hkv = k.shape[1]
-    B = qo_indptr.numel() - 1
+    B, total_q, Hq, D, Hkv = _prefill_shapes(q, k, v, qo_indptr, kv_indptr, o, lse)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     lib = load()
     s = num_splits or lib.attn_prefill_choose_splits(B, Hq, Hkv, D, int(max_q_len),
                                                      int(max_kv_len))
     need = lib.attn_prefill_workspace_bytes(total_q, Hq, D, s) if s > 1 else 0
+    _workspace(workspace, need)
+    _placed(q, k=k, v=v, qo_indptr=qo_indptr, kv_indptr=kv_indptr, o=o, lse=lse,
+            workspace=workspace)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if o is None:
@@ -262,8 +361,7 @@ def attn_prefill_splitkv(q, k, v, qo_indptr, kv_indptr, max_q_len, max_kv_len, s
     st = lib.attn_prefill_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(qo_indptr), _ptr(kv_indptr),
                                   _ptr(o), _ptr(lse), B, Hq, Hkv, D, int(max_q_len),
                                   int(max_kv_len), total_q, scale, int(bool(causal)), int(s),
-                                  _dtype_code(q), _ptr(workspace),
-                                  workspace.numel() if workspace is not None else 0,
+                                  _dtype_code(q), _ptr(workspace), _workspace(workspace, need),
                                   _stream(stream))
     check(st, "attn_prefill_splitkv")
     return o, lse
@@ -309,6 +407,23 @@ class BsrMask:
         if key not in cache:
             cache[key] = attn_bsr_plan(self._host_mask(), D, Hq, B)
         return cache[key]
+
+    def arrays(self) -> dict:
+        """The five mask arrays by name, after checking their dtypes and sizes
+        against the counts (the kernels index them without bounds)."""
+        nb1 = self.num_masks * (self.num_blocks + 1)
+        want = dict(full_indptr=(torch.int32, nb1), full_kblock=(torch.int32, self.nnz_full),
+                    part_indptr=(torch.int32, nb1), part_kblock=(torch.int32, self.nnz_part),
+                    part_bits=(torch.int64, 64 * self.nnz_part))
+        out = {}
+        for name, (dt, n) in want.items():
+            t = getattr(self, name)
+            if t.dtype != dt or t.dim() != 1:
+                raise TypeError(f"mask {name} must be 1-D {dt}, is {t.dtype} {tuple(t.shape)}")
+            if (t.numel() != n) if name.endswith("indptr") else (t.numel() < n):
+                raise ValueError(f"mask {name} holds {t.numel()} entries for {n}")
+            out["mask." + name] = t
+        return out
 
     def struct(self) -> AttnBsrMask:
         return AttnBsrMask(self.seq_len, self.num_blocks, self.nnz_full, self.nnz_part,
@@ -378,9 +493,23 @@ def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, strea
     choice for this mask and head dim)."""
     if kernel not in ("auto", "block", "row"):
         raise ValueError(f"kernel must be auto, block or row, not {kernel!r}")
-    _dev(q, k, v, o, lse)
+    _dims("q", q, 4)
+    _dims("k", k, 4)
     B, L, Hq, D = q.shape
     Hkv = k.shape[2]
+    if tuple(k.shape) != (B, L, Hkv, D):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected (B, L, Hkv, D) = "
+                         f"{(B, L, Hkv, D)}")
+    _shape("v", v, k.shape)
+    _same_dtype(q, k=k, v=v)
+    if mask.seq_len != L:
+        raise ValueError(f"mask covers {mask.seq_len} tokens, q has {L}")
+    if Hq % mask.num_masks:
+        raise ValueError(f"{mask.num_masks} stacked masks do not divide {Hq} query heads")
+    _shape("o", o, q.shape, q.dtype)
+    _shape("lse", lse, (B, L, Hq), torch.float32)
+    # the mask arrays are read by the kernels: they must sit on q's device
+    _placed(q, k=k, v=v, o=o, lse=lse, **mask.arrays())
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     if o is None:
         o = torch.empty_like(q)
@@ -408,8 +537,9 @@ def attn_prefill_bsr(q, k, v, mask: BsrMask, scale=None, o=None, lse=None, strea
 
 
 def attn_debug_split_ranges(kv_indptr, max_kv_len, num_splits, stream=None) -> torch.Tensor:
-    _dev(kv_indptr)
     B = kv_indptr.numel() - 1
+    _indptr("kv_indptr", kv_indptr, B)
+    _placed(kv_indptr)
     out = torch.empty((B, num_splits, 2), dtype=torch.int32, device=kv_indptr.device)
     check(load().attn_debug_split_ranges(_ptr(kv_indptr), B, int(max_kv_len), int(num_splits),
                                          _ptr(out), _stream(stream)), "attn_debug_split_ranges")
@@ -417,8 +547,9 @@ def attn_debug_split_ranges(kv_indptr, max_kv_len, num_splits, stream=None) -> t
 
 
 def attn_debug_flat_ranges(kv_indptr, max_kv_len, total_kv, num_pieces, stream=None):
-    _dev(kv_indptr)
     B = kv_indptr.numel() - 1
+    _indptr("kv_indptr", kv_indptr, B)
+    _placed(kv_indptr)
     s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces)
     out = torch.empty((B, s, 2), dtype=torch.int32, device=kv_indptr.device)
     check(load().attn_debug_flat_ranges(_ptr(kv_indptr), B, int(max_kv_len), int(total_kv),
@@ -428,6 +559,8 @@ def attn_debug_flat_ranges(kv_indptr, max_kv_len, total_kv, num_pieces, stream=N
 
 
 def attn_debug_bsr_decode(mask: BsrMask, stream=None) -> torch.Tensor:
+    arrays = mask.arrays()
+    _placed(mask.full_indptr, **arrays)
     L = mask.seq_len
     out = torch.empty((L, L), dtype=torch.uint8, device=mask.full_indptr.device)
     ms = mask.struct()

@@ -259,8 +259,12 @@ void decode_partial_mfma(DecodeArgs args) {
   // This workgroup's result for its heads: O (normalised), M (log2 units),
   // L.  A request held by a single split is final here; otherwise this is
   // partial i, merged by decode_merge_kernel.
+  // (a request longer than s chunks, which a consistent indptr rules out,
+  // counts as s splits: its keys past s * chunk are not reduced, and no
+  // slot beyond the workspace is ever named)
   const int n_b = int(args.kv_indptr[b + 1] - sr.base);
-  const int splits_b = args.partials_only ? 0 : (n_b + args.chunk - 1) / args.chunk;
+  int splits_b = args.partials_only ? 0 : (n_b + args.chunk - 1) / args.chunk;
+  splits_b = splits_b < args.s ? splits_b : args.s;
   auto emit = [&](int64_t row, int d, float O, float M, float L) {
     if (splits_b == 1) {  // the whole request in one split: final output
       static_cast<typename T::elem*>(args.o)[row * D + d] = typename T::elem(O / L);
@@ -620,9 +624,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (row >= rows) return;
   const int b = int(row / a.Hq);
   // The request's split count from kv_indptr and the chunk or piece
-  // length (an inconsistent indptr is capped at the slot count, so no read
-  // leaves the workspace); an empty request of the flat plan is written
-  // here (O = 0, LSE = -inf) and yields 0.
+  // length, capped at the slot count s in both plans, so that no read
+  // leaves the workspace even for an indptr inconsistent with max_kv_len;
+  // an empty request of the flat plan is written here (O = 0, LSE = -inf)
+  // and yields 0.
   const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
   auto split_count = [&]() -> int {
     int n;
@@ -638,6 +643,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       }
     } else {
       n = a.chunk > 0 ? int((kb1 - kb0 + a.chunk - 1) / a.chunk) : 0;
+      n = n < a.s ? n : a.s;
     }
     return n;
   };

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
   const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
   const int64_t row0 = int64_t(b) * H + 16 * hg;  // this workgroup's first query head row
   const int nh = H - 16 * hg < 16 ? H - 16 * hg : 16;  // heads in this group
-  const int splits_b = (n_b + a.chunk - 1) / a.chunk;
+  const int splits_b = min((n_b + a.chunk - 1) / a.chunk, a.s);  // s bounds the slots
   if (lo >= hi) {  // split unused by this request
     if (i == 0) {  // empty request: O = 0, LSE = -inf
       typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
   const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
   const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
   const int64_t row0 = int64_t(b) * H + 64 * hg;  // the workgroup's first head row
-  const int splits_b = (n_b + a.chunk - 1) / a.chunk;
+  const int splits_b = min((n_b + a.chunk - 1) / a.chunk, a.s);  // s bounds the slots
   if (lo >= hi) {  // split unused by this request
     if (i == 0) {  // empty request: O = 0, LSE = -inf
       typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;

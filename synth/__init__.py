@@ -208,6 +208,15 @@ WORKLOADS = {
     # longer sequence, one mask per group of 4 query heads
     "bsr_heads_prefill_fp16": Workload("bsr_heads_prefill_fp16", "bsr", 7, torch.float16, B=1,
                                        Hq=16, Hkv=16, D=64, L=8192, num_masks=4),
+    # the block-sparse workload's sliding window alone (256 keys): 310 of the
+    # 4,096 outer tiles hold a valid element, the rest are never read
+    "bsr_window_prefill_fp16": Workload("bsr_window_prefill_fp16", "bsr", 10, torch.float16,
+                                        B=1, Hq=16, Hkv=16, D=64, L=4096,
+                                        extra=dict(globals_per_block=0, random_blocks=0)),
+    # 16k tokens (the longest sequences of the STOF evaluation), one mask of
+    # the same recipe per group of 4 query heads
+    "bsr_long_prefill_fp16": Workload("bsr_long_prefill_fp16", "bsr", 11, torch.float16, B=1,
+                                      Hq=16, Hkv=16, D=64, L=16384, num_masks=4),
     # append / chunked prefill: 128 new tokens per request against a 16k history
     "append_prefill_bf16": Workload("append_prefill_bf16", "append", 6, torch.bfloat16, B=4,
                                     Hq=32, Hkv=8, D=128, L=16384, Lq=128, causal=True),

@@ -462,3 +462,111 @@ def test_bsr_plan_validation(lib):
              ctypes.byref(plan)) == 1
     assert lib.attn_prefill_bsr_rows(P, P, P, None, 1, P, None, 1, 256, 2, 2, 64, 0.1, 2,
                                      None) == 1
+
+
+# ---- the Python binding rejects bad tensors before any pointer is passed ----
+# Tensors on the "meta" device have shapes and dtypes but no storage: each
+# call below must raise in the binding's checks, ahead of the library call
+# (which would need real device memory).
+
+def _meta(*shape, dtype=torch.bfloat16):
+    return torch.empty(shape, dtype=dtype, device="meta")
+
+
+def _decode_meta(**kw):
+    a = dict(q=_meta(2, 8, 128), k=_meta(100, 2, 128), v=_meta(100, 2, 128),
+             kv_indptr=_meta(3, dtype=torch.int32))
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("bad,exc,msg", [
+    (dict(k=_meta(100, 2, 128, dtype=torch.float32)), TypeError, "k has dtype"),
+    (dict(v=_meta(100, 2, 64)), ValueError, "v has shape"),
+    (dict(k=_meta(100, 2, 64), v=_meta(100, 2, 64)), ValueError, "head dim"),
+    (dict(kv_indptr=_meta(4, dtype=torch.int32)), ValueError, r"B \+ 1"),
+    (dict(kv_indptr=_meta(3, dtype=torch.int64)), TypeError, "int32"),
+    (dict(o=_meta(2, 8, 128, dtype=torch.float32)), TypeError, "o has dtype"),
+    (dict(o=_meta(2, 8, 64)), ValueError, "o has shape"),
+    (dict(lse=_meta(2, 8, dtype=torch.bfloat16)), TypeError, "lse has dtype"),
+    (dict(workspace=_meta(16, dtype=torch.uint8)), ValueError, "workspace holds"),
+    (dict(kv_indptr=torch.zeros(3, dtype=torch.int32)), ValueError, "kv_indptr is on cpu"),
+    (dict(), ValueError, "on the GPU"),
+])
+def test_binding_decode_rejections(lib, bad, exc, msg):
+    import reduction_attention_amd as ra
+    for fn, extra in ((ra.attn_decode_splitkv, dict(num_splits=2)),
+                      (ra.attn_decode_splitkv_flat, dict(num_pieces=2))):
+        a = _decode_meta(**bad)
+        args = [a.pop(x) for x in ("q", "k", "v", "kv_indptr")]
+        with pytest.raises(exc, match=msg):
+            fn(*args, 50, **extra, **a)
+
+
+def test_binding_partials_merge_mla_rejections(lib):
+    import reduction_attention_amd as ra
+    q, k, v, kv = _decode_meta().values()
+    with pytest.raises(ValueError, match="o_part has shape"):
+        ra.attn_decode_partials(q, k, v, kv, 50, 2, o_part=_meta(2, 16, 64, dtype=torch.float32))
+    with pytest.raises(ValueError, match="m_part has shape"):
+        ra.attn_merge_lse(_meta(2, 16, 128, dtype=torch.float32), _meta(3, 16, dtype=torch.float32),
+                          _meta(2, 16, dtype=torch.float32))
+    with pytest.raises(TypeError, match="partials must be float32"):
+        ra.attn_merge_lse(_meta(2, 16, 128), _meta(2, 16), _meta(2, 16))
+    with pytest.raises(ValueError, match="o has shape"):
+        ra.attn_merge_lse(_meta(2, 16, 128, dtype=torch.float32), _meta(2, 16, dtype=torch.float32),
+                          _meta(2, 16, dtype=torch.float32), o=_meta(16, 64, dtype=torch.float32))
+    qm, kvm = _meta(2, 16, 576), _meta(100, 576)
+    with pytest.raises(TypeError, match="kv has dtype"):
+        ra.attn_mla_decode(qm, _meta(100, 576, dtype=torch.float16), kv, 50, 0.1)
+    with pytest.raises(ValueError, match="576"):
+        ra.attn_mla_decode(_meta(2, 16, 512), _meta(100, 512), kv, 50, 0.1)
+    with pytest.raises(ValueError, match="o has shape"):
+        ra.attn_mla_decode(qm, kvm, kv, 50, 0.1, o=_meta(2, 16, 576))
+    with pytest.raises(ValueError, match="workspace holds"):
+        ra.attn_mla_decode(qm, kvm, kv, 50, 0.1, num_splits=4, workspace=_meta(64, dtype=torch.uint8))
+
+
+def test_binding_prefill_rejections(lib):
+    import reduction_attention_amd as ra
+    q, k, v = _meta(300, 8, 128), _meta(300, 2, 128), _meta(300, 2, 128)
+    ind = _meta(3, dtype=torch.int32)
+    with pytest.raises(TypeError, match="v has dtype"):
+        ra.attn_prefill(q, k, _meta(300, 2, 128, dtype=torch.float16), ind, ind, 150, 150)
+    with pytest.raises(ValueError, match="kv_indptr must hold"):
+        ra.attn_prefill(q, k, v, ind, _meta(4, dtype=torch.int32), 150, 150)
+    with pytest.raises(ValueError, match="lse has shape"):
+        ra.attn_prefill(q, k, v, ind, ind, 150, 150, lse=_meta(300, 2, dtype=torch.float32))
+    with pytest.raises(ValueError, match="workspace holds"):
+        ra.attn_prefill_splitkv(q, k, v, ind, ind, 150, 150, num_splits=3,
+                                workspace=_meta(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="on the GPU"):
+        ra.attn_prefill(q, k, v, ind, ind, 150, 150)
+
+
+def test_binding_rejects_host_resident_mask(lib):
+    """attn_bsr_encode_host returns CPU tensors: passing them, not moved to
+    the device, is rejected before any kernel could read host memory."""
+    import reduction_attention_amd as ra
+    L = 256
+    m = ra.attn_bsr_encode_host(synth.window_mask(L, 70))
+    q, k, v = _meta(1, L, 4, 64, dtype=torch.float16), _meta(1, L, 2, 64, dtype=torch.float16), \
+        _meta(1, L, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="mask.full_indptr is on cpu"):
+        ra.attn_prefill_bsr(q, k, v, m, kernel="block")
+    with pytest.raises(ValueError, match="mask covers"):
+        ra.attn_prefill_bsr(_meta(1, 320, 4, 64, dtype=torch.float16),
+                            _meta(1, 320, 2, 64, dtype=torch.float16),
+                            _meta(1, 320, 2, 64, dtype=torch.float16), m, kernel="block")
+    with pytest.raises(ValueError, match="k has shape"):
+        ra.attn_prefill_bsr(q, _meta(1, L, 2, 128, dtype=torch.float16), v, m)
+    with pytest.raises(ValueError, match="on the GPU"):
+        ra.attn_debug_bsr_decode(m)
+    m3 = ra.attn_bsr_encode_host(torch.stack([synth.window_mask(L, 70)] * 3))
+    with pytest.raises(ValueError, match="do not divide"):
+        ra.attn_prefill_bsr(q, k, v, m3, kernel="block")
+    # a mask whose arrays disagree with its counts
+    bad = ra.attn_bsr_encode_host(synth.window_mask(L, 70))
+    bad.part_bits = bad.part_bits[:10]
+    with pytest.raises(ValueError, match="mask part_bits holds"):
+        ra.attn_prefill_bsr(q, k, v, bad, kernel="block")

@@ -101,23 +101,41 @@ def test_large_grid(dtype):
     check(f"bsr large grid {dtype}", o, o_ref, lse, lse_ref, dtype)
 
 
-def test_workload_sampled():
-    """B 1, L 4096, 16 heads, D 64, fp16; window 256 + 2 globals/64 + 6 random blocks."""
-    w = synth.workload("bsr_prefill_fp16")
+def oracle_workload(w, inp):
+    """Every (token, head) row of a block-sparse workload by the oracle, one
+    call per stacked mask over the query heads it serves (MHA: KV head h
+    serves query head h)."""
+    assert w.Hkv == w.Hq and w.B == 1
+    M = w.num_masks
+    masks = inp["mask"] if M > 1 else inp["mask"].unsqueeze(0)
+    hpm = w.Hq // M
+    q, k, v = (inp[x][0].cpu() for x in ("q", "k", "v"))
+    o = torch.empty((w.L, w.Hq, w.D), dtype=torch.float64)
+    lse = torch.empty((w.L, w.Hq), dtype=torch.float64)
+    for mi in range(M):
+        hs = slice(mi * hpm, (mi + 1) * hpm)
+        o[:, hs], lse[:, hs] = oracle.attention(q[:, hs], k[:, hs], v[:, hs], [0, w.L],
+                                                [0, w.L], w.scale, oracle.MASK_DENSE, masks[mi])
+    return o.unsqueeze(0), lse.unsqueeze(0)
+
+
+@pytest.mark.parametrize("name", ["bsr_prefill_fp16", "bsr_window_prefill_fp16",
+                                  "bsr_heads_prefill_fp16", "bsr_long_prefill_fp16"])
+def test_workload_every_row(name):
+    """The block-sparse workloads (L 4096 with the sparse recipe and with its
+    window alone; L 8192 and 16384 with one mask per 4 heads), fp16, D 64:
+    every row of both kernels against the oracle."""
+    w = synth.workload(name)
     inp = w.make(DEV)
-    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"])
-    print(f"mask density={inp['mask'].float().mean().item():.4f} full={m.nnz_full} "
-          f"part={m.nnz_part}", flush=True)
-    g = synth.gen(77)
-    n = 4000
-    t = torch.randint(0, w.L, (n,), generator=g)
-    h = torch.randint(0, w.Hq, (n,), generator=g)
-    rows = torch.stack([t, h], 1)
-    o_ref, lse_ref = oracle.attention(inp["q"][0], inp["k"][0], inp["v"][0], [0, w.L], [0, w.L],
-                                      w.scale, oracle.MASK_DENSE, inp["mask"], rows=rows)
-    check("bsr 4096 sampled", o[0][t.to(DEV), h.to(DEV)], o_ref, lse[0][t.to(DEV), h.to(DEV)],
-          lse_ref, torch.float16)
-    assert bool(torch.isfinite(o).all())
+    m = ra().attn_bsr_encode_host(inp["mask"])
+    print(f"{name}: L={w.L} masks={m.num_masks} full={m.nnz_full} part={m.nnz_part}; "
+          "oracle over every row ...", flush=True)
+    o_ref, lse_ref = oracle_workload(w, inp)
+    md = m.to(DEV)
+    for kernel in ("block", "row"):
+        o, lse = ra().attn_prefill_bsr(inp["q"], inp["k"], inp["v"], md, kernel=kernel)
+        torch.cuda.synchronize()
+        check(f"{name} {kernel}-wise every row", o, o_ref, lse, lse_ref, torch.float16)
 
 
 def test_unstored_tiles_never_read():
@@ -209,29 +227,6 @@ def test_per_head_masks_equal_separate_calls():
         assert torch.equal(o[:, :, h:h + 1], oh) and torch.equal(lse[:, :, h:h + 1], lh)
 
 
-def test_heads_workload_sampled():
-    """B 1, L 8192, 16 heads, D 64, fp16; 4 masks (one per 4 heads) of the sparse recipe."""
-    w = synth.workload("bsr_heads_prefill_fp16")
-    inp = w.make(DEV)
-    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"])
-    print(f"masks={m.num_masks} full={m.nnz_full} part={m.nnz_part}", flush=True)
-    g = synth.gen(78)
-    n = 1000
-    hpm = w.Hq // w.num_masks
-    q, k, v = (inp[x][0].cpu() for x in ("q", "k", "v"))
-    for mi in range(w.num_masks):
-        t = torch.randint(0, w.L, (n,), generator=g)
-        hl = torch.randint(0, hpm, (n,), generator=g)
-        hs = slice(mi * hpm, (mi + 1) * hpm)
-        o_ref, lse_ref = oracle.attention(q[:, hs], k[:, hs], v[:, hs], [0, w.L], [0, w.L],
-                                          w.scale, oracle.MASK_DENSE, inp["mask"][mi],
-                                          rows=torch.stack([t, hl], 1))
-        h = hl + mi * hpm
-        check(f"bsr heads 8192 sampled mask {mi}", o[0][t.to(DEV), h.to(DEV)], o_ref,
-              lse[0][t.to(DEV), h.to(DEV)], lse_ref, torch.float16)
-    assert bool(torch.isfinite(o).all())
-
-
 # ---- row-wise kernel -----------------------------------------------------------
 
 def small_mask(kind, L, seed):
@@ -291,31 +286,6 @@ def test_rows_unread_blocks_never_read():
     v2[:, 48:64] = float("nan")
     o2, l2, _ = bsr(q, k2, v2, dense, kernel="row")
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-
-
-@pytest.mark.parametrize("name", ["bsr_prefill_fp16", "bsr_heads_prefill_fp16"])
-def test_rows_workload_sampled(name):
-    """The sparse workloads through the row-wise kernel, sampled rows vs the oracle."""
-    w = synth.workload(name)
-    inp = w.make(DEV)
-    o, lse, m = bsr(inp["q"], inp["k"], inp["v"], inp["mask"], kernel="row")
-    g = synth.gen(79)
-    M = m.num_masks
-    hpm = w.Hq // M
-    q, k, v = (inp[x][0].cpu() for x in ("q", "k", "v"))
-    masks = inp["mask"] if M > 1 else inp["mask"].unsqueeze(0)
-    for mi in range(M):
-        n = 2000 // M
-        t = torch.randint(0, w.L, (n,), generator=g)
-        hl = torch.randint(0, hpm, (n,), generator=g)
-        hs = slice(mi * hpm, (mi + 1) * hpm)
-        o_ref, lse_ref = oracle.attention(q[:, hs], k[:, hs], v[:, hs], [0, w.L], [0, w.L],
-                                          w.scale, oracle.MASK_DENSE, masks[mi],
-                                          rows=torch.stack([t, hl], 1))
-        h = hl + mi * hpm
-        check(f"bsr rows {name} sampled mask {mi}", o[0][t.to(DEV), h.to(DEV)], o_ref,
-              lse[0][t.to(DEV), h.to(DEV)], lse_ref, torch.float16)
-    assert bool(torch.isfinite(o).all())
 
 
 def test_auto_kernel_matches_choice():

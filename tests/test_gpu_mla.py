@@ -64,24 +64,16 @@ def test_mla_workload_full_parity():
         check(f"mla workload s={ns or s}", o, o_ref, lse, lse_ref, torch.bfloat16)
 
 
-def test_mla_ragged_128_heads_sampled():
-    """128 heads on one device, ragged lengths in [128, 16384]: a seeded
-    sample of rows (first and last head of every request included)."""
+def test_mla_ragged_128_heads_every_row():
+    """128 heads on one device, ragged lengths in [128, 16384], bf16, the
+    automatic split count: every row against the oracle."""
     w = synth.workload("mla_ragged_decode_bf16")
     inp = w.make(DEV)
     L = inp["lengths"]
-    g = synth.gen(99)
-    pick = [(b, h) for b in range(w.B) for h in (0, w.Hq - 1)]
-    pick += [(int(b), int(h)) for b, h in zip(torch.randint(0, w.B, (448,), generator=g),
-                                              torch.randint(0, w.Hq, (448,), generator=g))]
-    rows = torch.tensor(pick, dtype=torch.int64)
-    o_ref, lse_ref = oracle_mla(inp["q"], inp["kv"], inp["kv_indptr"], w.scale, rows=rows)
+    o_ref, lse_ref = oracle_mla(inp["q"], inp["kv"], inp["kv_indptr"], w.scale)
     o, lse = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], max(L), w.scale)
     torch.cuda.synchronize()
-    oc, lc = o.cpu(), lse.cpu()
-    check("mla ragged 128 heads (sampled)", oc[rows[:, 0], rows[:, 1]], o_ref,
-          lc[rows[:, 0], rows[:, 1]], lse_ref, torch.bfloat16)
-    assert bool(torch.isfinite(o).all())
+    check("mla ragged 128 heads every row", o, o_ref, lse, lse_ref, torch.bfloat16)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])

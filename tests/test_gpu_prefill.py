@@ -56,30 +56,16 @@ def test_rows_without_keys():
     assert bool((o[:125] == 0).all()) and bool(torch.isinf(lse[:125]).all())
 
 
-def sample_rows(total_q, Hq, n, seed):
-    g = synth.gen(seed)
-    t = torch.randint(0, total_q, (n,), generator=g)
-    h = torch.randint(0, Hq, (n,), generator=g)
-    # always include the first and last row of each 4096-row request, every head
-    extra_t = torch.tensor([0, 4095, 4096, 8191] * 4)
-    extra_h = torch.tensor([0, 7, 31, 16] * 4)
-    return torch.stack([torch.cat([t, extra_t]), torch.cat([h, extra_h])], 1)
-
-
-def test_causal_prefill_workload_sampled():
-    """B 2, L 4096, 32/8 heads, D 128, bf16, causal: sampled rows vs the oracle."""
+def test_causal_prefill_workload_every_row():
+    """B 2, L 4096, 32/8 heads, D 128, bf16, causal: every (token, head) row
+    of O and LSE against the fp64 oracle."""
     w = synth.workload("causal_prefill_bf16")
     inp = w.make(DEV)
+    print(f"causal prefill {w.B}x{w.L}: oracle over every row ...", flush=True)
     o, lse = prefill(inp["q"], inp["k"], inp["v"], inp["qo_indptr"], inp["kv_indptr"], True)
-    rows = sample_rows(w.B * w.L, w.Hq, 3000, 99)
     o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], inp["qo_indptr"],
-                                      inp["kv_indptr"], w.scale, oracle.MASK_CAUSAL, rows=rows)
-    t, h = rows[:, 0], rows[:, 1]
-    check("causal prefill 2x4096 sampled", o[t.to(DEV), h.to(DEV)], o_ref, lse[t.to(DEV), h.to(DEV)],
-          lse_ref, torch.bfloat16)
-    # whole-output properties: finite everywhere, |O| bounded by max |V|
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
-    assert o.abs().max().item() <= inp["v"].abs().max().item() + 1e-2
+                                      inp["kv_indptr"], w.scale, oracle.MASK_CAUSAL)
+    check("causal prefill 2x4096 every row", o, o_ref, lse, lse_ref, torch.bfloat16)
 
 
 def test_decode_equals_last_prefill_row():
@@ -157,9 +143,9 @@ def test_splitkv_equals_prefill_when_one_split():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-def test_splitkv_append_workload_sampled():
+def test_splitkv_append_workload_every_row():
     """4 requests x 128 new tokens against 16,384 cached keys, 32/8 heads,
-    D 128, bf16, bottom-right causal, auto split count: sampled rows."""
+    D 128, bf16, bottom-right causal, automatic split count: every row."""
     w = synth.workload("append_prefill_bf16")
     inp = w.make(DEV)
     qo, kv = inp["qo_indptr"], inp["kv_indptr"]
@@ -168,12 +154,6 @@ def test_splitkv_append_workload_sampled():
     s = ra().attn_prefill_choose_splits(w.B, w.Hq, w.Hkv, w.D, lq, lk)
     assert s > 1
     o, lse = prefill_split(inp["q"], inp["k"], inp["v"], qo, kv, True, 0)
-    g = synth.gen(98)
-    total_q = int(qo[-1])
-    rows = torch.stack([torch.randint(0, total_q, (1500,), generator=g),
-                        torch.randint(0, w.Hq, (1500,), generator=g)], 1)
     o_ref, lse_ref = oracle.attention(inp["q"], inp["k"], inp["v"], qo, kv, w.scale,
-                                      oracle.MASK_CAUSAL, rows=rows)
-    t, h = rows[:, 0].to(DEV), rows[:, 1].to(DEV)
-    check(f"append 4x128 vs 16384, s={s}, sampled", o[t, h], o_ref, lse[t, h], lse_ref,
-          torch.bfloat16)
+                                      oracle.MASK_CAUSAL)
+    check(f"append 4x128 vs 16384, s={s}, every row", o, o_ref, lse, lse_ref, torch.bfloat16)
