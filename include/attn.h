@@ -24,9 +24,11 @@
  *
  * Conventions shared by every entry point:
  *   - Tensors are caller-owned device buffers, densely packed, 16-byte
- *     aligned.  The library never allocates or frees device memory, keeps
+ *     aligned.  No call allocates or frees device memory; the library keeps
  *     no pointer after returning, and never synchronises the stream except
- *     in the attn_debug_* exports.
+ *     in the attn_debug_* exports.  Its only device memory of its own is the
+ *     fixed scratch array of attn_decode_splitkv_noalloc (loaded with the
+ *     library, one per GPU).
  *   - All device work is enqueued, in order, on `hip_stream` (a
  *     hipStream_t; NULL = the default stream).  Calls return before the
  *     work finishes.
@@ -126,6 +128,27 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
                                   int Hq, int Hkv, int D, int max_kv_len, long long total_kv,
                                   float scale, int num_splits, int dtype, void* workspace,
                                   size_t workspace_bytes, void* hip_stream);
+
+/*
+ * attn_decode_splitkv for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops and harnesses that forbid
+ * hipMalloc): the same operation, arguments, kernels and results, without
+ * the workspace arguments.  The split partials go to a device array the
+ * library holds, ATTN_NOALLOC_SCRATCH_BYTES bytes on each GPU it runs on,
+ * kept until the process ends; no call allocates or frees memory.
+ * A split count whose partials (attn_decode_workspace_bytes(B, Hq, D, s))
+ * exceed that size is rejected with ATTN_EWORKSPACE before any device work.
+ * Every call on one GPU shares that GPU's array: calls whose work overlaps
+ * in time on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  The array's contents on entry do not matter
+ * (each call writes every partial it reads).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+attn_status_t attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v,
+                                          const int32_t* kv_indptr, void* o, float* lse, int B,
+                                          int Hq, int Hkv, int D, int max_kv_len,
+                                          long long total_kv, float scale, int num_splits,
+                                          int dtype, void* hip_stream);
 
 /*
  * The Split partials alone [CA "Split演算子によるSplit-Kの対応"]: the first

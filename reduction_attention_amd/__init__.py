@@ -4,6 +4,7 @@ C ABI: include/attn.h, implemented by libattn.so (HIP kernels).  This
 package is its thin Python binding; see ``api`` for the entry points.
 """
 from .api import (  # noqa: F401
+    NOALLOC_SCRATCH_BYTES,
     BsrMask,
     attn_bsr_encode_host,
     attn_bsr_plan,
@@ -17,6 +18,7 @@ from .api import (  # noqa: F401
     attn_decode_partials,
     attn_decode_splitkv,
     attn_decode_splitkv_flat,
+    attn_decode_splitkv_noalloc,
     attn_decode_workspace_bytes,
     attn_device_cu_count,
     attn_merge_lse,

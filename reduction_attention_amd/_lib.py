@@ -41,6 +41,8 @@ SIGNATURES = {
     "attn_decode_choose_splits": (_i32, [_i32, _i32, _i32, _i32, _i64, _i32]),
     "attn_decode_splitkv": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                    _i64, _f32, _i32, _i32, _vp, _sz, _vp]),
+    "attn_decode_splitkv_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                           _i32, _i64, _f32, _i32, _i32, _vp]),
     "attn_decode_partials": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                     _i32, _i32, _vp, _vp, _vp, _vp]),
     "attn_decode_flat_pieces": (_i32, [_i32, _i32, _i32, _i32, _i64]),

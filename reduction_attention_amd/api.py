@@ -146,6 +146,29 @@ def attn_decode_splitkv(q, k, v, kv_indptr, max_kv_len, scale=None, num_splits=0
     return o, lse
 
 
+# Bytes of the device array attn_decode_splitkv_noalloc keeps its partials in.
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attn_decode_splitkv_noalloc(q, k, v, kv_indptr, max_kv_len, o, lse=None, scale=None,
+                                num_splits=0, stream=None):
+    """Split-KV decode that allocates nothing: the caller passes the output
+    o [B,Hq,D] (q's dtype) and optionally lse [B,Hq] fp32; the split partials
+    go to the library's own device array.  Calls overlapping in time on one
+    GPU share that array and race.  Returns (o, lse)."""
+    if o is None:
+        raise ValueError("attn_decode_splitkv_noalloc writes into a caller-provided o")
+    B, Hq, D, Hkv = _decode_shapes(q, k, v, kv_indptr, o, lse)
+    _placed(q, k=k, v=v, kv_indptr=kv_indptr, o=o, lse=lse)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    st = load().attn_decode_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(kv_indptr), _ptr(o),
+                                            _ptr(lse), B, Hq, Hkv, D, int(max_kv_len),
+                                            int(k.shape[0]), scale, int(num_splits),
+                                            _dtype_code(q), _stream(stream))
+    check(st, "attn_decode_splitkv_noalloc")
+    return o, lse
+
+
 def attn_decode_flat_pieces(B, Hq, Hkv, D, total_kv) -> int:
     return int(load().attn_decode_flat_pieces(B, Hq, Hkv, D, int(total_kv)))
 

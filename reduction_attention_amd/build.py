@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "bsr_rows.hip", "mla.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "bsr_rows.hip", "mla.hip", "scratch.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

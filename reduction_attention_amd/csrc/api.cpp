@@ -47,6 +47,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxSplits = 256;
 constexpr int kMaxGroup = 16;
 constexpr int kMaxPieces = 65535;
+static_assert(rattn::kScratchBytes == ATTN_NOALLOC_SCRATCH_BYTES,
+              "scratch array size differs from the header's");
 
 }  // namespace
 
@@ -162,6 +164,22 @@ static attn_status_t check_decode(const void* q, const void* k, const void* v,
   return ATTN_OK;
 }
 
+// The two kernels of attn_decode_splitkv with s splits, the partials in
+// `workspace` (validated by the caller).
+static attn_status_t decode_run(const void* q, const void* k, const void* v,
+                                const int32_t* kv_indptr, void* o, float* lse, int B, int Hq,
+                                int Hkv, int D, int max_kv_len, long long total_kv, float scale,
+                                int s, int dtype, void* workspace, void* hip_stream) {
+  const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
+  const size_t rows = size_t(B) * Hq;
+  float* ws = static_cast<float*>(workspace);
+  rattn::DecodeArgs a{q, k, v, kv_indptr, o, lse, ws, ws + size_t(s) * rows * D,
+                      ws + size_t(s) * rows * D + size_t(s) * rows,
+                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype, 0,
+                      uniform_lengths(B, max_kv_len, total_kv)};
+  return hip_status(rattn::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+}
+
 attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
                                   const int32_t* kv_indptr, void* o, float* lse, int B, int Hq,
                                   int Hkv, int D, int max_kv_len, long long total_kv, float scale,
@@ -179,15 +197,33 @@ attn_status_t attn_decode_splitkv(const void* q, const void* k, const void* v,
     return fail(ATTN_EWORKSPACE, "decode: workspace needs %zu bytes, got %zu", need,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned16(workspace)) return fail(ATTN_EINVAL, "decode: workspace must be 16-byte aligned");
+  return decode_run(q, k, v, kv_indptr, o, lse, B, Hq, Hkv, D, max_kv_len, total_kv, scale, s,
+                    dtype, workspace, hip_stream);
+}
 
-  const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
-  const size_t rows = size_t(B) * Hq;
-  float* ws = static_cast<float*>(workspace);
-  rattn::DecodeArgs a{q, k, v, kv_indptr, o, lse, ws, ws + size_t(s) * rows * D,
-                      ws + size_t(s) * rows * D + size_t(s) * rows,
-                      B, Hq, Hkv, D, Hq / Hkv, s, chunk, scale * kLog2e, dtype, 0,
-                      uniform_lengths(B, max_kv_len, total_kv)};
-  return hip_status(rattn::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+attn_status_t attn_decode_splitkv_noalloc(const void* q, const void* k, const void* v,
+                                          const int32_t* kv_indptr, void* o, float* lse, int B,
+                                          int Hq, int Hkv, int D, int max_kv_len,
+                                          long long total_kv, float scale, int num_splits,
+                                          int dtype, void* hip_stream) {
+  attn_status_t cs = check_decode(q, k, v, kv_indptr, B, Hq, Hkv, D, max_kv_len, total_kv, scale,
+                                  num_splits, dtype);
+  if (cs != ATTN_OK) return cs;
+  if (!o) return fail(ATTN_EINVAL, "decode_noalloc: null output");
+  if (!aligned16(o)) return fail(ATTN_EINVAL, "decode_noalloc: o must be 16-byte aligned");
+  const int s = num_splits ? num_splits
+                           : attn_decode_choose_splits(B, Hq, Hkv, D, total_kv, max_kv_len);
+  const size_t need = attn_decode_workspace_bytes(B, Hq, D, s);
+  if (need > rattn::kScratchBytes)
+    return fail(ATTN_EWORKSPACE,
+                "decode_noalloc: %d splits need %zu bytes of partials, above the %zu-byte "
+                "scratch array (use attn_decode_splitkv with a workspace, or fewer splits)",
+                s, need, size_t(rattn::kScratchBytes));
+  void* scratch = nullptr;
+  attn_status_t hs = hip_status(rattn::scratch_address(&scratch), "decode_noalloc: scratch address");
+  if (hs != ATTN_OK) return hs;
+  return decode_run(q, k, v, kv_indptr, o, lse, B, Hq, Hkv, D, max_kv_len, total_kv, scale, s,
+                    dtype, scratch, hip_stream);
 }
 
 attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,

@@ -108,6 +108,12 @@ struct BsrArgs {
                        // stacked arrays (indptr entries (num_blocks + 1) per mask)
 };
 
+// Bytes of the per-device scratch array of the entry points that allocate
+// nothing, and its device address on the current device (looked up on the
+// first call for each device).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_address(void** out);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_flat(const DecodeArgs& a, hipStream_t st);
