@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattn.so")
+# ATTN_LIBRARY_PATH selects another build of the same library (the test
+# suite's sanitizer build of the host code, for one).
+LIB_PATH = os.environ.get("ATTN_LIBRARY_PATH") or os.path.join(_PKG, "libattn.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EWORKSPACE, ATTN_EHIP = range(5)
 ATTN_F32, ATTN_BF16, ATTN_F16 = 0, 1, 2
