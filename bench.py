@@ -47,8 +47,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
-    p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "mla", "mla_ragged", "bsr", "bsr_heads", "append",
-                                      "copy"],
+    p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "mla",
+                                      "mla_ragged", "bsr", "bsr_window", "bsr_heads", "bsr_long",
+                                      "append", "tiny", "sweep", "copy"],
                    default=None,
                    help="time one workload only (for profiler runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,6 +101,17 @@ def median(x):
     s = sorted(x)
     n = len(s)
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def pct(x, q):
+    """The q-quantile of x (nearest rank)."""
+    s = sorted(x)
+    return s[min(len(s) - 1, int(q * len(s)))]
+
+
+def spread(ms):
+    """p10 / p90 of per-step times in ms (rounded)."""
+    return dict(ms_p10=round(pct(ms, 0.1), 5), ms_p90=round(pct(ms, 0.9), 5))
 
 
 def decode_bytes(B, Hq, Hkv, D, total_kv, elem):
@@ -179,8 +191,8 @@ def bench_decode(torch, ra, synth, wname, args, timer, rotate=3):
     kernel_bytes = kvb + qb + ib  # what the partial kernel must read
     return dict(workload=wname, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, total_kv=total,
                 max_kv_len=max_len, splits=s, chunk=-(-max_len // s), dtype=str(q.dtype),
-                step_ms=step_ms, step_ms_p10=sorted(ms)[len(ms) // 10],
-                step_ms_p90=sorted(ms)[(9 * len(ms)) // 10], step_bytes=step_bytes,
+                step_ms=step_ms, step_ms_p10=pct(ms, 0.1), step_ms_p90=pct(ms, 0.9),
+                step_bytes=step_bytes, o=o, lse=lse,
                 kv_bytes=kvb, gbs=step_bytes / step_ms / 1e6, kernel_ms=kernel_ms,
                 kernel_bytes=kernel_bytes, kernel_gbs=kernel_bytes / kernel_ms / 1e6,
                 wall_s=wall, kv_copies_rotated=rotate, graph_step_ms=graph_ms)
@@ -208,7 +220,7 @@ def bench_decode_flat(torch, ra, synth, wname, args, timer):
     kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, total, q.element_size())
     t = median(ms)
     return dict(workload=wname, pieces=P, piece_len=-(-k.shape[0] // P), step_ms=t,
-                gbs=(kvb + qb + ob + lb + ib) / t / 1e6)
+                gbs=(kvb + qb + ob + lb + ib) / t / 1e6, **spread(ms))
 
 
 def bench_mla(torch, ra, synth, wname, args, timer):
@@ -235,7 +247,7 @@ def bench_mla(torch, ra, synth, wname, args, timer):
     # the library runs its 64-head kernel when H is a multiple of 64
     kernel = "mla_wide_kernel" if w.Hq >= 64 and w.Hq % 64 == 0 else "mla_decode_kernel"
     return dict(workload=wname, B=w.B, H=w.Hq, total_kv=total, max_kv_len=max_len, splits=s,
-                kernel=kernel, ms=t, bytes=byt, gbs=byt / t / 1e6,
+                kernel=kernel, ms=t, **spread(ms), bytes=byt, gbs=byt / t / 1e6,
                 frac=byt / t / 1e6 / HBM_PEAK_GBS, tflops=flops / t / 1e9,
                 frac_mfma=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
 
@@ -259,7 +271,7 @@ def bench_prefill(torch, ra, synth, args, timer):
     flops = causal_flops(w.B, w.Hq, w.L, w.D)
     t = median(ms)
     return dict(workload=w.name, B=w.B, L=w.L, Hq=w.Hq, Hkv=w.Hkv, D=w.D, dtype="bf16",
-                ms=t, flops=flops, tflops=flops / t / 1e9,
+                ms=t, **spread(ms), flops=flops, tflops=flops / t / 1e9,
                 frac=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
 
 
@@ -291,7 +303,8 @@ def bench_append(torch, ra, synth, args, timer):
     flops = append_flops(w.B, w.Hq, w.Lq, w.L, w.D)
     t, t1 = median(ms), median(ms1)
     return dict(workload=w.name, B=w.B, Lq=w.Lq, L=w.L, Hq=w.Hq, Hkv=w.Hkv, D=w.D,
-                dtype="bf16", splits=s, ms=t, flops=flops, tflops=flops / t / 1e9,
+                dtype="bf16", splits=s, ms=t, **spread(ms), flops=flops,
+                tflops=flops / t / 1e9,
                 frac=flops / t / 1e9 / MFMA_BF16_PEAK_TFS, ms_unsplit=t1,
                 tflops_unsplit=flops / t1 / 1e9)
 
@@ -311,11 +324,12 @@ def bench_bsr(torch, ra, synth, args, timer, name="bsr_prefill_fp16"):
     t0 = time.perf_counter()
     plan = m.plan(w.D, w.Hq, w.B)
     plan_s = time.perf_counter() - t0
-    times = {}
+    times, spreads = {}, {}
     for kern in ("block", "row"):
         ms, _ = timer.run(lambda i: ra.attn_prefill_bsr(q, k, v, md, o=o, lse=lse, stream=stream,
                                                         kernel=kern), args.steps, args.warmup)
         times[kern] = median(ms)
+        spreads[kern] = spread(ms)
     # every mask serves Hq / num_masks heads
     hpm = w.Hq // m.num_masks
     n_ot = m.nnz_full + m.nnz_part
@@ -325,6 +339,7 @@ def bench_bsr(torch, ra, synth, args, timer, name="bsr_prefill_fp16"):
     flops_valid = 4 * w.D * valid * hpm * w.B
     t = times[plan["kernel"]]  # what kernel="auto" runs
     return dict(workload=w.name, B=w.B, L=w.L, H=w.Hq, D=w.D, dtype="fp16", ms=t,
+                **spreads[plan["kernel"]],
                 kernel=plan["kernel"], ms_block=times["block"], ms_row=times["row"],
                 num_masks=m.num_masks, nnz_full=m.nnz_full, nnz_part=m.nnz_part,
                 row_blocks=plan["row_blocks"], model_block_us=plan["block_cost"],
@@ -345,43 +360,209 @@ def bench_copy(torch, args, timer):
     b = torch.empty(n, dtype=torch.uint8, device=dev)
     a.fill_(1)
     ms, _ = timer.run(lambda i: b.copy_(a), args.steps, args.warmup)
-    return dict(bytes_read=n, bytes_written=n, ms=median(ms), gbs=2 * n / median(ms) / 1e6)
+    return dict(bytes_read=n, bytes_written=n, ms=median(ms), **spread(ms),
+                gbs=2 * n / median(ms) / 1e6)
 
 
-def cpu_baseline(torch, synth, budget_s):
-    """The fp64 oracle on a bounded sample of the headline decode workload."""
-    import oracle
+def bench_tiny_decode(torch, ra, synth, args, timer):
+    """The tiny fp32 decode (1 request, 4/1 heads, D 64, 256 keys) at each of
+    its split counts: launch-latency bound, microseconds per step."""
+    w = synth.workload("tiny_decode_fp32")
+    inp = w.make("cuda:0")
+    q, k, v, kvp = inp["q"], inp["k"], inp["v"], inp["kv_indptr"]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for s in w.splits:
+        ws = torch.empty(ra.attn_decode_workspace_bytes(w.B, w.Hq, w.D, s), dtype=torch.uint8,
+                         device=q.device)
+        ms, _ = timer.run(lambda i: ra.attn_decode_splitkv(q, k, v, kvp, w.L, num_splits=s, o=o,
+                                                           lse=lse, workspace=ws, stream=stream),
+                          args.steps, args.warmup)
+        out[f"s{s}"] = dict(us=round(median(ms) * 1e3, 2), us_p10=round(pct(ms, 0.1) * 1e3, 2),
+                            us_p90=round(pct(ms, 0.9) * 1e3, 2))
+    return dict(workload=w.name, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, kv_len=w.L, dtype="fp32",
+                **out)
+
+
+def bench_split_sweep(torch, ra, synth, args, timer, splits=(4, 8, 16)):
+    """The headline decode step at a few split counts around the rule's."""
     w = synth.workload("llama3_8b_decode_bf16")
-    inp = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in w.make("cuda:0").items()}
-    threads = len(os.sched_getaffinity(0))
-    threads = min(threads, 16)
-    B, Hq = w.B, w.Hq
-    qo = list(range(B + 1))
-    # sample: (request, query head) rows in order, wrapping around, in
-    # batches grown until one batch takes about a second, for about budget_s
-    rows_all = [(b, h) for b in range(B) for h in range(Hq)]
-    n, pos, done = 8, 0, 0
-    t0 = time.perf_counter()
+    inp = w.make("cuda:0")
+    q, kvp = inp["q"], inp["kv_indptr"]
+    sets = [(inp["k"], inp["v"])] + [(inp["k"].clone(), inp["v"].clone()) for _ in range(2)]
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream()
+    kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, w.B * w.L, 2)
+    out = {}
+    for s in splits:
+        ws = torch.empty(ra.attn_decode_workspace_bytes(w.B, w.Hq, w.D, s), dtype=torch.uint8,
+                         device=q.device)
+
+        def step(i):
+            k, v = sets[i % 3]
+            ra.attn_decode_splitkv(q, k, v, kvp, w.L, num_splits=s, o=o, lse=lse, workspace=ws,
+                                   stream=stream)
+
+        ms, _ = timer.run(step, args.steps, args.warmup)
+        t = median(ms)
+        out[f"s{s}"] = dict(chunk=-(-w.L // s), us=round(t * 1e3, 2),
+                            gbs=round((kvb + qb + ob + lb + ib) / t / 1e6, 1))
+    return out
+
+
+def cpu_threads():
+    """Threads the oracle runs on: OMP_NUM_THREADS when it is set (the share
+    of the host's CPUs that goes with one GPU), else every CPU this process
+    may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    aff = len(os.sched_getaffinity(0))
+    return (int(env) if env.isdigit() and int(env) > 0 else aff), aff
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _grow(run, total, budget_s):
+    """Run ``run(start, n)`` on growing batches of a fixed seeded row order
+    until about budget_s seconds have passed; returns (rows done, seconds)."""
+    n, pos, t0 = 8, 0, time.perf_counter()
     while True:
-        sel = [rows_all[(pos + k) % len(rows_all)] for k in range(n)]
-        pos += n
         tb = time.perf_counter()
-        oracle.attention(inp["q"], inp["k"], inp["v"], qo, inp["kv_indptr"], w.scale,
-                         rows=torch.tensor(sel), nthreads=threads)
-        done += n
+        run(pos, n)
+        pos += n
         el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+        if el >= budget_s or pos >= total:
+            return pos, el
         if time.perf_counter() - tb < 1.0:
             n *= 2
-    elem = 2
-    kvb, qb, ob, lb, ib = decode_bytes(B, Hq, w.Hkv, w.D, B * w.L, elem)
+        n = min(n, total - pos)
+
+
+def cpu_baseline(torch, synth, budget_s, gpu_decode=None):
+    """The fp64 oracle, as it stands, on bounded samples of the workloads:
+    the headline decode (about ``budget_s`` seconds) and, with a quarter of
+    that each, the ragged decode, the causal prefill and the block-sparse
+    prefill, each as a rate in its own unit plus the extrapolated wall time
+    of one full oracle evaluation.  With ``gpu_decode`` = (o, lse) of the
+    headline decode, the sampled rows are also compared with the GPU's."""
+    import oracle
+    threads, aff = cpu_threads()
+
+    def host(inp):
+        return {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in inp.items()}
+
+    # -- headline decode: (request, query head) rows in order --------------
+    w = synth.workload("llama3_8b_decode_bf16")
+    inp = host(w.make("cuda:0"))
+    B, Hq = w.B, w.Hq
+    qo = list(range(B + 1))
+    rows_all = torch.tensor([(b, h) for b in range(B) for h in range(Hq)], dtype=torch.int64)
+    errs = []
+
+    def run_decode(pos, n):
+        sel = rows_all[torch.arange(pos, pos + n) % len(rows_all)]
+        o_r, l_r = oracle.attention(inp["q"], inp["k"], inp["v"], qo, inp["kv_indptr"], w.scale,
+                                    rows=sel, nthreads=threads)
+        if gpu_decode is not None and pos < len(rows_all):
+            keep = min(n, len(rows_all) - pos)
+            og, lg = gpu_decode
+            b, h = sel[:keep, 0], sel[:keep, 1]
+            errs.append(((og[b, h].double() - o_r[:keep]).abs().max().item(),
+                         (lg[b, h].double() - l_r[:keep]).abs().max().item(), keep))
+
+    done, el = _grow(run_decode, 10 ** 9, budget_s)
+    kvb, qb, ob, lb, ib = decode_bytes(B, Hq, w.Hkv, w.D, B * w.L, 2)
     step_bytes = kvb + qb + ob + lb + ib
     frac = done / len(rows_all)
-    return dict(value=step_bytes * frac / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{done} of the {len(rows_all)} (request, query head) rows of the decode "
-                       f"workload ({frac:.2f} steps) in {el:.1f} s, fp64 two-pass, OpenMP "
-                       f"{threads} threads; GB/s = the same algorithmic bytes per row as the GPU")
+    out = dict(value=step_bytes * frac / el / 1e9, unit="GB/s", cores=threads, kind="oracle",
+               sample=f"{done} of the {len(rows_all)} (request, query head) rows of the decode "
+                      f"workload ({frac:.2f} steps) in {el:.1f} s, fp64 two-pass, OpenMP "
+                      f"{threads} threads; GB/s = the same algorithmic bytes per row as the GPU",
+               host_cpus=aff, cpu_model=cpu_model(),
+               threads_note="OpenMP threads = OMP_NUM_THREADS when set (the host's CPU share "
+                            "for one GPU), else the process's CPU affinity count",
+               full_eval_s_est=round(el / frac, 3))
+    if errs:
+        out["parity_sample"] = dict(rows=sum(e[2] for e in errs),
+                                    max_abs_o=max(e[0] for e in errs),
+                                    max_abs_lse=max(e[1] for e in errs))
+    per = {"llama3_8b_decode_bf16": dict(value=round(out["value"], 3), unit="GB/s",
+                                         full_eval_s_est=out["full_eval_s_est"])}
+    sub = budget_s / 4
+    g = torch.Generator().manual_seed(12345)
+
+    # -- ragged decode: rows weighted by their request's length -------------
+    w = synth.workload("ragged_decode_bf16")
+    inp = host(w.make("cuda:0"))
+    lens = inp["lengths"]
+    order = torch.randperm(w.B * w.Hq, generator=g)
+    rows = torch.stack([order // w.Hq, order % w.Hq], 1)
+    work = 0
+
+    def run_ragged(pos, n):
+        nonlocal work
+        sel = rows[pos:pos + n]
+        oracle.attention(inp["q"], inp["k"], inp["v"], list(range(w.B + 1)), inp["kv_indptr"],
+                         w.scale, rows=sel, nthreads=threads)
+        work += sum(lens[int(b)] for b in sel[:, 0])
+
+    done, el = _grow(run_ragged, len(rows), sub)
+    frac = work / (w.Hq * sum(lens))
+    kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, sum(lens), 2)
+    per[w.name] = dict(value=round((kvb + qb + ob + lb + ib) * frac / el / 1e9, 3), unit="GB/s",
+                       rows=done, seconds=round(el, 2), full_eval_s_est=round(el / frac, 2))
+
+    # -- causal prefill: FLOPs of the sampled rows' valid keys ---------------
+    w = synth.workload("causal_prefill_bf16")
+    inp = host(w.make("cuda:0"))
+    order = torch.randperm(w.B * w.L * w.Hq, generator=g)
+    rows = torch.stack([order // w.Hq, order % w.Hq], 1)
+    flops = 0
+
+    def run_prefill(pos, n):
+        nonlocal flops
+        sel = rows[pos:pos + n]
+        oracle.attention(inp["q"], inp["k"], inp["v"], inp["qo_indptr"], inp["kv_indptr"],
+                         w.scale, oracle.MASK_CAUSAL, rows=sel, nthreads=threads)
+        flops += 4 * w.D * int(((sel[:, 0] % w.L) + 1).sum())
+
+    done, el = _grow(run_prefill, len(rows), sub)
+    total = causal_flops(w.B, w.Hq, w.L, w.D)
+    per[w.name] = dict(value=round(flops / el / 1e9, 3), unit="GFLOP/s", rows=done,
+                       seconds=round(el, 2), full_eval_s_est=round(el * total / flops, 1))
+
+    # -- block-sparse prefill: FLOPs over the valid (query, key) pairs -------
+    w = synth.workload("bsr_prefill_fp16")
+    inp = host(w.make("cuda:0"))
+    valid_per_row = inp["mask"].to(torch.int64).sum(1)
+    order = torch.randperm(w.L * w.Hq, generator=g)
+    rows = torch.stack([order // w.Hq, order % w.Hq], 1)
+    flops = 0
+
+    def run_bsr(pos, n):
+        nonlocal flops
+        sel = rows[pos:pos + n]
+        oracle.attention(inp["q"][0], inp["k"][0], inp["v"][0], [0, w.L], [0, w.L], w.scale,
+                         oracle.MASK_DENSE, inp["mask"], rows=sel, nthreads=threads)
+        flops += 4 * w.D * int(valid_per_row[sel[:, 0]].sum())
+
+    done, el = _grow(run_bsr, len(rows), sub)
+    total = 4 * w.D * int(valid_per_row.sum()) * w.Hq
+    per[w.name] = dict(value=round(flops / el / 1e9, 3), unit="GFLOP/s (valid pairs)",
+                       rows=done, seconds=round(el, 2), full_eval_s_est=round(el * total / flops, 1))
+    out["per_config"] = per
+    return out
 
 
 def main():
@@ -408,14 +589,20 @@ def main():
                                                        args, timer),
               "prefill": lambda: bench_prefill(torch, ra, synth, args, timer),
               "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
+              "bsr_window": lambda: bench_bsr(torch, ra, synth, args, timer,
+                                              "bsr_window_prefill_fp16"),
               "bsr_heads": lambda: bench_bsr(torch, ra, synth, args, timer,
                                              "bsr_heads_prefill_fp16"),
+              "bsr_long": lambda: bench_bsr(torch, ra, synth, args, timer,
+                                            "bsr_long_prefill_fp16"),
+              "tiny": lambda: bench_tiny_decode(torch, ra, synth, args, timer),
+              "sweep": lambda: bench_split_sweep(torch, ra, synth, args, timer),
               "append": lambda: bench_append(torch, ra, synth, args, timer),
               "mla": lambda: bench_mla(torch, ra, synth, "mla_decode_bf16", args, timer),
               "mla_ragged": lambda: bench_mla(torch, ra, synth, "mla_ragged_decode_bf16", args,
                                               timer),
               "copy": lambda: bench_copy(torch, args, timer)}[args.only]
-        r = fn()
+        r = {k: v for k, v in fn().items() if k not in ("o", "lse")}
         print(json.dumps({"only": args.only, **r}))
         return
 
@@ -434,7 +621,11 @@ def main():
                     unit="GB/s", frac=round(d["kernel_gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="rattn::decode_partial_mfma<rattn::BF16, 128, 4, 1>",
                     algorithmic_bytes=d["kernel_bytes"],
-                    avg_launch_us=round(d["kernel_ms"] * 1e3, 2))
+                    avg_launch_us=round(d["kernel_ms"] * 1e3, 2),
+                    # the whole step (partial kernel + merge + the gap between
+                    # them) against the same peak, on the step's algorithmic bytes
+                    step_achieved=round(d["gbs"], 1), step_frac=round(d["gbs"] / HBM_PEAK_GBS, 4),
+                    step_bytes=d["step_bytes"])
     out = {
         "metric": METRIC,
         "value": round(d["gbs"], 1),
@@ -454,6 +645,9 @@ def main():
                    "kv_copies_rotated": d["kv_copies_rotated"]},
         "roofline": roofline,
         "frac_of_hbm_peak": round(d["gbs"] / HBM_PEAK_GBS, 4),
+        "step_ms_p10": round(d["step_ms_p10"], 5),
+        "step_ms_p90": round(d["step_ms_p90"], 5),
+        "source_sha16": source_hash(all_sources=True),
     }
     if d["graph_step_ms"]:
         gb = d["step_bytes"] / d["graph_step_ms"] / 1e6
@@ -466,6 +660,7 @@ def main():
         p = bench_prefill(torch, ra, synth, args, timer)
         log(f"prefill: {p['ms']*1e3:.1f} us, {p['tflops']:.1f} TFLOP/s ({100*p['frac']:.1f}% of peak)")
         also["causal_prefill"] = dict(workload=p["workload"], ms=round(p["ms"], 4),
+                                      ms_p10=p["ms_p10"], ms_p90=p["ms_p90"],
                                       tflops=round(p["tflops"], 1), frac=round(p["frac"], 4),
                                       roofline=dict(bound="mfma", achieved=round(p["tflops"], 1),
                                                     peak=MFMA_BF16_PEAK_TFS, unit="TFLOP/s",
@@ -477,6 +672,7 @@ def main():
             f"P={rf['pieces']}; chunk plan {r['step_ms']*1e3:.1f} us, {r['gbs']:.0f} GB/s, "
             f"s={r['splits']}")
         also["ragged_decode"] = dict(workload=r["workload"], plan="flat", ms=round(rf["step_ms"], 4),
+                                     ms_p10=rf["ms_p10"], ms_p90=rf["ms_p90"],
                                      gbs=round(rf["gbs"], 1),
                                      frac=round(rf["gbs"] / HBM_PEAK_GBS, 4),
                                      total_kv=r["total_kv"], pieces=rf["pieces"],
@@ -494,29 +690,54 @@ def main():
             log(f"{name}: {m['ms']*1e3:.1f} us, {m['gbs']:.0f} GB/s, s={m['splits']}, "
                 f"{m['tflops']:.1f} TFLOP/s")
             also[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}
-        b = bench_bsr(torch, ra, synth, args, timer)
-        log(f"bsr: {b['ms']*1e3:.1f} us ({b['kernel']}-wise; block {b['ms_block']*1e3:.1f}, "
-            f"row {b['ms_row']*1e3:.1f}), {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
-        also["bsr_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}
-        bh = bench_bsr(torch, ra, synth, args, timer, "bsr_heads_prefill_fp16")
-        log(f"bsr per-head-group masks, L {bh['L']}: {bh['ms']*1e3:.1f} us ({bh['kernel']}-wise; "
-            f"block {bh['ms_block']*1e3:.1f}, row {bh['ms_row']*1e3:.1f})")
-        also["bsr_heads_prefill"] = {k: (round(v, 4) if isinstance(v, float) else v)
-                                     for k, v in bh.items()}
+        for name, key in (("bsr_prefill_fp16", "bsr_prefill"),
+                          ("bsr_window_prefill_fp16", "bsr_window_prefill"),
+                          ("bsr_heads_prefill_fp16", "bsr_heads_prefill"),
+                          ("bsr_long_prefill_fp16", "bsr_long_prefill")):
+            b = bench_bsr(torch, ra, synth, args, timer, name)
+            log(f"{name}: L {b['L']}, {b['nnz_full'] + b['nnz_part']} stored OTs: "
+                f"{b['ms']*1e3:.1f} us ({b['kernel']}-wise; block {b['ms_block']*1e3:.1f}, "
+                f"row {b['ms_row']*1e3:.1f}), {b['tflops_ot']:.1f} TFLOP/s at OT granularity")
+            also[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in b.items()}
+        t = bench_tiny_decode(torch, ra, synth, args, timer)
+        log(f"tiny fp32 decode: " + ", ".join(f"{k} {v['us']} us" for k, v in t.items()
+                                              if k.startswith("s")))
+        also["tiny_decode"] = t
+        also["decode_split_sweep"] = bench_split_sweep(torch, ra, synth, args, timer)
+        log("decode split sweep: " + ", ".join(f"{k} {v['us']} us"
+                                               for k, v in also["decode_split_sweep"].items()))
+        c = bench_copy(torch, args, timer)
+        log(f"device copy (1 GiB): {c['gbs']:.0f} GB/s")
+        also["copy"] = dict(bytes_read=c["bytes_read"], bytes_written=c["bytes_written"],
+                            ms=round(c["ms"], 4), ms_p10=c["ms_p10"], ms_p90=c["ms_p90"],
+                            gbs=round(c["gbs"], 1), frac=round(c["gbs"] / HBM_PEAK_GBS, 4),
+                            note="torch device copy of 1 GiB: a measured reference for the "
+                                 "HBM peak")
         out["also"] = also
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        out["cpu_baseline"] = cpu_baseline(torch, synth, args.cpu_seconds)
-        log(f"cpu baseline: {out['cpu_baseline']['value']:.3f} GB/s on "
-            f"{out['cpu_baseline']['cores']} threads")
+        out["cpu_baseline"] = cpu_baseline(torch, synth, args.cpu_seconds,
+                                           gpu_decode=(d["o"].cpu(), d["lse"].cpu()))
+        cb = out["cpu_baseline"]
+        log(f"cpu baseline: {cb['value']:.3f} GB/s on {cb['cores']} threads ({cb['cpu_model']}); "
+            + ", ".join(f"{k} {v['value']} {v['unit']}" for k, v in cb["per_config"].items()))
     print(json.dumps(out))
 
 
-def source_hash() -> str:
+def source_hash(all_sources=False) -> str:
+    """Hash of the decode kernel's sources (the key of the stored traffic
+    counters), or of every library source and header (the record's source
+    identity on a box without the repository's history)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("decode.hip", "device.hpp"):
-        with open(os.path.join(ROOT, "reduction_attention_amd", "csrc", f), "rb") as fh:
+    csrc = os.path.join(ROOT, "reduction_attention_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in ("decode.hip", "device.hpp")]
+    if all_sources:
+        files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                       if f.endswith((".hip", ".hpp", ".cpp")))
+        files.append(os.path.join(ROOT, "include", "attn.h"))
+    for f in files:
+        with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
