@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
     p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "mla",
-                                      "mla_ragged", "bsr", "bsr_window", "bsr_heads", "bsr_long",
+                                      "mla_ragged", "bsr", "bsr_window", "bsr_cols", "bsr_heads",
+                                      "bsr_long",
                                       "append", "tiny", "sweep", "copy"],
                    default=None,
                    help="time one workload only (for profiler runs)")
@@ -591,6 +592,8 @@ def main():
               "bsr": lambda: bench_bsr(torch, ra, synth, args, timer),
               "bsr_window": lambda: bench_bsr(torch, ra, synth, args, timer,
                                               "bsr_window_prefill_fp16"),
+              "bsr_cols": lambda: bench_bsr(torch, ra, synth, args, timer,
+                                            "bsr_cols_prefill_fp16"),
               "bsr_heads": lambda: bench_bsr(torch, ra, synth, args, timer,
                                              "bsr_heads_prefill_fp16"),
               "bsr_long": lambda: bench_bsr(torch, ra, synth, args, timer,
@@ -692,6 +695,7 @@ def main():
             also[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}
         for name, key in (("bsr_prefill_fp16", "bsr_prefill"),
                           ("bsr_window_prefill_fp16", "bsr_window_prefill"),
+                          ("bsr_cols_prefill_fp16", "bsr_cols_prefill"),
                           ("bsr_heads_prefill_fp16", "bsr_heads_prefill"),
                           ("bsr_long_prefill_fp16", "bsr_long_prefill")):
             b = bench_bsr(torch, ra, synth, args, timer, name)

@@ -653,4 +653,31 @@ __device__ __forceinline__ void pv_tile_tr(RowState<D> (&st)[RB],
   }
 }
 
+// Part-tile bitmaps in LDS, re-laid so that one query row's eight bytes are
+// adjacent: byte (ir*8 + r)*8 + ic = row r of inner tile (ir, ic), i.e.
+// byte r of bitmap word ir*8 + ic (threads 0..63 store word tid).
+__device__ __forceinline__ void bitmap_store(uint64_t word, uint8_t* bm, int tid) {
+  if (tid < 64) {
+    const int ir = tid >> 3, ic = tid & 7;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) bm[(ir * 8 + r) * 8 + ic] = uint8_t(word >> (8 * r));
+  }
+}
+
+// Workgroups are dealt to the eight XCDs round robin by linear index, and
+// each XCD has its own L2.  With Hq a multiple of 8 the (query block, head)
+// grid of the block-sparse kernels is walked so that XCD x serves heads
+// x * Hq / 8 .. (x + 1) * Hq / 8 - 1, every query block of them: the K/V of
+// those heads stay in that XCD's L2.
+__device__ __forceinline__ void bsr_block_head(int nb, int Hq, int& qblk, int& hq) {
+  if (Hq & 7) {
+    qblk = blockIdx.x;
+    hq = blockIdx.y;
+    return;
+  }
+  const int p = blockIdx.x + nb * blockIdx.y, x = p & 7, s = p >> 3;
+  hq = x * (Hq >> 3) + s / nb;
+  qblk = s % nb;
+}
+
 }  // namespace rattn

@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256) void bsr_rows_kernel(BsrArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, gq = lane >> 4;
-  const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  int qblk, hq;
+  bsr_block_head(a.num_blocks, a.Hq, qblk, hq);
+  const int b = blockIdx.z;
   const int64_t L = a.L;
   const int hk = hq / a.G;
   const int mrow = (hq / a.heads_per_mask) * (a.num_blocks + 1) + qblk;  // this head's mask

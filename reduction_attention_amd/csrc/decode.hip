@@ -445,7 +445,10 @@ __global__ void flat_ranges_kernel(DecodeArgs a, int32_t* ranges) {
 // fp32 partial kernel (VALU).  One wave per (split, KV head, request); lane
 // j scores key j of each 64-key tile against the G query heads, the wave
 // keeps per-head running max and sum, and lane d accumulates output dims d
-// and d + 64.  Used for fp32 inputs, whose sizes here are small.
+// and d + 64.  Each tile's V rows are loaded (coalesced, 16 bytes per lane)
+// at the start of the tile, so their latency overlaps the key loads and
+// the scores, and are read back from LDS by the value update.  Used for
+// fp32 inputs, whose sizes here are small (launch and latency bound).
 // -------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
@@ -465,6 +468,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
   }
   __shared__ float qs[16][D];
   __shared__ float ps[64][17];
+  __shared__ float vs[64][D + 4];  // the tile's V rows
   const float* q = static_cast<const float*>(args.q);
   for (int e = lane; e < G * D; e += 64) qs[e / D][e % D] = q[(row0 + e / D) * D + e % D];
   __syncthreads();
@@ -480,13 +484,23 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
 #pragma unroll
     for (int x = 0; x < DL; ++x) acc[h][x] = 0.f;
   }
+  constexpr int VPL = D / 4;  // float4 of the V tile per lane
   for (int t0 = 0; t0 < n; t0 += 64) {
+    const int kmax = n - t0 < 64 ? n - t0 : 64;
+    float4 vreg[VPL];
+#pragma unroll
+    for (int x = 0; x < VPL; ++x) {
+      const int e = x * 64 + lane, r = e / (D / 4), c = e % (D / 4);
+      const int rr = r < kmax ? r : kmax - 1;  // rows past the range repeat the last one
+      vreg[x] = *reinterpret_cast<const float4*>(vb + int64_t(t0 + rr) * row_stride + 4 * c);
+    }
     const int key = t0 + lane;
     const bool valid = key < n;
     const float* kr = kb + int64_t(valid ? key : n - 1) * row_stride;
     float sc[16];
 #pragma unroll
     for (int h = 0; h < 16; ++h) sc[h] = 0.f;
+#pragma unroll
     for (int d = 0; d < D; d += 4) {
       const float4 kv = *reinterpret_cast<const float4*>(kr + d);
 #pragma unroll
@@ -510,15 +524,18 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
       for (int xx = 0; xx < DL; ++xx) acc[h][xx] *= alpha;
       ps[lane][h] = p;
     }
+#pragma unroll
+    for (int x = 0; x < VPL; ++x) {
+      const int e = x * 64 + lane, r = e / (D / 4), c = e % (D / 4);
+      *reinterpret_cast<float4*>(&vs[r][4 * c]) = vreg[x];
+    }
     __syncthreads();
-    const int kmax = n - t0 < 64 ? n - t0 : 64;
     for (int j = 0; j < kmax; ++j) {
-      const float* vr = vb + int64_t(t0 + j) * row_stride;
 #pragma unroll
       for (int xx = 0; xx < DL; ++xx) {
         const int d = lane + 64 * xx;
         if (d < D) {
-          const float vv = vr[d];
+          const float vv = vs[j][d];
 #pragma unroll
           for (int h = 0; h < 16; ++h)
             if (h < G) acc[h][xx] += ps[j][h] * vv;

@@ -36,13 +36,7 @@ constexpr int kMlaDc = 512, kMlaDr = 64, kMlaD = kMlaDc + kMlaDr;  // cache row:
 constexpr int kMlaBK = 32;                      // keys per tile
 constexpr int kMlaChunks = kMlaD / 8;           // 16-byte chunks per cache row (72)
 constexpr int kMlaLdsRow = kMlaChunks + 1;      // LDS row: one pad chunk (rows 36 banks apart)
-#ifndef RATTN_MLA_WAVES
-#define RATTN_MLA_WAVES 4
-#endif
-#ifndef RATTN_MLA_STAGES
-#define RATTN_MLA_STAGES 2
-#endif
-constexpr int kMlaWaves = RATTN_MLA_WAVES;
+constexpr int kMlaWaves = 4;
 constexpr int kMlaThreads = 64 * kMlaWaves;
 // A tile goes from HBM straight into an LDS stage: 64-lane x 16-byte load
 // instructions, each filling 1 KB of the stage (37 per tile, the last one
@@ -52,7 +46,7 @@ constexpr int kMlaInstr = (kMlaBK * kMlaLdsRow + 63) / 64;  // 37
 constexpr int kMlaPerWave = (kMlaInstr + kMlaWaves - 1) / kMlaWaves;  // loads per wave and tile (at most)
 constexpr int kMlaStageBytes = kMlaInstr * 1024;
 constexpr int kMlaStage = kMlaStageBytes / 2;  // 16-bit elements per stage
-constexpr int kMlaStages = RATTN_MLA_STAGES;
+constexpr int kMlaStages = 2;
 // s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits 3:0 and 15:14; expcnt and
 // lgkmcnt fields at their no-wait maximum) that lets the loads of all
 // stages but two stay in flight: the tile the next step reads has arrived
@@ -338,10 +332,7 @@ constexpr int kMwBK = 32;
 constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 KB per tile
 constexpr int kMwPerWave = kMwInstr / 4;           // 9
 constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
-#ifndef RATTN_MLAW_STAGES
-#define RATTN_MLAW_STAGES 3
-#endif
-constexpr int kMwStages = RATTN_MLAW_STAGES;
+constexpr int kMwStages = 3;
 // A weight above 2^mw_overflow forces the exact pass: 2^64 for bf16 (its
 // range is fp32's, and sums of such weights stay far from overflow), 2^15
 // for fp16, whose largest finite value is just below 2^16.

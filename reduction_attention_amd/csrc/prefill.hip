@@ -32,27 +32,15 @@ namespace rattn {
 // natural layout with swizzled 16-byte slots; V is read through transposing
 // LDS reads (attn_core.hpp).  Two workgroups share a compute unit, so one's
 // start-up (its query rows and first tiles coming in from memory) and
-// barriers overlap the other's matrix work.  Shape knobs (waves, row
-// blocks, occupancy) were swept on MI355X; the defaults won.
+// barriers overlap the other's matrix work.  The shape below (waves per
+// workgroup, 32-row blocks per wave, workgroups per compute unit, keys per
+// tile) won a sweep on MI355X against 8 waves, two row blocks per wave, one
+// workgroup per compute unit and 32- or 128-key tiles.
 // ---------------------------------------------------------------------------
-#ifndef RATTN_PREFILL_WAVES
-#define RATTN_PREFILL_WAVES 4
-#endif
-#ifndef RATTN_PREFILL_RB
-#define RATTN_PREFILL_RB 1
-#endif
-#ifndef RATTN_PREFILL_OCC
-#define RATTN_PREFILL_OCC 2
-#endif
-#ifndef RATTN_PREFILL_XCD
-#define RATTN_PREFILL_XCD 1
-#endif
-constexpr int kPrefillWaves = RATTN_PREFILL_WAVES;
-constexpr int kPrefillRB = RATTN_PREFILL_RB;
-#ifndef RATTN_PREFILL_BK
-#define RATTN_PREFILL_BK 64
-#endif
-constexpr int kPrefillBK = RATTN_PREFILL_BK;
+constexpr int kPrefillWaves = 4;
+constexpr int kPrefillRB = 1;
+constexpr int kPrefillOcc = 2;
+constexpr int kPrefillBK = 64;
 constexpr int kPrefillBQ = 32 * kPrefillRB * kPrefillWaves;  // query rows per workgroup
 
 // Workgroups are dealt to the eight XCDs round robin by linear index, and
@@ -60,46 +48,39 @@ constexpr int kPrefillBQ = 32 * kPrefillRB * kPrefillWaves;  // query rows per w
 // (x % 8) * (Hq / 8) + x / 8, so each XCD serves a contiguous range of query
 // heads -- whole GQA groups -- and fetches their K/V into its own L2 only.
 __device__ __forceinline__ int xcd_head(int x, int hq_count) {
-  if (!RATTN_PREFILL_XCD || (hq_count & 7)) return x;
+  if (hq_count & 7) return x;
   return (x & 7) * (hq_count >> 3) + (x >> 3);
 }
 
 // The value update's schedule: N matrix ops (times RB), each fed by two
-// transposing LDS reads, with PV_DEPTH reads kept in flight ahead of them.
-#ifndef RATTN_PREFILL_PV_DEPTH
-#define RATTN_PREFILL_PV_DEPTH 8
-#endif
+// transposing LDS reads, with kPvDepth reads kept in flight ahead of them.
+constexpr int kPvDepth = 8;
 template <int N, int RB>
 __device__ __forceinline__ void lds_pipeline_pv() {
-#if RATTN_PREFILL_PV_DEPTH
-  __builtin_amdgcn_sched_group_barrier(0x100, RATTN_PREFILL_PV_DEPTH, 1);
+  __builtin_amdgcn_sched_group_barrier(0x100, kPvDepth, 1);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, RB, 1);
-    if (i < N - RATTN_PREFILL_PV_DEPTH / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    if (i < N - kPvDepth / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
   }
-#endif
 }
 
 // Schedule of a block of N operand reads from LDS, each feeding RB matrix
-// ops: keep DEPTH reads in flight ahead of the matrix ops.
-#ifndef RATTN_PREFILL_DEPTH
-#define RATTN_PREFILL_DEPTH 4
-#endif
+// ops: keep kLdsDepth reads in flight ahead of the matrix ops (two, three
+// and five measured no better than four).
+constexpr int kLdsDepth = 4;
 template <int N, int RB>
 __device__ __forceinline__ void lds_pipeline() {
-#if RATTN_PREFILL_DEPTH
-  __builtin_amdgcn_sched_group_barrier(0x100, RATTN_PREFILL_DEPTH, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, kLdsDepth, 0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
-    if (i + RATTN_PREFILL_DEPTH < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i + kLdsDepth < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-#endif
 }
 
 template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(64 * kPrefillWaves, RATTN_PREFILL_OCC)
+__global__ __launch_bounds__(64 * kPrefillWaves, kPrefillOcc)
 void prefill_kernel(PrefillArgs a) {
   constexpr int NT = 64 * kPrefillWaves, RB = kPrefillRB, BQ = kPrefillBQ, BK = kPrefillBK;
   typedef TileGeom<D, BK> Gm;
@@ -275,17 +256,6 @@ void prefill_kernel(PrefillArgs a) {
 // one head; grid (L/64, Hq, B).  Tiles: the row's full OTs, then its part OTs.
 // ---------------------------------------------------------------------------
 
-// Part-OT bitmaps in LDS, re-laid so that one lane's eight bytes are
-// adjacent: byte (ir*8 + r)*8 + ic = row r of inner tile (ir, ic), i.e.
-// byte r of bitmap word ir*8 + ic.
-__device__ __forceinline__ void bitmap_store(uint64_t word, uint8_t* bm, int tid) {
-  if (tid < 64) {
-    const int ir = tid >> 3, ic = tid & 7;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) bm[(ir * 8 + r) * 8 + ic] = uint8_t(word >> (8 * r));
-  }
-}
-
 // The part-OT predicate: x[kb][r] -> -inf where query (32*w + lane%32) of the
 // OT may not attend key 32*kb + 8*(r/4) + 4*h + r%4 of the OT.
 __device__ __forceinline__ void apply_part_mask(f32x16 (&x)[2], const uint8_t* bm, int w,
@@ -314,7 +284,9 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
   __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
-  const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  int qblk, hq;
+  bsr_block_head(a.num_blocks, a.Hq, qblk, hq);
+  const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int g = hq / a.G;
@@ -396,7 +368,9 @@ __global__ __launch_bounds__(256, 4) void bsr_kernel_halves(BsrArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2 * TE];
   __shared__ __attribute__((aligned(16))) uint8_t bm[2][512];
 
-  const int qblk = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  int qblk, hq;
+  bsr_block_head(a.num_blocks, a.Hq, qblk, hq);
+  const int b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rw = w & 1, kh = w >> 1, htid = tid & 127;  // row half, tile half, thread in half

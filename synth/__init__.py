@@ -213,6 +213,13 @@ WORKLOADS = {
     "bsr_window_prefill_fp16": Workload("bsr_window_prefill_fp16", "bsr", 10, torch.float16,
                                         B=1, Hq=16, Hkv=16, D=64, L=4096,
                                         extra=dict(globals_per_block=0, random_blocks=0)),
+    # global tokens as key columns only (2 per 64-block) plus an 8-key causal
+    # window: every outer tile is stored but sparse inside, the row-wise
+    # kernel's case
+    "bsr_cols_prefill_fp16": Workload("bsr_cols_prefill_fp16", "bsr", 12, torch.float16, B=1,
+                                      Hq=16, Hkv=16, D=64, L=4096,
+                                      extra=dict(window=8, symmetric_globals=False,
+                                                 random_blocks=0)),
     # 16k tokens (the longest sequences of the STOF evaluation), one mask of
     # the same recipe per group of 4 query heads
     "bsr_long_prefill_fp16": Workload("bsr_long_prefill_fp16", "bsr", 11, torch.float16, B=1,

@@ -120,11 +120,13 @@ def oracle_workload(w, inp):
 
 
 @pytest.mark.parametrize("name", ["bsr_prefill_fp16", "bsr_window_prefill_fp16",
-                                  "bsr_heads_prefill_fp16", "bsr_long_prefill_fp16"])
+                                  "bsr_cols_prefill_fp16", "bsr_heads_prefill_fp16",
+                                  "bsr_long_prefill_fp16"])
 def test_workload_every_row(name):
-    """The block-sparse workloads (L 4096 with the sparse recipe and with its
-    window alone; L 8192 and 16384 with one mask per 4 heads), fp16, D 64:
-    every row of both kernels against the oracle."""
+    """The block-sparse workloads (L 4096 with the sparse recipe, with its
+    window alone and with column globals over a narrow window; L 8192 and
+    16384 with one mask per 4 heads), fp16, D 64: every row of both kernels
+    against the oracle."""
     w = synth.workload(name)
     inp = w.make(DEV)
     m = ra().attn_bsr_encode_host(inp["mask"])
