@@ -246,11 +246,26 @@ def bench_mla(torch, ra, synth, wname, args, timer):
     byt = total * 576 * 2 + w.B * w.Hq * (576 * 2 + 512 * 2 + 4) + 4 * (w.B + 1)
     flops = 2 * w.Hq * total * (576 + 512)
     # the library runs its 64-head kernel when H is a multiple of 64
-    kernel = "mla_wide_kernel" if w.Hq >= 64 and w.Hq % 64 == 0 else "mla_decode_kernel"
-    return dict(workload=wname, B=w.B, H=w.Hq, total_kv=total, max_kv_len=max_len, splits=s,
-                kernel=kernel, ms=t, **spread(ms), bytes=byt, gbs=byt / t / 1e6,
-                frac=byt / t / 1e6 / HBM_PEAK_GBS, tflops=flops / t / 1e9,
-                frac_mfma=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
+    wide = w.Hq >= 64 and w.Hq % 64 == 0
+    kernel = "mla_wide_kernel" if wide else "mla_decode_kernel"
+    out = dict(workload=wname, B=w.B, H=w.Hq, total_kv=total, max_kv_len=max_len, plan="chunk",
+               splits=s, kernel=kernel, ms=t, **spread(ms), bytes=byt, gbs=byt / t / 1e6,
+               frac=byt / t / 1e6 / HBM_PEAK_GBS, tflops=flops / t / 1e9,
+               frac_mfma=flops / t / 1e9 / MFMA_BF16_PEAK_TFS)
+    if wide and max_len * w.B != total:
+        # ragged many-head batch: also time the flat plan (equal pieces of
+        # the packed cache) beside the chunk plan
+        P = ra.attn_mla_decode_flat_pieces(w.B, w.Hq, total)
+        wsf = torch.empty(max(ra.attn_mla_decode_flat_workspace_bytes(w.B, w.Hq, max_len, total, P),
+                              256), dtype=torch.uint8, device=q.device)
+        msf, _ = timer.run(lambda i: ra.attn_mla_decode_flat(q, kv, kvp, max_len, w.scale,
+                                                             num_pieces=P, o=o, lse=lse,
+                                                             workspace=wsf, stream=stream),
+                           args.steps, args.warmup)
+        tf = median(msf)
+        out["flat_plan"] = dict(pieces=P, piece_len=-(-total // P), ms=tf, gbs=byt / tf / 1e6,
+                                tflops=flops / tf / 1e9)
+    return out
 
 
 def causal_flops(B, Hq, L, D):
@@ -690,8 +705,10 @@ def main():
         for name, key in (("mla_decode_bf16", "mla_decode"),
                           ("mla_ragged_decode_bf16", "mla_ragged_decode")):
             m = bench_mla(torch, ra, synth, name, args, timer)
+            fp = m.get("flat_plan")
             log(f"{name}: {m['ms']*1e3:.1f} us, {m['gbs']:.0f} GB/s, s={m['splits']}, "
-                f"{m['tflops']:.1f} TFLOP/s")
+                f"{m['tflops']:.1f} TFLOP/s"
+                + (f"; flat plan {fp['ms']*1e3:.1f} us, P={fp['pieces']}" if fp else ""))
             also[key] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()}
         for name, key in (("bsr_prefill_fp16", "bsr_prefill"),
                           ("bsr_window_prefill_fp16", "bsr_window_prefill"),

@@ -272,6 +272,45 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
                               long long total_kv, float scale, int num_splits, int dtype,
                               void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Piece count attn_mla_decode_flat picks when num_pieces = 0: one 64-head
+ * workgroup per compute unit, P = CUs / (H / 64), capped so that no piece
+ * is shorter than 256 keys, within [1, 65535]; 1 for invalid arguments. */
+int attn_mla_decode_flat_pieces(int B, int H, long long total_kv);
+
+/* Workspace bytes of attn_mla_decode_flat: s * B * H * (512 + 2) * 4 with
+ * s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces), rounded
+ * up to 256 (0 for invalid arguments). */
+size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long long total_kv,
+                                            int num_pieces);
+
+/*
+ * MLA decode (the operation of attn_mla_decode) with the Split operator
+ * applied to the packed cache of the whole batch as one reduction dimension
+ * [CA "Split演算子によるSplit-Kの対応": the split is a symbol the scheduler
+ * fixes later; AB]: the rows [0, total_kv) of kv are cut into P pieces of
+ * c = ceil(total_kv / P) rows, and split i of request b is the request's
+ * intersection with the i-th piece it overlaps.  One 64-head workgroup
+ * reduces one piece for its heads (the request segments inside it one after
+ * another), so every workgroup streams the same number of cache rows
+ * whatever the length mix; the merge (log-sum-exp weights) then combines
+ * the pieces of each request and writes O = 0, LSE = -inf for empty
+ * requests.
+ * Arguments as attn_mla_decode, except:
+ * H           a multiple of 64 (the many-head kernel); others ATTN_EUNSUPPORTED.
+ * num_pieces  P in [1, 65535], or 0 for attn_mla_decode_flat_pieces.
+ * total_kv    the row count of kv (<= 2^31 - 1); every kv_indptr entry must
+ *   lie in [0, total_kv].  Rows outside every request are not read.
+ * workspace   at least attn_mla_decode_flat_workspace_bytes(B, H, max_kv_len,
+ *   total_kv, P) bytes (always needed); layout o_part [s, B*H, 512], m_part
+ *   [s, B*H], l_part [s, B*H] fp32, split i of request b in slot i.  Calls
+ *   that share one workspace must not overlap in time.
+ */
+attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t* kv_indptr,
+                                   void* o, float* lse, int B, int H, int Dc, int Dr,
+                                   int max_kv_len, long long total_kv, float scale, int num_pieces,
+                                   int dtype, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream);
+
 /*
  * Merge of Split partials [CA "Split演算子によるSplit-Kの対応"]: for each row r,
  *   M = max_i m_i over partials with l_i > 0;  w_i = l_i exp(m_i - M);

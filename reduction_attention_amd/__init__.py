@@ -24,6 +24,9 @@ from .api import (  # noqa: F401
     attn_merge_lse,
     attn_mla_decode,
     attn_mla_decode_choose_splits,
+    attn_mla_decode_flat,
+    attn_mla_decode_flat_pieces,
+    attn_mla_decode_flat_workspace_bytes,
     attn_mla_decode_workspace_bytes,
     attn_prefill,
     attn_prefill_bsr,

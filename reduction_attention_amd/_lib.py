@@ -57,6 +57,10 @@ SIGNATURES = {
     "attn_mla_decode_choose_splits": (_i32, [_i32, _i32, _i64, _i32]),
     "attn_mla_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64, _f32,
                                _i32, _i32, _vp, _sz, _vp]),
+    "attn_mla_decode_flat_pieces": (_i32, [_i32, _i32, _i64]),
+    "attn_mla_decode_flat_workspace_bytes": (_sz, [_i32, _i32, _i32, _i64, _i32]),
+    "attn_mla_decode_flat": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                    _f32, _i32, _i32, _vp, _sz, _vp]),
     "attn_merge_lse": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _vp]),
     "attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                             _f32, _i32, _i32, _vp]),

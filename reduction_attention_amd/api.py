@@ -257,6 +257,53 @@ def attn_mla_decode(q, kv, kv_indptr, max_kv_len, scale, num_splits=0, o=None, l
     return o, lse
 
 
+def attn_mla_decode_flat_pieces(B, H, total_kv) -> int:
+    return int(load().attn_mla_decode_flat_pieces(B, H, int(total_kv)))
+
+
+def attn_mla_decode_flat_workspace_bytes(B, H, max_kv_len, total_kv, num_pieces) -> int:
+    return int(load().attn_mla_decode_flat_workspace_bytes(B, H, int(max_kv_len), int(total_kv),
+                                                           int(num_pieces)))
+
+
+def attn_mla_decode_flat(q, kv, kv_indptr, max_kv_len, scale, num_pieces=0, o=None, lse=None,
+                         workspace=None, stream=None, want_lse=True):
+    """MLA decode with the packed cache cut into equal pieces (H a multiple
+    of 64).  q [B,H,576]; kv [total_kv,576] (or [total_kv,1,576]); kv_indptr
+    int32 [B+1].  Returns (o [B,H,512], lse [B,H])."""
+    _dims("q", q, 3)
+    B, H, Dq = q.shape
+    if kv.dim() == 3:
+        if kv.shape[1] != 1:
+            raise ValueError(f"kv must be [total_kv, 576] or [total_kv, 1, 576], not {tuple(kv.shape)}")
+        kv = kv.view(kv.shape[0], kv.shape[2])
+    _dims("kv", kv, 2)
+    if Dq != 576 or kv.shape[1] != 576:
+        raise ValueError("MLA decode expects 576-element query and cache rows (512 + 64)")
+    _same_dtype(q, kv=kv)
+    _indptr("kv_indptr", kv_indptr, B)
+    _shape("o", o, (B, H, 512), q.dtype)
+    _shape("lse", lse, (B, H), torch.float32)
+    lib = load()
+    total = kv.shape[0]
+    P = num_pieces or lib.attn_mla_decode_flat_pieces(B, H, total)
+    need = lib.attn_mla_decode_flat_workspace_bytes(B, H, int(max_kv_len), total, P)
+    _workspace(workspace, need)
+    _placed(q, kv=kv, kv_indptr=kv_indptr, o=o, lse=lse, workspace=workspace)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if o is None:
+        o = torch.empty((B, H, 512), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    st = lib.attn_mla_decode_flat(_ptr(q), _ptr(kv), _ptr(kv_indptr), _ptr(o), _ptr(lse), B, H,
+                                  512, 64, int(max_kv_len), total, float(scale), int(P),
+                                  _dtype_code(q), _ptr(workspace), _workspace(workspace, need),
+                                  _stream(stream))
+    check(st, "attn_mla_decode_flat")
+    return o, lse
+
+
 def attn_decode_partials(q, k, v, kv_indptr, max_kv_len, num_splits, scale=None, o_part=None,
                          m_part=None, l_part=None, stream=None):
     """Split partials only: (o_part [s,B*Hq,D], m_part [s,B*Hq], l_part [s,B*Hq]) fp32."""

@@ -321,11 +321,80 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
                     "mla_decode launch");
 }
 
-// ---- flat split plan -------------------------------------------------------
+// ---- MLA decode, flat plan ------------------------------------------------------
 
 static long long flat_piece_len(long long total_kv, int P) {
   return total_kv > 0 ? (total_kv + P - 1) / P : 0;
 }
+
+int attn_mla_decode_flat_pieces(int B, int H, long long total_kv) {
+  (void)B;
+  if (H <= 0 || H % 64 || total_kv <= 0) return 1;
+  // one many-head workgroup (64 heads, all of a compute unit's LDS) per
+  // compute unit: CUs / (H / 64) pieces, none shorter than 256 keys
+  long long P = attn_device_cu_count() / (H / 64);
+  const long long cap = (total_kv + 255) / 256;
+  if (P > cap) P = cap;
+  if (P < 1) P = 1;
+  if (P > kMaxPieces) P = kMaxPieces;
+  return int(P);
+}
+
+size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long long total_kv,
+                                            int num_pieces) {
+  const int s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces);
+  if (B <= 0 || H <= 0 || s <= 0) return 0;
+  const size_t bytes = size_t(s) * size_t(B) * size_t(H) * (512 + 2) * sizeof(float);
+  return (bytes + 255) & ~size_t(255);
+}
+
+attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t* kv_indptr, void* o,
+                                   float* lse, int B, int H, int Dc, int Dr, int max_kv_len,
+                                   long long total_kv, float scale, int num_pieces, int dtype,
+                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (!q || !kv || !kv_indptr || !o) return fail(ATTN_EINVAL, "mla_decode_flat: null pointer");
+  if (B < 1 || H < 1) return fail(ATTN_EINVAL, "mla_decode_flat: B and H must be >= 1");
+  if (H % 64)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode_flat: H = %d is not a multiple of 64", H);
+  if ((long long)B * H > (1LL << 30))
+    return fail(ATTN_EUNSUPPORTED, "mla_decode_flat: B * H above 2^30");
+  if (Dc != 512 || Dr != 64)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode_flat: latent/rotary widths %d/%d (supported: 512/64)",
+                Dc, Dr);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F16)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode_flat: dtype %d (16-bit only)", dtype);
+  if (max_kv_len < 0 || total_kv < 0) return fail(ATTN_EINVAL, "mla_decode_flat: negative length");
+  if ((long long)max_kv_len > total_kv)
+    return fail(ATTN_EINVAL, "mla_decode_flat: max_kv_len %d exceeds total_kv %lld", max_kv_len,
+                total_kv);
+  if (total_kv > 0x7fffffffLL)
+    return fail(ATTN_EUNSUPPORTED, "mla_decode_flat: total_kv above 2^31 - 1");
+  if (!std::isfinite(scale)) return fail(ATTN_EINVAL, "mla_decode_flat: scale is not finite");
+  if (num_pieces < 0 || num_pieces > kMaxPieces)
+    return fail(ATTN_EINVAL, "mla_decode_flat: num_pieces %d outside [0, %d]", num_pieces, kMaxPieces);
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(o))
+    return fail(ATTN_EINVAL, "mla_decode_flat: q, kv, o must be 16-byte aligned");
+  const int P = num_pieces ? num_pieces : attn_mla_decode_flat_pieces(B, H, total_kv);
+  const int s = attn_decode_flat_max_splits(max_kv_len, total_kv, P);
+  const size_t need = attn_mla_decode_flat_workspace_bytes(B, H, max_kv_len, total_kv, P);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_EWORKSPACE, "mla_decode_flat: workspace needs %zu bytes, got %zu", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned16(workspace))
+    return fail(ATTN_EINVAL, "mla_decode_flat: workspace must be 16-byte aligned");
+  const size_t rows = size_t(B) * H;
+  float* ws = static_cast<float*>(workspace);
+  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, ws, ws + size_t(s) * rows * 512,
+                   ws + size_t(s) * rows * 513, B, H, s, int(flat_piece_len(total_kv, P)),
+                   scale * kLog2e, dtype, 0};
+  a.flat = 1;
+  a.pieces = P;
+  a.total_kv = total_kv;
+  return hip_status(rattn::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)),
+                    "mla_decode_flat launch");
+}
+
+// ---- flat split plan -------------------------------------------------------
 
 int attn_decode_flat_pieces(int B, int Hq, int Hkv, int D, long long total_kv) {
   (void)B;

@@ -865,6 +865,9 @@ hipError_t launch_decode_merge_dv(const MlaArgs& m, hipStream_t st) {
   a.chunk = m.chunk;
   a.dtype = m.dtype;
   a.uniform = m.uniform;
+  a.flat = m.flat;
+  a.pieces = m.pieces;
+  a.total_kv = m.total_kv;
   // four waves (128 dims each) per row
   const dim3 grid(unsigned(int64_t(a.B) * a.Hq));
 #define RATTN_MERGE(TT)                                                                       \

@@ -53,6 +53,11 @@ struct MlaArgs {
   float scale_log2;
   int dtype;
   int uniform;
+  // Flat plan (as DecodeArgs): `pieces` pieces of `chunk` packed cache rows,
+  // s bounds any request's splits.
+  int flat = 0;
+  int pieces = 0;
+  int64_t total_kv = 0;
 };
 
 struct MergeArgs {

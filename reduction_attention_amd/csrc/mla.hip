@@ -308,25 +308,31 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // ---------------------------------------------------------------------------
 // Many heads (H a multiple of 64): the heads are the rows of the score
 // matrix, so the tile feeds 32x32x16 MFMAs with K and V from LDS as in
-// prefill.  Workgroup = 4 waves over 64 heads of one (chunk, request):
-// wave w takes head block hb = w / 2 (32 heads) and half dh = w % 2, i.e.
-// the dims 288 dh .. 288 dh + 287 of the score contraction and the output
-// dims 256 dh .. 256 dh + 255.  The two waves of a head block add their
-// partial scores through LDS (a + b = b + a exactly, so both hold the same
-// scores) and run the same softmax.
+// prefill.  Workgroup = 4 waves over 64 heads of one (chunk, request): wave
+// w takes all 64 heads (two blocks of 32, hb = 0, 1) over quarter dq = w of
+// the dims -- dims 144 dq .. 144 dq + 143 of the score contraction (nine
+// 16-dim steps) and output dims 128 dq .. 128 dq + 127.  Every K or V
+// operand a wave reads from LDS feeds two MFMAs, one per head block, and
+// the two blocks' matrix chains are independent.  The four waves exchange
+// their partial scores through LDS; wave w adds, in quarter order (0 + 1 +
+// 2 + 3), the scores of key quarter w only (keys 8 w + 4 h + 0..3 of the
+// tile in lane half h), forms their weights, and the weights (16-bit) go
+// back through LDS to all four waves for the value update.  So no weight is
+// computed twice; each wave's weight sum and running max cover its own
+// keys and are combined at the end.
 //
 // Softmax reference: the row max of the chunk's first tile, kept for the
-// whole chunk, so the value accumulators (in AGPRs) are never rescaled.  A
-// later weight above 2^64 (2^15 for fp16 operands) sets a flag; the
-// workgroup then runs the chunk again against the chunk's true row max
-// (found on the first pass), which no score exceeds.  Keys far below the reference only lose
-// weights that are negligible against the reference key's weight of 1.
+// whole chunk, so the value accumulators are never rescaled.  A later
+// weight above 2^64 (2^15 for fp16 operands) sets a flag; the workgroup
+// then runs the chunk again against the chunk's true row max (found on the
+// first pass), which no score exceeds.  Keys far below the reference only
+// lose weights that are negligible against the reference key's weight of 1.
 //
 // LDS: three stages of 32 cache rows in natural layout, 72 chunks of 16
 // bytes per row with the chunk index XOR-ed by f(row) = 2 (row % 4) +
 // (row / 4) % 2, so that both the 16-byte K reads (eight consecutive rows,
 // one chunk) and the transposing V reads (four consecutive rows, two
-// chunks) hit distinct banks; plus the score exchange (16 KB).
+// chunks) hit distinct banks; plus the score exchange (32 KB).
 // ---------------------------------------------------------------------------
 constexpr int kMwBK = 32;
 constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 KB per tile
@@ -338,10 +344,6 @@ constexpr int kMwStages = 3;
 // for fp16, whose largest finite value is just below 2^16.
 __device__ __forceinline__ constexpr float mw_overflow(BF16) { return 64.f; }
 __device__ __forceinline__ constexpr float mw_overflow(F16) { return 15.f; }
-// vmcnt(n): the loads of the newest kMwStages - 2 tiles (kMwPerWave per
-// wave and tile) may stay in flight
-constexpr int kMwAhead = (kMwStages - 2) * kMwPerWave;
-constexpr int kMwVmNext = 0x0F70 | (kMwAhead & 15) | ((kMwAhead >> 4) << 14);
 
 __device__ __forceinline__ int mw_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
@@ -356,49 +358,48 @@ __device__ __forceinline__ u32x2 mw_read_tr(lds_cchar* p) {
   return __builtin_bit_cast(u32x2, x);
 }
 
-template <class T>
+template <class T, bool FLAT>
 __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kMwStages * kMwStageBytes / 2];
   // score exchange, quarter-major so a wave's 16-byte accesses are
-  // consecutive across lanes: sx[w][k][lane] = lane's scores 4k .. 4k + 3
-  __shared__ __attribute__((aligned(16))) f32x4 sx[4][4][64];
+  // consecutive across lanes: sx[w][hb][k][lane] = lane's scores 4k .. 4k + 3
+  // of head block hb
+  __shared__ __attribute__((aligned(16))) f32x4 sx[4][2][4][64];
+  // weight exchange: px[w][hb][lane] = the lane's four 16-bit weights of key
+  // quarter w; and per-head maxima / sums combined across the waves
+  __shared__ __attribute__((aligned(16))) u32x2 px[4][2][64];
+  __shared__ float red[4][2][64];
   const int HG = a.H / 64;
   int hg, unit;
-  if (!mla_unit(blockIdx.x, HG, a.s * a.B, hg, unit)) return;
-  const int b = unit / a.s, i = unit % a.s;
+  if (!mla_unit(blockIdx.x, HG, FLAT ? a.pieces : a.s * a.B, hg, unit)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hb = w >> 1, dh = w & 1, h = lane >> 5, l32 = lane & 31;
+  const int dq = w, h = lane >> 5, l32 = lane & 31;
   const int H = a.H;
   const int64_t rows = int64_t(a.B) * H;
-  const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
-  const int n_b = int(kb1 - kb0);
-  const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
-  const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
+
+  // Keys [lo, hi) of request b for this workgroup's 64 heads: split slot i
+  // of the request's splits_b (final output when splits_b == 1).
+  auto segment = [&](int b, int lo, int hi, int i, int splits_b) {
+  const int64_t kb0 = a.kv_indptr[b];
   const int64_t row0 = int64_t(b) * H + 64 * hg;  // the workgroup's first head row
-  const int splits_b = min((n_b + a.chunk - 1) / a.chunk, a.s);  // s bounds the slots
-  if (lo >= hi) {  // split unused by this request
-    if (i == 0) {  // empty request: O = 0, LSE = -inf
-      typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
-      for (int e = tid; e < 64 * kMlaDc; e += 256) o[e] = typename T::elem(0.f);
-      if (a.lse && tid < 64) a.lse[row0 + tid] = -INFINITY;
-    }
-    return;
-  }
   const int n = hi - lo;
   const int ntiles = (n + kMwBK - 1) / kMwBK;
-  const int64_t row = row0 + 32 * hb + l32;  // this lane's head row
+  // this lane's head rows: row0 + l32 (block 0) and row0 + 32 + l32 (block 1)
+  const int64_t rowA = row0 + l32, rowB = row0 + 32 + l32;
 
-  // Q^T operand of the wave's 18 contraction steps: head l32, dims
-  // 16 (18 dh + u) + 8 h .. +8
-  u32x4 qb[18];
+  // Q^T operands of the nine contraction steps, both head blocks: head
+  // l32 (+ 32), dims 144 dq + 16 u + 8 h .. +8
+  u32x4 qa[9], qc[9];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + row * kMlaD + 288 * dh + 8 * h;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + rowA * kMlaD + 144 * dq + 8 * h;
 #pragma unroll
-    for (int u = 0; u < 18; ++u) qb[u] = ldg128(qp + 16 * u);
+    for (int u = 0; u < 9; ++u) qa[u] = ldg128(qp + 16 * u);
 #pragma unroll
-    for (int u = 0; u < 18; ++u) __asm__ volatile("" ::"v"(qb[u]));
+    for (int u = 0; u < 9; ++u) qc[u] = ldg128(qp + 32 * kMlaD + 16 * u);
+#pragma unroll
+    for (int u = 0; u < 9; ++u) __asm__ volatile("" ::"v"(qa[u]), "v"(qc[u]));
   }
 
   // direct-to-LDS loads: instruction x = w + 4k fills stage chunks
@@ -434,156 +435,264 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
   };
 
   // K operand reads (byte offsets in a stage): lane l32 reads key row l32,
-  // chunk ch = 2 (18 dh + u) + h, stored at slot ch ^ f(l32).  Chunks
-  // u and u + 4 are 8 apart and f only touches the low three bits, so four
-  // per-lane offsets and immediates cover the 18 reads.
+  // chunk ch = 18 dq + 2 u + h, stored at slot ch ^ f(l32).  Chunks u and
+  // u + 4 are 8 apart and f only touches the low three bits, so four
+  // per-lane offsets and immediates cover the nine reads.
   int kofs[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    kofs[u] = 2 * (l32 * kMlaD + 8 * ((2 * (18 * dh + u) + h) ^ mw_swz(l32)));
+  for (int u = 0; u < 4; ++u) kofs[u] = 2 * (l32 * kMlaD + 8 * ((18 * dq + 2 * u + h) ^ mw_swz(l32)));
   // V^T operand (transposing reads): lane q + 4e of its 16-lane group
   // points at key row k0 + e (k0 = 16 t + 4 h, then + 8) and dims
-  // 256 dh + 32 db + 16 g2 + 4 q; those rows have f = 2 e + h, and blocks
+  // 128 dq + 32 db + 16 g2 + 4 q; those rows have f = 2 e + h, and blocks
   // db and db + 2 are 8 chunks apart: two per-lane offsets (db even, odd)
   const int tq = lane & 3, te = (lane >> 2) & 3, g2 = (lane >> 4) & 1;
   int vofs[2];
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    const int dim = 256 * dh + 32 * d + 16 * g2 + 4 * tq;
+    const int dim = 128 * dq + 32 * d + 16 * g2 + 4 * tq;
     vofs[d] = 2 * ((4 * h + te) * kMlaD + 8 * ((dim >> 3) ^ (2 * te + h)) + (dim & 7));
   }
 
-  f32x16 o[8];  // O^T: head l32, dims 256 dh + 32 db + 8 (r / 4) + 4 h + r % 4
-  float l = 0.f, mref = 0.f, mrun = -INFINITY;
+  // O^T of both head blocks: head l32, dims 128 dq + 32 db + 8 (r / 4) + 4 h + r % 4
+  f32x16 oa[4], oc[4];
+  float la = 0.f, lc = 0.f, mra = 0.f, mrc = 0.f, mruna = -INFINITY, mrunc = -INFINITY;
   int flag = 0;
   const float c = a.scale_log2;
 
-  // one pass over the chunk; exact = 1: reference fixed to mref from the start
+  // max over the four waves of a per-head value (the same in lanes l and
+  // l ^ 32 on entry and exit); every wave calls it
+  auto wave_max = [&](float v, int hb) {
+    __syncthreads();
+    red[w][hb][lane] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0][hb][lane], red[1][hb][lane]), fmaxf(red[2][hb][lane], red[3][hb][lane]));
+  };
+  // this wave's key quarter of one head block's 32x32 score tile: scores
+  // (log2 units) masked past the chunk end, and their maximum
+  auto quarter = [&](const f32x4& s, int j, float (&x)[4]) {
+    const int key0 = j * kMwBK + 8 * dq + 4 * h;  // keys of x[e]: key0 + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = key0 + e < n ? s[e] * c : -INFINITY;
+    return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  };
+  // weights of the quarter against the reference, summed into l
+  auto weights = [&](const float (&x)[4], float mref, float& l) {
+    f32x4 p;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fexp2(x[e] - mref);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    typedef typename T::elem e4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(u32x2, __builtin_convertvector(p, e4));
+  };
+
+  // the partial scores of tile j (this wave's quarter of the dims), both
+  // head blocks
+  auto scores = [&](int j, f32x16& sa, f32x16& sc) {
+    lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sa[r] = 0.f;
+      sc[r] = 0.f;
+    }
+    lds_cchar* kp[4] = {cur + kofs[0], cur + kofs[1], cur + kofs[2], cur + kofs[3]};
+#pragma unroll
+    for (int u = 0; u < 9; ++u) {
+      const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
+      sa = T::mfma32(as<vec8>(ka), as<vec8>(qa[u]), sa);
+      sc = T::mfma32(as<vec8>(ka), as<vec8>(qc[u]), sc);
+    }
+  };
+  auto publish = [&](const f32x16& sa, const f32x16& sc) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      sx[w][0][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+      sx[w][1][k][lane] = f32x4{sc[4 * k], sc[4 * k + 1], sc[4 * k + 2], sc[4 * k + 3]};
+    }
+  };
+
+  // One pass over the chunk (exact = 1: reference fixed from the start),
+  // software-pipelined: step j computes the scores of tile j + 1 while it
+  // turns tile j's scores (exchanged at the end of step j - 1) into weights,
+  // then runs tile j's value update.  Stages: tile j (values), tile j + 1
+  // (keys), tile j + 2 streaming in.
   auto run = [&](bool exact) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-    l = 0.f;
-    int stage = 0;
-#pragma unroll
-    for (int t = 0; t < kMwStages - 1; ++t) dma(t);
-    __builtin_amdgcn_s_waitcnt(kMwVmNext);  // tile 0 is in
+      for (int r = 0; r < 16; ++r) {
+        oa[db][r] = 0.f;
+        oc[db][r] = 0.f;
+      }
+    la = 0.f;
+    lc = 0.f;
+    dma(0);
+    dma(1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0 and 1 are in
+    __syncthreads();
+    {
+      f32x16 sa, sc;
+      scores(0, sa, sc);
+      publish(sa, sc);
+    }
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
-      dma(j + kMwStages - 1);
-      lds_cchar* cur = (lds_cchar*)(lds) + stage * kMwStageBytes;
-      stage = stage == kMwStages - 1 ? 0 : stage + 1;
-      f32x16 sp;
+      dma(j + 2);
+      // tile j + 1's scores: independent of the weights below
+      f32x16 na, nc;
+      const bool more = j + 1 < ntiles;
+      if (more) scores(j + 1, na, nc);
+      // tile j: this wave's key quarter, the four waves' partial scores
+      // added in quarter order
+      f32x4 ta = sx[0][0][dq][lane], tc = sx[0][1][dq][lane];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sp[r] = 0.f;
-      lds_cchar* kp[4] = {cur + kofs[0], cur + kofs[1], cur + kofs[2], cur + kofs[3]};
-#pragma unroll
-      for (int u = 0; u < 18; ++u) {
-        const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
-        sp = T::mfma32(as<vec8>(ka), as<vec8>(qb[u]), sp);
+      for (int q2 = 1; q2 < 4; ++q2) {
+        ta += sx[q2][0][dq][lane];
+        tc += sx[q2][1][dq][lane];
       }
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        sx[w][k][lane] = f32x4{sp[4 * k], sp[4 * k + 1], sp[4 * k + 2], sp[4 * k + 3]};
-      __syncthreads();
-      f32x16 s;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const f32x4 other = sx[w ^ 1][k][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[4 * k + e] = sp[4 * k + e] + other[e];
-      }
-      // scores in log2 units; keys of this lane: 32 j + 8 (r / 4) + 4 h + r % 4
-      float x[16];
-      const int key0 = j * kMwBK;
-      const bool tail = key0 + kMwBK > n;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = s[r] * c;
-      if (tail) {  // the chunk's last tile: keys past its end
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + 8 * (r >> 2) + 4 * h + (r & 3) >= n) x[r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      float xa[4], xc[4];
+      const float mxa = quarter(ta, j, xa), mxc = quarter(tc, j, xc);
       if (!exact) {
-        mrun = fmaxf(mrun, mx);
-        if (j == 0) {
-          mref = max_halves(mx);  // tile 0 holds a valid key: finite
-        } else if (mx > mref + mw_overflow(T{})) {
+        mruna = fmaxf(mruna, mxa);
+        mrunc = fmaxf(mrunc, mxc);
+        if (j == 0) {  // the reference: tile 0's row max (tile 0 holds a valid key)
+          mra = wave_max(max_halves(mxa), 0);
+          mrc = wave_max(max_halves(mxc), 1);
+        } else if (mxa > mra + mw_overflow(T{}) || mxc > mrc + mw_overflow(T{})) {
           flag = 1;
         }
       }
-      vec8 pb[2];
-      float psum = 0.f;
+      px[w][0][lane] = weights(xa, mra, la);
+      px[w][1][lane] = weights(xc, mrc, lc);
+      __syncthreads();  // weights published; every wave is done reading sx
+      if (more) publish(na, nc);
+      // every key's weights: slots 8t .. 8t + 7 of the value update are key
+      // quarters 2t and 2t + 1
+      vec8 pa[2], pc[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        f32x8 p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = fexp2(x[8 * t + e] - mref);
-          psum += p[e];
-        }
-        pb[t] = T::cvt8(p);
+        const u32x2 a0 = px[2 * t][0][lane], a1 = px[2 * t + 1][0][lane];
+        const u32x2 c0 = px[2 * t][1][lane], c1 = px[2 * t + 1][1][lane];
+        pa[t] = as<vec8>(u32x4{a0[0], a0[1], a1[0], a1[1]});
+        pc[t] = as<vec8>(u32x4{c0[0], c0[1], c1[0], c1[1]});
       }
-      l += psum;
+      lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
       lds_cchar* vp[2] = {cur + vofs[0], cur + vofs[1]};
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           lds_cchar* p = vp[db & 1] + 128 * (db >> 1) + 2 * 16 * t * kMlaD;
           const u32x2 v0 = mw_read_tr(p);
           const u32x2 v1 = mw_read_tr(p + 2 * 8 * kMlaD);
           const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-          o[db] = T::mfma32(as<vec8>(av), pb[t], o[db]);
+          oa[db] = T::mfma32(as<vec8>(av), pa[t], oa[db]);
+          oc[db] = T::mfma32(as<vec8>(av), pc[t], oc[db]);
         }
-      __builtin_amdgcn_s_waitcnt(kMwVmNext);  // tile j + 1 has arrived
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
+      __syncthreads();  // tile j + 1's scores and tile j + 2 published, stage j free
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load outlives the pass
   };
   run(false);
   if (__syncthreads_or(flag)) {  // a score far above the first tile's max
-    mref = max_halves(mrun);
+    mra = wave_max(max_halves(mruna), 0);
+    mrc = wave_max(max_halves(mrunc), 1);
     __syncthreads();
     run(true);
   }
+  // the weight sums of the four key quarters
+  auto wave_sum = [&](float v, int hb) {
+    __syncthreads();
+    red[w][hb][lane] = v;
+    __syncthreads();
+    return ((red[0][hb][lane] + red[1][hb][lane]) + red[2][hb][lane]) + red[3][hb][lane];
+  };
+  la = wave_sum(la, 0);
+  lc = wave_sum(lc, 1);
 
-  l = sum_halves(l);
-  const float inv = 1.f / l;
-  if (splits_b == 1) {
-    typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 256 * dh + 4 * h;
+  auto store = [&](const f32x16 (&o)[4], float l, float mref, int64_t row) {
+    l = sum_halves(l);
+    const float inv = 1.f / l;
+    if (splits_b == 1) {
+      typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 128 * dq + 4 * h;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x8 y;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x8 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = o[db][4 * g4 + e] * inv;
-          y[4 + e] = 0.f;
+          for (int e = 0; e < 4; ++e) {
+            y[e] = o[db][4 * g4 + e] * inv;
+            y[4 + e] = 0.f;
+          }
+          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
         }
-        const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
+      if (a.lse && dq == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
+    } else {
+      float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 128 * dq + 4 * h;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x4 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = o[db][4 * g4 + e] * inv;
+          *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * g4) = y;
+        }
+      if (dq == 0 && h == 0) {
+        a.m_part[int64_t(i) * rows + row] = mref * kLn2;
+        a.l_part[int64_t(i) * rows + row] = l;
       }
-    if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
+    }
+  };
+  store(oa, la, mra, rowA);
+  store(oc, lc, mrc, rowB);
+  };
+
+  if constexpr (!FLAT) {
+    // chunk plan: split i of request b covers its keys [i c, (i + 1) c)
+    const int b = unit / a.s, i = unit % a.s;
+    const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
+    const int n_b = int(kb1 - kb0);
+    const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
+    const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
+    if (lo >= hi) {  // split unused by this request
+      if (i == 0) {  // empty request: O = 0, LSE = -inf
+        const int64_t row0 = int64_t(b) * H + 64 * hg;
+        typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
+        for (int e = tid; e < 64 * kMlaDc; e += 256) o[e] = typename T::elem(0.f);
+        if (a.lse && tid < 64) a.lse[row0 + tid] = -INFINITY;
+      }
+      return;
+    }
+    segment(b, lo, hi, i, min((n_b + a.chunk - 1) / a.chunk, a.s));  // s bounds the slots
   } else {
-    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 256 * dh + 4 * h;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = o[db][4 * g4 + e] * inv;
-        *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * g4) = y;
-      }
-    if (dh == 0 && h == 0) {
-      a.m_part[int64_t(i) * rows + row] = mref * kLn2;
-      a.l_part[int64_t(i) * rows + row] = l;
+    // flat plan: piece p = packed cache rows [p c, (p + 1) c); split i of a
+    // request is its intersection with the i-th piece it overlaps.  The
+    // pieces' request segments are reduced one after the other; requests
+    // inside one piece are final here, the others leave partials for the
+    // merge (which also writes empty requests).
+    const int64_t c = a.chunk, p = unit;
+    const int64_t pos0 = p * c, pos1 = pos0 + c < a.total_kv ? pos0 + c : a.total_kv;
+    if (pos0 >= pos1) return;
+    // first request that may hold row pos0: (indptr entries <= pos0) - 1,
+    // counted 64 entries per step across the lanes
+    int cnt = 0;
+    for (int j0 = 0; j0 <= a.B; j0 += 64) {
+      const int j = j0 + lane;
+      cnt += __popcll(__ballot(j <= a.B && int64_t(a.kv_indptr[j <= a.B ? j : a.B]) <= pos0));
+    }
+    for (int b = __builtin_amdgcn_readfirstlane(cnt > 0 ? cnt - 1 : 0); b < a.B; ++b) {
+      const int64_t r0 = a.kv_indptr[b], r1 = a.kv_indptr[b + 1];
+      if (r0 >= pos1) break;
+      const int64_t lo = r0 > pos0 ? r0 : pos0, hi = r1 < pos1 ? r1 : pos1;
+      if (lo >= hi) continue;  // empty request, or one that ends before pos0
+      const int splits_b = int((r1 - 1) / c - r0 / c) + 1;
+      const int i = int(p - r0 / c);
+      // (with a consistent indptr 0 <= i < s always holds; otherwise nothing
+      // is written outside the workspace)
+      if (splits_b > 1 && (i < 0 || i >= a.s)) continue;
+      segment(b, int(lo - r0), int(hi - r0), i, splits_b);
     }
   }
 }
@@ -591,16 +700,20 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
 template <class T>
 static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
   const int64_t units = int64_t(a.s) * a.B;
-  if (mla_wide(a.H)) {
+  if (a.flat) {  // the flat plan (many-head kernel only)
+    const int64_t nwg = 8 * (a.H / 64) * ((int64_t(a.pieces) + 7) / 8);
+    if (a.pieces > 0 && a.total_kv > 0)
+      hipLaunchKernelGGL((mla_wide_kernel<T, true>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
+  } else if (mla_wide(a.H)) {
     const int64_t nwg = 8 * (a.H / 64) * ((units + 7) / 8);
-    hipLaunchKernelGGL((mla_wide_kernel<T>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((mla_wide_kernel<T, false>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
   } else {
     const int HG = (a.H + 15) / 16;
     const int64_t nwg = 8 * HG * ((units + 7) / 8);
     hipLaunchKernelGGL((mla_decode_kernel<T>), dim3(unsigned(nwg)), dim3(kMlaThreads), 0, st, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.s == 1) return e;
+  if (e != hipSuccess || (a.s == 1 && !a.flat)) return e;
   return launch_decode_merge_dv(a, st);
 }
 

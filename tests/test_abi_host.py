@@ -570,3 +570,20 @@ def test_binding_rejects_host_resident_mask(lib):
     bad.part_bits = bad.part_bits[:10]
     with pytest.raises(ValueError, match="mask part_bits holds"):
         ra.attn_prefill_bsr(q, k, v, bad, kernel="block")
+
+
+def test_mla_flat_host_rules(lib):
+    # no device here: 256 compute units -> 256 / (H / 64) pieces, capped by 256-key pieces
+    assert lib.attn_mla_decode_flat_pieces(32, 128, 83638) == 128
+    assert lib.attn_mla_decode_flat_pieces(32, 64, 83638) == 256
+    assert lib.attn_mla_decode_flat_pieces(2, 128, 1000) == 4
+    s = lib.attn_decode_flat_max_splits(15143, 83638, 128)
+    raw = s * 32 * 128 * 514 * 4
+    assert lib.attn_mla_decode_flat_workspace_bytes(32, 128, 15143, 83638, 128) == (raw + 255) // 256 * 256
+    P = ctypes.c_void_p(256)
+    st = lib.attn_mla_decode_flat(P, P, P, P, None, 4, 48, 512, 64, 100, 400, 0.07, 0, 1, P,
+                                  1 << 30, None)
+    assert st == 2  # ATTN_EUNSUPPORTED: H not a multiple of 64
+    st = lib.attn_mla_decode_flat(P, P, P, P, None, 4, 64, 512, 64, 100, 400, 0.07, 0, 1, P, 16,
+                                  None)
+    assert st == 3  # ATTN_EWORKSPACE

@@ -126,3 +126,81 @@ def test_mla_bit_identical_reruns():
     b = ra().attn_mla_decode(inp["q"], inp["kv"], inp["kv_indptr"], w.L, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---- flat plan (equal pieces of the packed cache; many-head kernel) ---------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("H", [64, 128, 256])
+def test_mla_flat_small_ragged(dtype, H):
+    """Pieces shorter and longer than a tile, requests inside one piece and
+    spread over many, an empty request."""
+    lengths = [1, 31, 32, 33, 0, 300, 64, 517]
+    q, kv, kvp = mla_inputs(lengths, H, dtype, seed=100 + H)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    for P in (0, 1, 2, 3, 7, 50):
+        o, lse = ra().attn_mla_decode_flat(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                           num_pieces=P)
+        torch.cuda.synchronize()
+        check(f"mla flat {dtype} H={H} P={P}", o, o_ref, lse, lse_ref, dtype)
+        assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[4]).all())
+
+
+def test_mla_flat_rows_outside_requests_not_read():
+    """Cache rows before the first request and after the last one hold NaN:
+    the flat plan never reads them (output bit-identical to the clean run)."""
+    lengths = [70, 200, 5]
+    H = 64
+    q, kv, _ = mla_inputs(lengths, H, torch.bfloat16, seed=7)
+    pad = torch.full((40, DC + DR), float("nan"), dtype=torch.bfloat16)
+    kvp = torch.tensor([40, 110, 310, 315], dtype=torch.int32)
+    kv_pad = torch.cat([pad, kv, pad[:23]])
+    o1, l1 = ra().attn_mla_decode_flat(q.to(DEV), kv_pad.to(DEV), kvp.to(DEV), 200, 0.07,
+                                       num_pieces=5)
+    kv_zero = torch.cat([torch.zeros_like(pad), kv, torch.zeros_like(pad[:23])])
+    o2, l2 = ra().attn_mla_decode_flat(q.to(DEV), kv_zero.to(DEV), kvp.to(DEV), 200, 0.07,
+                                       num_pieces=5)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, lse_ref = oracle_mla(q, kv, synth.indptr(lengths), 0.07)
+    check("mla flat padded", o1, o_ref, l1, lse_ref, torch.bfloat16)
+
+
+def test_mla_flat_ragged_128_heads_every_row():
+    """128 heads, ragged lengths in [128, 16384], bf16, the flat plan at its
+    automatic piece count: every row against the oracle."""
+    w = synth.workload("mla_ragged_decode_bf16")
+    inp = w.make(DEV)
+    L = inp["lengths"]
+    P = ra().attn_mla_decode_flat_pieces(w.B, w.Hq, sum(L))
+    print(f"mla flat automatic pieces P={P}", flush=True)
+    o_ref, lse_ref = oracle_mla(inp["q"], inp["kv"], inp["kv_indptr"], w.scale)
+    o, lse = ra().attn_mla_decode_flat(inp["q"], inp["kv"], inp["kv_indptr"], max(L), w.scale)
+    torch.cuda.synchronize()
+    check("mla flat ragged 128 heads every row", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("P", [0, 4])
+def test_mla_flat_far_above_first_tile(P):
+    """The exact second pass inside a flat-plan segment (keys 2^70 above the
+    first tile's weights)."""
+    lengths = [300, 700, 33]
+    H = 64
+    g = synth.gen(61)
+    B = len(lengths)
+    base = torch.where(torch.rand(B, 1, DC + DR, generator=g) < 0.5, -1.0, 1.0)
+    q = (base + 0.25 * torch.randn(B, H, DC + DR, generator=g)).to(torch.bfloat16)
+    kv = (0.5 * torch.randn(sum(lengths), DC + DR, generator=g)).to(torch.bfloat16)
+    start = 0
+    for b, n in enumerate(lengths):
+        hot = [start + j for j in (40, 41, 250) if j < n]
+        kv[hot] = (2.0 * base[b, 0]).to(torch.bfloat16)
+        start += n
+    kvp = synth.indptr(lengths)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    o, lse = ra().attn_mla_decode_flat(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                       num_pieces=P)
+    torch.cuda.synchronize()
+    check(f"mla flat far-above P={P}", o, o_ref, lse, lse_ref, torch.bfloat16)
