@@ -4,6 +4,7 @@
 // before an argument check has passed.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -256,18 +257,35 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
   if (B <= 0 || H <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
   // Workgroups of 16 heads (64 for the many-head kernel) over one chunk.
   // Equal lengths: the largest power-of-two chunk >= 256 keys that gives
-  // every compute unit a workgroup.  Ragged: chunks counted as total/c +
-  // B/2, two 16-head workgroups per compute unit; many-head workgroups
-  // for half the units (their partials are 2 KB per head, so more,
-  // shorter chunks cost more in the merge than they gain in balance); and
-  // an odd s: workgroups are dealt to the eight XCDs round robin, and with
-  // s a multiple of eight the first splits (present in every request)
-  // would all land on the same XCDs while the last ones (mostly empty)
-  // land on the others.
+  // every compute unit a workgroup.  Ragged, 16-head kernel: chunks counted
+  // as total/c + B/2, two workgroups per compute unit, and an odd s:
+  // workgroups are dealt to the eight XCDs round robin, and with s a
+  // multiple of eight the first splits (present in every request) would all
+  // land on the same XCDs while the last ones (mostly empty) land on the
+  // others.  Ragged, 64-head kernel: below.
   const long long cus = attn_device_cu_count();
   const bool wide = rattn::mla_wide(H);
   const long long hg = wide ? H / 64 : (H + 15) / 16;
   const bool uniform = (long long)max_kv_len * B == total_kv;
+  if (wide && !uniform) {
+    // Packed units (only the splits a request has; about total_kv / c + B / 2
+    // of them, a request's last chunk being half full on average), hg
+    // workgroups each and one workgroup per compute unit (the kernel holds
+    // all of its LDS): the shortest chunk, at least 256 keys, whose units
+    // fill k rounds of 95% of the compute units, k the fewest rounds that
+    // leave half a round for chunks beside the requests' last ones.  The
+    // units of an XCD that do not fit its compute units wait for a whole
+    // chunk, so s is rounded down: the chunk ceil(max_kv_len / s) is then
+    // no shorter than c.
+    const double slots = 0.95 * double(cus) / double(hg);
+    const double k = std::ceil((B / 2.0 + slots / 2.0) / slots);
+    const double room = k * slots - B / 2.0;
+    const long long c = std::max(256LL, (long long)std::ceil(double(total_kv) / room));
+    long long s = max_kv_len / c;
+    if (s < 1) s = 1;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return int(s);
+  }
   long long c = 1;
   while (c < max_kv_len) c <<= 1;
   while (c > 256) {
@@ -317,6 +335,10 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
                    s > 1 ? ws + size_t(s) * rows * 513 : nullptr,
                    B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
                    uniform_lengths(B, max_kv_len, total_kv)};
+  a.total_kv = total_kv;
+  // the 64-head kernel's packed (request, split) units: request b owns
+  // max(1, min(ceil(len_b / c), s)) <= len_b / c + 1 of them
+  a.units = int(std::min((long long)s * B, (total_kv + a.chunk - 1) / a.chunk + B));
   return hip_status(rattn::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)),
                     "mla_decode launch");
 }

@@ -58,6 +58,9 @@ struct MlaArgs {
   int flat = 0;
   int pieces = 0;
   int64_t total_kv = 0;
+  // Chunk plan of the 64-head kernel: units (request, split) launched, at
+  // least sum over b of max(1, min(ceil(len_b / chunk), s)).
+  int units = 0;
 };
 
 struct MergeArgs {

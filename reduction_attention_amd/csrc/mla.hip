@@ -308,18 +308,18 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // ---------------------------------------------------------------------------
 // Many heads (H a multiple of 64): the heads are the rows of the score
 // matrix, so the tile feeds 32x32x16 MFMAs with K and V from LDS as in
-// prefill.  Workgroup = 4 waves over 64 heads of one (chunk, request): wave
-// w takes all 64 heads (two blocks of 32, hb = 0, 1) over quarter dq = w of
-// the dims -- dims 144 dq .. 144 dq + 143 of the score contraction (nine
-// 16-dim steps) and output dims 128 dq .. 128 dq + 127.  Every K or V
-// operand a wave reads from LDS feeds two MFMAs, one per head block, and
-// the two blocks' matrix chains are independent.  The four waves exchange
-// their partial scores through LDS; wave w adds, in quarter order (0 + 1 +
-// 2 + 3), the scores of key quarter w only (keys 8 w + 4 h + 0..3 of the
-// tile in lane half h), forms their weights, and the weights (16-bit) go
-// back through LDS to all four waves for the value update.  So no weight is
-// computed twice; each wave's weight sum and running max cover its own
-// keys and are combined at the end.
+// prefill.  Workgroup = 8 waves over 64 heads of one (chunk, request), two
+// waves per SIMD so that one's LDS and matrix latencies overlap the
+// other's work: wave w takes head block hb = w / 4 (32 heads) over quarter
+// dq = w % 4 of the dims -- dims 144 dq .. 144 dq + 143 of the score
+// contraction (nine 16-dim steps) and output dims 128 dq .. 128 dq + 127.
+// The four waves of a head block exchange their partial scores through
+// LDS; wave (hb, dq) adds, in quarter order (0 + 1 + 2 + 3), the scores of
+// key quarter dq only (keys 8 dq + 4 h + 0..3 of the tile in lane half h),
+// forms their weights, and the weights (16-bit) go back through LDS to the
+// four waves for the value update.  So no weight is computed twice; each
+// wave's weight sum and running max cover its own keys and are combined at
+// the end.
 //
 // Softmax reference: the row max of the chunk's first tile, kept for the
 // whole chunk, so the value accumulators are never rescaled.  A later
@@ -332,11 +332,13 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // bytes per row with the chunk index XOR-ed by f(row) = 2 (row % 4) +
 // (row / 4) % 2, so that both the 16-byte K reads (eight consecutive rows,
 // one chunk) and the transposing V reads (four consecutive rows, two
-// chunks) hit distinct banks; plus the score exchange (32 KB).
+// chunks) hit distinct banks; plus the score exchange (32 KB).  A tile
+// arrives through 36 direct-to-LDS load instructions of 1 KB, x = w + 8 k.
 // ---------------------------------------------------------------------------
 constexpr int kMwBK = 32;
 constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 KB per tile
-constexpr int kMwPerWave = kMwInstr / 4;           // 9
+constexpr int kMwWaves = 8;
+constexpr int kMwPerWave = (kMwInstr + kMwWaves - 1) / kMwWaves;  // 5 (waves 4..7: 4)
 constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
 constexpr int kMwStages = 3;
 // A weight above 2^mw_overflow forces the exact pass: 2^64 for bf16 (its
@@ -359,23 +361,24 @@ __device__ __forceinline__ u32x2 mw_read_tr(lds_cchar* p) {
 }
 
 template <class T, bool FLAT>
-__global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
+__global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kMwStages * kMwStageBytes / 2];
   // score exchange, quarter-major so a wave's 16-byte accesses are
-  // consecutive across lanes: sx[w][hb][k][lane] = lane's scores 4k .. 4k + 3
-  // of head block hb
+  // consecutive across lanes: sx[dq][hb][k][lane] = lane's scores 4k .. 4k + 3
+  // of head block hb, dim quarter dq
   __shared__ __attribute__((aligned(16))) f32x4 sx[4][2][4][64];
-  // weight exchange: px[w][hb][lane] = the lane's four 16-bit weights of key
-  // quarter w; and per-head maxima / sums combined across the waves
+  // weight exchange: px[dq][hb][lane] = the lane's four 16-bit weights of key
+  // quarter dq; and per-head maxima / sums combined across the four waves of
+  // a head block
   __shared__ __attribute__((aligned(16))) u32x2 px[4][2][64];
   __shared__ float red[4][2][64];
   const int HG = a.H / 64;
   int hg, unit;
-  if (!mla_unit(blockIdx.x, HG, FLAT ? a.pieces : a.s * a.B, hg, unit)) return;
+  if (!mla_unit(blockIdx.x, HG, FLAT ? a.pieces : a.units, hg, unit)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dq = w, h = lane >> 5, l32 = lane & 31;
+  const int dq = w & 3, hb = w >> 2, h = lane >> 5, l32 = lane & 31;
   const int H = a.H;
   const int64_t rows = int64_t(a.B) * H;
 
@@ -386,29 +389,27 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
   const int64_t row0 = int64_t(b) * H + 64 * hg;  // the workgroup's first head row
   const int n = hi - lo;
   const int ntiles = (n + kMwBK - 1) / kMwBK;
-  // this lane's head rows: row0 + l32 (block 0) and row0 + 32 + l32 (block 1)
-  const int64_t rowA = row0 + l32, rowB = row0 + 32 + l32;
+  // this lane's head row: head l32 of the wave's block
+  const int64_t rowA = row0 + 32 * hb + l32;
 
-  // Q^T operands of the nine contraction steps, both head blocks: head
-  // l32 (+ 32), dims 144 dq + 16 u + 8 h .. +8
-  u32x4 qa[9], qc[9];
+  // Q^T operands of the nine contraction steps: head 32 hb + l32, dims
+  // 144 dq + 16 u + 8 h .. +8
+  u32x4 qa[9];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + rowA * kMlaD + 144 * dq + 8 * h;
 #pragma unroll
     for (int u = 0; u < 9; ++u) qa[u] = ldg128(qp + 16 * u);
 #pragma unroll
-    for (int u = 0; u < 9; ++u) qc[u] = ldg128(qp + 32 * kMlaD + 16 * u);
-#pragma unroll
-    for (int u = 0; u < 9; ++u) __asm__ volatile("" ::"v"(qa[u]), "v"(qc[u]));
+    for (int u = 0; u < 9; ++u) __asm__ volatile("" ::"v"(qa[u]));
   }
 
-  // direct-to-LDS loads: instruction x = w + 4k fills stage chunks
+  // direct-to-LDS loads: instruction x = w + 8k (x < 36) fills stage chunks
   // 64x .. 64x + 63; lane chunk q = 64x + lane is row q / 72, slot q % 72,
   // holding chunk slot ^ f(row) of the row
   int voff[kMwPerWave];
 #pragma unroll
   for (int k = 0; k < kMwPerWave; ++k) {
-    const int q = 64 * (w + 4 * k) + lane;
+    const int q = 64 * (w + kMwWaves * k) + lane;
     const int r = q / kMlaChunks, c = q % kMlaChunks;
     voff[k] = (r * kMlaChunks + (c ^ mw_swz(r))) * 16;
   }
@@ -426,12 +427,13 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
     const uint32_t st = lds0 + uint32_t(tile % kMwStages) * kMwStageBytes;
 #pragma unroll
     for (int k = 0; k < kMwPerWave; ++k)
-      __asm__ volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(st + k * 4096)), "v"(voff[k]), "s"(rsv)
-          : "memory", "m0");
+      if (w + kMwWaves * k < kMwInstr)
+        __asm__ volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "buffer_load_dwordx4 %1, %2, 0 offen lds"
+            :
+            : "s"(__builtin_amdgcn_readfirstlane(st + k * 1024 * kMwWaves)), "v"(voff[k]), "s"(rsv)
+            : "memory", "m0");
   };
 
   // K operand reads (byte offsets in a stage): lane l32 reads key row l32,
@@ -453,17 +455,17 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
     vofs[d] = 2 * ((4 * h + te) * kMlaD + 8 * ((dim >> 3) ^ (2 * te + h)) + (dim & 7));
   }
 
-  // O^T of both head blocks: head l32, dims 128 dq + 32 db + 8 (r / 4) + 4 h + r % 4
-  f32x16 oa[4], oc[4];
-  float la = 0.f, lc = 0.f, mra = 0.f, mrc = 0.f, mruna = -INFINITY, mrunc = -INFINITY;
+  // O^T of the head block: head l32, dims 128 dq + 32 db + 8 (r / 4) + 4 h + r % 4
+  f32x16 oa[4];
+  float la = 0.f, mra = 0.f, mruna = -INFINITY;
   int flag = 0;
   const float c = a.scale_log2;
 
-  // max over the four waves of a per-head value (the same in lanes l and
-  // l ^ 32 on entry and exit); every wave calls it
-  auto wave_max = [&](float v, int hb) {
+  // max over the head block's four waves of a per-head value (the same in
+  // lanes l and l ^ 32 on entry and exit); every wave calls it
+  auto wave_max = [&](float v) {
     __syncthreads();
-    red[w][hb][lane] = v;
+    red[dq][hb][lane] = v;
     __syncthreads();
     return fmaxf(fmaxf(red[0][hb][lane], red[1][hb][lane]), fmaxf(red[2][hb][lane], red[3][hb][lane]));
   };
@@ -485,29 +487,23 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
     return __builtin_bit_cast(u32x2, __builtin_convertvector(p, e4));
   };
 
-  // the partial scores of tile j (this wave's quarter of the dims), both
-  // head blocks
-  auto scores = [&](int j, f32x16& sa, f32x16& sc) {
+  // the partial scores of tile j (this wave's quarter of the dims, its head
+  // block)
+  auto scores = [&](int j, f32x16& sa) {
     lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sa[r] = 0.f;
-      sc[r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) sa[r] = 0.f;
     lds_cchar* kp[4] = {cur + kofs[0], cur + kofs[1], cur + kofs[2], cur + kofs[3]};
 #pragma unroll
     for (int u = 0; u < 9; ++u) {
       const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
       sa = T::mfma32(as<vec8>(ka), as<vec8>(qa[u]), sa);
-      sc = T::mfma32(as<vec8>(ka), as<vec8>(qc[u]), sc);
     }
   };
-  auto publish = [&](const f32x16& sa, const f32x16& sc) {
+  auto publish = [&](const f32x16& sa) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      sx[w][0][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
-      sx[w][1][k][lane] = f32x4{sc[4 * k], sc[4 * k + 1], sc[4 * k + 2], sc[4 * k + 3]};
-    }
+    for (int k = 0; k < 4; ++k)
+      sx[dq][hb][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
   };
 
   // One pass over the chunk (exact = 1: reference fixed from the start),
@@ -519,61 +515,49 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        oa[db][r] = 0.f;
-        oc[db][r] = 0.f;
-      }
+      for (int r = 0; r < 16; ++r) oa[db][r] = 0.f;
     la = 0.f;
-    lc = 0.f;
     dma(0);
     dma(1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0 and 1 are in
     __syncthreads();
     {
-      f32x16 sa, sc;
-      scores(0, sa, sc);
-      publish(sa, sc);
+      f32x16 sa;
+      scores(0, sa);
+      publish(sa);
     }
     __syncthreads();
     for (int j = 0; j < ntiles; ++j) {
       dma(j + 2);
       // tile j + 1's scores: independent of the weights below
-      f32x16 na, nc;
+      f32x16 na;
       const bool more = j + 1 < ntiles;
-      if (more) scores(j + 1, na, nc);
+      if (more) scores(j + 1, na);
       // tile j: this wave's key quarter, the four waves' partial scores
       // added in quarter order
-      f32x4 ta = sx[0][0][dq][lane], tc = sx[0][1][dq][lane];
+      f32x4 ta = sx[0][hb][dq][lane];
 #pragma unroll
-      for (int q2 = 1; q2 < 4; ++q2) {
-        ta += sx[q2][0][dq][lane];
-        tc += sx[q2][1][dq][lane];
-      }
-      float xa[4], xc[4];
-      const float mxa = quarter(ta, j, xa), mxc = quarter(tc, j, xc);
+      for (int q2 = 1; q2 < 4; ++q2) ta += sx[q2][hb][dq][lane];
+      float xa[4];
+      const float mxa = quarter(ta, j, xa);
       if (!exact) {
         mruna = fmaxf(mruna, mxa);
-        mrunc = fmaxf(mrunc, mxc);
         if (j == 0) {  // the reference: tile 0's row max (tile 0 holds a valid key)
-          mra = wave_max(max_halves(mxa), 0);
-          mrc = wave_max(max_halves(mxc), 1);
-        } else if (mxa > mra + mw_overflow(T{}) || mxc > mrc + mw_overflow(T{})) {
+          mra = wave_max(max_halves(mxa));
+        } else if (mxa > mra + mw_overflow(T{})) {
           flag = 1;
         }
       }
-      px[w][0][lane] = weights(xa, mra, la);
-      px[w][1][lane] = weights(xc, mrc, lc);
+      px[dq][hb][lane] = weights(xa, mra, la);
       __syncthreads();  // weights published; every wave is done reading sx
-      if (more) publish(na, nc);
+      if (more) publish(na);
       // every key's weights: slots 8t .. 8t + 7 of the value update are key
       // quarters 2t and 2t + 1
-      vec8 pa[2], pc[2];
+      vec8 pa[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const u32x2 a0 = px[2 * t][0][lane], a1 = px[2 * t + 1][0][lane];
-        const u32x2 c0 = px[2 * t][1][lane], c1 = px[2 * t + 1][1][lane];
+        const u32x2 a0 = px[2 * t][hb][lane], a1 = px[2 * t + 1][hb][lane];
         pa[t] = as<vec8>(u32x4{a0[0], a0[1], a1[0], a1[1]});
-        pc[t] = as<vec8>(u32x4{c0[0], c0[1], c1[0], c1[1]});
       }
       lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
       lds_cchar* vp[2] = {cur + vofs[0], cur + vofs[1]};
@@ -586,7 +570,6 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
           const u32x2 v1 = mw_read_tr(p + 2 * 8 * kMlaD);
           const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
           oa[db] = T::mfma32(as<vec8>(av), pa[t], oa[db]);
-          oc[db] = T::mfma32(as<vec8>(av), pc[t], oc[db]);
         }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
       __syncthreads();  // tile j + 1's scores and tile j + 2 published, stage j free
@@ -594,20 +577,18 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
   };
   run(false);
   if (__syncthreads_or(flag)) {  // a score far above the first tile's max
-    mra = wave_max(max_halves(mruna), 0);
-    mrc = wave_max(max_halves(mrunc), 1);
+    mra = wave_max(max_halves(mruna));
     __syncthreads();
     run(true);
   }
   // the weight sums of the four key quarters
-  auto wave_sum = [&](float v, int hb) {
+  auto wave_sum = [&](float v) {
     __syncthreads();
-    red[w][hb][lane] = v;
+    red[dq][hb][lane] = v;
     __syncthreads();
     return ((red[0][hb][lane] + red[1][hb][lane]) + red[2][hb][lane]) + red[3][hb][lane];
   };
-  la = wave_sum(la, 0);
-  lc = wave_sum(lc, 1);
+  la = wave_sum(la);
 
   auto store = [&](const f32x16 (&o)[4], float l, float mref, int64_t row) {
     l = sum_halves(l);
@@ -646,26 +627,57 @@ __global__ __launch_bounds__(256, 1) void mla_wide_kernel(MlaArgs a) {
     }
   };
   store(oa, la, mra, rowA);
-  store(oc, lc, mrc, rowB);
   };
 
   if constexpr (!FLAT) {
-    // chunk plan: split i of request b covers its keys [i c, (i + 1) c)
-    const int b = unit / a.s, i = unit % a.s;
+    // chunk plan: split i of request b covers its keys [i c, (i + 1) c).
+    // Units are packed: request b owns n_b = min(ceil(len_b / c), s)
+    // consecutive units (one for an empty request, which writes its zero
+    // rows), so no workgroup slot goes to a split the request does not
+    // have and the units dealt to each XCD carry nearly equal work.  The
+    // request of this unit is found by a prefix sum of n_b over the
+    // requests, 64 at a time across the lanes.
+    const int64_t c = a.chunk;
+    int b = -1, i = 0;
+    int base = 0;  // units owned by the requests before j0 (at most s * B < 2^27)
+    for (int j0 = 0; j0 < a.B; j0 += 64) {
+      const int j = j0 + lane;
+      int nb = 0;
+      if (j < a.B) {
+        const int64_t len = int64_t(a.kv_indptr[j + 1]) - a.kv_indptr[j];
+        nb = len > 0 ? int(min((len + c - 1) / c, int64_t(a.s))) : 1;
+      }
+      int incl = nb;  // inclusive prefix sum across the lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+      }
+      const int first = base + incl - nb;
+      const uint64_t hit = __ballot(nb > 0 && unit >= first && unit < first + nb);
+      if (hit) {
+        const int l = __ffsll((unsigned long long)hit) - 1;
+        b = j0 + l;
+        i = int(unit - __shfl(first, l));
+        break;
+      }
+      base += __shfl(incl, 63);
+    }
+    if (b < 0) return;  // past the last unit
+    b = __builtin_amdgcn_readfirstlane(b);
+    i = __builtin_amdgcn_readfirstlane(i);
     const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
     const int n_b = int(kb1 - kb0);
-    const int lo = int(int64_t(i) * a.chunk < n_b ? int64_t(i) * a.chunk : n_b);
-    const int hi = lo + a.chunk < n_b ? lo + a.chunk : n_b;
-    if (lo >= hi) {  // split unused by this request
-      if (i == 0) {  // empty request: O = 0, LSE = -inf
-        const int64_t row0 = int64_t(b) * H + 64 * hg;
-        typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
-        for (int e = tid; e < 64 * kMlaDc; e += 256) o[e] = typename T::elem(0.f);
-        if (a.lse && tid < 64) a.lse[row0 + tid] = -INFINITY;
-      }
+    if (n_b <= 0) {  // empty request: O = 0, LSE = -inf
+      const int64_t row0 = int64_t(b) * H + 64 * hg;
+      typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
+      for (int e = tid; e < 64 * kMlaDc; e += 64 * kMwWaves) o[e] = typename T::elem(0.f);
+      if (a.lse && tid < 64) a.lse[row0 + tid] = -INFINITY;
       return;
     }
-    segment(b, lo, hi, i, min((n_b + a.chunk - 1) / a.chunk, a.s));  // s bounds the slots
+    const int lo = int(int64_t(i) * c);
+    const int hi = lo + c < n_b ? int(lo + c) : n_b;
+    segment(b, lo, hi, i, int(min((int64_t(n_b) + c - 1) / c, int64_t(a.s))));
   } else {
     // flat plan: piece p = packed cache rows [p c, (p + 1) c); split i of a
     // request is its intersection with the i-th piece it overlaps.  The
@@ -703,10 +715,10 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
   if (a.flat) {  // the flat plan (many-head kernel only)
     const int64_t nwg = 8 * (a.H / 64) * ((int64_t(a.pieces) + 7) / 8);
     if (a.pieces > 0 && a.total_kv > 0)
-      hipLaunchKernelGGL((mla_wide_kernel<T, true>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((mla_wide_kernel<T, true>), dim3(unsigned(nwg)), dim3(64 * kMwWaves), 0, st, a);
   } else if (mla_wide(a.H)) {
-    const int64_t nwg = 8 * (a.H / 64) * ((units + 7) / 8);
-    hipLaunchKernelGGL((mla_wide_kernel<T, false>), dim3(unsigned(nwg)), dim3(256), 0, st, a);
+    const int64_t nwg = 8 * (a.H / 64) * ((int64_t(a.units) + 7) / 8);
+    hipLaunchKernelGGL((mla_wide_kernel<T, false>), dim3(unsigned(nwg)), dim3(64 * kMwWaves), 0, st, a);
   } else {
     const int HG = (a.H + 15) / 16;
     const int64_t nwg = 8 * HG * ((units + 7) / 8);

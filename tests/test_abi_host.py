@@ -152,10 +152,13 @@ def test_mla_host_rules(lib):
     # 128 heads: the many-head kernel, two 64-head groups per chunk;
     # c = 1024 is the first to give 2 * 32 * 4 = 256 workgroups
     assert lib.attn_mla_decode_choose_splits(32, 128, 32 * 4096, 4096) == 4
-    # ragged: 100000 keys, longest 16000, 128 heads: c = 2048 gives
-    # 2 * (49 + 16) >= 128 workgroups (half the CUs); s = ceil(16000 / 2048)
-    # = 8, made odd
-    assert lib.attn_mla_decode_choose_splits(32, 128, 100000, 16000) == 9
+    # ragged, 128 heads (packed units of the many-head kernel): room for
+    # 0.95 * 256 / 2 - 32 / 2 = 105.6 units beside the requests' last
+    # chunks, c = ceil(100000 / 105.6) = 947, s = floor(16000 / 947) = 16
+    assert lib.attn_mla_decode_choose_splits(32, 128, 100000, 16000) == 16
+    # many requests: 512 of them take two rounds and more; k = 3 rounds
+    # leave 3 * 121.6 - 256 = 108.8 units, c = 14119 > 16000 / 2: s = 1
+    assert lib.attn_mla_decode_choose_splits(512, 128, 512 * 3000, 16000) == 1
     # the same batch at 16 heads (one 16-head group): two workgroups per CU
     # would need c < 256, so c stops at 256: s = ceil(16000 / 256) = 63
     assert lib.attn_mla_decode_choose_splits(32, 16, 100000, 16000) == 63

@@ -50,6 +50,29 @@ def test_mla_small_ragged(dtype, H):
     assert bool((o[4] == 0).all()) and bool(torch.isinf(lse[4]).all())
 
 
+@pytest.mark.parametrize("H", [64, 128])
+def test_mla_many_requests_packed_units(H):
+    """150 requests (the many-head kernel finds a unit's request by a prefix
+    sum over 64 requests per step, so three steps), a tenth of them empty,
+    the others 1 .. 400 keys: every split count from one unit per request to
+    more splits than the longest request has tiles."""
+    g = torch.Generator().manual_seed(31)
+    lengths = torch.randint(1, 401, (150,), generator=g)
+    lengths[torch.randperm(150, generator=g)[:15]] = 0
+    lengths = lengths.tolist()
+    q, kv, kvp = mla_inputs(lengths, H, torch.bfloat16, seed=32)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    for s in (0, 1, 2, 5, 17):
+        print(f"mla packed units H={H} B=150 s={s}", flush=True)
+        o, lse = ra().attn_mla_decode(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                      num_splits=s)
+        torch.cuda.synchronize()
+        check(f"mla packed H={H} s={s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+        empty = [b for b, n in enumerate(lengths) if n == 0]
+        assert bool((o[empty] == 0).all()) and bool(torch.isinf(lse[empty]).all())
+
+
 def test_mla_workload_full_parity():
     """32 requests x 4096 cached tokens, 16 heads, bf16: every row."""
     w = synth.workload("mla_decode_bf16")
