@@ -224,15 +224,20 @@ attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void*
  * up to 256; 0 for invalid arguments. */
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
 
-/* The split count attn_mla_decode picks when num_splits = 0: s = ceil(max_kv_len
- * / c) with c the largest power of two >= 256 keys such that hg * chunks
- * reaches one workgroup per compute unit for equal lengths (chunks =
- * B * ceil(max_kv_len / c)); for ragged lengths (chunks = total_kv / c +
- * B / 2, and s made odd so that the splits of the requests spread over the
- * eight XCDs) two per compute unit with 16-head workgroups, one per two
- * compute units with 64-head ones.  hg = H / 64 when H is a multiple of 64
- * (the many-head kernel), else ceil(H / 16).  Within [1, 256].  Fitted to
- * sweeps on MI355X. */
+/* The split count attn_mla_decode picks when num_splits = 0.  hg = H / 64
+ * workgroups per chunk when H is a multiple of 64 (the many-head kernel),
+ * else ceil(H / 16).
+ *  - equal lengths: s = ceil(max_kv_len / c), c the largest power of two
+ *    >= 256 keys such that hg * B * ceil(max_kv_len / c) reaches one
+ *    workgroup per compute unit;
+ *  - ragged, 16-head workgroups: the same with chunks counted as total_kv /
+ *    c + B / 2, two workgroups per compute unit, and s made odd (so that
+ *    the requests' first splits do not all land on the same XCDs);
+ *  - ragged, many-head kernel (which launches only the chunks a request
+ *    has): with slots = 0.95 * CUs / hg and k the fewest rounds such that
+ *    k * slots - B / 2 >= slots / 2, c = max(256, ceil(total_kv / (k *
+ *    slots - B / 2))) and s = floor(max_kv_len / c).
+ * Within [1, 256].  Fitted to sweeps on MI355X. */
 int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len);
 
 /*
@@ -255,6 +260,12 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
  * o         [B, H, 512]           element type `dtype`
  * lse       [B, H] fp32 (natural log), or NULL
  * Dc, Dr      512 and 64 (other widths: ATTN_EUNSUPPORTED)
+ * max_kv_len  the longest request (keys past max_kv_len of a request are not
+ *   attended: s chunks of ceil(max_kv_len / s) keys cover it)
+ * total_kv    kv_indptr[B] - kv_indptr[0]; the many-head kernel launches
+ *   min(s * B, ceil(total_kv / c) + B) workgroups per 64 heads, one per
+ *   (request, chunk) the request has, so a smaller total_kv leaves
+ *   requests unwritten.
  * num_splits  s in [1, 256], or 0 for attn_mla_decode_choose_splits; s = 1
  *   needs no workspace (may be NULL).
  * workspace   at least attn_mla_decode_workspace_bytes(B, H, s) bytes when
