@@ -849,35 +849,6 @@ hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t 
   return hipGetLastError();
 }
 
-// The decode merge for MLA's 512-wide latent outputs (chunk plan).
-hipError_t launch_decode_merge_dv(const MlaArgs& m, hipStream_t st) {
-  DecodeArgs a{};
-  a.kv_indptr = m.kv_indptr;
-  a.o = m.o;
-  a.lse = m.lse;
-  a.o_part = m.o_part;
-  a.m_part = m.m_part;
-  a.l_part = m.l_part;
-  a.B = m.B;
-  a.Hq = m.H;
-  a.D = 512;
-  a.s = m.s;
-  a.chunk = m.chunk;
-  a.dtype = m.dtype;
-  a.uniform = m.uniform;
-  a.flat = m.flat;
-  a.pieces = m.pieces;
-  a.total_kv = m.total_kv;
-  // four waves (128 dims each) per row
-  const dim3 grid(unsigned(int64_t(a.B) * a.Hq));
-#define RATTN_MERGE(TT)                                                                       \
-  if (a.uniform) hipLaunchKernelGGL((decode_merge_kernel<512, TT, 16>), grid, dim3(256), 0, st, a); \
-  else hipLaunchKernelGGL((decode_merge_kernel<512, TT, 32>), grid, dim3(256), 0, st, a)
-  if (a.dtype == 1) { RATTN_MERGE(__bf16); } else { RATTN_MERGE(_Float16); }
-#undef RATTN_MERGE
-  return hipGetLastError();
-}
-
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
   if (a.dtype == 0) {

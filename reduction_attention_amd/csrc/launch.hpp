@@ -131,7 +131,6 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 // head count is a multiple of 64, the 16-head kernel otherwise.
 inline bool mla_wide(int H) { return H >= 64 && H % 64 == 0; }
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st);
-hipError_t launch_decode_merge_dv(const MlaArgs& a, hipStream_t st);  // value width 512
 hipError_t launch_split_ranges(const int32_t* kv_indptr, int B, int s, int chunk, int32_t* ranges,
                                hipStream_t st);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);

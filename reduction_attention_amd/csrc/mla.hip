@@ -709,6 +709,108 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the split partials (512-wide latent outputs), the log-sum-exp
+// merge of the Split operator: M = max m_i, w_i = l_i e^{m_i - M},
+// O = sum w_i o_i / sum w_i, LSE = M + ln sum w_i.  One wave per (request,
+// head) row; lane l holds dims 8l .. 8l + 7, so one split's partial row is a
+// single 2 KB read by the wave (two 16-byte loads per lane), and the splits
+// arrive in batches of SB whose loads are all issued before the first is
+// used (one memory round trip per batch; a batch's slots past the last
+// split re-read the last one and weigh it 0).  A request's split count comes from
+// kv_indptr and the chunk (or piece) length, capped at s, so no read leaves
+// the workspace; requests held by one split were written by the kernel
+// itself.  An empty request of the flat plan is written here (O = 0, LSE =
+// -inf); the chunk plan's kernel writes its own.
+// ---------------------------------------------------------------------------
+template <class T, int SB>
+__global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = int64_t(a.B) * a.H;
+  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int b = int(row / a.H);
+  const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
+  const int64_t c = a.chunk;
+  int64_t n64 = 0;
+  if (c > 0 && kb1 > kb0) n64 = a.flat ? (kb1 - 1) / c - kb0 / c + 1 : (kb1 - kb0 + c - 1) / c;
+  const int n = int(n64 < a.s ? n64 : a.s);
+  typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 8 * lane;
+  if (n == 0 && a.flat) {
+    *reinterpret_cast<u32x4*>(orow) = u32x4{0u, 0u, 0u, 0u};
+    if (a.lse && lane == 0) a.lse[row] = -INFINITY;
+  }
+  if (n <= 1) return;
+
+  // splits [i0, i0 + cnt) of one batch of 64: partial rows read SB at a
+  // time, each weighed by lane j's weight
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 x0[SB], x1[SB];
+  auto load = [&](int i0, int j0, int cnt) {
+    const float* op = a.o_part + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
+      const float* pj = op + int64_t(jj) * rows * kMlaDc;
+      x0[j] = *reinterpret_cast<const f32x4*>(pj);
+      x1[j] = *reinterpret_cast<const f32x4*>(pj + 4);
+    }
+  };
+  auto add = [&](float wi, int j0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int jj = j0 + j < 64 ? j0 + j : 63;
+      float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), jj));
+      wj = j0 + j < cnt ? wj : 0.f;
+      acc0 += wj * x0[j];
+      acc1 += wj * x1[j];
+    }
+  };
+  // the first 64 splits' (m, l) and the first SB partial rows go out
+  // together, before any of them is used
+  const int cnt0 = n < 64 ? n : 64;
+  float m0 = -INFINITY, l0 = 0.f;
+  if (lane < cnt0) {
+    m0 = a.m_part[int64_t(lane) * rows + row];
+    l0 = a.l_part[int64_t(lane) * rows + row];
+  }
+  load(0, 0, cnt0);
+  float M = m0;
+  for (int i = 64 + lane; i < n; i += 64) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
+  float wsum = 0.f;
+  {
+    const float wi = lane < cnt0 ? l0 * fexp2((m0 - M) * kLog2e) : 0.f;
+    wsum += wi;
+    add(wi, 0, cnt0);
+    for (int j0 = SB; j0 < cnt0; j0 += SB) {
+      load(0, j0, cnt0);
+      add(wi, j0, cnt0);
+    }
+  }
+  for (int i0 = 64; i0 < n; i0 += 64) {  // more than 64 splits
+    const int cnt = n - i0 < 64 ? n - i0 : 64;
+    float wi = 0.f;
+    if (lane < cnt) {
+      const int64_t k = int64_t(i0 + lane) * rows + row;
+      wi = a.l_part[k] * fexp2((a.m_part[k] - M) * kLog2e);
+    }
+    wsum += wi;
+    for (int j0 = 0; j0 < cnt; j0 += SB) {
+      load(i0, j0, cnt);
+      add(wi, j0, cnt);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) wsum += shfl_xor(wsum, off);
+  const float inv = 1.f / wsum;
+  const f32x8 y = {acc0[0] * inv, acc0[1] * inv, acc0[2] * inv, acc0[3] * inv,
+                   acc1[0] * inv, acc1[1] * inv, acc1[2] * inv, acc1[3] * inv};
+  *reinterpret_cast<u32x4*>(orow) = __builtin_bit_cast(u32x4, T::cvt8(y));
+  if (a.lse && lane == 0) a.lse[row] = M + flog2(wsum) * kLn2;
+}
+
 template <class T>
 static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
   const int64_t units = int64_t(a.s) * a.B;
@@ -726,7 +828,11 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (a.s == 1 && !a.flat)) return e;
-  return launch_decode_merge_dv(a, st);
+  const int64_t rows = int64_t(a.B) * a.H;
+  const dim3 grid(unsigned((rows + 3) / 4));
+  if (a.s <= 8) hipLaunchKernelGGL((mla_merge_kernel<T, 8>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((mla_merge_kernel<T, 16>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t st) {
