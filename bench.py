@@ -44,7 +44,7 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--splits", type=int, default=0, help="force the decode split count")
     p.add_argument("--only", choices=["decode", "prefill", "ragged", "ragged_flat", "mla",
@@ -402,8 +402,8 @@ def bench_tiny_decode(torch, ra, synth, args, timer):
                 **out)
 
 
-def bench_split_sweep(torch, ra, synth, args, timer, splits=(4, 8, 16)):
-    """The headline decode step at a few split counts around the rule's."""
+def bench_split_sweep(torch, ra, synth, args, timer, splits=(1, 2, 4, 8, 16, 32, 64)):
+    """The headline decode step at split counts 1 .. 64 (the rule picks 8)."""
     w = synth.workload("llama3_8b_decode_bf16")
     inp = w.make("cuda:0")
     q, kvp = inp["q"], inp["kv_indptr"]
@@ -414,8 +414,8 @@ def bench_split_sweep(torch, ra, synth, args, timer, splits=(4, 8, 16)):
     kvb, qb, ob, lb, ib = decode_bytes(w.B, w.Hq, w.Hkv, w.D, w.B * w.L, 2)
     out = {}
     for s in splits:
-        ws = torch.empty(ra.attn_decode_workspace_bytes(w.B, w.Hq, w.D, s), dtype=torch.uint8,
-                         device=q.device)
+        ws = torch.empty(max(ra.attn_decode_workspace_bytes(w.B, w.Hq, w.D, s), 256),
+                         dtype=torch.uint8, device=q.device)
 
         def step(i):
             k, v = sets[i % 3]
