@@ -74,6 +74,32 @@ def test_decode_chunk_and_flat_in_graphs():
         check_replays(g, (o, lse), eager, lambda: scratch.mul_(1.0001))
 
 
+def test_decode_noalloc_in_graph():
+    """The entry point that allocates nothing, for callers under graph
+    capture: its split partials live in the library's own device array, so
+    the graph holds no workspace.  (The first call, made eagerly here as a
+    serving loop would before capturing, looks the array's address up.)"""
+    lengths = [700, 1, 64, 0, 513, 2048]
+    q, k, v, kv = synth.decode_inputs(len(lengths), 8, 2, 128, lengths, torch.bfloat16, seed=5)
+    q, k, v, kv = q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV)
+    B, Hq, D = q.shape
+    s = 5
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=DEV)
+    call = lambda st: ra().attn_decode_splitkv_noalloc(q, k, v, kv, max(lengths), o, lse=lse,
+                                                        num_splits=s, stream=st)
+    call(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    eager = (o.clone(), lse.clone())
+    ws = torch.empty(ra().attn_decode_workspace_bytes(B, Hq, D, s), dtype=torch.uint8, device=DEV)
+    o2, l2 = ra().attn_decode_splitkv(q, k, v, kv, max(lengths), num_splits=s, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, eager[0]) and torch.equal(l2, eager[1])
+    g = capture(call)
+    scratch = torch.randn(1 << 20, device=DEV)
+    check_replays(g, (o, lse), eager, lambda: scratch.mul_(1.0001))
+
+
 def test_mla_and_prefill_in_one_graph():
     g0 = synth.gen(4)
     qm = synth.randn((3, 16, 576), torch.bfloat16, g0).to(DEV)
