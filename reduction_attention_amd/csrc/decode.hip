@@ -564,60 +564,100 @@ __global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
 }
 
 // -------------------------------------------------------------------------
-// LSE merge (standalone): one wave per row.  Lanes first load the splits'
-// (m, l) side by side and reduce them across the wave; then lane d adds
-// dims d and d + 64 of every usable partial.
+// LSE merge (standalone): one wave per row; lane l holds dims V l .. V l +
+// V - 1 (V = D / 64).  The splits' (m, l) -- the first 64 side by side
+// across the lanes -- and the partial rows of the first kMergeBatch splits
+// are loaded together, then the rest of the partial rows kMergeBatch at a
+// time, each batch's loads issued before any is used: one memory round
+// trip per batch.  A split with l = 0 (no valid key for the row) has
+// weight 0 and its partial row, although loaded, never enters the sum (a
+// uniform branch skips it), so whatever an unused slot holds is harmless.
 // -------------------------------------------------------------------------
+constexpr int kMergeBatch = 8;
 template <int D, class OutT>
 __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
-  constexpr int DL = (D + 63) / 64;
+  constexpr int V = D / 64;
   const int lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= a.rows) return;
   const int64_t rows = a.rows;
-  float M = -INFINITY;
-  for (int i = lane; i < a.s; i += 64) {
-    const float li = a.l_part[int64_t(i) * rows + row];
-    if (li > 0.f) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
+  const int s = a.s;
+  float x[kMergeBatch][V];
+  // partial rows j0 .. j0 + kMergeBatch - 1 of splits [i0, i0 + cnt) (slots
+  // past cnt re-read the last one)
+  auto load = [&](int i0, int j0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
+      const float* op = a.o_part + (int64_t(i0 + jj) * rows + row) * D + V * lane;
+      if constexpr (V == 2) {
+        const float2 y = *reinterpret_cast<const float2*>(op);
+        x[j][0] = y.x;
+        x[j][1] = y.y;
+      } else {
+        x[j][0] = *op;
+      }
+    }
+  };
+  float acc[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = 0.f;
+  auto add = [&](float wi, int j0, int cnt) {
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (j0 + j >= cnt) break;
+      const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), j0 + j));
+      if (wj == 0.f) continue;  // an unused slot: never multiplied
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] += wj * x[j][e];
+    }
+  };
+
+  const int cnt0 = s < 64 ? s : 64;
+  float mi = -INFINITY, li = 0.f;
+  if (lane < cnt0) {
+    li = a.l_part[int64_t(lane) * rows + row];
+    mi = a.m_part[int64_t(lane) * rows + row];
+  }
+  if (cnt0 > 0) load(0, 0, cnt0);
+  float M = li > 0.f ? mi : -INFINITY;
+  for (int i = 64 + lane; i < s; i += 64) {
+    const float l2 = a.l_part[int64_t(i) * rows + row];
+    if (l2 > 0.f) M = fmaxf(M, a.m_part[int64_t(i) * rows + row]);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, shfl_xor(M, off));
-  float acc[DL];
-#pragma unroll
-  for (int x = 0; x < DL; ++x) acc[x] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int i0 = 0; i0 < a.s; i0 += 64) {
-      const int i = i0 + lane;
-      float wi = 0.f;
-      if (i < a.s) {
-        const float li = a.l_part[int64_t(i) * rows + row];
-        if (li > 0.f) wi = li * fexp2((a.m_part[int64_t(i) * rows + row] - M) * kLog2e);
-      }
-      float ws = wi;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ws += shfl_xor(ws, off);
-      wsum += ws;
-      const int n = a.s - i0 < 64 ? a.s - i0 : 64;
-      for (int j = 0; j < n; ++j) {
-        const float wj = __shfl(wi, j, 64);
-        if (wj == 0.f) continue;  // unused partial: its o is never read
-        const float* op = a.o_part + (int64_t(i0 + j) * rows + row) * D;
-#pragma unroll
-        for (int x = 0; x < DL; ++x) {
-          const int d = lane + 64 * x;
-          if (d < D) acc[x] += wj * op[d];
-        }
+    {
+      const float wi = li > 0.f ? li * fexp2((mi - M) * kLog2e) : 0.f;
+      wsum += wi;
+      add(wi, 0, cnt0);
+      for (int j0 = kMergeBatch; j0 < cnt0; j0 += kMergeBatch) {
+        load(0, j0, cnt0);
+        add(wi, j0, cnt0);
       }
     }
+    for (int i0 = 64; i0 < s; i0 += 64) {  // more than 64 splits
+      const int cnt = s - i0 < 64 ? s - i0 : 64;
+      float wi = 0.f;
+      if (lane < cnt) {
+        const float l2 = a.l_part[int64_t(i0 + lane) * rows + row];
+        if (l2 > 0.f) wi = l2 * fexp2((a.m_part[int64_t(i0 + lane) * rows + row] - M) * kLog2e);
+      }
+      wsum += wi;
+      for (int j0 = 0; j0 < cnt; j0 += kMergeBatch) {
+        load(i0, j0, cnt);
+        add(wi, j0, cnt);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wsum += shfl_xor(wsum, off);
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  OutT* o = static_cast<OutT*>(a.o) + row * D;
+  OutT* o = static_cast<OutT*>(a.o) + row * D + V * lane;
 #pragma unroll
-  for (int x = 0; x < DL; ++x) {
-    const int d = lane + 64 * x;
-    if (d < D) o[d] = OutT(acc[x] * inv);
-  }
+  for (int e = 0; e < V; ++e) o[e] = OutT(acc[e] * inv);
   if (a.lse && lane == 0) a.lse[row] = wsum > 0.f ? M + flog2(wsum) * kLn2 : -INFINITY;
 }
 
