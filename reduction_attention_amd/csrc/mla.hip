@@ -13,8 +13,9 @@
 // c = ceil(max_kv_len / s) (Cleave article on tip.co.jp, "Split演算子による
 // Split-Kの対応"), one workgroup per (16 query heads, chunk, request) -- or
 // per 64 heads when the head count is a multiple of 64 (mla_wide_kernel,
-// below); the partials are merged with log-sum-exp weights by the decode
-// merge kernel.
+// below, whose chunks are packed so that only the chunks a request has are
+// launched); the partials are merged with log-sum-exp weights by
+// mla_merge_kernel (end of this file).
 // Inside a chunk, 32-key tiles of cache rows are staged in LDS and each tile
 // feeds the score, the online max/sum and the value update in one pass
 // ("複数リダクションのスケジューリング": iterative tiling, horizontal fusion).

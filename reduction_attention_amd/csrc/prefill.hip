@@ -534,7 +534,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.s == 1) return e;
-  // split partials -> o / lse by log-sum-exp weights (the decode merge)
+  // split partials -> o / lse by log-sum-exp weights (the standalone merge,
+  // as attn_merge_lse)
   MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, int(a.rows), a.D, a.o, a.dtype, a.lse};
   return launch_merge(m, st);
 }
