@@ -236,7 +236,9 @@ size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
  *  - ragged, many-head kernel (which launches only the chunks a request
  *    has): with slots = 0.95 * CUs / hg and k the fewest rounds such that
  *    k * slots - B / 2 >= slots / 2, c = max(256, ceil(total_kv / (k *
- *    slots - B / 2))) and s = floor(max_kv_len / c).
+ *    slots - B / 2))) and s = floor(max_kv_len / c), raised to
+ *    min(floor(CUs / (hg B)), floor(max_kv_len / 256)) when that is larger
+ *    (B * s units fit one per compute unit whatever the lengths).
  * Within [1, 256].  Fitted to sweeps on MI355X. */
 int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len);
 

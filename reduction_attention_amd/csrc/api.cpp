@@ -282,6 +282,12 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
     const double room = k * slots - B / 2.0;
     const long long c = std::max(256LL, (long long)std::ceil(double(total_kv) / room));
     long long s = max_kv_len / c;
+    // B * s bounds the unit count exactly, so any s with B * s units at most
+    // one per compute unit is safe whatever the lengths; where the lengths
+    // are nearly equal (the last chunks nearly full, which B / 2 does not
+    // see) that bound allows more splits than the estimate.
+    const long long s_exact = std::min((long long)(cus / hg) / B, (long long)max_kv_len / 256);
+    if (s_exact > s) s = s_exact;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
     return int(s);

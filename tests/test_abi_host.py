@@ -156,6 +156,10 @@ def test_mla_host_rules(lib):
     # 0.95 * 256 / 2 - 32 / 2 = 105.6 units beside the requests' last
     # chunks, c = ceil(100000 / 105.6) = 947, s = floor(16000 / 947) = 16
     assert lib.attn_mla_decode_choose_splits(32, 128, 100000, 16000) == 16
+    # 64 nearly equal requests (4000 .. 4099 keys): the estimate alone gives
+    # s = 1 (64 units, half the compute units idle); B * s <= 256 / 2 allows
+    # s = 2 whatever the lengths
+    assert lib.attn_mla_decode_choose_splits(64, 128, 64 * 4050, 4099) == 2
     # many requests: 512 of them take two rounds and more; k = 3 rounds
     # leave 3 * 121.6 - 256 = 108.8 units, c = 14119 > 16000 / 2: s = 1
     assert lib.attn_mla_decode_choose_splits(512, 128, 512 * 3000, 16000) == 1
