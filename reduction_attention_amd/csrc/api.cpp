@@ -91,10 +91,17 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   return (bytes + 255) & ~size_t(255);
 }
 
-// Every request has max_kv_len keys iff the lengths (each at most
-// max_kv_len) add up to B * max_kv_len.
+// Nearly equal lengths: every request provably holds at least 15/16 of the
+// longest one's keys, since with each length at most max_kv_len the
+// shortest is at least total_kv - (B - 1) * max_kv_len.  Such a batch takes
+// the equal-length decode shape: its chunks are all full but each
+// request's last, which is nearly full too, so workgroups that each own a
+// whole chunk stay balanced (equal lengths, the bound's exact case, are
+// included).
 static int uniform_lengths(int B, int max_kv_len, long long total_kv) {
-  return (long long)max_kv_len * B == total_kv ? 1 : 0;
+  if (B <= 0 || max_kv_len <= 0) return 0;
+  const long long shortest = total_kv - (long long)(B - 1) * max_kv_len;
+  return 16 * shortest >= 15LL * max_kv_len ? 1 : 0;
 }
 
 int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv, int max_kv_len) {
@@ -105,9 +112,9 @@ int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv,
   long long c = 1;
   while (c < max_kv_len) c <<= 1;  // one split per request at most
   if (uniform_lengths(B, max_kv_len, total_kv)) {
-    // Equal lengths: workgroups of up to four KV heads, each wave streaming
-    // a whole chunk.  Largest power-of-two chunk >= 256 that gives every
-    // compute unit a workgroup.
+    // Equal (or nearly equal) lengths: workgroups of up to four KV heads,
+    // each wave streaming a whole chunk.  Largest power-of-two chunk >= 256
+    // that gives every compute unit a workgroup.
     const int hpw = Hkv >= 4 ? 4 : Hkv >= 2 ? 2 : 1;
     const long long groups = (Hkv + hpw - 1) / hpw;
     while (c > 256 && groups * B * ((max_kv_len + c - 1) / c) < cus) c >>= 1;

@@ -54,6 +54,29 @@ def test_llama3_8b_decode_full_parity():
     check("llama3-8b decode s=1", o1, o_ref, lse1, lse_ref, torch.bfloat16)
 
 
+@pytest.mark.parametrize("kind", ["one_shorter", "jittered"])
+def test_nearly_equal_lengths_take_the_equal_length_shape(kind):
+    """Lengths that differ a little (every request provably holds at least
+    15/16 of the longest's keys) take the equal-length decode shape and its
+    batched merge; with s = 16 the shorter request has fewer splits than s,
+    so the merge's batch holds slots the request never wrote.  Every row."""
+    if kind == "one_shorter":
+        lengths = [4096] * 15 + [3840]
+    else:
+        g = torch.Generator().manual_seed(12)
+        lengths = torch.randint(4090, 4097, (16,), generator=g).tolist()
+    assert 16 * (sum(lengths) - 15 * max(lengths)) >= 15 * max(lengths)
+    q, k, v, kv = synth.decode_inputs(16, 32, 8, 128, lengths, torch.bfloat16, seed=13)
+    scale = 128 ** -0.5
+    o_ref, lse_ref = oracle.attention(q, k, v, list(range(17)), kv, scale)
+    qd, kd, vd, kvd = q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV)
+    for s in (0, 3, 8, 16):
+        print(f"nearly equal lengths ({kind}) s={s}", flush=True)
+        o, lse = ra().attn_decode_splitkv(qd, kd, vd, kvd, max(lengths), num_splits=s)
+        torch.cuda.synchronize()
+        check(f"nearly equal lengths {kind} s={s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
 def test_ragged_serving_decode_full_parity():
     """64 requests, 64/8 heads, D 128, log-uniform lengths in [128, 32768], bf16."""
     w = synth.workload("ragged_decode_bf16")
