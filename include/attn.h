@@ -85,10 +85,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits);
 /* The split count s the library picks when num_splits = 0, as
  * s = ceil(max_kv_len / c) clamped to [1, 256], with c the largest power of
  * two >= 256 keys such that:
- *  - equal or nearly equal request lengths (16 * (total_kv - (B - 1) *
- *    max_kv_len) >= 15 * max_kv_len: every request holds at least 15/16 of
- *    the longest's keys), where attn_decode_splitkv's workgroup takes up
- *    to four KV heads: ceil(Hkv / hpw) * B * ceil(max_kv_len / c)
+ *  - equal or nearly equal request lengths (16 * total_kv >= 15 * B *
+ *    max_kv_len: the mean length at least 15/16 of the longest), where
+ *    attn_decode_splitkv's workgroup takes up to four KV heads:
+ *    ceil(Hkv / hpw) * B * ceil(max_kv_len / c)
  *    workgroups (hpw = 4, 2 or 1, at most Hkv) reach one per compute unit;
  *  - otherwise, one KV head per workgroup: Hkv * (total_kv / c + B / 2)
  *    workgroups reach four per compute unit.

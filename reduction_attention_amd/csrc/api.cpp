@@ -91,17 +91,14 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int D, int num_splits) {
   return (bytes + 255) & ~size_t(255);
 }
 
-// Nearly equal lengths: every request provably holds at least 15/16 of the
-// longest one's keys, since with each length at most max_kv_len the
-// shortest is at least total_kv - (B - 1) * max_kv_len.  Such a batch takes
-// the equal-length decode shape: its chunks are all full but each
-// request's last, which is nearly full too, so workgroups that each own a
-// whole chunk stay balanced (equal lengths, the bound's exact case, are
-// included).
+// Equal or nearly equal lengths: the mean length is at least 15/16 of the
+// longest (equal lengths are the exact case).  Nearly all the keys then sit
+// in full chunks, so the equal-length shapes, whose workgroups each own a
+// whole chunk, stay balanced; they are correct for any lengths (a chunk
+// past a request's end is empty), only slower where lengths spread widely.
 static int uniform_lengths(int B, int max_kv_len, long long total_kv) {
   if (B <= 0 || max_kv_len <= 0) return 0;
-  const long long shortest = total_kv - (long long)(B - 1) * max_kv_len;
-  return 16 * shortest >= 15LL * max_kv_len ? 1 : 0;
+  return 16 * total_kv >= 15LL * B * max_kv_len ? 1 : 0;
 }
 
 int attn_decode_choose_splits(int B, int Hq, int Hkv, int D, long long total_kv, int max_kv_len) {
@@ -273,7 +270,7 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
   const long long cus = attn_device_cu_count();
   const bool wide = rattn::mla_wide(H);
   const long long hg = wide ? H / 64 : (H + 15) / 16;
-  const bool uniform = (long long)max_kv_len * B == total_kv;
+  const bool uniform = uniform_lengths(B, max_kv_len, total_kv) != 0;  // or nearly equal
   if (wide && !uniform) {
     // Packed units (only the splits a request has; about total_kv / c + B / 2
     // of them, a request's last chunk being half full on average), hg

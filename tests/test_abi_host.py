@@ -65,8 +65,8 @@ def test_split_rule(lib):
     assert lib.attn_decode_choose_splits(16, 32, 8, 128, 16 * 4096, 4096) == 8
     # equal lengths, 2 KV heads (two-head workgroups): 4 x 1024 keys -> c = 256, s = 4
     assert lib.attn_decode_choose_splits(4, 8, 2, 128, 4 * 1024, 1024) == 4
-    # nearly equal lengths (every request provably >= 15/16 of the longest)
-    # take the equal-length rule: 16 requests of 4090 .. 4096 keys, s = 8
+    # nearly equal lengths (mean >= 15/16 of the longest) take the
+    # equal-length rule: 16 requests of 4090 .. 4096 keys, s = 8
     assert lib.attn_decode_choose_splits(16, 32, 8, 128, 16 * 4093, 4096) == 8
     # ragged: 226896 keys over 64 requests, longest 27752 -> c = 2048, s = 14
     assert lib.attn_decode_choose_splits(64, 64, 8, 128, 226896, 27752) == 14
