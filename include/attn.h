@@ -266,10 +266,10 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
  * Dc, Dr      512 and 64 (other widths: ATTN_EUNSUPPORTED)
  * max_kv_len  the longest request (keys past max_kv_len of a request are not
  *   attended: s chunks of ceil(max_kv_len / s) keys cover it)
- * total_kv    kv_indptr[B] - kv_indptr[0]; the many-head kernel launches
- *   min(s * B, ceil(total_kv / c) + B) workgroups per 64 heads, one per
- *   (request, chunk) the request has, so a smaller total_kv leaves
- *   requests unwritten.
+ * total_kv    kv_indptr[B] - kv_indptr[0]; for ragged lengths the
+ *   many-head kernel launches min(s * B, ceil(total_kv / c) + B) workgroups
+ *   per 64 heads, one per (request, chunk) the request has, so a smaller
+ *   total_kv leaves requests unwritten.
  * num_splits  s in [1, 256], or 0 for attn_mla_decode_choose_splits; s = 1
  *   needs no workspace (may be NULL).
  * workspace   at least attn_mla_decode_workspace_bytes(B, H, s) bytes when

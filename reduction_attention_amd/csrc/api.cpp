@@ -259,20 +259,13 @@ size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
 
 int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_len) {
   if (B <= 0 || H <= 0 || max_kv_len <= 256 || total_kv <= 0) return 1;
-  // Workgroups of 16 heads (64 for the many-head kernel) over one chunk.
-  // Equal lengths: the largest power-of-two chunk >= 256 keys that gives
-  // every compute unit a workgroup.  Ragged, 16-head kernel: chunks counted
-  // as total/c + B/2, two workgroups per compute unit, and an odd s:
-  // workgroups are dealt to the eight XCDs round robin, and with s a
-  // multiple of eight the first splits (present in every request) would all
-  // land on the same XCDs while the last ones (mostly empty) land on the
-  // others.  Ragged, 64-head kernel: below.
+  // hg workgroups (16 heads each, 64 for the many-head kernel) per chunk.
   const long long cus = attn_device_cu_count();
   const bool wide = rattn::mla_wide(H);
   const long long hg = wide ? H / 64 : (H + 15) / 16;
   const bool uniform = uniform_lengths(B, max_kv_len, total_kv) != 0;  // or nearly equal
   if (wide && !uniform) {
-    // Packed units (only the splits a request has; about total_kv / c + B / 2
+    // Packed units (only the chunks a request has; about total_kv / c + B / 2
     // of them, a request's last chunk being half full on average), hg
     // workgroups each and one workgroup per compute unit (the kernel holds
     // all of its LDS): the shortest chunk, at least 256 keys, whose units
@@ -287,20 +280,26 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
     const long long c = std::max(256LL, (long long)std::ceil(double(total_kv) / room));
     long long s = max_kv_len / c;
     // B * s bounds the unit count exactly, so any s with B * s units at most
-    // one per compute unit is safe whatever the lengths; where the lengths
-    // are nearly equal (the last chunks nearly full, which B / 2 does not
-    // see) that bound allows more splits than the estimate.
-    const long long s_exact = std::min((long long)(cus / hg) / B, (long long)max_kv_len / 256);
+    // one per compute unit is safe whatever the lengths, and may exceed the
+    // estimate's s where it counts the last chunks as half full.
+    const long long s_exact = std::min(cus / hg / B, (long long)max_kv_len / 256);
     if (s_exact > s) s = s_exact;
     if (s < 1) s = 1;
     if (s > kMaxSplits) s = kMaxSplits;
     return int(s);
   }
+  // Equal (or nearly equal) lengths: the largest power-of-two chunk >= 256
+  // keys that gives every compute unit a workgroup.  Ragged, 16-head
+  // kernel: chunks counted as total/c + B/2, two workgroups per compute
+  // unit, and an odd s: its workgroups are dealt to the eight XCDs round
+  // robin by (request, split) slot, and with s a multiple of eight the first
+  // splits (present in every request) would all land on the same XCDs while
+  // the last ones (mostly empty) land on the others.
   long long c = 1;
   while (c < max_kv_len) c <<= 1;
   while (c > 256) {
     const long long chunks = uniform ? B * ((max_kv_len + c - 1) / c) : (total_kv + c - 1) / c + B / 2;
-    if (2 * hg * chunks >= (uniform ? 2 : wide ? 1 : 4) * cus) break;
+    if (hg * chunks >= (uniform ? 1 : 2) * cus) break;
     c >>= 1;
   }
   long long s = (max_kv_len + c - 1) / c;
@@ -346,9 +345,12 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
                    B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
                    uniform_lengths(B, max_kv_len, total_kv)};
   a.total_kv = total_kv;
-  // the 64-head kernel's packed (request, split) units: request b owns
-  // max(1, min(ceil(len_b / c), s)) <= len_b / c + 1 of them
-  a.units = int(std::min((long long)s * B, (total_kv + a.chunk - 1) / a.chunk + B));
+  // the 64-head kernel's units: for ragged lengths packed (request b owns
+  // max(1, min(ceil(len_b / c), s)) <= len_b / c + 1 of them), else all
+  // s * B (request b, split i at b s + i: no lookup at start-up)
+  a.packed = a.uniform ? 0 : 1;
+  a.units = a.packed ? int(std::min((long long)s * B, (total_kv + a.chunk - 1) / a.chunk + B))
+                     : s * B;
   return hip_status(rattn::launch_mla_decode(a, static_cast<hipStream_t>(hip_stream)),
                     "mla_decode launch");
 }

@@ -58,9 +58,11 @@ struct MlaArgs {
   int flat = 0;
   int pieces = 0;
   int64_t total_kv = 0;
-  // Chunk plan of the 64-head kernel: units (request, split) launched, at
-  // least sum over b of max(1, min(ceil(len_b / chunk), s)).
+  // Chunk plan of the 64-head kernel: units (request, split) launched; when
+  // packed (ragged lengths), at least sum over b of max(1, min(ceil(len_b /
+  // chunk), s)), else s * B with unit b s + i.
   int units = 0;
+  int packed = 0;
 };
 
 struct MergeArgs {

@@ -67,6 +67,45 @@ __device__ __forceinline__ bool mla_unit(int L, int HG, int units, int& hg, int&
   return unit < units;
 }
 
+// Chunk plan of the many-head kernel on ragged batches, packed: request b
+// owns n_b = min(ceil(len_b / c), s)
+// consecutive units (one for an empty request, which writes its zero rows),
+// so no workgroup slot goes to a split the request does not have and the
+// units dealt to each XCD carry nearly equal work.  The request of a unit is
+// found by a prefix sum of n_b over the requests, 64 at a time across the
+// lanes (the result is uniform over the wave).  Returns false past the last
+// unit.
+__device__ __forceinline__ bool mla_packed_unit(const MlaArgs& a, int unit, int lane, int& b, int& i) {
+  const int64_t c = a.chunk;
+  b = -1;
+  i = 0;
+  int base = 0;  // units owned by the requests before j0 (at most s * B < 2^27)
+  for (int j0 = 0; j0 < a.B; j0 += 64) {
+    const int j = j0 + lane;
+    int nb = 0;
+    if (j < a.B) {
+      const int64_t len = int64_t(a.kv_indptr[j + 1]) - a.kv_indptr[j];
+      nb = len > 0 ? int(min((len + c - 1) / c, int64_t(a.s))) : 1;
+    }
+    int incl = nb;  // inclusive prefix sum across the lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    const int first = base + incl - nb;
+    const uint64_t hit = __ballot(nb > 0 && unit >= first && unit < first + nb);
+    if (hit) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      b = __builtin_amdgcn_readfirstlane(j0 + l);
+      i = __builtin_amdgcn_readfirstlane(unit - __shfl(first, l));
+      return true;
+    }
+    base += __shfl(incl, 63);
+  }
+  return false;
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16) at a byte offset from base: see
 // the lane layout at its use below.
 __device__ __forceinline__ u32x2 mla_tr_read(const uint16_t* base, int byte_off) {
@@ -631,45 +670,16 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   };
 
   if constexpr (!FLAT) {
-    // chunk plan: split i of request b covers its keys [i c, (i + 1) c).
-    // Units are packed: request b owns n_b = min(ceil(len_b / c), s)
-    // consecutive units (one for an empty request, which writes its zero
-    // rows), so no workgroup slot goes to a split the request does not
-    // have and the units dealt to each XCD carry nearly equal work.  The
-    // request of this unit is found by a prefix sum of n_b over the
-    // requests, 64 at a time across the lanes.
+    // chunk plan: split i of request b covers its keys [i c, (i + 1) c);
+    // unit b s + i for equal lengths, packed units (mla_packed_unit) for
+    // ragged ones
     const int64_t c = a.chunk;
-    int b = -1, i = 0;
-    int base = 0;  // units owned by the requests before j0 (at most s * B < 2^27)
-    for (int j0 = 0; j0 < a.B; j0 += 64) {
-      const int j = j0 + lane;
-      int nb = 0;
-      if (j < a.B) {
-        const int64_t len = int64_t(a.kv_indptr[j + 1]) - a.kv_indptr[j];
-        nb = len > 0 ? int(min((len + c - 1) / c, int64_t(a.s))) : 1;
-      }
-      int incl = nb;  // inclusive prefix sum across the lanes
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d);
-        if (lane >= d) incl += t;
-      }
-      const int first = base + incl - nb;
-      const uint64_t hit = __ballot(nb > 0 && unit >= first && unit < first + nb);
-      if (hit) {
-        const int l = __ffsll((unsigned long long)hit) - 1;
-        b = j0 + l;
-        i = int(unit - __shfl(first, l));
-        break;
-      }
-      base += __shfl(incl, 63);
-    }
-    if (b < 0) return;  // past the last unit
-    b = __builtin_amdgcn_readfirstlane(b);
-    i = __builtin_amdgcn_readfirstlane(i);
+    int b = unit / a.s, i = unit % a.s;
+    if (a.packed && !mla_packed_unit(a, unit, lane, b, i)) return;  // past the last unit
     const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
     const int n_b = int(kb1 - kb0);
     if (n_b <= 0) {  // empty request: O = 0, LSE = -inf
+      if (i != 0) return;  // (direct mapping: written by its split 0)
       const int64_t row0 = int64_t(b) * H + 64 * hg;
       typename T::elem* o = static_cast<typename T::elem*>(a.o) + row0 * kMlaDc;
       for (int e = tid; e < 64 * kMlaDc; e += 64 * kMwWaves) o[e] = typename T::elem(0.f);
@@ -677,6 +687,7 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
       return;
     }
     const int lo = int(int64_t(i) * c);
+    if (lo >= n_b) return;  // a split the request does not have (direct mapping)
     const int hi = lo + c < n_b ? int(lo + c) : n_b;
     segment(b, lo, hi, i, int(min((int64_t(n_b) + c - 1) / c, int64_t(a.s))));
   } else {
@@ -814,7 +825,6 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
 
 template <class T>
 static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
-  const int64_t units = int64_t(a.s) * a.B;
   if (a.flat) {  // the flat plan (many-head kernel only)
     const int64_t nwg = 8 * (a.H / 64) * ((int64_t(a.pieces) + 7) / 8);
     if (a.pieces > 0 && a.total_kv > 0)
@@ -824,7 +834,7 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((mla_wide_kernel<T, false>), dim3(unsigned(nwg)), dim3(64 * kMwWaves), 0, st, a);
   } else {
     const int HG = (a.H + 15) / 16;
-    const int64_t nwg = 8 * HG * ((units + 7) / 8);
+    const int64_t nwg = 8 * HG * ((int64_t(a.s) * a.B + 7) / 8);
     hipLaunchKernelGGL((mla_decode_kernel<T>), dim3(unsigned(nwg)), dim3(kMlaThreads), 0, st, a);
   }
   hipError_t e = hipGetLastError();

@@ -73,6 +73,24 @@ def test_mla_many_requests_packed_units(H):
         assert bool((o[empty] == 0).all()) and bool(torch.isinf(lse[empty]).all())
 
 
+@pytest.mark.parametrize("lengths", [[512] * 8, [512] * 7 + [300], [1000, 990, 1000, 995]])
+def test_mla_many_heads_equal_lengths(lengths):
+    """128 heads, equal or nearly equal lengths (mean at least 15/16 of the
+    longest): the many-head kernel maps unit b s + i straight to its request
+    and split, so splits past a shorter request's end are skipped in the
+    kernel; every split count against the oracle."""
+    H = 128
+    q, kv, kvp = mla_inputs(lengths, H, torch.bfloat16, seed=41)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    for s in (0, 1, 2, 3, 4, 7):
+        print(f"mla 128 heads lengths {lengths} s={s}", flush=True)
+        o, lse = ra().attn_mla_decode(q.to(DEV), kv.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                      num_splits=s)
+        torch.cuda.synchronize()
+        check(f"mla 128h equal-ish s={s}", o, o_ref, lse, lse_ref, torch.bfloat16)
+
+
 def test_mla_workload_full_parity():
     """32 requests x 4096 cached tokens, 16 heads, bf16: every row."""
     w = synth.workload("mla_decode_bf16")
