@@ -251,9 +251,13 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
 
 // ---- multi-head latent attention decode ---------------------------------------
 
+// MLA workspace layout: o_part [s, B*H, 512] in the inputs' 16-bit type, then
+// m_part [s, B*H] and l_part [s, B*H] (fp32).
+static size_t mla_workspace_raw(size_t s, size_t rows) { return s * rows * (512 * 2 + 2 * sizeof(float)); }
+
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
   if (B <= 0 || H <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
-  const size_t bytes = size_t(num_splits) * size_t(B) * size_t(H) * (512 + 2) * sizeof(float);
+  const size_t bytes = mla_workspace_raw(size_t(num_splits), size_t(B) * size_t(H));
   return (bytes + 255) & ~size_t(255);
 }
 
@@ -338,10 +342,10 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
   if (s > 1 && !aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  float* ws = static_cast<float*>(workspace);
+  char* ws = static_cast<char*>(workspace);
+  float* mws = s > 1 ? reinterpret_cast<float*>(ws + size_t(s) * rows * 512 * 2) : nullptr;
   rattn::MlaArgs a{q, kv, kv_indptr, o, lse,
-                   s > 1 ? ws : nullptr, s > 1 ? ws + size_t(s) * rows * 512 : nullptr,
-                   s > 1 ? ws + size_t(s) * rows * 513 : nullptr,
+                   s > 1 ? ws : nullptr, mws, s > 1 ? mws + size_t(s) * rows : nullptr,
                    B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
                    uniform_lengths(B, max_kv_len, total_kv)};
   a.total_kv = total_kv;
@@ -378,7 +382,7 @@ size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long l
                                             int num_pieces) {
   const int s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces);
   if (B <= 0 || H <= 0 || s <= 0) return 0;
-  const size_t bytes = size_t(s) * size_t(B) * size_t(H) * (512 + 2) * sizeof(float);
+  const size_t bytes = mla_workspace_raw(size_t(s), size_t(B) * size_t(H));
   return (bytes + 255) & ~size_t(255);
 }
 
@@ -417,9 +421,10 @@ attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t*
   if (!aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode_flat: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  float* ws = static_cast<float*>(workspace);
-  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, ws, ws + size_t(s) * rows * 512,
-                   ws + size_t(s) * rows * 513, B, H, s, int(flat_piece_len(total_kv, P)),
+  char* ws = static_cast<char*>(workspace);
+  float* mws = reinterpret_cast<float*>(ws + size_t(s) * rows * 512 * 2);
+  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, ws, mws, mws + size_t(s) * rows, B, H, s,
+                   int(flat_piece_len(total_kv, P)),
                    scale * kLog2e, dtype, 0};
   a.flat = 1;
   a.pieces = P;

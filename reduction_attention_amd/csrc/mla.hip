@@ -30,6 +30,7 @@
 // P^T, V^T from transposing LDS reads).
 #include "device.hpp"
 #include "launch.hpp"
+#include <type_traits>
 
 namespace rattn {
 
@@ -335,9 +336,19 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
     }
     if (a.lse && w == 0 && h4 == 0) a.lse[row] = (m + flog2(l)) * kLn2;
   } else {
-    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
+    typename T::elem* prow =
+        static_cast<typename T::elem*>(a.o_part) + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) *reinterpret_cast<f32x4*>(prow + 16 * blk) = o[blk] * inv;
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x8 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[r] = o[blk][r] * inv;
+        y[4 + r] = 0.f;
+      }
+      const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+      *reinterpret_cast<u32x2*>(prow + 16 * blk) = u32x2{bits[0], bits[1]};
+    }
     if (w == 0 && h4 == 0) {
       a.m_part[int64_t(i) * rows + row] = m * kLn2;
       a.l_part[int64_t(i) * rows + row] = l;
@@ -348,18 +359,22 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // ---------------------------------------------------------------------------
 // Many heads (H a multiple of 64): the heads are the rows of the score
 // matrix, so the tile feeds 32x32x16 MFMAs with K and V from LDS as in
-// prefill.  Workgroup = 8 waves over 64 heads of one (chunk, request), two
-// waves per SIMD so that one's LDS and matrix latencies overlap the
-// other's work: wave w takes head block hb = w / 4 (32 heads) over quarter
-// dq = w % 4 of the dims -- dims 144 dq .. 144 dq + 143 of the score
-// contraction (nine 16-dim steps) and output dims 128 dq .. 128 dq + 127.
-// The four waves of a head block exchange their partial scores through
-// LDS; wave (hb, dq) adds, in quarter order (0 + 1 + 2 + 3), the scores of
-// key quarter dq only (keys 8 dq + 4 h + 0..3 of the tile in lane half h),
-// forms their weights, and the weights (16-bit) go back through LDS to the
-// four waves for the value update.  So no weight is computed twice; each
-// wave's weight sum and running max cover its own keys and are combined at
-// the end.
+// prefill.  Workgroup = 4 waves over 64 heads of one (chunk, request), one
+// wave per SIMD: wave w takes head block hb = w / 2 (32 heads) and half
+// dh = w % 2 of the dims -- dims 288 dh .. 288 dh + 287 of the score
+// contraction (eighteen 16-dim steps) and output dims 256 dh .. 256 dh +
+// 255.  The two waves of a head block swap their partial scores through
+// LDS once per tile; each adds the pair in the same order (half 0 + half
+// 1), so both hold the same full scores, run the same online softmax and
+// feed the same weights to their own output half: no weight crosses
+// waves.
+//
+// Schedule (one barrier per tile): step j turns tile j's swapped partial
+// scores into weights, issues the load of tile j + 2, computes and
+// publishes tile j + 1's partial scores, runs tile j's value update, then
+// waits for its loads and meets the other waves.  LDS holds three stages
+// (tile j: values, tile j + 1: keys, tile j + 2: streaming in) and the
+// partial scores double-buffered by tile parity.
 //
 // Softmax reference: the row max of the chunk's first tile, kept for the
 // whole chunk, so the value accumulators are never rescaled.  A later
@@ -368,19 +383,19 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // first pass), which no score exceeds.  Keys far below the reference only
 // lose weights that are negligible against the reference key's weight of 1.
 //
-// LDS: three stages of 32 cache rows in natural layout, 72 chunks of 16
-// bytes per row with the chunk index XOR-ed by f(row) = 2 (row % 4) +
-// (row / 4) % 2, so that both the 16-byte K reads (eight consecutive rows,
-// one chunk) and the transposing V reads (four consecutive rows, two
-// chunks) hit distinct banks; plus the score exchange (32 KB).  A tile
-// arrives through 36 direct-to-LDS load instructions of 1 KB, x = w + 8 k.
+// LDS rows: 72 chunks of 16 bytes per cache row with the chunk index XOR-ed
+// by f(row) = 2 (row % 4) + (row / 4) % 2, so that both the 16-byte K reads
+// (eight consecutive rows, one chunk) and the transposing V reads (four
+// consecutive rows, two chunks) hit distinct banks.  A tile arrives through
+// 36 direct-to-LDS load instructions of 1 KB, x = w + 4 k.
 // ---------------------------------------------------------------------------
 constexpr int kMwBK = 32;
 constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 KB per tile
-constexpr int kMwWaves = 8;
-constexpr int kMwPerWave = (kMwInstr + kMwWaves - 1) / kMwWaves;  // 5 (waves 4..7: 4)
+constexpr int kMwWaves = 4;
+constexpr int kMwPerWave = kMwInstr / kMwWaves;    // 9
 constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
 constexpr int kMwStages = 3;
+static_assert(kMwInstr % kMwWaves == 0, "every wave issues the same loads");
 // A weight above 2^mw_overflow forces the exact pass: 2^64 for bf16 (its
 // range is fp32's, and sums of such weights stay far from overflow), 2^15
 // for fp16, whose largest finite value is just below 2^16.
@@ -404,21 +419,16 @@ template <class T, bool FLAT>
 __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kMwStages * kMwStageBytes / 2];
-  // score exchange, quarter-major so a wave's 16-byte accesses are
-  // consecutive across lanes: sx[dq][hb][k][lane] = lane's scores 4k .. 4k + 3
-  // of head block hb, dim quarter dq
-  __shared__ __attribute__((aligned(16))) f32x4 sx[4][2][4][64];
-  // weight exchange: px[dq][hb][lane] = the lane's four 16-bit weights of key
-  // quarter dq; and per-head maxima / sums combined across the four waves of
-  // a head block
-  __shared__ __attribute__((aligned(16))) u32x2 px[4][2][64];
-  __shared__ float red[4][2][64];
+  // partial scores, by tile parity: sx[j & 1][hb][dh][k][lane] = the lane's
+  // partial scores 4k .. 4k + 3 of head block hb, dim half dh (16-byte
+  // accesses consecutive across lanes)
+  __shared__ __attribute__((aligned(16))) f32x4 sx[2][2][2][4][64];
   const int HG = a.H / 64;
   int hg, unit;
   if (!mla_unit(blockIdx.x, HG, FLAT ? a.pieces : a.units, hg, unit)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int dq = w & 3, hb = w >> 2, h = lane >> 5, l32 = lane & 31;
+  const int dh = w & 1, hb = w >> 1, h = lane >> 5, l32 = lane & 31;
   const int H = a.H;
   const int64_t rows = int64_t(a.B) * H;
 
@@ -432,18 +442,17 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   // this lane's head row: head l32 of the wave's block
   const int64_t rowA = row0 + 32 * hb + l32;
 
-  // Q^T operands of the nine contraction steps: head 32 hb + l32, dims
-  // 144 dq + 16 u + 8 h .. +8
-  u32x4 qa[9];
+  // Q^T operands of the eighteen contraction steps: head 32 hb + l32, dims
+  // 288 dh + 16 u + 8 h .. +8.  Issued here and waited for together with the
+  // first two tiles (run, below), so the two memory round trips overlap.
+  u32x4 qa[18];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + rowA * kMlaD + 144 * dq + 8 * h;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + rowA * kMlaD + 288 * dh + 8 * h;
 #pragma unroll
-    for (int u = 0; u < 9; ++u) qa[u] = ldg128(qp + 16 * u);
-#pragma unroll
-    for (int u = 0; u < 9; ++u) __asm__ volatile("" ::"v"(qa[u]));
+    for (int u = 0; u < 18; ++u) qa[u] = ldg128(qp + 16 * u);
   }
 
-  // direct-to-LDS loads: instruction x = w + 8k (x < 36) fills stage chunks
+  // direct-to-LDS loads: instruction x = w + 4k fills stage chunks
   // 64x .. 64x + 63; lane chunk q = 64x + lane is row q / 72, slot q % 72,
   // holding chunk slot ^ f(row) of the row
   int voff[kMwPerWave];
@@ -467,176 +476,188 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     const uint32_t st = lds0 + uint32_t(tile % kMwStages) * kMwStageBytes;
 #pragma unroll
     for (int k = 0; k < kMwPerWave; ++k)
-      if (w + kMwWaves * k < kMwInstr)
-        __asm__ volatile(
-            "s_mov_b32 m0, %0\n\t"
-            "buffer_load_dwordx4 %1, %2, 0 offen lds"
-            :
-            : "s"(__builtin_amdgcn_readfirstlane(st + k * 1024 * kMwWaves)), "v"(voff[k]), "s"(rsv)
-            : "memory", "m0");
+      __asm__ volatile(
+          "s_mov_b32 m0, %0\n\t"
+          "buffer_load_dwordx4 %1, %2, 0 offen lds"
+          :
+          : "s"(__builtin_amdgcn_readfirstlane(st + k * 1024 * kMwWaves)), "v"(voff[k]), "s"(rsv)
+          : "memory", "m0");
   };
 
   // K operand reads (byte offsets in a stage): lane l32 reads key row l32,
-  // chunk ch = 18 dq + 2 u + h, stored at slot ch ^ f(l32).  Chunks u and
+  // chunk ch = 36 dh + 2 u + h, stored at slot ch ^ f(l32).  Chunks u and
   // u + 4 are 8 apart and f only touches the low three bits, so four
-  // per-lane offsets and immediates cover the nine reads.
+  // per-lane offsets and immediates cover the eighteen reads.
   int kofs[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) kofs[u] = 2 * (l32 * kMlaD + 8 * ((18 * dq + 2 * u + h) ^ mw_swz(l32)));
+  for (int u = 0; u < 4; ++u) kofs[u] = 2 * (l32 * kMlaD + 8 * ((36 * dh + 2 * u + h) ^ mw_swz(l32)));
   // V^T operand (transposing reads): lane q + 4e of its 16-lane group
   // points at key row k0 + e (k0 = 16 t + 4 h, then + 8) and dims
-  // 128 dq + 32 db + 16 g2 + 4 q; those rows have f = 2 e + h, and blocks
+  // 256 dh + 32 db + 16 g2 + 4 q; those rows have f = 2 e + h, and blocks
   // db and db + 2 are 8 chunks apart: two per-lane offsets (db even, odd)
   const int tq = lane & 3, te = (lane >> 2) & 3, g2 = (lane >> 4) & 1;
   int vofs[2];
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    const int dim = 128 * dq + 32 * d + 16 * g2 + 4 * tq;
+    const int dim = 256 * dh + 32 * d + 16 * g2 + 4 * tq;
     vofs[d] = 2 * ((4 * h + te) * kMlaD + 8 * ((dim >> 3) ^ (2 * te + h)) + (dim & 7));
   }
 
-  // O^T of the head block: head l32, dims 128 dq + 32 db + 8 (r / 4) + 4 h + r % 4
-  f32x16 oa[4];
+  // O^T of the wave: head l32, dims 256 dh + 32 db + 8 (r / 4) + 4 h + r % 4
+  f32x16 oa[8];
   float la = 0.f, mra = 0.f, mruna = -INFINITY;
   int flag = 0;
-  const float c = a.scale_log2;
+  const float c = fabsf(a.scale_log2);
 
-  // max over the head block's four waves of a per-head value (the same in
-  // lanes l and l ^ 32 on entry and exit); every wave calls it
-  auto wave_max = [&](float v) {
-    __syncthreads();
-    red[dq][hb][lane] = v;
-    __syncthreads();
-    return fmaxf(fmaxf(red[0][hb][lane], red[1][hb][lane]), fmaxf(red[2][hb][lane], red[3][hb][lane]));
+  // LDS byte offsets are formed once per tile as (per-lane base + stage)
+  // behind an empty asm, so that every read below is that base plus an
+  // immediate (the compiler would otherwise keep one full address per read
+  // and add the stage to each of them every tile).
+  auto opaque = [](int v) {
+    __asm__ volatile("" : "+v"(v));
+    return v;
   };
-  // this wave's key quarter of one head block's 32x32 score tile: scores
-  // (log2 units) masked past the chunk end, and their maximum
-  auto quarter = [&](const f32x4& s, int j, float (&x)[4]) {
-    const int key0 = j * kMwBK + 8 * dq + 4 * h;  // keys of x[e]: key0 + e
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = key0 + e < n ? s[e] * c : -INFINITY;
-    return fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  };
-  // weights of the quarter against the reference, summed into l
-  auto weights = [&](const float (&x)[4], float mref, float& l) {
-    f32x4 p;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = fexp2(x[e] - mref);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    typedef typename T::elem e4 __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(u32x2, __builtin_convertvector(p, e4));
-  };
+  const int lds_base = int(uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)lds)));
 
-  // the partial scores of tile j (this wave's quarter of the dims, its head
-  // block)
-  auto scores = [&](int j, f32x16& sa) {
-    lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
+  // this wave's partial scores of the tile in stage `so` (its half of the
+  // dims)
+  auto scores = [&](int so, f32x16& sa) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = 0.f;
-    lds_cchar* kp[4] = {cur + kofs[0], cur + kofs[1], cur + kofs[2], cur + kofs[3]};
+    lds_cchar* kp[4];
 #pragma unroll
-    for (int u = 0; u < 9; ++u) {
+    for (int u = 0; u < 4; ++u) kp[u] = (lds_cchar*)(size_t)opaque(lds_base + so + kofs[u]);
+#pragma unroll
+    for (int u = 0; u < 18; ++u) {
       const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
       sa = T::mfma32(as<vec8>(ka), as<vec8>(qa[u]), sa);
     }
   };
-  auto publish = [&](const f32x16& sa) {
+  auto publish = [&](int j, const f32x16& sa) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      sx[dq][hb][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+      sx[j & 1][hb][dh][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
   };
 
-  // One pass over the chunk (exact = 1: reference fixed from the start),
-  // software-pipelined: step j computes the scores of tile j + 1 while it
-  // turns tile j's scores (exchanged at the end of step j - 1) into weights,
-  // then runs tile j's value update.  Stages: tile j (values), tile j + 1
-  // (keys), tile j + 2 streaming in.
+  // One step of the pass (see the schedule above) for tile j; `last` marks
+  // the chunk's last tile, whose keys past the chunk end are masked (kept
+  // out of the loop so that the loop body is one basic block the compiler
+  // can interleave).  Scores stay unscaled until the exponent: with the
+  // scale c >= 0 (a negative scale was moved into the query signs), the
+  // tile max is c times the max of the raw scores and each weight is
+  // exp2(fma(s, c, -m)).
+  f32x16 own;  // this wave's partial scores of the tile the step turns into weights
+  int sv = 0, sk = kMwStageBytes;  // stages of tile j (values) and tile j + 1 (keys)
+  auto step = [&](int j, bool exact, auto last) {
+    // the partner's partial scores of tile j
+    f32x4 o4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o4[k] = sx[j & 1][hb][dh ^ 1][k][lane];
+    dma(j + 2);
+    // tile j + 1's partial scores (past the last tile: a stage of zeros or
+    // stale rows, never used)
+    f32x16 nxt;
+    scores(sk, nxt);
+    // tile j: the pair's partial scores added half 0 + half 1; keys of
+    // sc[r]: j * 32 + 8 (r / 4) + 4 h + r % 4
+    f32x16 sc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc[4 * k + e] = dh == 0 ? own[4 * k + e] + o4[k][e] : o4[k][e] + own[4 * k + e];
+    bool valid[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      valid[r] = true;
+      if constexpr (decltype(last)::value) valid[r] = j * kMwBK + 4 * h + 8 * (r >> 2) + (r & 3) < n;
+    }
+    float mx = valid[0] ? sc[0] : -INFINITY;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, valid[r] ? sc[r] : -INFINITY);
+    mx = max_halves(mx) * c;  // the tile's row max of head l32 (log2 units)
+    if (!exact) {
+      mruna = fmaxf(mruna, mx);
+      // the reference: tile 0's row max (tile 0 holds a valid key)
+      flag |= (j > 0) & (mx > mra + mw_overflow(T{}));
+      mra = j == 0 ? mx : mra;
+    }
+    // weights: slots 8t .. 8t + 7 of the value update are sc[8t .. 8t + 7]
+    vec8 pa[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x8 p;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fexp2(__builtin_fmaf(sc[8 * t + e], c, -mra));
+        if constexpr (decltype(last)::value) p[e] = valid[8 * t + e] ? p[e] : 0.f;
+      }
+      la += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      pa[t] = T::cvt8(p);
+    }
+    publish(j + 1, nxt);
+    // tile j's value update
+    lds_cchar* vp[2] = {(lds_cchar*)(size_t)opaque(lds_base + sv + vofs[0]),
+                        (lds_cchar*)(size_t)opaque(lds_base + sv + vofs[1])};
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        lds_cchar* p = vp[db & 1] + 128 * (db >> 1) + 2 * 16 * t * kMlaD;
+        const u32x2 v0 = mw_read_tr(p);
+        const u32x2 v1 = mw_read_tr(p + 2 * 8 * kMlaD);
+        const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
+        oa[db] = T::mfma32(as<vec8>(av), pa[t], oa[db]);
+      }
+    own = nxt;
+    sv = sk;
+    sk = sk == (kMwStages - 1) * kMwStageBytes ? 0 : sk + kMwStageBytes;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
+    __syncthreads();  // tile j + 1's partials and tile j + 2 published, stage j free
+  };
+  // One pass over the chunk (exact = 1: reference fixed from the start).
   auto run = [&](bool exact) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oa[db][r] = 0.f;
     la = 0.f;
+    sv = 0;
+    sk = kMwStageBytes;
     dma(0);
     dma(1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0 and 1 are in
-    __syncthreads();
-    {
-      f32x16 sa;
-      scores(0, sa);
-      publish(sa);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0 and 1 (and the queries) are in
+    if (!exact) {
+      // a negative scale flips the sign of every query element instead (the
+      // sign bit of both 16-bit formats is bit 15), so that c >= 0 below;
+      // the empty asm keeps the flip after the wait above
+      const uint32_t sgn = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+#pragma unroll
+      for (int u = 0; u < 18; ++u) {
+        __asm__ volatile("" : "+v"(qa[u]));
+        qa[u] ^= sgn;
+      }
     }
     __syncthreads();
-    for (int j = 0; j < ntiles; ++j) {
-      dma(j + 2);
-      // tile j + 1's scores: independent of the weights below
-      f32x16 na;
-      const bool more = j + 1 < ntiles;
-      if (more) scores(j + 1, na);
-      // tile j: this wave's key quarter, the four waves' partial scores
-      // added in quarter order
-      f32x4 ta = sx[0][hb][dq][lane];
-#pragma unroll
-      for (int q2 = 1; q2 < 4; ++q2) ta += sx[q2][hb][dq][lane];
-      float xa[4];
-      const float mxa = quarter(ta, j, xa);
-      if (!exact) {
-        mruna = fmaxf(mruna, mxa);
-        if (j == 0) {  // the reference: tile 0's row max (tile 0 holds a valid key)
-          mra = wave_max(max_halves(mxa));
-        } else if (mxa > mra + mw_overflow(T{})) {
-          flag = 1;
-        }
-      }
-      px[dq][hb][lane] = weights(xa, mra, la);
-      __syncthreads();  // weights published; every wave is done reading sx
-      if (more) publish(na);
-      // every key's weights: slots 8t .. 8t + 7 of the value update are key
-      // quarters 2t and 2t + 1
-      vec8 pa[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x2 a0 = px[2 * t][hb][lane], a1 = px[2 * t + 1][hb][lane];
-        pa[t] = as<vec8>(u32x4{a0[0], a0[1], a1[0], a1[1]});
-      }
-      lds_cchar* cur = (lds_cchar*)(lds) + (j % kMwStages) * kMwStageBytes;
-      lds_cchar* vp[2] = {cur + vofs[0], cur + vofs[1]};
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          lds_cchar* p = vp[db & 1] + 128 * (db >> 1) + 2 * 16 * t * kMlaD;
-          const u32x2 v0 = mw_read_tr(p);
-          const u32x2 v1 = mw_read_tr(p + 2 * 8 * kMlaD);
-          const u32x4 av = {v0[0], v0[1], v1[0], v1[1]};
-          oa[db] = T::mfma32(as<vec8>(av), pa[t], oa[db]);
-        }
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
-      __syncthreads();  // tile j + 1's scores and tile j + 2 published, stage j free
-    }
+    scores(0, own);
+    publish(0, own);
+    __syncthreads();
+    for (int j = 0; j < ntiles - 1; ++j) step(j, exact, std::false_type{});
+    step(ntiles - 1, exact, std::true_type{});
   };
   run(false);
   if (__syncthreads_or(flag)) {  // a score far above the first tile's max
-    mra = wave_max(max_halves(mruna));
-    __syncthreads();
+    mra = mruna;
     run(true);
   }
-  // the weight sums of the four key quarters
-  auto wave_sum = [&](float v) {
-    __syncthreads();
-    red[dq][hb][lane] = v;
-    __syncthreads();
-    return ((red[0][hb][lane] + red[1][hb][lane]) + red[2][hb][lane]) + red[3][hb][lane];
-  };
-  la = wave_sum(la);
 
-  auto store = [&](const f32x16 (&o)[4], float l, float mref, int64_t row) {
+  auto store = [&](const f32x16 (&o)[8], float l, float mref, int64_t row) {
     l = sum_halves(l);
     const float inv = 1.f / l;
     if (splits_b == 1) {
-      typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 128 * dq + 4 * h;
+      typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 256 * dh + 4 * h;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           f32x8 y;
@@ -648,19 +669,24 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
           const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
           *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
         }
-      if (a.lse && dq == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
+      if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
     } else {
-      float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 128 * dq + 4 * h;
+      typename T::elem* prow =
+          static_cast<typename T::elem*>(a.o_part) + (int64_t(i) * rows + row) * kMlaDc + 256 * dh + 4 * h;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 8; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          f32x4 y;
+          f32x8 y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = o[db][4 * g4 + e] * inv;
-          *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * g4) = y;
+          for (int e = 0; e < 4; ++e) {
+            y[e] = o[db][4 * g4 + e] * inv;
+            y[4 + e] = 0.f;
+          }
+          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+          *reinterpret_cast<u32x2*>(prow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
         }
-      if (dq == 0 && h == 0) {
+      if (dh == 0 && h == 0) {
         a.m_part[int64_t(i) * rows + row] = mref * kLn2;
         a.l_part[int64_t(i) * rows + row] = l;
       }
@@ -726,10 +752,14 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
 // merge of the Split operator: M = max m_i, w_i = l_i e^{m_i - M},
 // O = sum w_i o_i / sum w_i, LSE = M + ln sum w_i.  One wave per (request,
 // head) row; lane l holds dims 8l .. 8l + 7, so one split's partial row is a
-// single 2 KB read by the wave (two 16-byte loads per lane), and the splits
+// single 1 KB read by the wave (one 16-byte load per lane), and the splits
 // arrive in batches of SB whose loads are all issued before the first is
 // used (one memory round trip per batch; a batch's slots past the last
-// split re-read the last one and weigh it 0).  A request's split count comes from
+// split re-read the last one and weigh it 0).  The partial rows are kept in
+// the inputs' 16-bit type: a normalised partial is a convex combination of
+// value rows, so it stays within their range, and its rounding error
+// (2^-9 relative for bf16) is no larger than the final output's; it halves
+// the bytes the kernels write at their end and the merge reads.  A request's split count comes from
 // kv_indptr and the chunk (or piece) length, capped at s, so no read leaves
 // the workspace; requests held by one split were written by the kernel
 // itself.  An empty request of the flat plan is written here (O = 0, LSE =
@@ -757,15 +787,14 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   // splits [i0, i0 + cnt) of one batch of 64: partial rows read SB at a
   // time, each weighed by lane j's weight
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 x0[SB], x1[SB];
+  u32x4 xr[SB];  // partial rows: eight 16-bit dims per lane
   auto load = [&](int i0, int j0, int cnt) {
-    const float* op = a.o_part + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
+    const typename T::elem* op =
+        static_cast<const typename T::elem*>(a.o_part) + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
-      const float* pj = op + int64_t(jj) * rows * kMlaDc;
-      x0[j] = *reinterpret_cast<const f32x4*>(pj);
-      x1[j] = *reinterpret_cast<const f32x4*>(pj + 4);
+      xr[j] = *reinterpret_cast<const u32x4*>(op + int64_t(jj) * rows * kMlaDc);
     }
   };
   auto add = [&](float wi, int j0, int cnt) {
@@ -774,8 +803,9 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
       const int jj = j0 + j < 64 ? j0 + j : 63;
       float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), jj));
       wj = j0 + j < cnt ? wj : 0.f;
-      acc0 += wj * x0[j];
-      acc1 += wj * x1[j];
+      const f32x8 x = __builtin_convertvector(as<typename T::vec8>(xr[j]), f32x8);
+      acc0 += wj * f32x4{x[0], x[1], x[2], x[3]};
+      acc1 += wj * f32x4{x[4], x[5], x[6], x[7]};
     }
   };
   // the first 64 splits' (m, l) and the first SB partial rows go out
