@@ -395,7 +395,9 @@ constexpr int kMwWaves = 4;
 constexpr int kMwPerWave = kMwInstr / kMwWaves;    // 9
 constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
 constexpr int kMwStages = 3;
+constexpr int kMwOutRow = 528;  // LDS bytes per head row of the output staging
 static_assert(kMwInstr % kMwWaves == 0, "every wave issues the same loads");
+static_assert(kMwWaves * 32 * kMwOutRow <= kMwStages * kMwStageBytes, "output staging fits the stages");
 // A weight above 2^mw_overflow forces the exact pass: 2^64 for bf16 (its
 // range is fp32's, and sums of such weights stay far from overflow), 2^15
 // for fp16, whose largest finite value is just below 2^16.
@@ -403,6 +405,28 @@ __device__ __forceinline__ constexpr float mw_overflow(BF16) { return 64.f; }
 __device__ __forceinline__ constexpr float mw_overflow(F16) { return 15.f; }
 
 __device__ __forceinline__ int mw_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Instruction order of one step (one wave per SIMD, so the wave's own
+// order decides what overlaps): the four exchange reads and the first four
+// key reads, then each score MFMA followed by the next key read; then eight
+// transposing value reads, and each value MFMA followed by two more.  Keeping
+// reads that far ahead of their MFMAs measured best against 2-8 key and
+// 4-16 value reads ahead, and against one interleaving of both phases.
+__device__ __forceinline__ void mw_schedule() {
+  constexpr int kKeyAhead = 4, kValAhead = 8;
+  __builtin_amdgcn_sched_group_barrier(0x100, 4 + kKeyAhead, 0);  // LDS reads
+#pragma unroll
+  for (int i = 0; i < 18; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if (i + kKeyAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kValAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (2 * i + kValAhead < 32) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+}
 
 typedef __attribute__((address_space(3))) const char lds_cchar;
 __device__ __forceinline__ u32x4 mw_read128(lds_cchar* p) {
@@ -612,6 +636,7 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     own = nxt;
     sv = sk;
     sk = sk == (kMwStages - 1) * kMwStageBytes ? 0 : sk + kMwStageBytes;
+    mw_schedule();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
     __syncthreads();  // tile j + 1's partials and tile j + 2 published, stage j free
   };
@@ -651,48 +676,56 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     run(true);
   }
 
+  // The wave's output block (32 heads x 256 dims, 16-bit) goes out through
+  // LDS (the stages are free once every wave has passed the last step's
+  // barrier): the accumulator layout gives each lane 4 dims of a head per
+  // register group, which would make every store instruction touch 32 rows;
+  // read back, each half-wave holds 512 contiguous bytes of one head row.
+  // Rows are 528 bytes apart in LDS (32 heads x 528 = 16.5 KB per wave).
   auto store = [&](const f32x16 (&o)[8], float l, float mref, int64_t row) {
     l = sum_halves(l);
     const float inv = 1.f / l;
-    if (splits_b == 1) {
-      typename T::elem* orow = static_cast<typename T::elem*>(a.o) + row * kMlaDc + 256 * dh + 4 * h;
+    typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    __attribute__((address_space(3))) char* blk =
+        (__attribute__((address_space(3))) char*)lds + w * (32 * kMwOutRow);
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+    for (int db = 0; db < 8; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x8 y;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x8 y;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = o[db][4 * g4 + e] * inv;
-            y[4 + e] = 0.f;
-          }
-          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
+        for (int e = 0; e < 4; ++e) {
+          y[e] = o[db][4 * g4 + e] * inv;
+          y[4 + e] = 0.f;
         }
-      if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
-    } else {
-      typename T::elem* prow =
-          static_cast<typename T::elem*>(a.o_part) + (int64_t(i) * rows + row) * kMlaDc + 256 * dh + 4 * h;
-#pragma unroll
-      for (int db = 0; db < 8; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x8 y;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = o[db][4 * g4 + e] * inv;
-            y[4 + e] = 0.f;
-          }
-          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-          *reinterpret_cast<u32x2*>(prow + 32 * db + 8 * g4) = u32x2{bits[0], bits[1]};
-        }
-      if (dh == 0 && h == 0) {
-        a.m_part[int64_t(i) * rows + row] = mref * kLn2;
-        a.l_part[int64_t(i) * rows + row] = l;
+        const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+        *reinterpret_cast<lds_u32x2*>(blk + l32 * kMwOutRow + 2 * (32 * db + 8 * g4 + 4 * h)) =
+            u32x2{bits[0], bits[1]};
       }
+    // LDS accesses of one wave complete in issue order; the fence keeps the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // store k: head 2k + h of the wave's block, dims 256 dh + 8 l32 .. +8
+    typename T::elem* base = splits_b == 1 ? static_cast<typename T::elem*>(a.o)
+                                           : static_cast<typename T::elem*>(a.o_part) + int64_t(i) * rows * kMlaDc;
+    const int64_t hrow0 = row0 + 32 * hb + h;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const u32x4 v = *reinterpret_cast<lds_u32x4*>(blk + (2 * k + h) * kMwOutRow + 16 * l32);
+      *reinterpret_cast<u32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 8 * l32) = v;
+    }
+    if (splits_b == 1) {
+      if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
+    } else if (dh == 0 && h == 0) {
+      a.m_part[int64_t(i) * rows + row] = mref * kLn2;
+      a.l_part[int64_t(i) * rows + row] = l;
     }
   };
   store(oa, la, mra, rowA);
+  __syncthreads();  // (flat plan) the next segment's first loads reuse the stages
   };
 
   if constexpr (!FLAT) {
