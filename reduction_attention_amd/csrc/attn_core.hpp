@@ -359,37 +359,53 @@ __device__ __forceinline__ void softmax_pv(RowState<D>& st, const f32x16 (&s)[BK
   pv_tile<T, D, BK>(st, pb, vlds, lane);
 }
 
-// Final normalisation and store of the wave's rows.  orow points at dim 0 of
-// this lane's query row (nullptr if the row does not exist); lse_out at its
-// LSE slot or nullptr.
+// Final normalisation and store of the wave's 32 rows, through LDS: the
+// accumulator layout gives each lane 4 dims of its row per register group,
+// so a direct store instruction would write 16 bytes into each of 32 rows.
+// Here the rows go to `stage` (the wave's own LDS area of 32 * (2D + 16)
+// bytes, free by then) and come back as 16-byte row pieces: each store
+// instruction writes 64 / (D / 8) whole rows.  obase points at dim 0 of the
+// wave's first row, rows ostride elements apart; rows nvalid .. 31 are not
+// written.  lse_out points at the LSE slot of this lane's row (lane % 32),
+// or is nullptr.
 template <class T, int D>
-__device__ __forceinline__ void row_store(const RowState<D>& st, uint16_t* orow, float* lse_out,
-                                          int lane) {
+__device__ __forceinline__ void row_store_staged(const RowState<D>& st, uint16_t* obase, int64_t ostride,
+                                                 int nvalid, float* lse_out,
+                                                 __attribute__((address_space(3))) char* stage, int lane) {
+  constexpr int RS = 2 * D + 16;        // LDS bytes per row
+  constexpr int LPR = 2 * D / 16;       // lanes per row on the way out
+  constexpr int RPI = 64 / LPR;         // rows per store instruction
   float l = sum_halves(st.l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int h = lane >> 5;
-  if (orow) {
+  const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x8 y;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      f32x8 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = st.o[db][4 * g4 + e] * inv;
-          y[4 + e] = 0.f;
-        }
-        const typename T::vec8 yb = T::cvt8(y);
-        const u32x4 bits = __builtin_bit_cast(u32x4, yb);
-        u32x2 out;
-        out[0] = bits[0];
-        out[1] = bits[1];
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * g4 + 4 * h) = out;
+      for (int e = 0; e < 4; ++e) {
+        y[e] = st.o[db][4 * g4 + e] * inv;
+        y[4 + e] = 0.f;
       }
+      const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + l32 * RS + 2 * (32 * db + 8 * g4 + 4 * h)) =
+          u32x2{bits[0], bits[1]};
+    }
+  // one wave's LDS accesses complete in issue order; the fences keep the
+  // compiler from moving the reads above the writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = RPI * k + rr;
+    const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(stage + r * RS + 16 * cc);
+    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + r * ostride + 8 * cc) = v;
   }
   if (lse_out && h == 0) *lse_out = l > 0.f ? (st.m + flog2(l)) * kLn2 : -INFINITY;
 }
-
 
 // A split's partial result for the wave's 32 rows: O normalised by the
 // split's own sum (fp32), the reference max m in natural-log units and the

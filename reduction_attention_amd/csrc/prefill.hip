@@ -240,9 +240,15 @@ void prefill_kernel(PrefillArgs a) {
     const bool row_ok = oq < n_q;
     const int64_t row = (q_begin + oq) * a.Hq + hq;
     if (a.s == 1) {
-      uint16_t* orow = row_ok ? static_cast<uint16_t*>(a.o) + row * D : nullptr;
+      // the output goes through LDS, waves 0-1 in the K stages and 2-3 in the
+      // V stages (free after the last step's barrier)
+      static_assert(NT == 256 && 2 * 32 * (2 * D + 16) <= 2 * TE * 2, "two waves' rows fit one stage pair");
+      __attribute__((address_space(3))) char* stage =
+          (__attribute__((address_space(3))) char*)(w < 2 ? lds_k : lds_v) + (w & 1) * 32 * (2 * D + 16);
+      const int q0 = q0w + 32 * rb;
+      uint16_t* obase = static_cast<uint16_t*>(a.o) + ((q_begin + q0) * a.Hq + hq) * D;
       float* lse = (row_ok && a.lse) ? a.lse + row : nullptr;
-      row_store<T, D>(st[rb], orow, lse, lane);
+      row_store_staged<T, D>(st[rb], obase, int64_t(a.Hq) * D, n_q - q0, lse, stage, lane);
     } else {
       const int64_t prow = int64_t(si) * a.rows + row;
       row_store_partial<D>(st[rb], row_ok ? a.o_part + prow * D : nullptr, a.m_part + prow,
@@ -345,9 +351,12 @@ __global__ __launch_bounds__(128, 2) void bsr_kernel(BsrArgs a) {
     __syncthreads();
   }
 
+  // the output goes through the free K stages (attn_core.hpp, row_store_staged)
+  static_assert(NT == 128 && 2 * 32 * (2 * D + 16) <= 2 * TE * 2, "the waves' rows fit the K stages");
   const int64_t orow_idx = (int64_t(b) * L + my_q) * a.Hq + hq;
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + orow_idx * D;
-  row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
+  uint16_t* obase = static_cast<uint16_t*>(a.o) + ((int64_t(b) * L + qblk * 64 + 32 * w) * a.Hq + hq) * D;
+  row_store_staged<T, D>(st[0], obase, int64_t(a.Hq) * D, 32, a.lse ? a.lse + orow_idx : nullptr,
+                         (__attribute__((address_space(3))) char*)lds_k + w * 32 * (2 * D + 16), lane);
 }
 
 // The D = 64 form: two halves of a row's stored tiles in one workgroup.
@@ -466,9 +475,13 @@ __global__ __launch_bounds__(256, 4) void bsr_kernel_halves(BsrArgs a) {
     st[0].l = st[0].l * a1 + l2 * a2;
     st[0].m = M;
   }
+  // the output goes through the V slots past the (m, l) exchange (attn_core.hpp,
+  // row_store_staged)
+  static_assert(1024 + 2 * 32 * (2 * D + 16) <= 2 * TE * 2, "the waves' rows fit the V slots");
   const int64_t orow_idx = (int64_t(b) * L + my_q) * a.Hq + hq;
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + orow_idx * D;
-  row_store<T, D>(st[0], orow, a.lse ? a.lse + orow_idx : nullptr, lane);
+  uint16_t* obase = static_cast<uint16_t*>(a.o) + ((int64_t(b) * L + qblk * 64 + 32 * rw) * a.Hq + hq) * D;
+  row_store_staged<T, D>(st[0], obase, int64_t(a.Hq) * D, 32, a.lse ? a.lse + orow_idx : nullptr,
+                         (__attribute__((address_space(3))) char*)lds_v + 1024 + rw * 32 * (2 * D + 16), lane);
 }
 
 // Dense expansion of the two-level mask with the kernel's own predicate:
