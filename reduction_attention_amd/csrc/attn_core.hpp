@@ -410,15 +410,24 @@ __device__ __forceinline__ void row_store_staged(const RowState<D>& st, uint16_t
 // A split's partial result for the wave's 32 rows: O normalised by the
 // split's own sum (fp32), the reference max m in natural-log units and the
 // sum l relative to it; a row without valid keys gets O = 0, m = -inf,
-// l = 0.  orow points at dim 0 of the lane's row in the partial output (or
-// is nullptr when the row does not exist).
+// l = 0.  Like row_store_staged, the rows go out through the wave's LDS
+// area `stage` (32 * 4D bytes, free by then): 16-byte piece c of row r sits
+// at slot c ^ (r % (D / 4)), so both the writes (32 rows, one piece) and the
+// reads (whole rows) spread over the banks.  obase points at dim 0 of the
+// wave's first row in the partial output, rows ostride elements apart; rows
+// nvalid .. 31 are not written.  m_out and l_out point at this lane's row
+// (lane % 32), or are nullptr when it does not exist.
 template <int D>
-__device__ __forceinline__ void row_store_partial(const RowState<D>& st, float* orow, float* m_out,
-                                                  float* l_out, int lane) {
+__device__ __forceinline__ void row_store_partial_staged(const RowState<D>& st, float* obase, int64_t ostride,
+                                                         int nvalid, float* m_out, float* l_out,
+                                                         __attribute__((address_space(3))) char* stage,
+                                                         int lane) {
+  constexpr int NC = D / 4;             // 16-byte pieces per row
+  constexpr int RPI = 64 / NC;          // rows per store instruction
+  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
   const float l = sum_halves(st.l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const int h = lane >> 5;
-  if (!orow) return;
+  const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -426,9 +435,20 @@ __device__ __forceinline__ void row_store_partial(const RowState<D>& st, float* 
       f32x4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = st.o[db][4 * g4 + e] * inv;
-      *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g4 + 4 * h) = y;
+      const int c = 8 * db + 2 * g4 + h;  // dims 4c .. 4c + 3
+      *reinterpret_cast<lds_f32x4*>(stage + l32 * (4 * D) + 16 * (c ^ (l32 % NC))) = y;
     }
-  if (h == 0) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int rr = lane / NC, cc = lane % NC;
+#pragma unroll
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = RPI * k + rr;
+    const f32x4 v = *reinterpret_cast<lds_f32x4*>(stage + r * (4 * D) + 16 * (cc ^ (r % NC)));
+    if (r < nvalid) *reinterpret_cast<f32x4*>(obase + r * ostride + 4 * cc) = v;
+  }
+  if (m_out && h == 0) {
     *m_out = l > 0.f ? st.m * kLn2 : -INFINITY;
     *l_out = l;
   }

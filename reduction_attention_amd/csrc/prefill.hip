@@ -250,9 +250,16 @@ void prefill_kernel(PrefillArgs a) {
       float* lse = (row_ok && a.lse) ? a.lse + row : nullptr;
       row_store_staged<T, D>(st[rb], obase, int64_t(a.Hq) * D, n_q - q0, lse, stage, lane);
     } else {
+      // fp32 partial rows through LDS: 16 KB per wave at D = 128, waves 0-1
+      // in the K stages and 2-3 in the V stages
+      static_assert(NT == 256 && 2 * 32 * 4 * D <= 2 * TE * 2, "two waves' rows fit one stage pair");
+      __attribute__((address_space(3))) char* stage =
+          (__attribute__((address_space(3))) char*)(w < 2 ? lds_k : lds_v) + (w & 1) * 32 * 4 * D;
+      const int q0 = q0w + 32 * rb;
       const int64_t prow = int64_t(si) * a.rows + row;
-      row_store_partial<D>(st[rb], row_ok ? a.o_part + prow * D : nullptr, a.m_part + prow,
-                           a.l_part + prow, lane);
+      float* obase = a.o_part + (int64_t(si) * a.rows + (q_begin + q0) * a.Hq + hq) * D;
+      row_store_partial_staged<D>(st[rb], obase, int64_t(a.Hq) * D, n_q - q0, row_ok ? a.m_part + prow : nullptr,
+                                  row_ok ? a.l_part + prow : nullptr, stage, lane);
     }
   }
 }
