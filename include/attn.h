@@ -221,10 +221,9 @@ attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void*
 
 /* ---- multi-head latent attention (MLA) decode, absorbed form ----------- */
 
-/* Workspace bytes of attn_mla_decode with s splits: s * B * H * (512 * 2 + 8)
- * (the normalised partial outputs of the 512-wide latent part in the inputs'
- * 16-bit type, then fp32 maxima and sums), rounded up to 256; 0 for invalid
- * arguments. */
+/* Workspace bytes of attn_mla_decode with s splits: s * B * H * (512 + 2) * 4
+ * (fp32 partial outputs of the 512-wide latent part, maxima, sums), rounded
+ * up to 256; 0 for invalid arguments. */
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
 
 /* The split count attn_mla_decode picks when num_splits = 0.  hg = H / 64
@@ -293,7 +292,7 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
  * is shorter than 256 keys, within [1, 65535]; 1 for invalid arguments. */
 int attn_mla_decode_flat_pieces(int B, int H, long long total_kv);
 
-/* Workspace bytes of attn_mla_decode_flat: s * B * H * (512 * 2 + 8) with
+/* Workspace bytes of attn_mla_decode_flat: s * B * H * (512 + 2) * 4 with
  * s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces), rounded
  * up to 256 (0 for invalid arguments). */
 size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long long total_kv,

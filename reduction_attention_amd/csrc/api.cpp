@@ -251,9 +251,8 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
 
 // ---- multi-head latent attention decode ---------------------------------------
 
-// MLA workspace layout: o_part [s, B*H, 512] in the inputs' 16-bit type, then
-// m_part [s, B*H] and l_part [s, B*H] (fp32).
-static size_t mla_workspace_raw(size_t s, size_t rows) { return s * rows * (512 * 2 + 2 * sizeof(float)); }
+// MLA workspace layout: o_part [s, B*H, 512], m_part [s, B*H], l_part [s, B*H] (fp32).
+static size_t mla_workspace_raw(size_t s, size_t rows) { return s * rows * (512 + 2) * sizeof(float); }
 
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
   if (B <= 0 || H <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
@@ -342,8 +341,8 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
   if (s > 1 && !aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  char* ws = static_cast<char*>(workspace);
-  float* mws = s > 1 ? reinterpret_cast<float*>(ws + size_t(s) * rows * 512 * 2) : nullptr;
+  float* ws = static_cast<float*>(workspace);
+  float* mws = s > 1 ? ws + size_t(s) * rows * 512 : nullptr;
   rattn::MlaArgs a{q, kv, kv_indptr, o, lse,
                    s > 1 ? ws : nullptr, mws, s > 1 ? mws + size_t(s) * rows : nullptr,
                    B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
@@ -421,8 +420,8 @@ attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t*
   if (!aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode_flat: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  char* ws = static_cast<char*>(workspace);
-  float* mws = reinterpret_cast<float*>(ws + size_t(s) * rows * 512 * 2);
+  float* ws = static_cast<float*>(workspace);
+  float* mws = ws + size_t(s) * rows * 512;
   rattn::MlaArgs a{q, kv, kv_indptr, o, lse, ws, mws, mws + size_t(s) * rows, B, H, s,
                    int(flat_piece_len(total_kv, P)),
                    scale * kLog2e, dtype, 0};

@@ -45,7 +45,7 @@ struct MlaArgs {
   const int32_t* kv_indptr;
   void* o;
   float* lse;
-  void* o_part;   // [s, B*H, 512], the inputs' 16-bit type
+  float* o_part;  // [s, B*H, 512]
   float* m_part;  // [s, B*H]
   float* l_part;  // [s, B*H]
   int B, H;

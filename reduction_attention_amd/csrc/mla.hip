@@ -336,19 +336,9 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
     }
     if (a.lse && w == 0 && h4 == 0) a.lse[row] = (m + flog2(l)) * kLn2;
   } else {
-    typename T::elem* prow =
-        static_cast<typename T::elem*>(a.o_part) + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
+    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-      f32x8 y;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        y[r] = o[blk][r] * inv;
-        y[4 + r] = 0.f;
-      }
-      const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-      *reinterpret_cast<u32x2*>(prow + 16 * blk) = u32x2{bits[0], bits[1]};
-    }
+    for (int blk = 0; blk < NB; ++blk) *reinterpret_cast<f32x4*>(prow + 16 * blk) = o[blk] * inv;
     if (w == 0 && h4 == 0) {
       a.m_part[int64_t(i) * rows + row] = m * kLn2;
       a.l_part[int64_t(i) * rows + row] = l;
@@ -676,52 +666,81 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     run(true);
   }
 
-  // The wave's output block (32 heads x 256 dims, 16-bit) goes out through
-  // LDS (the stages are free once every wave has passed the last step's
-  // barrier): the accumulator layout gives each lane 4 dims of a head per
-  // register group, which would make every store instruction touch 32 rows;
-  // read back, each half-wave holds 512 contiguous bytes of one head row.
-  // Rows are 528 bytes apart in LDS (32 heads x 528 = 16.5 KB per wave).
+  // The wave's output block (32 heads x 256 dims) goes out through LDS (the
+  // stages are free once every wave has passed the last step's barrier):
+  // the accumulator layout gives each lane 4 dims of a head per register
+  // group, which would make every store instruction touch 32 rows; read
+  // back, each half-wave holds contiguous bytes of one head row.  Final
+  // rows (16-bit) take one pass through a 32 x 528-byte area per wave;
+  // fp32 partial rows take two passes of 128 dims through 32 x 512 bytes,
+  // 16-byte piece c of row r at slot c ^ r (so the 32 rows written with one
+  // piece, and the rows read back, spread over the banks).
   auto store = [&](const f32x16 (&o)[8], float l, float mref, int64_t row) {
     l = sum_halves(l);
     const float inv = 1.f / l;
     typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     __attribute__((address_space(3))) char* blk =
         (__attribute__((address_space(3))) char*)lds + w * (32 * kMwOutRow);
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        f32x8 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[e] = o[db][4 * g4 + e] * inv;
-          y[4 + e] = 0.f;
-        }
-        const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-        *reinterpret_cast<lds_u32x2*>(blk + l32 * kMwOutRow + 2 * (32 * db + 8 * g4 + 4 * h)) =
-            u32x2{bits[0], bits[1]};
-      }
-    // LDS accesses of one wave complete in issue order; the fence keeps the
-    // compiler from moving the reads above the writes
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // store k: head 2k + h of the wave's block, dims 256 dh + 8 l32 .. +8
-    typename T::elem* base = splits_b == 1 ? static_cast<typename T::elem*>(a.o)
-                                           : static_cast<typename T::elem*>(a.o_part) + int64_t(i) * rows * kMlaDc;
-    const int64_t hrow0 = row0 + 32 * hb + h;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const u32x4 v = *reinterpret_cast<lds_u32x4*>(blk + (2 * k + h) * kMwOutRow + 16 * l32);
-      *reinterpret_cast<u32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 8 * l32) = v;
-    }
+    const int64_t hrow0 = row0 + 32 * hb + h;  // store k below: head 2k + h of the block
+    auto wave_fence = [] {
+      // LDS accesses of one wave complete in issue order; the fences keep
+      // the compiler from moving reads above writes (or writes above reads)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
     if (splits_b == 1) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          f32x8 y;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = o[db][4 * g4 + e] * inv;
+            y[4 + e] = 0.f;
+          }
+          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
+          *reinterpret_cast<lds_u32x2*>(blk + l32 * kMwOutRow + 2 * (32 * db + 8 * g4 + 4 * h)) =
+              u32x2{bits[0], bits[1]};
+        }
+      wave_fence();
+      typename T::elem* base = static_cast<typename T::elem*>(a.o);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const u32x4 v = *reinterpret_cast<lds_u32x4*>(blk + (2 * k + h) * kMwOutRow + 16 * l32);
+        *reinterpret_cast<u32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 8 * l32) = v;
+      }
       if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
-    } else if (dh == 0 && h == 0) {
-      a.m_part[int64_t(i) * rows + row] = mref * kLn2;
-      a.l_part[int64_t(i) * rows + row] = l;
+    } else {
+      float* base = a.o_part + int64_t(i) * rows * kMlaDc;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (half) wave_fence();  // the first pass's reads are done
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = o[4 * half + db][4 * g4 + e] * inv;
+            const int c = 8 * db + 2 * g4 + h;  // dims 4c .. 4c + 3 of this pass
+            *reinterpret_cast<lds_f32x4*>(blk + l32 * 512 + 16 * (c ^ l32)) = y;
+          }
+        wave_fence();
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int r = 2 * k + h;
+          const f32x4 v = *reinterpret_cast<lds_f32x4*>(blk + r * 512 + 16 * (l32 ^ r));
+          *reinterpret_cast<f32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 128 * half + 4 * l32) = v;
+        }
+      }
+      if (dh == 0 && h == 0) {
+        a.m_part[int64_t(i) * rows + row] = mref * kLn2;
+        a.l_part[int64_t(i) * rows + row] = l;
+      }
     }
   };
   store(oa, la, mra, rowA);
@@ -785,14 +804,13 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
 // merge of the Split operator: M = max m_i, w_i = l_i e^{m_i - M},
 // O = sum w_i o_i / sum w_i, LSE = M + ln sum w_i.  One wave per (request,
 // head) row; lane l holds dims 8l .. 8l + 7, so one split's partial row is a
-// single 1 KB read by the wave (one 16-byte load per lane), and the splits
+// single 2 KB read by the wave (two 16-byte loads per lane), and the splits
 // arrive in batches of SB whose loads are all issued before the first is
 // used (one memory round trip per batch; a batch's slots past the last
-// split re-read the last one and weigh it 0).  The partial rows are kept in
-// the inputs' 16-bit type: a normalised partial is a convex combination of
-// value rows, so it stays within their range, and its rounding error
-// (2^-9 relative for bf16) is no larger than the final output's; it halves
-// the bytes the kernels write at their end and the merge reads.  A request's split count comes from
+// split re-read the last one and weigh it 0).  The partial rows stay fp32:
+// a split over a few keys can be dominated by one value row, and a 16-bit
+// copy of it would add that row's rounding error (2^-9 relative in bf16) to
+// the output's own.  A request's split count comes from
 // kv_indptr and the chunk (or piece) length, capped at s, so no read leaves
 // the workspace; requests held by one split were written by the kernel
 // itself.  An empty request of the flat plan is written here (O = 0, LSE =
@@ -820,14 +838,15 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   // splits [i0, i0 + cnt) of one batch of 64: partial rows read SB at a
   // time, each weighed by lane j's weight
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  u32x4 xr[SB];  // partial rows: eight 16-bit dims per lane
+  f32x4 x0[SB], x1[SB];
   auto load = [&](int i0, int j0, int cnt) {
-    const typename T::elem* op =
-        static_cast<const typename T::elem*>(a.o_part) + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
+    const float* op = a.o_part + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
-      xr[j] = *reinterpret_cast<const u32x4*>(op + int64_t(jj) * rows * kMlaDc);
+      const float* pj = op + int64_t(jj) * rows * kMlaDc;
+      x0[j] = *reinterpret_cast<const f32x4*>(pj);
+      x1[j] = *reinterpret_cast<const f32x4*>(pj + 4);
     }
   };
   auto add = [&](float wi, int j0, int cnt) {
@@ -836,9 +855,8 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
       const int jj = j0 + j < 64 ? j0 + j : 63;
       float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), jj));
       wj = j0 + j < cnt ? wj : 0.f;
-      const f32x8 x = __builtin_convertvector(as<typename T::vec8>(xr[j]), f32x8);
-      acc0 += wj * f32x4{x[0], x[1], x[2], x[3]};
-      acc1 += wj * f32x4{x[4], x[5], x[6], x[7]};
+      acc0 += wj * x0[j];
+      acc1 += wj * x1[j];
     }
   };
   // the first 64 splits' (m, l) and the first SB partial rows go out
