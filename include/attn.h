@@ -221,9 +221,10 @@ attn_status_t attn_decode_splitkv_flat(const void* q, const void* k, const void*
 
 /* ---- multi-head latent attention (MLA) decode, absorbed form ----------- */
 
-/* Workspace bytes of attn_mla_decode with s splits: s * B * H * (512 + 2) * 4
- * (fp32 partial outputs of the 512-wide latent part, maxima, sums), rounded
- * up to 256; 0 for invalid arguments. */
+/* Workspace bytes of attn_mla_decode with s splits: s * B * H * (512 * 2 +
+ * 6 * 4) (partial outputs of the 512-wide latent part in fp16, each 128-dim
+ * quarter divided by a power-of-two scale kept in fp32, then fp32 maxima and
+ * sums), rounded up to 256; 0 for invalid arguments. */
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits);
 
 /* The split count attn_mla_decode picks when num_splits = 0.  hg = H / 64
@@ -273,7 +274,8 @@ int attn_mla_decode_choose_splits(int B, int H, long long total_kv, int max_kv_l
  * num_splits  s in [1, 256], or 0 for attn_mla_decode_choose_splits; s = 1
  *   needs no workspace (may be NULL).
  * workspace   at least attn_mla_decode_workspace_bytes(B, H, s) bytes when
- *   s > 1; layout o_part [s, B*H, 512], m_part [s, B*H], l_part [s, B*H] fp32.
+ *   s > 1; layout o_part [s, B*H, 512] fp16, then fp32 x_part [s, B*H, 4]
+ *   (o_part's 128-dim quarters hold o / x), m_part [s, B*H], l_part [s, B*H].
  *   Calls that share one workspace must not overlap in time.
  * A request with no key yields O = 0, LSE = -inf.  A workgroup serves 64
  * heads when H is a multiple of 64, else 16; any H >= 1 is accepted.  The
@@ -292,7 +294,7 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
  * is shorter than 256 keys, within [1, 65535]; 1 for invalid arguments. */
 int attn_mla_decode_flat_pieces(int B, int H, long long total_kv);
 
-/* Workspace bytes of attn_mla_decode_flat: s * B * H * (512 + 2) * 4 with
+/* Workspace bytes of attn_mla_decode_flat: s * B * H * (512 * 2 + 6 * 4) with
  * s = attn_decode_flat_max_splits(max_kv_len, total_kv, num_pieces), rounded
  * up to 256 (0 for invalid arguments). */
 size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long long total_kv,
@@ -316,8 +318,8 @@ size_t attn_mla_decode_flat_workspace_bytes(int B, int H, int max_kv_len, long l
  * total_kv    the row count of kv (<= 2^31 - 1); every kv_indptr entry must
  *   lie in [0, total_kv].  Rows outside every request are not read.
  * workspace   at least attn_mla_decode_flat_workspace_bytes(B, H, max_kv_len,
- *   total_kv, P) bytes (always needed); layout o_part [s, B*H, 512], m_part
- *   [s, B*H], l_part [s, B*H] fp32, split i of request b in slot i.  Calls
+ *   total_kv, P) bytes (always needed); layout as attn_mla_decode's
+ *   (o_part fp16, x_part, m_part, l_part), split i of request b in slot i.  Calls
  *   that share one workspace must not overlap in time.
  */
 attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t* kv_indptr,

@@ -251,8 +251,19 @@ attn_status_t attn_decode_partials(const void* q, const void* k, const void* v,
 
 // ---- multi-head latent attention decode ---------------------------------------
 
-// MLA workspace layout: o_part [s, B*H, 512], m_part [s, B*H], l_part [s, B*H] (fp32).
-static size_t mla_workspace_raw(size_t s, size_t rows) { return s * rows * (512 + 2) * sizeof(float); }
+// MLA workspace layout: o_part [s, B*H, 512] (fp16 bits), then the fp32
+// arrays x_part [s, B*H, 4] (scale of each 128-dim quarter of a partial
+// row), m_part [s, B*H] and l_part [s, B*H].
+static size_t mla_workspace_raw(size_t s, size_t rows) {
+  return s * rows * (512 * sizeof(uint16_t) + (4 + 2) * sizeof(float));
+}
+static void mla_workspace_split(void* workspace, size_t s, size_t rows, rattn::MlaArgs& a) {
+  if (!workspace) return;
+  a.o_part = static_cast<uint16_t*>(workspace);
+  a.x_part = reinterpret_cast<float*>(a.o_part + s * rows * 512);
+  a.m_part = a.x_part + s * rows * 4;
+  a.l_part = a.m_part + s * rows;
+}
 
 size_t attn_mla_decode_workspace_bytes(int B, int H, int num_splits) {
   if (B <= 0 || H <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
@@ -341,12 +352,10 @@ attn_status_t attn_mla_decode(const void* q, const void* kv, const int32_t* kv_i
   if (s > 1 && !aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  float* ws = static_cast<float*>(workspace);
-  float* mws = s > 1 ? ws + size_t(s) * rows * 512 : nullptr;
-  rattn::MlaArgs a{q, kv, kv_indptr, o, lse,
-                   s > 1 ? ws : nullptr, mws, s > 1 ? mws + size_t(s) * rows : nullptr,
+  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, nullptr, nullptr, nullptr, nullptr,
                    B, H, s, max_kv_len > 0 ? (max_kv_len + s - 1) / s : 1, scale * kLog2e, dtype,
                    uniform_lengths(B, max_kv_len, total_kv)};
+  if (s > 1) mla_workspace_split(workspace, size_t(s), rows, a);
   a.total_kv = total_kv;
   // the 64-head kernel's units: for ragged lengths packed (request b owns
   // max(1, min(ceil(len_b / c), s)) <= len_b / c + 1 of them), else all
@@ -420,11 +429,10 @@ attn_status_t attn_mla_decode_flat(const void* q, const void* kv, const int32_t*
   if (!aligned16(workspace))
     return fail(ATTN_EINVAL, "mla_decode_flat: workspace must be 16-byte aligned");
   const size_t rows = size_t(B) * H;
-  float* ws = static_cast<float*>(workspace);
-  float* mws = ws + size_t(s) * rows * 512;
-  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, ws, mws, mws + size_t(s) * rows, B, H, s,
+  rattn::MlaArgs a{q, kv, kv_indptr, o, lse, nullptr, nullptr, nullptr, nullptr, B, H, s,
                    int(flat_piece_len(total_kv, P)),
                    scale * kLog2e, dtype, 0};
+  mla_workspace_split(workspace, size_t(s), rows, a);
   a.flat = 1;
   a.pieces = P;
   a.total_kv = total_kv;

@@ -45,9 +45,10 @@ struct MlaArgs {
   const int32_t* kv_indptr;
   void* o;
   float* lse;
-  float* o_part;  // [s, B*H, 512]
-  float* m_part;  // [s, B*H]
-  float* l_part;  // [s, B*H]
+  uint16_t* o_part;  // [s, B*H, 512] fp16, each 128-dim quarter divided by its x_part scale
+  float* x_part;     // [s, B*H, 4] power-of-two scale of each quarter of the partial row
+  float* m_part;     // [s, B*H]
+  float* l_part;     // [s, B*H]
   int B, H;
   int s, chunk;
   float scale_log2;

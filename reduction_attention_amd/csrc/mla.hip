@@ -116,6 +116,18 @@ __device__ __forceinline__ u32x2 mla_tr_read(const uint16_t* base, int byte_off)
   return __builtin_bit_cast(u32x2, x);
 }
 
+// Split partials are kept in fp16 with each 128-dim quarter of a row divided
+// by a power of two 2^e, e the binary exponent of the quarter's largest
+// magnitude: every stored value then lies within [-1, 1], where fp16 keeps
+// 11 significant bits, so a stored element is off by at most 2^-12 of the
+// quarter's largest value (a bf16 copy would be off by up to 2^-9 of the
+// element), and neither the inputs' range nor fp16's can overflow it.
+// Dividing by a power of two is exact; the scale 2^e goes to x_part.
+__device__ __forceinline__ int mla_part_exp(float amax) {
+  const int e = __builtin_amdgcn_frexp_expf(amax);
+  return e < -126 ? -126 : (e > 127 ? 127 : e);
+}
+
 template <class T>
 __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
@@ -336,9 +348,29 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
     }
     if (a.lse && w == 0 && h4 == 0) a.lse[row] = (m + flog2(l)) * kLn2;
   } else {
-    float* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
+    // the wave's dims are quarter w of the row (lanes c16 + 16 h4 hold them)
+    static_assert(16 * NB == 128, "one wave per 128-dim quarter");
+    float amax = 0.f;
 #pragma unroll
-    for (int blk = 0; blk < NB; ++blk) *reinterpret_cast<f32x4*>(prow + 16 * blk) = o[blk] * inv;
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(o[blk][r]));
+    amax = fmaxf(amax, shfl_xor(amax, 16));
+    amax = fmaxf(amax, shfl_xor(amax, 32));
+    const int e = mla_part_exp(amax * inv);
+    uint16_t* prow = a.o_part + (int64_t(i) * rows + row) * kMlaDc + 16 * NB * w + 4 * h4;
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      f32x8 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        y[r] = __builtin_amdgcn_ldexpf(o[blk][r] * inv, -e);
+        y[4 + r] = 0.f;
+      }
+      const u32x4 bits = __builtin_bit_cast(u32x4, F16::cvt8(y));
+      *reinterpret_cast<u32x2*>(prow + 16 * blk) = u32x2{bits[0], bits[1]};
+    }
+    if (h4 == 0) a.x_part[(int64_t(i) * rows + row) * 4 + w] = __builtin_amdgcn_ldexpf(1.f, e);
     if (w == 0 && h4 == 0) {
       a.m_part[int64_t(i) * rows + row] = m * kLn2;
       a.l_part[int64_t(i) * rows + row] = l;
@@ -670,73 +702,66 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   // stages are free once every wave has passed the last step's barrier):
   // the accumulator layout gives each lane 4 dims of a head per register
   // group, which would make every store instruction touch 32 rows; read
-  // back, each half-wave holds contiguous bytes of one head row.  Final
-  // rows (16-bit) take one pass through a 32 x 528-byte area per wave;
-  // fp32 partial rows take two passes of 128 dims through 32 x 512 bytes,
-  // 16-byte piece c of row r at slot c ^ r (so the 32 rows written with one
-  // piece, and the rows read back, spread over the banks).
+  // back from a 32 x 528-byte area per wave, each half-wave holds 512
+  // contiguous bytes of one head row.  Final rows are written in the
+  // inputs' 16-bit type, split partials in fp16 with each 128-dim quarter
+  // scaled by its power of two (mla_part_exp).
   auto store = [&](const f32x16 (&o)[8], float l, float mref, int64_t row) {
     l = sum_halves(l);
     const float inv = 1.f / l;
     typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
     typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-    typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
     __attribute__((address_space(3))) char* blk =
         (__attribute__((address_space(3))) char*)lds + w * (32 * kMwOutRow);
     const int64_t hrow0 = row0 + 32 * hb + h;  // store k below: head 2k + h of the block
-    auto wave_fence = [] {
-      // LDS accesses of one wave complete in issue order; the fences keep
-      // the compiler from moving reads above writes (or writes above reads)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    if (splits_b == 1) {
+    const bool final_rows = splits_b == 1;
+    // quarters 2 dh + qq of the row: value blocks db = 4 qq .. 4 qq + 3,
+    // held by this lane and its partner l ^ 32
+    int e[2] = {0, 0};
+    if (!final_rows) {
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int qq = 0; qq < 2; ++qq) {
+        float amax = 0.f;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          f32x8 y;
+        for (int db = 4 * qq; db < 4 * qq + 4; ++db)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y[e] = o[db][4 * g4 + e] * inv;
-            y[4 + e] = 0.f;
-          }
-          const u32x4 bits = __builtin_bit_cast(u32x4, T::cvt8(y));
-          *reinterpret_cast<lds_u32x2*>(blk + l32 * kMwOutRow + 2 * (32 * db + 8 * g4 + 4 * h)) =
-              u32x2{bits[0], bits[1]};
-        }
-      wave_fence();
-      typename T::elem* base = static_cast<typename T::elem*>(a.o);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const u32x4 v = *reinterpret_cast<lds_u32x4*>(blk + (2 * k + h) * kMwOutRow + 16 * l32);
-        *reinterpret_cast<u32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 8 * l32) = v;
+          for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[db][r]));
+        e[qq] = mla_part_exp(max_halves(amax) * inv);
       }
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x8 y;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          y[k] = final_rows ? o[db][4 * g4 + k] * inv
+                            : __builtin_amdgcn_ldexpf(o[db][4 * g4 + k] * inv, -e[db >> 2]);
+          y[4 + k] = 0.f;
+        }
+        const u32x4 bits = final_rows ? __builtin_bit_cast(u32x4, T::cvt8(y))
+                                      : __builtin_bit_cast(u32x4, F16::cvt8(y));
+        *reinterpret_cast<lds_u32x2*>(blk + l32 * kMwOutRow + 2 * (32 * db + 8 * g4 + 4 * h)) =
+            u32x2{bits[0], bits[1]};
+      }
+    // LDS accesses of one wave complete in issue order; the fences keep the
+    // compiler from moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint16_t* base = final_rows ? static_cast<uint16_t*>(a.o) : a.o_part + int64_t(i) * rows * kMlaDc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const u32x4 v = *reinterpret_cast<lds_u32x4*>(blk + (2 * k + h) * kMwOutRow + 16 * l32);
+      *reinterpret_cast<u32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 8 * l32) = v;
+    }
+    if (final_rows) {
       if (a.lse && dh == 0 && h == 0) a.lse[row] = (mref + flog2(l)) * kLn2;
     } else {
-      float* base = a.o_part + int64_t(i) * rows * kMlaDc;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (half) wave_fence();  // the first pass's reads are done
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            f32x4 y;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) y[e] = o[4 * half + db][4 * g4 + e] * inv;
-            const int c = 8 * db + 2 * g4 + h;  // dims 4c .. 4c + 3 of this pass
-            *reinterpret_cast<lds_f32x4*>(blk + l32 * 512 + 16 * (c ^ l32)) = y;
-          }
-        wave_fence();
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-          const int r = 2 * k + h;
-          const f32x4 v = *reinterpret_cast<lds_f32x4*>(blk + r * 512 + 16 * (l32 ^ r));
-          *reinterpret_cast<f32x4*>(base + (hrow0 + 2 * k) * kMlaDc + 256 * dh + 128 * half + 4 * l32) = v;
-        }
-      }
+      if (h == 0)
+        *reinterpret_cast<f32x2*>(a.x_part + (int64_t(i) * rows + row) * 4 + 2 * dh) =
+            f32x2{__builtin_amdgcn_ldexpf(1.f, e[0]), __builtin_amdgcn_ldexpf(1.f, e[1])};
       if (dh == 0 && h == 0) {
         a.m_part[int64_t(i) * rows + row] = mref * kLn2;
         a.l_part[int64_t(i) * rows + row] = l;
@@ -803,18 +828,19 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
 // Merge of the split partials (512-wide latent outputs), the log-sum-exp
 // merge of the Split operator: M = max m_i, w_i = l_i e^{m_i - M},
 // O = sum w_i o_i / sum w_i, LSE = M + ln sum w_i.  One wave per (request,
-// head) row; lane l holds dims 8l .. 8l + 7, so one split's partial row is a
-// single 2 KB read by the wave (two 16-byte loads per lane), and the splits
-// arrive in batches of SB whose loads are all issued before the first is
-// used (one memory round trip per batch; a batch's slots past the last
-// split re-read the last one and weigh it 0).  The partial rows stay fp32:
-// a split over a few keys can be dominated by one value row, and a 16-bit
-// copy of it would add that row's rounding error (2^-9 relative in bf16) to
-// the output's own.  A request's split count comes from
-// kv_indptr and the chunk (or piece) length, capped at s, so no read leaves
-// the workspace; requests held by one split were written by the kernel
-// itself.  An empty request of the flat plan is written here (O = 0, LSE =
-// -inf); the chunk plan's kernel writes its own.
+// head) row; lane l holds dims 8l .. 8l + 7 (quarter l / 16 of the row), so
+// one split's partial row is a single 1 KB read by the wave (one 16-byte
+// load per lane), and the splits arrive in batches of SB whose loads are
+// all issued before the first is used (one memory round trip per batch; a
+// batch's slots past the last split re-read the last one and weigh it 0).
+// The partial rows are fp16 with a power-of-two scale per quarter
+// (mla_part_exp); lane j of the wave forms split j's weight times each of
+// its four scales, and every lane takes the one of its own quarter.  A
+// request's split count comes from kv_indptr and the chunk (or piece)
+// length, capped at s, so no read leaves the workspace; requests held by
+// one split were written by the kernel itself.  An empty request of the
+// flat plan is written here (O = 0, LSE = -inf); the chunk plan's kernel
+// writes its own.
 // ---------------------------------------------------------------------------
 template <class T, int SB>
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
@@ -834,38 +860,45 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
     if (a.lse && lane == 0) a.lse[row] = -INFINITY;
   }
   if (n <= 1) return;
+  const int qt = lane >> 4;  // the lane's quarter of the row
 
   // splits [i0, i0 + cnt) of one batch of 64: partial rows read SB at a
-  // time, each weighed by lane j's weight
+  // time, each weighed by lane j's weight for this lane's quarter
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 x0[SB], x1[SB];
+  u32x4 xr[SB];
   auto load = [&](int i0, int j0, int cnt) {
-    const float* op = a.o_part + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
+    const uint16_t* op = a.o_part + (int64_t(i0) * rows + row) * kMlaDc + 8 * lane;
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
-      const float* pj = op + int64_t(jj) * rows * kMlaDc;
-      x0[j] = *reinterpret_cast<const f32x4*>(pj);
-      x1[j] = *reinterpret_cast<const f32x4*>(pj + 4);
+      xr[j] = *reinterpret_cast<const u32x4*>(op + int64_t(jj) * rows * kMlaDc);
     }
   };
-  auto add = [&](float wi, int j0, int cnt) {
+  auto add = [&](f32x4 wq, int j0, int cnt) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int jj = j0 + j < 64 ? j0 + j : 63;
-      float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), jj));
+      float w4[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w4[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[k]), jj));
+      float wj = qt == 0 ? w4[0] : (qt == 1 ? w4[1] : (qt == 2 ? w4[2] : w4[3]));
       wj = j0 + j < cnt ? wj : 0.f;
-      acc0 += wj * x0[j];
-      acc1 += wj * x1[j];
+      const f32x8 x = __builtin_convertvector(as<f16x8>(xr[j]), f32x8);
+      acc0 += wj * f32x4{x[0], x[1], x[2], x[3]};
+      acc1 += wj * f32x4{x[4], x[5], x[6], x[7]};
     }
   };
-  // the first 64 splits' (m, l) and the first SB partial rows go out
-  // together, before any of them is used
+  // the first 64 splits' (m, l, scales) and the first SB partial rows go
+  // out together, before any of them is used
   const int cnt0 = n < 64 ? n : 64;
   float m0 = -INFINITY, l0 = 0.f;
+  f32x4 x0 = {0.f, 0.f, 0.f, 0.f};
   if (lane < cnt0) {
-    m0 = a.m_part[int64_t(lane) * rows + row];
-    l0 = a.l_part[int64_t(lane) * rows + row];
+    const int64_t k = int64_t(lane) * rows + row;
+    m0 = a.m_part[k];
+    l0 = a.l_part[k];
+    x0 = *reinterpret_cast<const f32x4*>(a.x_part + 4 * k);
   }
   load(0, 0, cnt0);
   float M = m0;
@@ -876,23 +909,27 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   {
     const float wi = lane < cnt0 ? l0 * fexp2((m0 - M) * kLog2e) : 0.f;
     wsum += wi;
-    add(wi, 0, cnt0);
+    const f32x4 wq = wi * x0;
+    add(wq, 0, cnt0);
     for (int j0 = SB; j0 < cnt0; j0 += SB) {
       load(0, j0, cnt0);
-      add(wi, j0, cnt0);
+      add(wq, j0, cnt0);
     }
   }
   for (int i0 = 64; i0 < n; i0 += 64) {  // more than 64 splits
     const int cnt = n - i0 < 64 ? n - i0 : 64;
     float wi = 0.f;
+    f32x4 xi = {0.f, 0.f, 0.f, 0.f};
     if (lane < cnt) {
       const int64_t k = int64_t(i0 + lane) * rows + row;
       wi = a.l_part[k] * fexp2((a.m_part[k] - M) * kLog2e);
+      xi = *reinterpret_cast<const f32x4*>(a.x_part + 4 * k);
     }
     wsum += wi;
+    const f32x4 wq = wi * xi;
     for (int j0 = 0; j0 < cnt; j0 += SB) {
       load(i0, j0, cnt);
-      add(wi, j0, cnt);
+      add(wq, j0, cnt);
     }
   }
 #pragma unroll

@@ -147,7 +147,7 @@ def test_flat_validation(lib, kw, status):
 
 def test_mla_host_rules(lib):
     for B, H, s in [(32, 16, 16), (1, 128, 3)]:
-        raw = s * B * H * (512 + 2) * 4
+        raw = s * B * H * (512 * 2 + 6 * 4)
         assert lib.attn_mla_decode_workspace_bytes(B, H, s) == (raw + 255) // 256 * 256
     assert lib.attn_mla_decode_workspace_bytes(1, 16, 0) == 0
     # 32 x 4096 tokens, one 16-head group: c = 512 gives 256 workgroups (one per CU)
@@ -588,7 +588,7 @@ def test_mla_flat_host_rules(lib):
     assert lib.attn_mla_decode_flat_pieces(32, 64, 83638) == 256
     assert lib.attn_mla_decode_flat_pieces(2, 128, 1000) == 4
     s = lib.attn_decode_flat_max_splits(15143, 83638, 128)
-    raw = s * 32 * 128 * 514 * 4
+    raw = s * 32 * 128 * (512 * 2 + 6 * 4)
     assert lib.attn_mla_decode_flat_workspace_bytes(32, 128, 15143, 83638, 128) == (raw + 255) // 256 * 256
     P = ctypes.c_void_p(256)
     st = lib.attn_mla_decode_flat(P, P, P, P, None, 4, 48, 512, 64, 100, 400, 0.07, 0, 1, P,
