@@ -391,12 +391,15 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // feed the same weights to their own output half: no weight crosses
 // waves.
 //
-// Schedule (one barrier per tile): step j turns tile j's swapped partial
-// scores into weights, issues the load of tile j + 2, computes and
-// publishes tile j + 1's partial scores, runs tile j's value update, then
-// waits for its loads and meets the other waves.  LDS holds three stages
-// (tile j: values, tile j + 1: keys, tile j + 2: streaming in) and the
-// partial scores double-buffered by tile parity.
+// Schedule (two barriers per tile): step j turns tile j's swapped partial
+// scores into weights, issues the load of tile j + 3 and computes tile
+// j + 1's partial scores; a barrier then marks that every wave has read
+// its partner's partials of tile j, so the one exchange buffer takes tile
+// j + 1's; the step runs tile j's value update, waits for tile j + 2's
+// loads and meets the other waves.  LDS holds four stages (tile j: values,
+// tile j + 1: keys, tiles j + 2 and j + 3: streaming in, so a tile's loads
+// have two steps to arrive: with one, the wait for them took a third of
+// the step) and one tile's partial scores: 160 KB.
 //
 // Softmax reference: the row max of the chunk's first tile, kept for the
 // whole chunk, so the value accumulators are never rescaled.  A later
@@ -416,7 +419,7 @@ constexpr int kMwInstr = kMwBK * kMlaChunks / 64;  // 36 load instructions of 1 
 constexpr int kMwWaves = 4;
 constexpr int kMwPerWave = kMwInstr / kMwWaves;    // 9
 constexpr int kMwStageBytes = kMwInstr * 1024;     // 36,864
-constexpr int kMwStages = 3;
+constexpr int kMwStages = 4;
 constexpr int kMwOutRow = 528;  // LDS bytes per head row of the output staging
 static_assert(kMwInstr % kMwWaves == 0, "every wave issues the same loads");
 static_assert(kMwWaves * 32 * kMwOutRow <= kMwStages * kMwStageBytes, "output staging fits the stages");
@@ -434,14 +437,16 @@ __device__ __forceinline__ int mw_swz(int row) { return ((row & 3) << 1) | ((row
 // transposing value reads, and each value MFMA followed by two more.  Keeping
 // reads that far ahead of their MFMAs measured best against 2-8 key and
 // 4-16 value reads ahead, and against one interleaving of both phases.
-__device__ __forceinline__ void mw_schedule() {
-  constexpr int kKeyAhead = 4, kValAhead = 8;
+constexpr int kKeyAhead = 4, kValAhead = 8;
+__device__ __forceinline__ void mw_schedule_scores() {
   __builtin_amdgcn_sched_group_barrier(0x100, 4 + kKeyAhead, 0);  // LDS reads
 #pragma unroll
   for (int i = 0; i < 18; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
     if (i + kKeyAhead < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
+}
+__device__ __forceinline__ void mw_schedule_values() {
   __builtin_amdgcn_sched_group_barrier(0x100, kValAhead, 0);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -465,10 +470,10 @@ template <class T, bool FLAT>
 __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   typedef typename T::vec8 vec8;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kMwStages * kMwStageBytes / 2];
-  // partial scores, by tile parity: sx[j & 1][hb][dh][k][lane] = the lane's
-  // partial scores 4k .. 4k + 3 of head block hb, dim half dh (16-byte
-  // accesses consecutive across lanes)
-  __shared__ __attribute__((aligned(16))) f32x4 sx[2][2][2][4][64];
+  // partial scores of one tile: sx[hb][dh][k][lane] = the lane's partial
+  // scores 4k .. 4k + 3 of head block hb, dim half dh (16-byte accesses
+  // consecutive across lanes)
+  __shared__ __attribute__((aligned(16))) f32x4 sx[2][2][4][64];
   const int HG = a.H / 64;
   int hg, unit;
   if (!mla_unit(blockIdx.x, HG, FLAT ? a.pieces : a.units, hg, unit)) return;
@@ -511,23 +516,39 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
   typedef int i32x4 __attribute__((ext_vector_type(4)));
   const uint64_t cbase = uint64_t(size_t(static_cast<const uint16_t*>(a.kv) + (kb0 + lo) * kMlaD));
   const uint32_t lds0 = uint32_t(size_t((__attribute__((address_space(3))) uint16_t*)lds)) + w * 1024;
-  auto dma = [&](int tile) {
+  // A tile's loads are issued one at a time between the score MFMAs of the
+  // step (dma_part), so that the wave never stalls on a full load queue; no
+  // LDS access of the step touches the stage being filled (the barriers
+  // that end each step order the rest), so the asm carries no memory
+  // clobber and the compiler may keep LDS reads in flight across it.
+  struct DmaTile {
+    i32x4 rsv;
+    uint32_t st;
+  };
+  auto dma_tile = [&](int tile) {
     const int key0 = tile * kMwBK;
     int left = n - key0;
     left = left < 0 ? 0 : (left > kMwBK ? kMwBK : left);
     const uint64_t addr = cbase + uint64_t(uint32_t(key0)) * (2 * kMlaD);
-    const i32x4 rsv = {__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
-                       __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
-                       __builtin_amdgcn_readfirstlane(left * 2 * kMlaD), 0x00020000};
-    const uint32_t st = lds0 + uint32_t(tile % kMwStages) * kMwStageBytes;
+    DmaTile d;
+    d.rsv = i32x4{__builtin_amdgcn_readfirstlane(int(uint32_t(addr))),
+                  __builtin_amdgcn_readfirstlane(int(uint32_t(addr >> 32) & 0xffffu)),
+                  __builtin_amdgcn_readfirstlane(left * 2 * kMlaD), 0x00020000};
+    d.st = lds0 + uint32_t(tile % kMwStages) * kMwStageBytes;
+    return d;
+  };
+  auto dma_part = [&](const DmaTile& d, int k) {
+    __asm__ volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(d.st + k * 1024 * kMwWaves)), "v"(voff[k]), "s"(d.rsv)
+        : "m0");
+  };
+  auto dma = [&](int tile) {
+    const DmaTile d = dma_tile(tile);
 #pragma unroll
-    for (int k = 0; k < kMwPerWave; ++k)
-      __asm__ volatile(
-          "s_mov_b32 m0, %0\n\t"
-          "buffer_load_dwordx4 %1, %2, 0 offen lds"
-          :
-          : "s"(__builtin_amdgcn_readfirstlane(st + k * 1024 * kMwWaves)), "v"(voff[k]), "s"(rsv)
-          : "memory", "m0");
+    for (int k = 0; k < kMwPerWave; ++k) dma_part(d, k);
   };
 
   // K operand reads (byte offsets in a stage): lane l32 reads key row l32,
@@ -567,7 +588,8 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
 
   // this wave's partial scores of the tile in stage `so` (its half of the
   // dims)
-  auto scores = [&](int so, f32x16& sa) {
+  // (with a tile to load: its nine loads go out after the odd MFMAs)
+  auto scores = [&](int so, f32x16& sa, const DmaTile* d) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sa[r] = 0.f;
     lds_cchar* kp[4];
@@ -577,12 +599,13 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     for (int u = 0; u < 18; ++u) {
       const u32x4 ka = mw_read128(kp[u & 3] + 128 * (u >> 2));
       sa = T::mfma32(as<vec8>(ka), as<vec8>(qa[u]), sa);
+      if (d && (u & 1)) dma_part(*d, u >> 1);
     }
   };
-  auto publish = [&](int j, const f32x16& sa) {
+  auto publish = [&](const f32x16& sa) {
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      sx[j & 1][hb][dh][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
+      sx[hb][dh][k][lane] = f32x4{sa[4 * k], sa[4 * k + 1], sa[4 * k + 2], sa[4 * k + 3]};
   };
 
   // One step of the pass (see the schedule above) for tile j; `last` marks
@@ -598,12 +621,12 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     // the partner's partial scores of tile j
     f32x4 o4[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o4[k] = sx[j & 1][hb][dh ^ 1][k][lane];
-    dma(j + 2);
+    for (int k = 0; k < 4; ++k) o4[k] = sx[hb][dh ^ 1][k][lane];
+    const DmaTile dn = dma_tile(j + 3);
     // tile j + 1's partial scores (past the last tile: a stage of zeros or
-    // stale rows, never used)
+    // stale rows, never used), with tile j + 3's loads
     f32x16 nxt;
-    scores(sk, nxt);
+    scores(sk, nxt, &dn);
     // tile j: the pair's partial scores added half 0 + half 1; keys of
     // sc[r]: j * 32 + 8 (r / 4) + 4 h + r % 4
     f32x16 sc;
@@ -641,7 +664,11 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
       la += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       pa[t] = T::cvt8(p);
     }
-    publish(j + 1, nxt);
+    mw_schedule_scores();
+    // every wave has read its partner's partials of tile j: the single
+    // exchange buffer can take tile j + 1's
+    __syncthreads();
+    publish(nxt);
     // tile j's value update
     lds_cchar* vp[2] = {(lds_cchar*)(size_t)opaque(lds_base + sv + vofs[0]),
                         (lds_cchar*)(size_t)opaque(lds_base + sv + vofs[1])};
@@ -658,8 +685,11 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     own = nxt;
     sv = sk;
     sk = sk == (kMwStages - 1) * kMwStageBytes ? 0 : sk + kMwStageBytes;
-    mw_schedule();
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 2 has arrived
+    mw_schedule_values();
+    // vmcnt(9): tile j + 2 has arrived, tile j + 3's nine loads may still be
+    // in flight
+    static_assert(kMwPerWave == 9, "vmcnt immediate below");
+    __builtin_amdgcn_s_waitcnt(0x0F79);
     __syncthreads();  // tile j + 1's partials and tile j + 2 published, stage j free
   };
   // One pass over the chunk (exact = 1: reference fixed from the start).
@@ -674,6 +704,7 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
     dma(0);
     dma(1);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tiles 0 and 1 (and the queries) are in
+    dma(2);
     if (!exact) {
       // a negative scale flips the sign of every query element instead (the
       // sign bit of both 16-bit formats is bit 15), so that c >= 0 below;
@@ -686,14 +717,27 @@ __global__ __launch_bounds__(64 * kMwWaves, 1) void mla_wide_kernel(MlaArgs a) {
       }
     }
     __syncthreads();
-    scores(0, own);
-    publish(0, own);
+    scores(0, own, nullptr);
+    publish(own);
     __syncthreads();
     for (int j = 0; j < ntiles - 1; ++j) step(j, exact, std::false_type{});
     step(ntiles - 1, exact, std::true_type{});
+    // the last steps' loads (past the chunk: zeros) land before the stages
+    // are reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  };
+  // any wave's flag, through the (now free) exchange buffer
+  auto any_flag = [&](int f) {
+    int* fl = reinterpret_cast<int*>(&sx[0][0][0][0]);
+    const uint64_t bal = __ballot(f != 0);
+    if (lane == 0) fl[w] = bal != 0;
+    __syncthreads();
+    const int r = fl[0] | fl[1] | fl[2] | fl[3];
+    __syncthreads();  // every wave has read the flags before the buffer is reused
+    return r;
   };
   run(false);
-  if (__syncthreads_or(flag)) {  // a score far above the first tile's max
+  if (any_flag(flag)) {  // a score far above the first tile's max
     mra = mruna;
     run(true);
   }
