@@ -34,6 +34,8 @@
 
 namespace rattn {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kMlaDc = 512, kMlaDr = 64, kMlaD = kMlaDc + kMlaDr;  // cache row: 576 elements
 constexpr int kMlaBK = 32;                      // keys per tile
 constexpr int kMlaChunks = kMlaD / 8;           // 16-byte chunks per cache row (72)
