@@ -1006,7 +1006,8 @@ static hipError_t launch_mla_t(const MlaArgs& a, hipStream_t st) {
   const int64_t rows = int64_t(a.B) * a.H;
   const dim3 grid(unsigned((rows + 3) / 4));
   if (a.s <= 8) hipLaunchKernelGGL((mla_merge_kernel<T, 8>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((mla_merge_kernel<T, 16>), grid, dim3(256), 0, st, a);
+  else if (a.s <= 16) hipLaunchKernelGGL((mla_merge_kernel<T, 16>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((mla_merge_kernel<T, 20>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
