@@ -160,6 +160,31 @@ def test_mla_equal_scores_give_mean_of_latents(H):
         assert (lse[b].double().cpu() - ln_n).abs().max().item() <= 1e-4
 
 
+@pytest.mark.parametrize("H", [16, 128])
+@pytest.mark.parametrize("k", [20, -30])
+def test_mla_split_partials_value_range(H, k):
+    """Latent parts scaled by 2^k and query latents by 2^-k (bf16, exact):
+    every score is unchanged and O scales by exactly 2^k.  The split
+    partials are stored in fp16 with a power-of-two scale per 128 dims, so
+    values of 4 x 2^20 (above fp16's 65504) and of 2^-30 (below its smallest
+    subnormal) must come through the merge intact: O / 2^k matches the
+    unscaled oracle, and the LSE is the oracle's."""
+    lengths = [700, 33, 0, 1500, 257]
+    q, kv, kvp = mla_inputs(lengths, H, torch.bfloat16, seed=71)
+    scale = 192 ** -0.5
+    o_ref, lse_ref = oracle_mla(q, kv, kvp, scale)
+    qs, kvs = q.clone(), kv.clone()
+    qs[..., :DC] = (q[..., :DC].float() * 2.0 ** -k).to(torch.bfloat16)
+    kvs[:, :DC] = (kv[:, :DC].float() * 2.0 ** k).to(torch.bfloat16)
+    for s in (3, 8):
+        o, lse = ra().attn_mla_decode(qs.to(DEV), kvs.to(DEV), kvp.to(DEV), max(lengths), scale,
+                                      num_splits=s)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(o).all())
+        check(f"mla partial range H={H} 2^{k} s={s}", o.float() * 2.0 ** -k, o_ref, lse, lse_ref,
+              torch.bfloat16)
+
+
 def test_mla_bit_identical_reruns():
     w = synth.workload("mla_decode_bf16")
     inp = w.make(DEV)
