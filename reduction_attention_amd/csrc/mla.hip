@@ -400,8 +400,8 @@ __global__ __launch_bounds__(kMlaThreads, 8 / kMlaWaves) void mla_decode_kernel(
 // j + 1's; the step runs tile j's value update, waits for tile j + 2's
 // loads and meets the other waves.  LDS holds four stages (tile j: values,
 // tile j + 1: keys, tiles j + 2 and j + 3: streaming in, so a tile's loads
-// have two steps to arrive: with one, the wait for them took a third of
-// the step) and one tile's partial scores: 160 KB.
+// have two steps to arrive; timing copies without the loads ran a third
+// faster) and one tile's partial scores: 160 KB.
 //
 // Softmax reference: the row max of the chunk's first tile, kept for the
 // whole chunk, so the value accumulators are never rescaled.  A later
