@@ -578,7 +578,9 @@ template <int D, class OutT>
 __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
   constexpr int V = D / 64;
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  // (the wave index read as uniform: the row's indptr entries and split
+  // count then live in scalar registers and the loops stay uniform)
+  const int64_t row = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (row >= a.rows) return;
   const int64_t rows = a.rows;
   const int s = a.s;
@@ -675,7 +677,10 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DL = (DW + 63) / 64;
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.B) * a.Hq;
-  const int64_t gw = int64_t(blockIdx.x) * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  // (the wave index read as uniform: the row's indptr entries and split
+  // count then live in scalar registers and the loops stay uniform)
+  const int64_t gw =
+      int64_t(blockIdx.x) * (blockDim.x >> 6) + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int64_t row = gw / NSL;
   const int d0 = int(gw % NSL) * DW;  // this wave's first dim
   if (row >= rows) return;

@@ -892,7 +892,9 @@ template <class T, int SB>
 __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t rows = int64_t(a.B) * a.H;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  // (the wave index read as uniform: the row's indptr entries and split
+  // count then live in scalar registers and the loops stay uniform)
+  const int64_t row = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   if (row >= rows) return;
   const int b = int(row / a.H);
   const int64_t kb0 = a.kv_indptr[b], kb1 = a.kv_indptr[b + 1];
@@ -924,11 +926,14 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int jj = j0 + j < 64 ? j0 + j : 63;
-      float w4[4];
+      // split jj's weight times the scale of this lane's quarter, picked
+      // with selects (no branches)
+      float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[0]), jj));
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        w4[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[k]), jj));
-      float wj = qt == 0 ? w4[0] : (qt == 1 ? w4[1] : (qt == 2 ? w4[2] : w4[3]));
+      for (int k = 1; k < 4; ++k) {
+        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[k]), jj));
+        wj = qt == k ? wk : wj;
+      }
       wj = j0 + j < cnt ? wj : 0.f;
       const f32x8 x = __builtin_convertvector(as<f16x8>(xr[j]), f32x8);
       acc0 += wj * f32x4{x[0], x[1], x[2], x[3]};
