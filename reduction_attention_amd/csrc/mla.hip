@@ -922,22 +922,40 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
       xr[j] = *reinterpret_cast<const u32x4*>(op + int64_t(jj) * rows * kMlaDc);
     }
   };
-  auto add = [&](f32x4 wq, int j0, int cnt) {
+  // Lane j of a batch of 64 splits publishes split j's weight times its
+  // four quarter scales in an LDS table (zero past the batch's count, and
+  // in the padding past 64 that a last read of SB splits may reach); each
+  // lane then reads its quarter's weights four splits at a time.
+  constexpr int WT = 64 + 32;  // table row: 64 splits, then zeros
+  static_assert(SB <= 32, "a batch's reads stay inside a table row");
+  __shared__ __attribute__((aligned(16))) float wtab[4][4][WT];  // [wave][quarter][split]
+  float* wt = &wtab[__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6))][0][0];
+  if (lane < 32) {
 #pragma unroll
-    for (int j = 0; j < SB; ++j) {
-      const int jj = j0 + j < 64 ? j0 + j : 63;
-      // split jj's weight times the scale of this lane's quarter, picked
-      // with selects (no branches)
-      float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[0]), jj));
+    for (int k = 0; k < 4; ++k) wt[WT * k + 64 + lane] = 0.f;
+  }
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto publish = [&](f32x4 wq) {
+    wave_sync();  // the previous batch's reads are done
 #pragma unroll
-      for (int k = 1; k < 4; ++k) {
-        const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wq[k]), jj));
-        wj = qt == k ? wk : wj;
+    for (int k = 0; k < 4; ++k) wt[WT * k + lane] = wq[k];
+    wave_sync();
+  };
+  auto add = [&](int j0) {
+    static_assert(SB % 4 == 0, "weights are read four at a time");
+#pragma unroll
+    for (int j4 = 0; j4 < SB; j4 += 4) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(wt + WT * qt + j0 + j4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x8 x = __builtin_convertvector(as<f16x8>(xr[j4 + e]), f32x8);
+        acc0 += w4[e] * f32x4{x[0], x[1], x[2], x[3]};
+        acc1 += w4[e] * f32x4{x[4], x[5], x[6], x[7]};
       }
-      wj = j0 + j < cnt ? wj : 0.f;
-      const f32x8 x = __builtin_convertvector(as<f16x8>(xr[j]), f32x8);
-      acc0 += wj * f32x4{x[0], x[1], x[2], x[3]};
-      acc1 += wj * f32x4{x[4], x[5], x[6], x[7]};
     }
   };
   // the first 64 splits' (m, l, scales) and the first SB partial rows go
@@ -960,11 +978,11 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
   {
     const float wi = lane < cnt0 ? l0 * fexp2((m0 - M) * kLog2e) : 0.f;
     wsum += wi;
-    const f32x4 wq = wi * x0;
-    add(wq, 0, cnt0);
+    publish(wi * x0);
+    add(0);
     for (int j0 = SB; j0 < cnt0; j0 += SB) {
       load(0, j0, cnt0);
-      add(wq, j0, cnt0);
+      add(j0);
     }
   }
   for (int i0 = 64; i0 < n; i0 += 64) {  // more than 64 splits
@@ -977,10 +995,10 @@ __global__ __launch_bounds__(256) void mla_merge_kernel(MlaArgs a) {
       xi = *reinterpret_cast<const f32x4*>(a.x_part + 4 * k);
     }
     wsum += wi;
-    const f32x4 wq = wi * xi;
+    publish(wi * xi);
     for (int j0 = 0; j0 < cnt; j0 += SB) {
       load(i0, j0, cnt);
-      add(wq, j0, cnt);
+      add(j0);
     }
   }
 #pragma unroll
