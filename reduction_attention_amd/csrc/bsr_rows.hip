@@ -157,10 +157,13 @@ __global__ __launch_bounds__(256) void bsr_rows_kernel(BsrArgs a) {
     for (int u = 0; u < NU; ++u) s = T::mfma16(as<vec8>(R.k[u]), as<vec8>(qv[u]), s);
     // s[r]: query i, key 4 gq + r of the block; its bit is r8 * 8 + c8 with
     // r8 = i % 8 and c8 = 4 (gq % 2) + r in the word loaded above
-    const uint32_t nib = uint32_t(R.word >> ((i & 7) * 8 + 4 * (gq & 1))) & 0xFu;
+    // (bit r of the nibble, sign-extended, selects the score or -inf)
+    const int nib = int(uint32_t(R.word >> ((i & 7) * 8 + 4 * (gq & 1))));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (!((nib >> r) & 1u)) s[r] = -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t keep = uint32_t(__builtin_amdgcn_sbfe(nib, r, 1));
+      s[r] = __uint_as_float((__float_as_uint(s[r]) & keep) | (0xFF800000u & ~keep));
+    }
     const float mx = max_rows4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]))) * c;
     // lazy rescale (see kRescaleSlack); uniform over the lanes of a query
     const bool need = mx > m + kRescaleSlack;

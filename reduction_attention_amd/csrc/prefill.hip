@@ -271,20 +271,27 @@ void prefill_kernel(PrefillArgs a) {
 
 // The part-OT predicate: x[kb][r] -> -inf where query (32*w + lane%32) of the
 // OT may not attend key 32*kb + 8*(r/4) + 4*h + r%4 of the OT.
+// Each element takes two vector ops: the sign-extended bit (0 or all ones)
+// and a bitwise select between the score and -inf.
 __device__ __forceinline__ void apply_part_mask(f32x16 (&x)[2], const uint8_t* bm, int w,
                                                 int lane) {
   const int rq = 32 * w + (lane & 31);
   const int h = lane >> 5;
   const uint64_t bytes = *reinterpret_cast<const uint64_t*>(bm + rq * 8);  // [ic] for row rq
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < 2; ++kb) {
+    // bytes 4 kb .. 4 kb + 3, shifted so that nibble h of byte 4 kb + r4
+    // starts at bit 8 r4
+    const int wv = int(uint32_t(bytes >> (32 * kb)) >> (4 * h));
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const uint32_t nib = uint32_t(bytes >> (8 * (4 * kb + r4) + 4 * h)) & 0xFu;
+    for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (!((nib >> e) & 1u)) x[kb][4 * r4 + e] = -INFINITY;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t keep = uint32_t(__builtin_amdgcn_sbfe(wv, 8 * r4 + e, 1));
+        const uint32_t xb = __float_as_uint(x[kb][4 * r4 + e]);
+        x[kb][4 * r4 + e] = __uint_as_float((xb & keep) | (0xFF800000u & ~keep));
+      }
+  }
 }
 
 template <class T, int D>
