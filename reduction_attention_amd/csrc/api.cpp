@@ -812,13 +812,13 @@ attn_status_t attn_prefill_bsr_rows(const void* q, const void* k, const void* v,
 // floor plus a cost per unit of work summed over heads and batch entries
 // (per stored outer tile for the block-wise kernel, per (16-row slab,
 // 16-key block) for the row-wise one).  Fitted (least squares on relative
-// error) to a sweep of both kernels over nine mask families at L 1024 and
-// 4096, D 64 and 128 (fp16, 16 heads): the model picks the faster kernel in
-// 33 of the 36 cases, the other three being near ties (0.7%, 3.6%) and one
-// 12% miss on a narrow window at D 128.
+// error) to kernel-trace durations of both kernels over nine mask families
+// at L 1024 and 4096, D 64 and 128 (fp16, 16 heads): the model picks the
+// faster kernel in 34 of the 36 cases; the two others are ties within
+// 0.7 us.
 struct BsrCost { double b0, b1, r0, r1; };
 static BsrCost bsr_cost(int D) {
-  return D == 64 ? BsrCost{9.5, 1.59e-3, 9.4, 0.333e-3} : BsrCost{12.8, 4.43e-3, 8.7, 0.673e-3};
+  return D == 64 ? BsrCost{7.2, 1.68e-3, 7.1, 0.336e-3} : BsrCost{9.9, 4.36e-3, 6.8, 0.671e-3};
 }
 
 attn_status_t attn_bsr_plan_host(const int32_t* full_indptr, const int32_t* part_indptr,
