@@ -442,7 +442,186 @@ __global__ void flat_ranges_kernel(DecodeArgs a, int32_t* ranges) {
 }
 
 // -------------------------------------------------------------------------
-// fp32 partial kernel (VALU).  One wave per (split, KV head, request); lane
+// fp32 partial kernel at D = 64 (VALU), for fp32 inputs (small sizes here:
+// launch and latency bound).  Workgroup = four waves per (split, KV head, request);
+// wave w reduces the key tiles w, w + 4, ... of the split with its own
+// online softmax, so that the tiles of a short split run side by side
+// rather than one after another.  In a tile of KT keys lane j scores key j
+// against the G query heads (the queries staged in LDS), the wave keeps
+// per-head running max and sum, and accumulates the value update from the
+// tile's V rows, which are loaded (coalesced, 16 bytes per
+// lane) at the start of the tile into the wave's own LDS slot, so their
+// latency overlaps the key loads and the scores (lane d accumulates output
+// dim d).  The four waves' (O, m, l)
+// are combined through LDS with log-sum-exp weights.  With one split and
+// no partials requested the result is final (O / l and the LSE);
+// otherwise it is split i's partial.  GP is G rounded up to a power of two
+// (at most 16): the query rows past G are zeros in LDS and every per-head
+// loop runs to GP without a branch; only the first G heads are written.
+// -------------------------------------------------------------------------
+template <int D, int GP>
+__global__ __launch_bounds__(256) void decode_partial_f32(DecodeArgs args) {
+  constexpr int W = 4;                 // waves per workgroup
+  static_assert(D == 64, "D = 128 takes decode_partial_f32_wave");
+  constexpr int KT = 64;               // keys per tile (LDS slot of 17 KB per wave)
+  constexpr int DL = (D + 63) / 64;    // output dims per lane
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = args.G, Hq = args.Hq;
+  const int64_t rows = int64_t(args.B) * Hq;
+  const SplitRange sr = split_range(args.kv_indptr, b, i, args.chunk);
+  const int64_t row0 = int64_t(b) * Hq + int64_t(g) * G;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool final_out = args.s == 1 && !args.partials_only;
+  if (sr.lo >= sr.hi) {  // unused split, or an empty request (uniform over the workgroup)
+    if (tid < G) {
+      if (final_out) {  // empty request: O = 0, LSE = -inf
+        float* o = static_cast<float*>(args.o) + (row0 + tid) * D;
+        for (int d = 0; d < D; ++d) o[d] = 0.f;
+        if (args.lse) args.lse[row0 + tid] = -INFINITY;
+      } else {
+        args.m_part[int64_t(i) * rows + row0 + tid] = -INFINITY;
+        args.l_part[int64_t(i) * rows + row0 + tid] = 0.f;
+      }
+    }
+    return;
+  }
+  __shared__ float qs[GP][D];
+  __shared__ float ps[W][KT][GP + 1];
+  __shared__ float vs[W][KT][D + 4];  // each wave's tile of V rows
+  __shared__ float red_m[W][GP], red_l[W][GP];
+  const float* q = static_cast<const float*>(args.q);
+  for (int e = tid; e < GP * D; e += 64 * W)
+    qs[e / D][e % D] = e < G * D ? q[(row0 + e / D) * D + e % D] : 0.f;
+  __syncthreads();
+  const int64_t row_stride = int64_t(args.Hkv) * D;
+  const float* kb = static_cast<const float*>(args.k) + (sr.base + sr.lo) * row_stride + int64_t(g) * D;
+  const float* vb = static_cast<const float*>(args.v) + (sr.base + sr.lo) * row_stride + int64_t(g) * D;
+  const int n = sr.hi - sr.lo;
+  float m[GP], l[GP], acc[GP][DL];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int x = 0; x < DL; ++x) acc[h][x] = 0.f;
+  }
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  constexpr int VPL = KT * D / 4 / 64;  // float4 of the V tile per lane
+#pragma nounroll
+  for (int t0 = KT * w; t0 < n; t0 += KT * W) {
+    const int kmax = n - t0 < KT ? n - t0 : KT;
+    float4 vreg[VPL];
+#pragma unroll
+    for (int x = 0; x < VPL; ++x) {
+      const int e = x * 64 + lane, r = e / (D / 4), c = e % (D / 4);
+      const int rr = r < kmax ? r : kmax - 1;  // rows past the range repeat the last one
+      vreg[x] = *reinterpret_cast<const float4*>(vb + int64_t(t0 + rr) * row_stride + 4 * c);
+    }
+    const bool valid = lane < kmax;
+    const float* kr = kb + int64_t(t0 + (valid ? lane : kmax - 1)) * row_stride;
+    // The query rows are read from LDS afresh in every tile (their LDS
+    // address passes through an empty asm): loop-invariant, they would
+    // otherwise be hoisted out of the tile loop into GP * D registers.
+    uint32_t qaddr = uint32_t(size_t((__attribute__((address_space(3))) float*)&qs[0][0]));
+    __asm__ volatile("" : "+v"(qaddr));
+    const __attribute__((address_space(3))) float* qp =
+        (const __attribute__((address_space(3))) float*)(size_t)qaddr;
+    float sc[GP];
+#pragma unroll
+    for (int h = 0; h < GP; ++h) sc[h] = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+      const float4 kv = *reinterpret_cast<const float4*>(kr + d);
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+        sc[h] += qp[h * D + d] * kv.x + qp[h * D + d + 1] * kv.y + qp[h * D + d + 2] * kv.z +
+                 qp[h * D + d + 3] * kv.w;
+    }
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float x = valid ? sc[h] * args.scale_log2 : -INFINITY;
+      float mx = x;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, shfl_xor(mx, off));
+      const float m_new = fmaxf(m[h], mx);  // finite: key t0 is valid
+      const float alpha = fexp2(m[h] - m_new);
+      const float p = fexp2(x - m_new);
+      m[h] = m_new;
+      l[h] = l[h] * alpha + p;
+#pragma unroll
+      for (int xx = 0; xx < DL; ++xx) acc[h][xx] *= alpha;
+      if (lane < KT) ps[w][lane][h] = p;
+    }
+#pragma unroll
+    for (int x = 0; x < VPL; ++x) {
+      const int e = x * 64 + lane, r = e / (D / 4), c = e % (D / 4);
+      *reinterpret_cast<float4*>(&vs[w][r][4 * c]) = vreg[x];
+    }
+    wave_sync();  // this wave's weights and V rows are in its LDS slot
+#pragma unroll 8
+    for (int j = 0; j < kmax; ++j) {
+#pragma unroll
+      for (int xx = 0; xx < DL; ++xx) {
+        const float vv = vs[w][j][lane + 64 * xx];
+#pragma unroll
+        for (int h = 0; h < GP; ++h) acc[h][xx] += ps[w][j][h] * vv;
+      }
+    }
+    wave_sync();  // the slot's reads are done before the next tile's writes
+  }
+  // combine the waves: m (log2 units, the same in every lane) and the
+  // lane-summed l per head, and the unnormalised O rows in the V slots
+  // (free once every wave has passed the barrier below)
+  __syncthreads();
+  float* red_o = &vs[0][0][0];  // [W][GP][D]
+  static_assert(W * GP * D <= W * KT * (D + 4), "the waves' rows fit the V slots");
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    float ls = l[h];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ls += shfl_xor(ls, off);
+    if (lane == 0) {
+      red_m[w][h] = m[h];  // -inf for a wave without a tile
+      red_l[w][h] = ls;
+    }
+#pragma unroll
+    for (int xx = 0; xx < DL; ++xx) red_o[(w * GP + h) * D + lane + 64 * xx] = acc[h][xx];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * D; e += 64 * W) {
+    const int h = e / D, d = e % D;
+    float M = red_m[0][h];
+#pragma unroll
+    for (int k2 = 1; k2 < W; ++k2) M = fmaxf(M, red_m[k2][h]);  // finite: wave 0 has a tile
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < W; ++k2) {
+      const float f = fexp2(red_m[k2][h] - M);
+      L += red_l[k2][h] * f;
+      O += red_o[(k2 * GP + h) * D + d] * f;
+    }
+    const int64_t row = row0 + h;
+    if (final_out) {
+      static_cast<float*>(args.o)[row * D + d] = O / L;
+      if (d == 0 && args.lse) args.lse[row] = (M + flog2(L)) * kLn2;
+    } else {
+      args.o_part[(int64_t(i) * rows + row) * D + d] = O / L;
+      if (d == 0) {
+        args.m_part[int64_t(i) * rows + row] = M * kLn2;
+        args.l_part[int64_t(i) * rows + row] = L;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
+// fp32 partial kernel at D = 128 (VALU).  One wave per (split, KV head,
+// request), always writing split partials; lane
 // j scores key j of each 64-key tile against the G query heads, the wave
 // keeps per-head running max and sum, and lane d accumulates output dims d
 // and d + 64.  Each tile's V rows are loaded (coalesced, 16 bytes per lane)
@@ -451,7 +630,7 @@ __global__ void flat_ranges_kernel(DecodeArgs a, int32_t* ranges) {
 // fp32 inputs, whose sizes here are small (launch and latency bound).
 // -------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64) void decode_partial_f32(DecodeArgs args) {
+__global__ __launch_bounds__(64) void decode_partial_f32_wave(DecodeArgs args) {
   constexpr int DL = (D + 63) / 64;  // output dims per lane
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = args.G, Hq = args.Hq;
@@ -830,13 +1009,31 @@ static void launch_partial_mfma(const DecodeArgs& a, hipStream_t st) {
   }
 }
 
+// fp32 partial kernel at D = 64 at the padded head count of G (1, 2, 4, 8
+// or 16)
+template <int D>
+static void launch_partial_f32_d(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.s, a.Hkv, a.B), block(256);
+  if (a.G <= 1) hipLaunchKernelGGL((decode_partial_f32<D, 1>), grid, block, 0, st, a);
+  else if (a.G <= 2) hipLaunchKernelGGL((decode_partial_f32<D, 2>), grid, block, 0, st, a);
+  else if (a.G <= 4) hipLaunchKernelGGL((decode_partial_f32<D, 4>), grid, block, 0, st, a);
+  else if (a.G <= 8) hipLaunchKernelGGL((decode_partial_f32<D, 8>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((decode_partial_f32<D, 16>), grid, block, 0, st, a);
+}
+
+// D = 128: the one-wave kernel, which always writes split partials
+static void launch_partial_f32(const DecodeArgs& a, hipStream_t st) {
+  if (a.D == 64) launch_partial_f32_d<64>(a, st);
+  else hipLaunchKernelGGL(decode_partial_f32_wave<128>, dim3(a.s, a.Hkv, a.B), dim3(64), 0, st, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
-  if (a.dtype == 0) {  // fp32: partial kernel, then the standalone merge
-    if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
+  if (a.dtype == 0) {  // fp32: partial kernel, then (s > 1) the standalone merge
+    launch_partial_f32(a, st);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // one split at D = 64: the kernel's result is final
+    if (e != hipSuccess || (a.s == 1 && a.D == 64)) return e;
     MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, a.B * a.Hq, a.D, a.o, 0, a.lse};
     return launch_merge(m, st);
   } else {  // 16-bit: MFMA partial kernel, then the merge of multi-split requests
@@ -897,8 +1094,7 @@ hipError_t launch_flat_ranges(const DecodeArgs& a, int32_t* ranges, hipStream_t 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st) {
   const dim3 grid(a.s, a.Hkv, a.B);
   if (a.dtype == 0) {
-    if (a.D == 64) hipLaunchKernelGGL(decode_partial_f32<64>, grid, dim3(64), 0, st, a);
-    else hipLaunchKernelGGL(decode_partial_f32<128>, grid, dim3(64), 0, st, a);
+    launch_partial_f32(a, st);
   } else {
     launch_partial_mfma(a, st);
   }
