@@ -90,7 +90,7 @@ def test_ragged_serving_decode_full_parity():
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
 def test_small_ragged_shapes(dtype, D, G):
     lengths = [1, 31, 32, 33, 0, 300, 64, 517]
     Hkv = 2
@@ -199,12 +199,14 @@ def test_workspace_reused_across_calls():
 
 
 @pytest.mark.parametrize("s", [1, 3, 8])
-def test_partials_match_oracle_split(s):
-    """attn_decode_partials against the oracle's per-split partials, then merged."""
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_partials_match_oracle_split(s, dtype, D):
+    """attn_decode_partials against the oracle's per-split partials, then merged
+    (bf16 on the MFMA kernel, fp32 on the four-wave VALU kernel)."""
     lengths = [700, 1, 64, 0, 513]
-    q, k, v, kv = synth.decode_inputs(len(lengths), 8, 2, 128, lengths, torch.bfloat16, seed=s)
+    q, k, v, kv = synth.decode_inputs(len(lengths), 8, 2, D, lengths, dtype, seed=s)
     o_ref, lse_ref, op_ref, mp_ref, lp_ref = oracle.split_decode(q, k, v, kv, max(lengths),
-                                                                 1 / 128 ** 0.5, s)
+                                                                 1 / D ** 0.5, s)
     op, mp, lp = ra().attn_decode_partials(q.to(DEV), k.to(DEV), v.to(DEV), kv.to(DEV),
                                            max(lengths), s)
     torch.cuda.synchronize()
@@ -214,12 +216,13 @@ def test_partials_match_oracle_split(s):
     do = (op.cpu().double() - op_ref)[used].abs().max().item()
     dm = (mp.cpu().double() - mp_ref)[used].abs().max().item()
     dl = ((lp.cpu().double() - lp_ref) / lp_ref)[used].abs().max().item()
-    print(f"partials s={s}: max|do|={do:.2e} max|dm|={dm:.2e} max rel dl={dl:.2e}", flush=True)
-    assert do <= TOL_O[torch.bfloat16] and dm <= 1e-3 and dl <= 1e-3
+    print(f"partials {dtype} s={s}: max|do|={do:.2e} max|dm|={dm:.2e} max rel dl={dl:.2e}",
+          flush=True)
+    assert do <= TOL_O[dtype] and dm <= 1e-3 and dl <= 1e-3
     o, lse = ra().attn_merge_lse(op, mp, lp, o_dtype=torch.float32)
     torch.cuda.synchronize()
-    check(f"partials+merge s={s}", o.view(len(lengths), 8, 128), o_ref, lse.view(len(lengths), 8),
-          lse_ref, torch.bfloat16)
+    check(f"partials+merge {dtype} s={s}", o.view(len(lengths), 8, D), o_ref,
+          lse.view(len(lengths), 8), lse_ref, dtype)
 
 
 # ---- flat split plan (packed key array cut into equal pieces) -------------
