@@ -370,8 +370,9 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v,
                            void* hip_stream);
 
 /* Workspace bytes attn_prefill_splitkv needs for `num_splits` splits:
- * num_splits * total_q * Hq * (D + 2) * 4 (fp32 partial outputs, maxima,
- * sums), rounded up to 256 bytes; 0 for invalid arguments. */
+ * num_splits * total_q * Hq * (2 D + 12) (fp16 partial outputs, then fp32
+ * maxima, sums and row scales), rounded up to 256 bytes; 0 for invalid
+ * arguments. */
 size_t attn_prefill_workspace_bytes(long long total_q, int Hq, int D, int num_splits);
 
 /* The split count attn_prefill_splitkv picks when num_splits = 0: 1 when the
@@ -395,9 +396,11 @@ int attn_prefill_choose_splits(int B, int Hq, int Hkv, int D, int max_q_len, int
  *   s = 1 is attn_prefill itself (no workspace needed).
  * workspace  device memory of at least attn_prefill_workspace_bytes(total_q,
  *   Hq, D, s) bytes, 16-byte aligned; contents on entry do not matter.
- *   Layout: o_part [s, total_q*Hq, D], then m_part and l_part
- *   [s, total_q*Hq], fp32 (row = query row * Hq + head); a split without
- *   valid keys for a row leaves (m, l) = (-inf, 0) there.  Calls sharing one
+ *   Layout: o_part [s, total_q*Hq, D] fp16, then m_part, l_part and x_part
+ *   [s, total_q*Hq] fp32 (row = query row * Hq + head): split i's
+ *   normalised output row is o_part[i, row, :] * x_part[i, row], a power
+ *   of two that brings the row's largest magnitude into [1/2, 1); a split
+ *   without valid keys for a row leaves (m, l) = (-inf, 0) there.  Calls sharing one
  *   workspace must not overlap in time.
  * Two kernels are enqueued on hip_stream: the split partials, then the merge.
  * Supported: as attn_prefill, with ceil(max_q_len / 128) * s <= 65535 and

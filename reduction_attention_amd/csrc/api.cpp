@@ -577,7 +577,8 @@ attn_status_t attn_prefill(const void* q, const void* k, const void* v, const in
 
 size_t attn_prefill_workspace_bytes(long long total_q, int Hq, int D, int num_splits) {
   if (total_q < 0 || Hq < 1 || D < 1 || num_splits < 1) return 0;
-  const size_t raw = size_t(num_splits) * size_t(total_q) * size_t(Hq) * size_t(D + 2) * 4;
+  // fp16 partial rows, then fp32 m, l and row scales
+  const size_t raw = size_t(num_splits) * size_t(total_q) * size_t(Hq) * (size_t(D) * 2 + 12);
   return (raw + 255) / 256 * 256;
 }
 
@@ -638,14 +639,17 @@ attn_status_t attn_prefill_splitkv(const void* q, const void* k, const void* v,
   if (s > 1 && !aligned16(workspace))
     return fail(ATTN_EINVAL, "prefill_splitkv: workspace must be 16-byte aligned");
   const int chunk = max_kv_len > 0 ? (max_kv_len + s - 1) / s : 0;
-  float* ws = static_cast<float*>(workspace);
+  // workspace: fp16 o_part [s, rows, D], then fp32 m_part, l_part, x_part [s, rows]
+  uint16_t* wo = static_cast<uint16_t*>(workspace);
+  float* wf = reinterpret_cast<float*>(wo + size_t(s) * size_t(rows) * D);
   rattn::PrefillArgs a{q, k, v, qo_indptr, kv_indptr, o, lse, B, Hq, Hkv, D, Hq / Hkv,
                        max_q_len, max_kv_len, scale * kLog2e, causal, dtype,
                        s, chunk,
-                       s > 1 ? ws : nullptr,
-                       s > 1 ? ws + size_t(s) * size_t(rows) * D : nullptr,
-                       s > 1 ? ws + size_t(s) * size_t(rows) * (D + 1) : nullptr,
-                       rows};
+                       s > 1 ? wo : nullptr,
+                       s > 1 ? wf : nullptr,
+                       s > 1 ? wf + size_t(s) * size_t(rows) : nullptr,
+                       rows,
+                       s > 1 ? wf + 2 * size_t(s) * size_t(rows) : nullptr};
   return hip_status(rattn::launch_prefill(a, static_cast<hipStream_t>(hip_stream)),
                     "prefill_splitkv launch");
 }

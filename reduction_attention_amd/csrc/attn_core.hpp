@@ -408,49 +408,65 @@ __device__ __forceinline__ void row_store_staged(const RowState<D>& st, uint16_t
 }
 
 // A split's partial result for the wave's 32 rows: O normalised by the
-// split's own sum (fp32), the reference max m in natural-log units and the
-// sum l relative to it; a row without valid keys gets O = 0, m = -inf,
-// l = 0.  Like row_store_staged, the rows go out through the wave's LDS
-// area `stage` (32 * 4D bytes, free by then): 16-byte piece c of row r sits
-// at slot c ^ (r % (D / 4)), so both the writes (32 rows, one piece) and the
-// reads (whole rows) spread over the banks.  obase points at dim 0 of the
-// wave's first row in the partial output, rows ostride elements apart; rows
-// nvalid .. 31 are not written.  m_out and l_out point at this lane's row
-// (lane % 32), or are nullptr when it does not exist.
+// split's own sum and divided by a power of two 2^e per row (e the binary
+// exponent of the row's largest magnitude, so every stored value lies in
+// [-1, 1], where fp16 keeps 11 significant bits: a stored element is off by
+// at most 2^-12 of the row's largest value, and neither the inputs' range
+// nor fp16's can overflow it), the scale 2^e, the reference max m in
+// natural-log units and the sum l relative to it; a row without valid keys
+// gets O = 0, scale 1, m = -inf, l = 0.  The rows go out through the
+// wave's LDS area `stage` (32 * (2D + 16) bytes, free by then) as 16-byte
+// row pieces, as in row_store_staged.  obase points at dim 0 of the wave's
+// first row in the partial output, rows ostride elements apart; rows
+// nvalid .. 31 are not written.  m_out, l_out and x_out point at this
+// lane's row (lane % 32), or are nullptr when it does not exist.
 template <int D>
-__device__ __forceinline__ void row_store_partial_staged(const RowState<D>& st, float* obase, int64_t ostride,
-                                                         int nvalid, float* m_out, float* l_out,
+__device__ __forceinline__ void row_store_partial_staged(const RowState<D>& st, uint16_t* obase,
+                                                         int64_t ostride, int nvalid, float* m_out,
+                                                         float* l_out, float* x_out,
                                                          __attribute__((address_space(3))) char* stage,
                                                          int lane) {
-  constexpr int NC = D / 4;             // 16-byte pieces per row
-  constexpr int RPI = 64 / NC;          // rows per store instruction
-  typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+  constexpr int RS = 2 * D + 16;        // LDS bytes per row
+  constexpr int LPR = 2 * D / 16;       // lanes per row on the way out
+  constexpr int RPI = 64 / LPR;         // rows per store instruction
   const float l = sum_halves(st.l);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  float amax = 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(st.o[db][r]));
+  int e = __builtin_amdgcn_frexp_expf(max_halves(amax) * inv);
+  e = e < -126 ? -126 : (e > 127 ? 127 : e);
   const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4 y;
+      f32x8 y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = st.o[db][4 * g4 + e] * inv;
-      const int c = 8 * db + 2 * g4 + h;  // dims 4c .. 4c + 3
-      *reinterpret_cast<lds_f32x4*>(stage + l32 * (4 * D) + 16 * (c ^ (l32 % NC))) = y;
+      for (int k = 0; k < 4; ++k) {
+        y[k] = __builtin_amdgcn_ldexpf(st.o[db][4 * g4 + k] * inv, -e);
+        y[4 + k] = 0.f;
+      }
+      const u32x4 bits = __builtin_bit_cast(u32x4, F16::cvt8(y));
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(stage + l32 * RS + 2 * (32 * db + 8 * g4 + 4 * h)) =
+          u32x2{bits[0], bits[1]};
     }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int rr = lane / NC, cc = lane % NC;
+  const int rr = lane / LPR, cc = lane % LPR;
 #pragma unroll
   for (int k = 0; k < 32 / RPI; ++k) {
     const int r = RPI * k + rr;
-    const f32x4 v = *reinterpret_cast<lds_f32x4*>(stage + r * (4 * D) + 16 * (cc ^ (r % NC)));
-    if (r < nvalid) *reinterpret_cast<f32x4*>(obase + r * ostride + 4 * cc) = v;
+    const u32x4 v = *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(stage + r * RS + 16 * cc);
+    if (r < nvalid) *reinterpret_cast<u32x4*>(obase + r * ostride + 8 * cc) = v;
   }
   if (m_out && h == 0) {
     *m_out = l > 0.f ? st.m * kLn2 : -INFINITY;
     *l_out = l;
+    *x_out = __builtin_amdgcn_ldexpf(1.f, e);
   }
 }
 

@@ -753,7 +753,7 @@ __global__ __launch_bounds__(64) void decode_partial_f32_wave(DecodeArgs args) {
 // uniform branch skips it), so whatever an unused slot holds is harmless.
 // -------------------------------------------------------------------------
 constexpr int kMergeBatch = 8;
-template <int D, class OutT>
+template <int D, class OutT, bool H>
 __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
   constexpr int V = D / 64;
   const int lane = threadIdx.x & 63;
@@ -770,35 +770,51 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       const int jj = j0 + j < cnt ? j0 + j : cnt - 1;
-      const float* op = a.o_part + (int64_t(i0 + jj) * rows + row) * D + V * lane;
-      if constexpr (V == 2) {
-        const float2 y = *reinterpret_cast<const float2*>(op);
-        x[j][0] = y.x;
-        x[j][1] = y.y;
+      const int64_t e0 = (int64_t(i0 + jj) * rows + row) * D + V * lane;
+      if constexpr (H) {  // fp16 rows; their scale is folded into the weight
+        const uint16_t* op = a.o_part16 + e0;
+        if constexpr (V == 2) {
+          const uint32_t y = *reinterpret_cast<const uint32_t*>(op);
+          x[j][0] = F16::to_f32(uint16_t(y));
+          x[j][1] = F16::to_f32(uint16_t(y >> 16));
+        } else {
+          x[j][0] = F16::to_f32(*op);
+        }
       } else {
-        x[j][0] = *op;
+        const float* op = a.o_part + e0;
+        if constexpr (V == 2) {
+          const float2 y = *reinterpret_cast<const float2*>(op);
+          x[j][0] = y.x;
+          x[j][1] = y.y;
+        } else {
+          x[j][0] = *op;
+        }
       }
     }
   };
+  // the scale of split i's row (lane i of a batch), 1 for fp32 rows
+  auto scale_of = [&](int i) { return H ? a.x_part[int64_t(i) * rows + row] : 1.f; };
   float acc[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) acc[e] = 0.f;
-  auto add = [&](float wi, int j0, int cnt) {
+  auto add = [&](float wi, float xi, int j0, int cnt) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       if (j0 + j >= cnt) break;
       const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wi), j0 + j));
       if (wj == 0.f) continue;  // an unused slot: never multiplied
+      const float sj = H ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xi), j0 + j)) : 1.f;
 #pragma unroll
-      for (int e = 0; e < V; ++e) acc[e] += wj * x[j][e];
+      for (int e = 0; e < V; ++e) acc[e] += wj * (H ? x[j][e] * sj : x[j][e]);
     }
   };
 
   const int cnt0 = s < 64 ? s : 64;
-  float mi = -INFINITY, li = 0.f;
+  float mi = -INFINITY, li = 0.f, xi = 1.f;
   if (lane < cnt0) {
     li = a.l_part[int64_t(lane) * rows + row];
     mi = a.m_part[int64_t(lane) * rows + row];
+    xi = scale_of(lane);
   }
   if (cnt0 > 0) load(0, 0, cnt0);
   float M = li > 0.f ? mi : -INFINITY;
@@ -813,23 +829,24 @@ __global__ __launch_bounds__(256) void merge_lse_kernel(MergeArgs a) {
     {
       const float wi = li > 0.f ? li * fexp2((mi - M) * kLog2e) : 0.f;
       wsum += wi;
-      add(wi, 0, cnt0);
+      add(wi, xi, 0, cnt0);
       for (int j0 = kMergeBatch; j0 < cnt0; j0 += kMergeBatch) {
         load(0, j0, cnt0);
-        add(wi, j0, cnt0);
+        add(wi, xi, j0, cnt0);
       }
     }
     for (int i0 = 64; i0 < s; i0 += 64) {  // more than 64 splits
       const int cnt = s - i0 < 64 ? s - i0 : 64;
-      float wi = 0.f;
+      float wi = 0.f, x2 = 1.f;
       if (lane < cnt) {
         const float l2 = a.l_part[int64_t(i0 + lane) * rows + row];
         if (l2 > 0.f) wi = l2 * fexp2((a.m_part[int64_t(i0 + lane) * rows + row] - M) * kLog2e);
+        x2 = scale_of(i0 + lane);
       }
       wsum += wi;
       for (int j0 = 0; j0 < cnt; j0 += kMergeBatch) {
         load(i0, j0, cnt);
-        add(wi, j0, cnt);
+        add(wi, x2, j0, cnt);
       }
     }
 #pragma unroll
@@ -1104,7 +1121,11 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const dim3 grid((a.rows + 3) / 4);
   if (a.rows == 0) return hipSuccess;
-#define RATTN_MERGE(DD, TT) hipLaunchKernelGGL((merge_lse_kernel<DD, TT>), grid, dim3(256), 0, st, a)
+#define RATTN_MERGE(DD, TT)                                                                    \
+  do {                                                                                         \
+    if (a.o_part16) hipLaunchKernelGGL((merge_lse_kernel<DD, TT, true>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((merge_lse_kernel<DD, TT, false>), grid, dim3(256), 0, st, a);     \
+  } while (0)
   if (a.D == 64) {
     if (a.o_dtype == 0) RATTN_MERGE(64, float);
     else if (a.o_dtype == 1) RATTN_MERGE(64, __bf16);

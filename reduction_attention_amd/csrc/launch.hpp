@@ -74,6 +74,10 @@ struct MergeArgs {
   void* o;
   int o_dtype;
   float* lse;
+  // fp16 partial rows scaled by x_part (row i of split j is
+  // o_part16[j, i, :] * x_part[j, i]) in place of o_part, when not null
+  const uint16_t* o_part16 = nullptr;
+  const float* x_part = nullptr;
 };
 
 struct PrefillArgs {
@@ -91,14 +95,16 @@ struct PrefillArgs {
   int dtype;
   // Split of the key dimension (Split operator): s chunks of `chunk` keys
   // per request.  s = 1 writes o / lse; s > 1 writes, for every split i,
-  // the normalised partial output o_part[i, row, :] and its (m, l) (m in
-  // natural-log units; m = -inf, l = 0 for a split without valid keys),
-  // row = (qo_indptr[b] + query) * Hq + head, rows rows in all.
+  // the normalised partial output as fp16 o_part[i, row, :] times the
+  // power of two x_part[i, row], and its (m, l) (m in natural-log units;
+  // m = -inf, l = 0 for a split without valid keys), row = (qo_indptr[b] +
+  // query) * Hq + head, rows rows in all.
   int s, chunk;
-  float* o_part;
+  uint16_t* o_part;
   float* m_part;
   float* l_part;
   int64_t rows;
+  float* x_part;
 };
 
 struct BsrArgs {

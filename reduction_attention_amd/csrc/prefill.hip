@@ -250,16 +250,15 @@ void prefill_kernel(PrefillArgs a) {
       float* lse = (row_ok && a.lse) ? a.lse + row : nullptr;
       row_store_staged<T, D>(st[rb], obase, int64_t(a.Hq) * D, n_q - q0, lse, stage, lane);
     } else {
-      // fp32 partial rows through LDS: 16 KB per wave at D = 128, waves 0-1
-      // in the K stages and 2-3 in the V stages
-      static_assert(NT == 256 && 2 * 32 * 4 * D <= 2 * TE * 2, "two waves' rows fit one stage pair");
+      // fp16 partial rows (scaled per row) through LDS, as above
       __attribute__((address_space(3))) char* stage =
-          (__attribute__((address_space(3))) char*)(w < 2 ? lds_k : lds_v) + (w & 1) * 32 * 4 * D;
+          (__attribute__((address_space(3))) char*)(w < 2 ? lds_k : lds_v) + (w & 1) * 32 * (2 * D + 16);
       const int q0 = q0w + 32 * rb;
       const int64_t prow = int64_t(si) * a.rows + row;
-      float* obase = a.o_part + (int64_t(si) * a.rows + (q_begin + q0) * a.Hq + hq) * D;
+      uint16_t* obase = a.o_part + (int64_t(si) * a.rows + (q_begin + q0) * a.Hq + hq) * D;
       row_store_partial_staged<D>(st[rb], obase, int64_t(a.Hq) * D, n_q - q0, row_ok ? a.m_part + prow : nullptr,
-                                  row_ok ? a.l_part + prow : nullptr, stage, lane);
+                                  row_ok ? a.l_part + prow : nullptr, row_ok ? a.x_part + prow : nullptr,
+                                  stage, lane);
     }
   }
 }
@@ -563,7 +562,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (e != hipSuccess || a.s == 1) return e;
   // split partials -> o / lse by log-sum-exp weights (the standalone merge,
   // as attn_merge_lse)
-  MergeArgs m{a.o_part, a.m_part, a.l_part, a.s, int(a.rows), a.D, a.o, a.dtype, a.lse};
+  MergeArgs m{nullptr, a.m_part, a.l_part, a.s, int(a.rows), a.D, a.o, a.dtype, a.lse, a.o_part, a.x_part};
   return launch_merge(m, st);
 }
 

@@ -232,7 +232,7 @@ def test_prefill_splitkv_validation(lib, kw, status):
 
 def test_prefill_split_rule_and_workspace(lib):
     for tq, Hq, D, s in [(128, 8, 128, 4), (4096, 32, 64, 1), (1, 1, 128, 256)]:
-        raw = s * tq * Hq * (D + 2) * 4
+        raw = s * tq * Hq * (2 * D + 12)  # fp16 rows, fp32 m, l and row scales
         assert lib.attn_prefill_workspace_bytes(tq, Hq, D, s) == (raw + 255) // 256 * 256
     assert lib.attn_prefill_workspace_bytes(16, 8, 128, 0) == 0
     # 4 requests x 128 new tokens x 32 heads = 128 query-tile workgroups < 512
